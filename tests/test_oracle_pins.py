@@ -1,0 +1,405 @@
+"""Pins of the fp64 oracle against what the pages and the mathematics fix.
+
+None of these checks re-runs the oracle's own formula: each compares it with
+an independent result -- a closed form from the literature (sorted sparsemax,
+exact sort-based 1.5-entmax), brute-force support enumeration with a library
+root finder, the strict bound of Proposition 1 (AdaSplash-2 pages, page 3
+section 2.1), hand-derived fixtures under tests/golden/, the softmax limit,
+central finite differences and exact invariants of the gradient.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+from scipy.optimize import brentq
+from scipy.special import softmax
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ------------------------------------------------------------------------------------------------
+# independent closed forms (written from the papers that define them, not from the oracle)
+# ------------------------------------------------------------------------------------------------
+
+def sparsemax_closed_form(z):
+    """Sparsemax (alpha = 2) by sorting: Martins & Astudillo (2016), Algorithm 1."""
+    z = np.asarray(z, dtype=np.float64)
+    zs = np.sort(z)[::-1]
+    cs = np.cumsum(zs)
+    k = np.arange(1, z.size + 1)
+    ok = 1.0 + k * zs > cs
+    kz = k[ok][-1]
+    tau = (cs[kz - 1] - 1.0) / kz
+    return np.maximum(z - tau, 0.0), tau
+
+
+def entmax15_closed_form(z):
+    """Exact 1.5-entmax by sorting: Peters, Niculae & Martins (2019), sort-based algorithm.
+
+    On x = z/2 and a candidate support of the k largest entries, the threshold
+    solves k tau^2 - 2 tau S1 + S2 - 1 = 0 (smaller root); the support is the k
+    whose root lies between the k-th and (k+1)-th largest x.
+    """
+    x = np.asarray(z, dtype=np.float64) / 2.0
+    xs = np.sort(x)[::-1]
+    n = x.size
+    for k in range(1, n + 1):
+        top = xs[:k]
+        mean = top.mean()
+        ss = ((top - mean) ** 2).sum()
+        disc = (1.0 - ss) / k
+        if disc < 0:
+            continue
+        tau = mean - math.sqrt(disc)
+        nxt = xs[k] if k < n else -np.inf
+        if xs[k - 1] > tau >= nxt:
+            return np.maximum(x - tau, 0.0) ** 2, tau
+    raise AssertionError("no consistent support")
+
+
+def brute_force_tau(x, alpha):
+    """tau* by enumerating every support S and solving sum_S (x - tau)^kappa = 1 with brentq."""
+    kappa = 1.0 / (alpha - 1.0)
+    n = x.size
+    found = []
+    for r in range(1, n + 1):
+        for S in itertools.combinations(range(n), r):
+            xs = x[list(S)]
+            lo_s, hi_s = xs.max() - 1.0, xs.min()
+            if lo_s >= hi_s:          # tau* >= x_max - 1 would cut min_S x off
+                continue
+            lo_s -= 1e-9              # keep phi(lo) > 0 despite rounding of (x_max - lo)
+            phi = lambda t: np.sum((xs - t) ** kappa) - 1.0
+            if phi(hi_s) >= 0:        # the root would not lie below min_S x
+                continue
+            t = brentq(phi, lo_s, hi_s, xtol=1e-15, rtol=1e-15, maxiter=500)
+            rest = np.delete(x, list(S))
+            if rest.size == 0 or rest.max() <= t:
+                found.append(t)
+    assert len(found) == 1, found
+    return found[0]
+
+
+# ------------------------------------------------------------------------------------------------
+# tau*, p
+# ------------------------------------------------------------------------------------------------
+
+def test_golden_entmax_values():
+    with open(os.path.join(GOLDEN, "entmax_small.json")) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        p, tau = oracle.entmax(np.array(c["z"]), c["alpha"])
+        assert abs(tau - c["tau"]) < 1e-11, c
+        np.testing.assert_allclose(p, c["p"], atol=1e-11)
+
+
+@pytest.mark.parametrize("n", [1, 2, 7, 256, 4096])
+def test_sparsemax_closed_form(n):
+    rng = np.random.default_rng(n)
+    for scale in (0.1, 1.0, 5.0):
+        for _ in range(5):
+            z = rng.standard_normal(n) * scale
+            p_ref, t_ref = sparsemax_closed_form(z)
+            p, t = oracle.entmax(z, 2.0)
+            assert abs(t - t_ref) < 1e-11
+            np.testing.assert_array_equal(p > 0, p_ref > 0)
+            np.testing.assert_allclose(p, p_ref, atol=1e-11)
+
+
+@pytest.mark.parametrize("n", [1, 2, 7, 256, 4096])
+def test_entmax15_closed_form(n):
+    rng = np.random.default_rng(100 + n)
+    for scale in (0.1, 1.0, 5.0):
+        for _ in range(5):
+            z = rng.standard_normal(n) * scale
+            p_ref, t_ref = entmax15_closed_form(z)
+            p, t = oracle.entmax(z, 1.5)
+            assert abs(t - t_ref) < 1e-11
+            np.testing.assert_array_equal(p > 0, p_ref > 0)
+            np.testing.assert_allclose(p, p_ref, atol=1e-11)
+
+
+@pytest.mark.parametrize("alpha", [1.25, 1.5, 2.0, 3.0])
+def test_brute_force_supports(alpha):
+    rng = np.random.default_rng(int(alpha * 100))
+    for n in range(1, 9):
+        for _ in range(6):
+            x = rng.standard_normal(n) * rng.choice([0.2, 1.0, 3.0])
+            t_ref = brute_force_tau(x, alpha)
+            t = oracle.entmax_tau(x, alpha)
+            assert abs(t - t_ref) < 1e-10, (alpha, x)
+
+
+@pytest.mark.parametrize("alpha", [1.25, 1.5, 2.0, 3.0])
+def test_distribution_properties(alpha):
+    """Rows sum to one with exact zeros; shift and permutation behave as the definition says."""
+    rng = np.random.default_rng(7)
+    for n in (1, 5, 300):
+        z = rng.standard_normal(n) * 2.0
+        p, t = oracle.entmax(z, alpha)
+        assert abs(p.sum() - 1.0) < 1e-9
+        x = (alpha - 1.0) * z
+        assert np.all(p[x <= t] == 0.0) and np.all(p[x > t] > 0.0)
+        c = 0.7
+        p2, t2 = oracle.entmax(z + c, alpha)
+        assert abs(t2 - (t + (alpha - 1.0) * c)) < 1e-9
+        np.testing.assert_allclose(p2, p, atol=1e-9)
+        perm = rng.permutation(n)
+        p3, t3 = oracle.entmax(z[perm], alpha)
+        assert abs(t3 - t) < 1e-11
+        np.testing.assert_allclose(p3, p[perm], atol=1e-11)
+        # tau* lies in the bracket [x_max - 1, x_max - n^(1 - alpha)]
+        assert x.max() - 1.0 - 1e-12 <= t <= x.max() - n ** (1.0 - alpha) + 1e-12
+
+
+def test_softmax_limit():
+    """As alpha -> 1, alpha-entmax approaches softmax at first order in alpha - 1."""
+    rng = np.random.default_rng(3)
+    errs = []
+    for am1 in (1e-1, 1e-2, 1e-3):
+        e = 0.0
+        for _ in range(8):
+            z = rng.standard_normal(256)
+            p, _ = oracle.entmax(z, 1.0 + am1)
+            e = max(e, np.abs(p - softmax(z)).max())
+        errs.append(e)
+    assert errs[0] > errs[1] > errs[2]
+    assert errs[1] < 0.25 * errs[0] and errs[2] < 0.25 * errs[1]
+    assert errs[2] < 5e-3
+
+
+# ------------------------------------------------------------------------------------------------
+# histogram and Proposition 1
+# ------------------------------------------------------------------------------------------------
+
+def test_golden_histograms():
+    with open(os.path.join(GOLDEN, "histogram_anchored.json")) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        counts, T = oracle.histogram(np.array(c["x"]), c["B"])
+        assert T == c["T"], c
+        expect = np.zeros(c["B"], dtype=np.int32)
+        for k, v in c["nonzero"].items():
+            expect[int(k)] = v
+        np.testing.assert_array_equal(counts, expect)
+        if "tau_h" in c:
+            th = oracle.tau_from_hist(counts, T, c["B"], c["alpha"])
+            assert abs(th - c["tau_h"]) < 1e-11
+            ts = oracle.entmax_tau(np.array(c["x"]), c["alpha"])
+            assert abs(ts - c["tau_star"]) < 1e-11
+
+
+@pytest.mark.parametrize("alpha", [1.25, 1.5, 2.0, 3.0])
+@pytest.mark.parametrize("B", [8, 16])
+def test_proposition1_strict(alpha, B):
+    """tau* - h < tau_h <= tau*, h = 1/B, on random rows of many sizes and spreads."""
+    rng = np.random.default_rng(int(alpha * 1000) + B)
+    h = 1.0 / B
+    for n in (1, 2, 7, 256, 4096):
+        for spread in (0.3, 1.0, 3.0, 10.0):
+            for _ in range(6 if n < 4096 else 2):
+                x = rng.standard_normal(n) * spread * (alpha - 1.0) + rng.uniform(-5, 5)
+                counts, T = oracle.histogram(x, B)
+                assert counts[B - 1] >= 1
+                th = oracle.tau_from_hist(counts, T, B, alpha)
+                ts = oracle.entmax_tau(x, alpha)
+                assert th <= ts + 1e-11
+                assert ts - th < h
+
+
+@pytest.mark.parametrize("alpha", [1.5, 2.0])
+def test_proposition1_is_strict_for_a_dominant_score(alpha):
+    """One dominant score half a bin above a grid line: the gap is h/2, not h.
+
+    A window anchored at x_max itself (bins relative to the row maximum) would
+    put x_max on the top bin's lower edge plus h and give tau* - tau_h = h
+    exactly; the anchored grid must not.
+    """
+    B = 16
+    h = 1.0 / B
+    for base in (-3, 0, 2, 7):
+        xmax = (base * B + 0.5) / B
+        x = np.array([xmax, xmax - 5.0, xmax - 9.0])
+        counts, T = oracle.histogram(x, B)
+        th = oracle.tau_from_hist(counts, T, B, alpha)
+        ts = oracle.entmax_tau(x, alpha)
+        assert abs(ts - (xmax - 1.0)) < 1e-11
+        assert abs((ts - th) - 0.5 * h) < 1e-10
+
+
+def test_histogram_shift_by_grid_steps():
+    """Shifting a row by m grid steps shifts T by m and leaves the counts unchanged."""
+    rng = np.random.default_rng(11)
+    for B in (8, 16):
+        x = np.round(rng.standard_normal(500) * 64) / 64.0
+        c0, T0 = oracle.histogram(x, B)
+        for m in (-7, 3, 40):
+            c1, T1 = oracle.histogram(x + m / B, B)
+            assert T1 == T0 + m
+            np.testing.assert_array_equal(c1, c0)
+
+
+def test_support_within_histogram_window():
+    """The support at tau_h contains the true support (page 5 section 2A)."""
+    rng = np.random.default_rng(5)
+    for alpha in (1.5, 2.0):
+        for _ in range(20):
+            x = rng.standard_normal(1000) * 2.0 * (alpha - 1.0)
+            counts, T = oracle.histogram(x, 16)
+            th = oracle.tau_from_hist(counts, T, 16, alpha)
+            ts = oracle.entmax_tau(x, alpha)
+            assert np.all((x > ts) <= (x > th))
+
+
+# ------------------------------------------------------------------------------------------------
+# attention forward
+# ------------------------------------------------------------------------------------------------
+
+def _rand_problem(rng, n, d, scale=1.0):
+    q = rng.standard_normal((n, d)) * scale
+    k = rng.standard_normal((n, d)) * scale
+    v = rng.standard_normal((n, d))
+    return q, k, v
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_attention_forward_closed_forms(causal):
+    rng = np.random.default_rng(21)
+    n, d = 96, 16
+    q, k, v = _rand_problem(rng, n, d, 1.5)
+    scale = 1.0 / math.sqrt(d)
+    for alpha, ref in ((2.0, sparsemax_closed_form), (1.5, entmax15_closed_form)):
+        f = oracle.attn_fwd_head(q, k, v, alpha, causal, 16, 32, scale)
+        for i in range(n):
+            nv = i + 1 if causal else n
+            s = scale * (q[i] @ k[:nv].T)
+            p, t = ref(s)
+            assert abs(f["tau"][i] - t) < 1e-10
+            np.testing.assert_allclose(f["o"][i], p @ v[:nv], atol=1e-10)
+            assert abs(f["psum"][i] - 1.0) < 1e-9
+            bits = np.zeros(f["rowbits"].shape[1], dtype=np.uint32)
+            for j in np.nonzero(p > 0)[0]:
+                J = j // 32
+                bits[J // 32] |= np.uint32(1) << np.uint32(J % 32)
+            np.testing.assert_array_equal(f["rowbits"][i], bits)
+
+
+def test_causal_first_row_and_mask_shape():
+    rng = np.random.default_rng(2)
+    n, d = 128, 8
+    q, k, v = _rand_problem(rng, n, d)
+    scale = 1.0 / math.sqrt(d)
+    for alpha in (1.5, 2.0, 3.0):
+        f = oracle.attn_fwd_head(q, k, v, alpha, True, 16, 32, scale)
+        np.testing.assert_allclose(f["o"][0], v[0], atol=1e-12)
+        x00 = (alpha - 1.0) * scale * (q[0] @ k[0])
+        assert abs(f["tau"][0] - (x00 - 1.0)) < 1e-11
+        m = oracle.block_mask(f["rowbits"], 32)
+        for I in range(m.shape[0]):
+            assert m[I, 0] != 0                       # every row has a non-zero weight
+            assert m[I, 0] >> np.uint32(I + 1) == 0   # nothing above the causal diagonal
+
+
+# ------------------------------------------------------------------------------------------------
+# attention backward
+# ------------------------------------------------------------------------------------------------
+
+def _loss(q, k, v, do, alpha, causal, scale):
+    f = oracle.attn_fwd_head(q, k, v, alpha, causal, 16, 32, scale, threads=1)
+    return float((f["o"] * do).sum()), f
+
+
+@pytest.mark.parametrize("alpha", [1.25, 1.5, 2.0, 3.0])
+@pytest.mark.parametrize("causal", [False, True])
+def test_gradients_finite_differences(alpha, causal):
+    """Analytic backward vs central differences of L = sum(O * dO) in fp64."""
+    n, d = 10, 4
+    scale = 1.0 / math.sqrt(d)
+    seed = 0
+    while True:
+        rng = np.random.default_rng(1000 * seed + int(alpha * 10) + causal)
+        q, k, v = _rand_problem(rng, n, d, 1.2)
+        do = rng.standard_normal((n, d))
+        L0, f = _loss(q, k, v, do, alpha, causal, scale)
+        if f["xgap"].min() > 1e-3 and seed < 50:
+            break
+        seed += 1
+    r = oracle.attn_bwd_rows_head(q, k, v, do, f["tau"], alpha, causal, scale, threads=1)
+    kk = oracle.attn_bwd_keys_group(q[None], k, v, do[None], f["tau"][None], r["delta"][None],
+                                    alpha, causal, scale, threads=1)
+    eps = 1e-5
+    for name, arr, grad in (("q", q, r["dq"]), ("k", k, kk["dk"]), ("v", v, kk["dv"])):
+        num = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            a1, a2 = arr.copy(), arr.copy()
+            a1[idx] += eps
+            a2[idx] -= eps
+            args1 = {"q": q, "k": k, "v": v}
+            args2 = {"q": q, "k": k, "v": v}
+            args1[name], args2[name] = a1, a2
+            L1, _ = _loss(args1["q"], args1["k"], args1["v"], do, alpha, causal, scale)
+            L2, _ = _loss(args2["q"], args2["k"], args2["v"], do, alpha, causal, scale)
+            num[idx] = (L1 - L2) / (2 * eps)
+        err = np.linalg.norm(num - grad) / max(np.linalg.norm(num), 1e-12)
+        assert err < 1e-5, (name, err)
+
+
+def test_gradient_invariants_gqa():
+    """sum_j dK_j = 0 (rows of dS sum to zero) and sum_j dV_j = sum_i dO_i over the group."""
+    rng = np.random.default_rng(9)
+    b, hq, hkv, n, d = 1, 4, 2, 64, 8
+    q = rng.standard_normal((b, hq, n, d)) * 1.5
+    k = rng.standard_normal((b, hkv, n, d)) * 1.5
+    v = rng.standard_normal((b, hkv, n, d))
+    do = rng.standard_normal((b, hq, n, d))
+    for alpha in (1.5, 2.0):
+        res = oracle.attn_full(q, k, v, do, alpha, True, 16, 32, 32, threads=4)
+        G = hq // hkv
+        for kh in range(hkv):
+            np.testing.assert_allclose(res["dk"][0, kh].sum(0), 0.0, atol=1e-9)
+            np.testing.assert_allclose(res["dv"][0, kh].sum(0),
+                                       do[0, kh * G:(kh + 1) * G].sum((0, 1)), atol=1e-9)
+
+
+def test_sparsemax_backward_projection_form():
+    """At alpha = 2 the Jacobian is a projection: dS = 1_S (dP - mean_S dP)."""
+    rng = np.random.default_rng(4)
+    n, d = 80, 8
+    q, k, v = _rand_problem(rng, n, d, 2.0)
+    do = rng.standard_normal((n, d))
+    scale = 1.0 / math.sqrt(d)
+    f = oracle.attn_fwd_head(q, k, v, 2.0, True, 16, 32, scale)
+    r = oracle.attn_bwd_rows_head(q, k, v, do, f["tau"], 2.0, True, scale)
+    for i in range(n):
+        s = scale * (q[i] @ k[:i + 1].T)
+        p, _ = sparsemax_closed_form(s)
+        S = p > 0
+        dp = do[i] @ v[:i + 1].T
+        ds = np.where(S, dp - dp[S].mean(), 0.0)
+        np.testing.assert_allclose(r["dq"][i], scale * ds @ k[:i + 1], atol=1e-10)
+
+
+def test_backward_softmax_limit():
+    """As alpha -> 1 the entmax backward approaches the softmax-attention backward."""
+    rng = np.random.default_rng(8)
+    n, d = 48, 8
+    q, k, v = _rand_problem(rng, n, d)
+    do = rng.standard_normal((n, d))
+    scale = 1.0 / math.sqrt(d)
+    S = scale * q @ k.T
+    P = softmax(S, axis=1)
+    dP = do @ v.T
+    dS = P * (dP - (P * dP).sum(1, keepdims=True))
+    dq_soft = scale * dS @ k
+    errs = []
+    for am1 in (1e-1, 1e-2, 1e-3):
+        alpha = 1.0 + am1
+        f = oracle.attn_fwd_head(q, k, v, alpha, False, 16, 32, scale)
+        r = oracle.attn_bwd_rows_head(q, k, v, do, f["tau"], alpha, False, scale)
+        errs.append(np.abs(r["dq"] - dq_soft).max())
+    assert errs[1] < 0.25 * errs[0] and errs[2] < 0.25 * errs[1]

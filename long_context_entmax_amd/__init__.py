@@ -1,0 +1,253 @@
+"""alpha-entmax attention (AdaSplash-2 method) on AMD MI355X -- Python binding.
+
+Thin ctypes layer over ``libentmax_attn.so`` (C ABI in ``include/entmax_attn.h``):
+it checks tensor placement, allocates outputs and workspace with PyTorch and passes
+raw device pointers and the current HIP stream. Every step of the computation runs
+in the library's HIP kernels; there is no fallback path -- if the library is not
+built, every call raises.
+
+    o, tau, mask, aux = fwd(q, k, v, alpha=1.5, causal=True, block=(64, 64), bins=16)
+    dq, dk, dv = bwd(q, k, v, do, tau, mask, aux, alpha=1.5, causal=True, block=(64, 64), bins=16)
+    o = entmax_attention(q, k, v, alpha=1.5)          # autograd-aware
+
+Shapes: q, do [b, hq, n, d]; k, v [b, hkv, n, d]; dtype float32 or bfloat16.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from collections import namedtuple
+from typing import Optional, Tuple
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libentmax_attn.so")
+
+ENTMAX_F32, ENTMAX_BF16 = 0, 1
+STATUS = {0: "ok", 1: "null pointer", 2: "invalid shape", 3: "invalid alpha", 4: "unsupported",
+          5: "misaligned pointer", 6: "workspace", 7: "HIP runtime error"}
+
+
+class EntmaxError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"entmax_attn: {STATUS.get(status, status)}: {detail}")
+        self.status = status
+
+
+class Desc(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("heads_q", ctypes.c_int32), ("heads_kv", ctypes.c_int32),
+        ("seqlen", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32),
+        ("alpha", ctypes.c_float), ("causal", ctypes.c_int32), ("block_q", ctypes.c_int32),
+        ("block_k", ctypes.c_int32), ("n_bins", ctypes.c_int32), ("scale", ctypes.c_float),
+        ("max_iters", ctypes.c_int32), ("tol", ctypes.c_float),
+    ]
+
+
+class KernelTime(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 32), ("total_ms", ctypes.c_double), ("launches", ctypes.c_int64)]
+
+
+_lib = None
+_vp = ctypes.c_void_p
+_sz = ctypes.c_size_t
+_DP = ctypes.POINTER(Desc)
+
+EXPORTS = [
+    "entmax_attn_fwd_workspace_bytes", "entmax_attn_bwd_workspace_bytes", "entmax_attn_aux_bytes",
+    "entmax_attn_mask_words", "entmax_attn_fwd", "entmax_attn_bwd", "entmax_status_string",
+    "entmax_last_error", "entmax_attn_profile", "entmax_attn_profile_read",
+]
+
+
+def lib() -> ctypes.CDLL:
+    """Load the HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m long_context_entmax_amd.build` (hipcc, gfx950)")
+        L = ctypes.CDLL(LIB_PATH)
+        for f in ("entmax_attn_fwd_workspace_bytes", "entmax_attn_bwd_workspace_bytes",
+                  "entmax_attn_aux_bytes", "entmax_attn_mask_words"):
+            getattr(L, f).restype = _sz
+            getattr(L, f).argtypes = [_DP]
+        L.entmax_attn_fwd.restype = ctypes.c_int
+        L.entmax_attn_fwd.argtypes = [_DP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+        L.entmax_attn_bwd.restype = ctypes.c_int
+        L.entmax_attn_bwd.argtypes = [_DP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+        L.entmax_status_string.restype = ctypes.c_char_p
+        L.entmax_status_string.argtypes = [ctypes.c_int]
+        L.entmax_last_error.restype = ctypes.c_char_p
+        L.entmax_last_error.argtypes = []
+        L.entmax_attn_profile.restype = ctypes.c_int
+        L.entmax_attn_profile.argtypes = [ctypes.c_int]
+        L.entmax_attn_profile_read.restype = ctypes.c_int
+        L.entmax_attn_profile_read.argtypes = [ctypes.POINTER(KernelTime), ctypes.c_int,
+                                               ctypes.POINTER(ctypes.c_int)]
+        _lib = L
+    return _lib
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise EntmaxError(status, lib().entmax_last_error().decode())
+
+
+def make_desc(batch: int, heads_q: int, heads_kv: int, seqlen: int, head_dim: int, dtype: int,
+              alpha: float, causal: bool, block: Tuple[int, int], bins: int,
+              scale: Optional[float] = None, max_iters: int = 0, tol: float = 0.0) -> Desc:
+    return Desc(batch, heads_q, heads_kv, seqlen, head_dim, dtype, float(alpha), int(bool(causal)),
+                int(block[0]), int(block[1]), int(bins), float(scale or 0.0), int(max_iters), float(tol))
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _desc_for(q, k, alpha, causal, block, bins, scale, max_iters, tol) -> Desc:
+    torch = _torch()
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q and k must be [batch, heads, seqlen, head_dim]")
+    if q.dtype == torch.bfloat16:
+        dt = ENTMAX_BF16
+    elif q.dtype == torch.float32:
+        dt = ENTMAX_F32
+    else:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    b, hq, n, d = q.shape
+    return make_desc(b, hq, k.shape[1], n, d, dt, alpha, causal, block, bins, scale, max_iters, tol)
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(dev) -> int:
+    torch = _torch()
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _require_gpu(*ts) -> None:
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("entmax_attn runs on the GPU only: tensors must be on a HIP device")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def mask_shape(n: int, block: Tuple[int, int]) -> Tuple[int, int]:
+    Tr, Tc = n // block[0], n // block[1]
+    return Tr, (Tc + 31) // 32
+
+
+FwdOut = namedtuple("FwdOut", "o tau mask aux hist tau_h")
+
+
+def fwd(q, k, v, alpha: float = 1.5, causal: bool = True, block=(64, 64), bins: int = 16,
+        scale: Optional[float] = None, max_iters: int = 0, tol: float = 0.0,
+        return_hist: bool = False, stats=None, workspace=None, out=None) -> FwdOut:
+    """alpha-entmax attention forward. Returns (o, tau, mask, aux, hist, tau_h); o is float32.
+
+    hist/tau_h are the histogram stage's counts [b,hq,n,B] and lower bound [b,hq,n]
+    (None unless return_hist). ``stats``: optional int64 CUDA tensor [32] (accumulated).
+    ``out``: optional FwdOut of preallocated tensors to write into.
+    """
+    torch = _torch()
+    _require_gpu(q, k, v)
+    desc = _desc_for(q, k, alpha, causal, block, bins, scale, max_iters, tol)
+    L = lib()
+    b, hq, n, d = q.shape
+    dev = q.device
+    Tr, W = mask_shape(n, block)
+    if out is None:
+        o = torch.empty(q.shape, dtype=torch.float32, device=dev)
+        tau = torch.empty((b, hq, n), dtype=torch.float32, device=dev)
+        mask = torch.empty((b, hq, Tr, W), dtype=torch.int32, device=dev)
+        aux = torch.empty((b, hq, n, d), dtype=torch.float32, device=dev)
+        hist = torch.empty((b, hq, n, bins), dtype=torch.int32, device=dev) if return_hist else None
+        tau_h = torch.empty((b, hq, n), dtype=torch.float32, device=dev) if return_hist else None
+    else:
+        o, tau, mask, aux, hist, tau_h = out
+    nbytes = L.entmax_attn_fwd_workspace_bytes(ctypes.byref(desc))
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+    _check(L.entmax_attn_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(tau),
+                             _ptr(mask), _ptr(aux), _ptr(hist), _ptr(tau_h), _ptr(stats),
+                             _ptr(workspace), workspace.numel(), _stream(dev)))
+    return FwdOut(o, tau, mask, aux, hist, tau_h)
+
+
+def bwd(q, k, v, do, tau, mask, aux, alpha: float = 1.5, causal: bool = True, block=(64, 64),
+        bins: int = 16, scale: Optional[float] = None, workspace=None, out=None):
+    """alpha-entmax attention backward: (dq, dk, dv) given the forward's tau, mask, aux."""
+    torch = _torch()
+    _require_gpu(q, k, v, do, tau, mask, aux)
+    desc = _desc_for(q, k, alpha, causal, block, bins, scale, 0, 0.0)
+    L = lib()
+    dev = q.device
+    if out is None:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    else:
+        dq, dk, dv = out
+    nbytes = L.entmax_attn_bwd_workspace_bytes(ctypes.byref(desc))
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+    _check(L.entmax_attn_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(tau),
+                             _ptr(mask), _ptr(aux), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+                             workspace.numel(), _stream(dev)))
+    return dq, dk, dv
+
+
+def workspace_bytes(desc: Desc) -> Tuple[int, int]:
+    L = lib()
+    return (L.entmax_attn_fwd_workspace_bytes(ctypes.byref(desc)),
+            L.entmax_attn_bwd_workspace_bytes(ctypes.byref(desc)))
+
+
+def profile(enable: bool) -> None:
+    """Record hipEvents around every kernel launch of the library (see profile_read)."""
+    _check(lib().entmax_attn_profile(int(bool(enable))))
+
+
+def profile_read() -> dict:
+    """Per-kernel {name: (total_ms, launches)} since the last read (waits for the events)."""
+    arr = (KernelTime * 64)()
+    cnt = ctypes.c_int(0)
+    _check(lib().entmax_attn_profile_read(arr, 64, ctypes.byref(cnt)))
+    return {arr[i].name.decode(): (arr[i].total_ms, int(arr[i].launches)) for i in range(min(cnt.value, 64))}
+
+
+def _make_function():
+    torch = _torch()
+
+    class EntmaxAttentionFn(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, q, k, v, alpha, causal, block, bins, scale):
+            r = fwd(q, k, v, alpha, causal, block, bins, scale)
+            ctx.save_for_backward(q, k, v, r.tau, r.mask, r.aux)
+            ctx.cfg = (alpha, causal, block, bins, scale)
+            return r.o.to(q.dtype)
+
+        @staticmethod
+        def backward(ctx, do):
+            q, k, v, tau, mask, aux = ctx.saved_tensors
+            alpha, causal, block, bins, scale = ctx.cfg
+            dq, dk, dv = bwd(q, k, v, do.contiguous(), tau, mask, aux, alpha, causal, block, bins, scale)
+            return dq, dk, dv, None, None, None, None, None
+
+    return EntmaxAttentionFn
+
+
+_fn = None
+
+
+def entmax_attention(q, k, v, alpha: float = 1.5, causal: bool = True, block=(64, 64), bins: int = 16,
+                     scale: Optional[float] = None):
+    """Differentiable alpha-entmax attention (forward and backward in the HIP library)."""
+    global _fn
+    if _fn is None:
+        _fn = _make_function()
+    return _fn.apply(q, k, v, alpha, causal, tuple(block), bins, scale)

@@ -1,0 +1,385 @@
+// C ABI of the alpha-entmax attention library: argument checks, workspace layout,
+// launch sequencing and kernel timing. See include/entmax_attn.h for the contract.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <map>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/entmax_attn.h"
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace entmax {
+
+static thread_local char t_err[512];
+
+static entmax_status fail(entmax_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(t_err, sizeof(t_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+static entmax_status hip_fail(hipError_t e, const char* what) {
+  return fail(ENTMAX_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// ------------------------------------------------------------------------------------------
+// kernel timing
+// ------------------------------------------------------------------------------------------
+namespace {
+struct Pending {
+  const char* name;
+  hipEvent_t a, b;
+};
+std::mutex g_mu;
+bool g_on = false;
+std::vector<Pending> g_pending;
+std::vector<hipEvent_t> g_pool;
+thread_local const char* t_name = nullptr;
+thread_local hipEvent_t t_start = nullptr;
+
+hipEvent_t take_event() {
+  std::lock_guard<std::mutex> lk(g_mu);
+  if (!g_pool.empty()) {
+    hipEvent_t e = g_pool.back();
+    g_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+}  // namespace
+
+void prof_begin(const char* name, hipStream_t s) {
+  t_start = nullptr;
+  if (!g_on) return;
+  hipEvent_t e = take_event();
+  if (!e) return;
+  if (hipEventRecord(e, s) != hipSuccess) return;
+  t_name = name;
+  t_start = e;
+}
+
+void prof_end(hipStream_t s) {
+  if (!g_on || !t_start) return;
+  hipEvent_t e = take_event();
+  if (!e) return;
+  if (hipEventRecord(e, s) != hipSuccess) return;
+  std::lock_guard<std::mutex> lk(g_mu);
+  g_pending.push_back({t_name, t_start, e});
+  t_start = nullptr;
+}
+
+// ------------------------------------------------------------------------------------------
+// argument checks and derived sizes
+// ------------------------------------------------------------------------------------------
+struct Derived {
+  int b, hq, hkv, n, D, G, dtype, causal, Br, Bc, B, max_iters;
+  float alpha, scale, tol, kappa;
+  int mode;               // 1: alpha = 2, 2: alpha = 1.5, 0: other
+  int Tr, Tc, W, WT, nkb, NW32;
+  size_t es;              // element size
+  // forward decomposition
+  int QW, GP, RH, RG;
+};
+
+static bool pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+
+static entmax_status derive(const entmax_attn_desc* d, Derived& o) {
+  if (!d) return fail(ENTMAX_ERR_NULL, "desc is NULL");
+  o.b = d->batch; o.hq = d->heads_q; o.hkv = d->heads_kv; o.n = d->seqlen; o.D = d->head_dim;
+  if (o.b < 0 || o.hq < 0 || o.hkv < 0 || o.n < 0 || o.D <= 0)
+    return fail(ENTMAX_ERR_SHAPE, "negative size (batch %d, heads %d/%d, seqlen %d, head_dim %d)",
+                o.b, o.hq, o.hkv, o.n, o.D);
+  if (o.hkv == 0 && o.hq != 0) return fail(ENTMAX_ERR_SHAPE, "heads_kv is 0 but heads_q is %d", o.hq);
+  if (o.hkv > 0 && o.hq % o.hkv != 0)
+    return fail(ENTMAX_ERR_SHAPE, "heads_q (%d) is not a multiple of heads_kv (%d)", o.hq, o.hkv);
+  if (!(d->alpha > 1.0f && d->alpha <= 16.0f) || !isfinite(d->alpha))
+    return fail(ENTMAX_ERR_ALPHA, "alpha must be finite and in (1, 16], got %g", (double)d->alpha);
+  if (d->dtype != ENTMAX_F32 && d->dtype != ENTMAX_BF16)
+    return fail(ENTMAX_ERR_UNSUPPORTED, "dtype %d is not F32 (0) or BF16 (1)", d->dtype);
+  if (o.D != 64 && o.D != 128) return fail(ENTMAX_ERR_UNSUPPORTED, "head_dim %d: only 64 and 128", o.D);
+  o.Br = d->block_q; o.Bc = d->block_k;
+  if (!(o.Br == 32 || o.Br == 64 || o.Br == 128) || !(o.Bc == 32 || o.Bc == 64 || o.Bc == 128))
+    return fail(ENTMAX_ERR_UNSUPPORTED, "blocks %dx%d: each must be 32, 64 or 128", o.Br, o.Bc);
+  if (o.n % o.Br != 0 || o.n % o.Bc != 0)
+    return fail(ENTMAX_ERR_SHAPE, "seqlen %d is not a multiple of the blocks %dx%d", o.n, o.Br, o.Bc);
+  if (o.n > (1 << 19)) return fail(ENTMAX_ERR_UNSUPPORTED, "seqlen %d > 524288", o.n);
+  o.B = d->n_bins;
+  if (!pow2(o.B) || o.B < 2 || o.B > 16)
+    return fail(ENTMAX_ERR_UNSUPPORTED, "n_bins %d: must be 2, 4, 8 or 16", o.B);
+  if (d->causal != 0 && d->causal != 1) return fail(ENTMAX_ERR_SHAPE, "causal must be 0 or 1");
+  o.causal = d->causal;
+  o.max_iters = d->max_iters == 0 ? (d->alpha > 2.0f ? 15 : 8) : d->max_iters;
+  if (o.max_iters < 1 || o.max_iters > 15)
+    return fail(ENTMAX_ERR_SHAPE, "max_iters %d: must be 0 (default) or 1..15", d->max_iters);
+  if (!(d->scale >= 0.0f) || !isfinite(d->scale)) return fail(ENTMAX_ERR_SHAPE, "scale must be >= 0 and finite");
+  if (!(d->tol >= 0.0f) || !isfinite(d->tol)) return fail(ENTMAX_ERR_SHAPE, "tol must be >= 0 and finite");
+  o.dtype = d->dtype;
+  o.alpha = d->alpha;
+  o.scale = d->scale == 0.0f ? (float)(1.0 / sqrt((double)o.D)) : d->scale;
+  o.tol = d->tol == 0.0f ? ldexpf(1.0f, -20) : d->tol;
+  o.kappa = (float)(1.0 / ((double)o.alpha - 1.0));
+  o.mode = (o.alpha == 2.0f) ? 1 : (o.alpha == 1.5f ? 2 : 0);
+  o.G = o.hkv > 0 ? o.hq / o.hkv : 1;
+  o.Tr = o.n / o.Br;
+  o.Tc = o.n / o.Bc;
+  o.W = (o.Tc + 31) / 32;
+  o.WT = (o.Tr + 31) / 32;
+  o.nkb = o.n / 32;
+  o.NW32 = (o.nkb + 31) / 32;
+  o.es = o.dtype == ENTMAX_BF16 ? 2 : 4;
+  o.QW = o.D == 64 ? 64 : 32;
+  o.GP = 1;
+  for (int gp : {4, 2}) {
+    if (o.G % gp == 0 && ((4 / gp) * o.QW) % o.Br == 0) {
+      o.GP = gp;
+      break;
+    }
+  }
+  o.RH = (4 / o.GP) * o.QW;
+  o.RG = (o.n + o.RH - 1) / o.RH;
+  return ENTMAX_OK;
+}
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+static size_t fwd_ws(const Derived& o) { return align256((size_t)o.b * o.hkv * o.D * o.n * o.es); }
+
+struct BwdLayout {
+  size_t delta, maskT, qt, dot, kt, total;
+};
+static BwdLayout bwd_ws(const Derived& o) {
+  BwdLayout L;
+  size_t off = 0;
+  L.delta = off; off += align256((size_t)o.b * o.hq * o.n * 4);
+  L.maskT = off; off += align256((size_t)o.b * o.hq * o.Tc * o.WT * 4);
+  L.qt = off; off += align256((size_t)o.b * o.hq * o.D * o.n * o.es);
+  L.dot = off; off += align256((size_t)o.b * o.hq * o.D * o.n * o.es);
+  L.kt = off; off += align256((size_t)o.b * o.hkv * o.D * o.n * o.es);
+  L.total = off;
+  return L;
+}
+
+static bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+static WgMap make_map(int U, int R) {
+  WgMap m;
+  m.U = U;
+  m.R = R;
+  m.xcd = (U > 0 && U % 8 == 0) ? 1 : 0;
+  return m;
+}
+
+}  // namespace entmax
+
+using namespace entmax;
+
+extern "C" {
+
+size_t entmax_attn_fwd_workspace_bytes(const entmax_attn_desc* desc) {
+  Derived o;
+  if (derive(desc, o) != ENTMAX_OK) return 0;
+  return fwd_ws(o);
+}
+
+size_t entmax_attn_bwd_workspace_bytes(const entmax_attn_desc* desc) {
+  Derived o;
+  if (derive(desc, o) != ENTMAX_OK) return 0;
+  return bwd_ws(o).total;
+}
+
+size_t entmax_attn_aux_bytes(const entmax_attn_desc* desc) {
+  Derived o;
+  if (derive(desc, o) != ENTMAX_OK) return 0;
+  return (size_t)o.b * o.hq * o.n * o.D * sizeof(float);
+}
+
+size_t entmax_attn_mask_words(const entmax_attn_desc* desc) {
+  Derived o;
+  if (derive(desc, o) != ENTMAX_OK) return 0;
+  return (size_t)o.b * o.hq * o.Tr * o.W;
+}
+
+entmax_status entmax_attn_fwd(const entmax_attn_desc* desc, const void* q, const void* k, const void* v,
+                              void* o_, float* tau, uint32_t* block_mask, void* aux, int32_t* hist_counts,
+                              float* tau_h, uint64_t* stats, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  Derived o;
+  entmax_status st = derive(desc, o);
+  if (st != ENTMAX_OK) return st;
+  const size_t elems = (size_t)o.b * o.hq * o.n;
+  if (elems == 0) return ENTMAX_OK;
+  if (!q || !k || !v || !o_ || !tau || !block_mask || !aux)
+    return fail(ENTMAX_ERR_NULL, "q, k, v, o, tau, block_mask and aux are required");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o_, 16) || !aligned(aux, 16) ||
+      !aligned(tau, 4) || !aligned(block_mask, 4) || (hist_counts && !aligned(hist_counts, 4)) ||
+      (tau_h && !aligned(tau_h, 4)) || (stats && !aligned(stats, 8)))
+    return fail(ENTMAX_ERR_ALIGN, "q, k, v, o, aux need 16-byte alignment; tau, mask, counts 4-byte");
+  const size_t need = fwd_ws(o);
+  if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
+    return fail(ENTMAX_ERR_WORKSPACE, "forward workspace: need %zu bytes, 256-byte aligned (got %zu)", need,
+                workspace_bytes);
+  hipStream_t s = (hipStream_t)stream;
+
+  PrepParams tp{};
+  tp.src[0] = v;
+  tp.dst[0] = workspace;
+  tp.heads[0] = o.b * o.hkv;
+  tp.ntrans = 1;
+  tp.n = o.n;
+  tp.D = o.D;
+  hipError_t e = launch_transpose(tp, o.dtype, s);
+  if (e != hipSuccess) return hip_fail(e, "transpose of V");
+
+  FwdParams p{};
+  p.q = q; p.k = k; p.vt = workspace; p.o = (float*)o_; p.tau = tau; p.mask = block_mask; p.aux = (float*)aux;
+  p.hist = hist_counts; p.tau_h = tau_h; p.stats = (unsigned long long*)stats;
+  p.b = o.b; p.hq = o.hq; p.hkv = o.hkv; p.n = o.n; p.G = o.G;
+  p.causal = o.causal; p.Br = o.Br; p.Bc = o.Bc; p.B = o.B; p.max_iters = o.max_iters;
+  p.cx = (float)(((double)o.alpha - 1.0) * (double)o.scale);
+  p.alpha = o.alpha; p.kappa = o.kappa; p.tol = o.tol;
+  p.GP = o.GP; p.RH = o.RH; p.RG = o.RG;
+  p.nkb = o.nkb; p.NW32 = o.NW32; p.Tr = o.Tr; p.Tc = o.Tc; p.W = o.W;
+  p.map = make_map(o.b * o.hkv, (o.G / o.GP) * o.RG);
+  prof_begin("entmax_fwd", s);
+  e = launch_fwd(p, o.dtype, o.D, o.mode, s);
+  prof_end(s);
+  if (e != hipSuccess) return hip_fail(e, "forward kernel");
+  return ENTMAX_OK;
+}
+
+entmax_status entmax_attn_bwd(const entmax_attn_desc* desc, const void* q, const void* k, const void* v,
+                              const void* dout, const float* tau, const uint32_t* block_mask, const void* aux,
+                              void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  Derived o;
+  entmax_status st = derive(desc, o);
+  if (st != ENTMAX_OK) return st;
+  if ((size_t)o.b * o.hq * o.n == 0) return ENTMAX_OK;
+  if (!q || !k || !v || !dout || !tau || !block_mask || !aux || !dq || !dk || !dv)
+    return fail(ENTMAX_ERR_NULL, "q, k, v, dout, tau, block_mask, aux, dq, dk and dv are required");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(dout, 16) || !aligned(aux, 16) ||
+      !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(tau, 16) ||
+      !aligned(block_mask, 4))
+    return fail(ENTMAX_ERR_ALIGN, "tensors need 16-byte alignment (block_mask 4-byte)");
+  const BwdLayout L = bwd_ws(o);
+  if (!workspace || workspace_bytes < L.total || !aligned(workspace, 256))
+    return fail(ENTMAX_ERR_WORKSPACE, "backward workspace: need %zu bytes, 256-byte aligned (got %zu)", L.total,
+                workspace_bytes);
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+
+  PrepParams pp{};
+  pp.src[0] = q;    pp.dst[0] = ws + L.qt;  pp.heads[0] = o.b * o.hq;
+  pp.src[1] = dout; pp.dst[1] = ws + L.dot; pp.heads[1] = o.b * o.hq;
+  pp.src[2] = k;    pp.dst[2] = ws + L.kt;  pp.heads[2] = o.b * o.hkv;
+  pp.ntrans = 3;
+  pp.n = o.n;
+  pp.D = o.D;
+  pp.dout = dout;
+  pp.aux = (const float*)aux;
+  pp.delta = (float*)(ws + L.delta);
+  pp.rows = o.b * o.hq * o.n;
+  pp.mask = block_mask;
+  pp.maskT = (uint32_t*)(ws + L.maskT);
+  pp.planes = o.b * o.hq;
+  pp.Tr = o.Tr; pp.Tc = o.Tc; pp.W = o.W; pp.WT = o.WT;
+  hipError_t e = launch_bwd_prep(pp, o.dtype, s);
+  if (e != hipSuccess) return hip_fail(e, "backward preparation");
+
+  BwdParams p{};
+  p.q = q; p.k = k; p.v = v; p.dout = dout;
+  p.qt = ws + L.qt; p.dot = ws + L.dot; p.kt = ws + L.kt;
+  p.tau = tau; p.delta = (const float*)(ws + L.delta);
+  p.mask = block_mask; p.maskT = (const uint32_t*)(ws + L.maskT);
+  p.dq = dq; p.dk = dk; p.dv = dv;
+  p.b = o.b; p.hq = o.hq; p.hkv = o.hkv; p.n = o.n; p.G = o.G;
+  p.causal = o.causal; p.Br = o.Br; p.Bc = o.Bc;
+  p.cx = (float)(((double)o.alpha - 1.0) * (double)o.scale);
+  p.scale = o.scale; p.kappa = o.kappa;
+  p.Tr = o.Tr; p.Tc = o.Tc; p.W = o.W; p.WT = o.WT;
+
+  p.map = make_map(o.b * o.hkv, o.Tc);
+  prof_begin("entmax_bwd_dkv", s);
+  e = launch_bwd_dkv(p, o.dtype, o.D, o.mode, s);
+  prof_end(s);
+  if (e != hipSuccess) return hip_fail(e, "dK/dV kernel");
+
+  p.map = make_map(o.b * o.hkv, o.G * o.Tr);
+  prof_begin("entmax_bwd_dq", s);
+  e = launch_bwd_dq(p, o.dtype, o.D, o.mode, s);
+  prof_end(s);
+  if (e != hipSuccess) return hip_fail(e, "dQ kernel");
+  return ENTMAX_OK;
+}
+
+const char* entmax_status_string(entmax_status s) {
+  switch (s) {
+    case ENTMAX_OK: return "ok";
+    case ENTMAX_ERR_NULL: return "null pointer";
+    case ENTMAX_ERR_SHAPE: return "invalid shape";
+    case ENTMAX_ERR_ALPHA: return "invalid alpha";
+    case ENTMAX_ERR_UNSUPPORTED: return "unsupported configuration";
+    case ENTMAX_ERR_ALIGN: return "misaligned pointer";
+    case ENTMAX_ERR_WORKSPACE: return "workspace missing or too small";
+    case ENTMAX_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* entmax_last_error(void) { return t_err; }
+
+entmax_status entmax_attn_profile(int enable) {
+  g_on = enable != 0;
+  return ENTMAX_OK;
+}
+
+entmax_status entmax_attn_profile_read(entmax_kernel_time* out, int max_entries, int* n_entries) {
+  std::vector<Pending> pend;
+  {
+    std::lock_guard<std::mutex> lk(g_mu);
+    pend.swap(g_pending);
+  }
+  std::map<std::string, std::pair<double, int64_t>> acc;
+  std::vector<std::string> order;
+  entmax_status st = ENTMAX_OK;
+  for (auto& r : pend) {
+    float ms = 0.f;
+    hipError_t e = hipEventSynchronize(r.b);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.a, r.b);
+    if (e != hipSuccess) st = hip_fail(e, "profile event");
+    if (!acc.count(r.name)) order.push_back(r.name);
+    acc[r.name].first += ms;
+    acc[r.name].second += 1;
+  }
+  {
+    std::lock_guard<std::mutex> lk(g_mu);
+    for (auto& r : pend) {
+      g_pool.push_back(r.a);
+      g_pool.push_back(r.b);
+    }
+  }
+  int cnt = 0;
+  for (auto& name : order) {
+    if (out && cnt < max_entries) {
+      memset(out[cnt].name, 0, sizeof(out[cnt].name));
+      strncpy(out[cnt].name, name.c_str(), sizeof(out[cnt].name) - 1);
+      out[cnt].total_ms = acc[name].first;
+      out[cnt].launches = acc[name].second;
+    }
+    ++cnt;
+  }
+  if (n_entries) *n_entries = cnt;
+  return st;
+}
+
+}  // extern "C"

@@ -1,0 +1,325 @@
+// Backward of alpha-entmax attention: dK/dV per key block and dQ per query tile, each
+// walking only the set bits of the block mask (AdaSplash-2 pages, page 1 section 2.3 and
+// page 3 section 2.3: the mask lets the backward skip all-zero blocks; local accumulators
+// instead of atomics).
+//
+// Gradient (the exact alpha-entmax Jacobian; the pages do not spell it out): with
+// x = (alpha-1) s, d = [x - tau]_+, p = d^kappa, g = d^(kappa-1), dP_ij = dO_i . v_j and
+// delta_i = dO_i . o~_i,
+//   dS_ij = g_ij (dP_ij - delta_i),  dq_i = scale sum_j dS_ij k_j,
+//   dk_j  = scale sum_i dS_ij q_i,   dv_j = sum_i p_ij dO_i.
+//
+// k_bwd_dkv: one work group per (batch, KV head, key block J). Wave w owns the 32-key
+// sub-block w % KC of J and every (NS)-th item of the list (query head of the GQA group,
+// query tile with bit J set, 32-row chunk); K and V of the sub-block stay in registers,
+// dK and dV accumulate in registers and the waves that share a sub-block add their sums
+// in LDS in a fixed order (deterministic, no atomics).
+// k_bwd_dq: one work group per (batch, query head, query tile I); wave w owns the 32-row
+// chunk w % QCB and every NS-th (key block, 32-key sub-block) item of row I's bits.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace entmax {
+
+template <typename T, int D, int MODE>
+__global__ __launch_bounds__(256, 1) void k_bwd_dkv(BwdParams p) {
+  constexpr int DS = D / 16, DC = D / 32;
+  extern __shared__ float red[];
+  int unit, rank;
+  if (!wgmap_get(p.map, blockIdx.x, unit, rank)) return;
+  const int lane = lane_id(), c = lane & 31, h = lane >> 5, w = wave_id();
+  const int bi = unit / p.hkv, kvh = unit % p.hkv;
+  const int J = rank;
+  const int KC = p.Bc / 32, NS = 4 / KC;
+  const int ks = w % KC, slot = w / KC;
+  const int key0 = J * p.Bc + 32 * ks;
+  const int n = p.n;
+  const int QCB = p.Br / 32;
+  const float cx = p.cx, kappa = p.kappa;
+
+  const size_t kvbase = (size_t)(bi * p.hkv + kvh) * n;
+  const T* K = reinterpret_cast<const T*>(p.k) + kvbase * D;
+  const T* V = reinterpret_cast<const T*>(p.v) + kvbase * D;
+  Frag<T> kb[DS], vb[DS];
+#pragma unroll
+  for (int s = 0; s < DS; ++s) {
+    load_frag(kb[s], K + (size_t)(key0 + c) * D + 16 * s + 8 * h);
+    load_frag(vb[s], V + (size_t)(key0 + c) * D + 16 * s + 8 * h);
+  }
+  f32x16 dk[DC], dv[DC];
+#pragma unroll
+  for (int dc = 0; dc < DC; ++dc) {
+    dk[dc] = f32x16{};
+    dv[dc] = f32x16{};
+  }
+
+  int t = 0;
+  for (int g = 0; g < p.G; ++g) {
+    const int head = kvh * p.G + g;
+    const size_t qbase = (size_t)(bi * p.hq + head) * n;
+    const T* Q = reinterpret_cast<const T*>(p.q) + qbase * D;
+    const T* DO = reinterpret_cast<const T*>(p.dout) + qbase * D;
+    const T* Qt = reinterpret_cast<const T*>(p.qt) + qbase * D;     // [D][n] of this head
+    const T* DOt = reinterpret_cast<const T*>(p.dot) + qbase * D;
+    const float* tau = p.tau + qbase;
+    const float* delta = p.delta + qbase;
+    const uint32_t* colw = p.maskT + ((size_t)(bi * p.hq + head) * p.Tc + J) * p.WT;
+    for (int wi = 0; wi < p.WT; ++wi) {
+      uint32_t word = uniform_u32(colw[wi]);
+      while (word) {
+        const int I = wi * 32 + __builtin_ctz(word);
+        word &= word - 1;
+        for (int qc = 0; qc < QCB; ++qc, ++t) {
+          if (t % NS != slot) continue;
+          const int q0 = I * p.Br + 32 * qc;
+          if (p.causal && key0 > q0 + 31) continue;     // sub-tile above the diagonal
+          Frag<T> qa[DS];
+#pragma unroll
+          for (int s = 0; s < DS; ++s) load_frag(qa[s], Q + (size_t)(q0 + c) * D + 16 * s + 8 * h);
+          f32x16 S = f32x16{};
+#pragma unroll
+          for (int s = 0; s < DS; ++s) mma16(S, qa[s], kb[s]);   // S[q][key]
+          f32x4 tv[4], dv4[4];
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            tv[g4] = *reinterpret_cast<const f32x4*>(tau + q0 + 8 * g4 + 4 * h);
+            dv4[g4] = *reinterpret_cast<const f32x4*>(delta + q0 + 8 * g4 + 4 * h);
+          }
+          const bool diag = p.causal && key0 + 31 > q0;
+          f32x16 P, G;
+          bool any = false;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int qrow = q0 + acc_row(r, h);
+            const bool valid = !diag || (key0 + c <= qrow);
+            const float tt = valid ? (cx * S[r] - tv[r >> 2][r & 3]) : -1.0f;
+            const float dm = fmaxf(tt, 0.f);
+            P[r] = Weight<MODE>::p(dm, kappa);
+            G[r] = Weight<MODE>::g(tt > 0.f ? dm : 0.f, kappa);
+            any = any || (tt > 0.f);
+          }
+          if (ballot(any) == 0) continue;
+          Frag<T> da[DS];
+#pragma unroll
+          for (int s = 0; s < DS; ++s) load_frag(da[s], DO + (size_t)(q0 + c) * D + 16 * s + 8 * h);
+          f32x16 dP = f32x16{};
+#pragma unroll
+          for (int s = 0; s < DS; ++s) mma16(dP, da[s], vb[s]);  // dP[q][key]
+          f32x16 dS;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) dS[r] = G[r] * (dP[r] - dv4[r >> 2][r & 3]);
+#pragma unroll
+          for (int m = 0; m < 2; ++m) {
+            Frag<T> pf, sf;
+            acc_frag(pf, P, m);
+            acc_frag(sf, dS, m);
+#pragma unroll
+            for (int dc = 0; dc < DC; ++dc) {
+              Frag<T> qt, dt;
+              load_frag(qt, Qt + (size_t)(32 * dc + c) * n + q0 + 16 * m + 8 * h);
+              load_frag(dt, DOt + (size_t)(32 * dc + c) * n + q0 + 16 * m + 8 * h);
+              mma16(dv[dc], dt, pf);   // dV^T[d][key] += dO^T P
+              mma16(dk[dc], qt, sf);   // dK^T[d][key] += Q^T dS
+            }
+          }
+        }
+      }
+    }
+  }
+
+  // sum the NS partial accumulators of each sub-block in slot order 0, 1, ...
+  float* buf = red + (size_t)ks * (2 * DC * 16 * 64);
+  for (int sl = 1; sl < NS; ++sl) {
+    __syncthreads();
+    if (slot == sl) {
+#pragma unroll
+      for (int dc = 0; dc < DC; ++dc)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          buf[((0 * DC + dc) * 16 + r) * 64 + lane] = dk[dc][r];
+          buf[((1 * DC + dc) * 16 + r) * 64 + lane] = dv[dc][r];
+        }
+    }
+    __syncthreads();
+    if (slot == 0) {
+#pragma unroll
+      for (int dc = 0; dc < DC; ++dc)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          dk[dc][r] += buf[((0 * DC + dc) * 16 + r) * 64 + lane];
+          dv[dc][r] += buf[((1 * DC + dc) * 16 + r) * 64 + lane];
+        }
+    }
+  }
+  if (slot == 0) {
+    T* dK = reinterpret_cast<T*>(p.dk) + (kvbase + key0 + c) * D;
+    T* dV = reinterpret_cast<T*>(p.dv) + (kvbase + key0 + c) * D;
+    const float sc = p.scale;
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d0 = 32 * dc + 8 * g4 + 4 * h;
+        store4(dK + d0, sc * dk[dc][4 * g4], sc * dk[dc][4 * g4 + 1], sc * dk[dc][4 * g4 + 2],
+               sc * dk[dc][4 * g4 + 3]);
+        store4(dV + d0, dv[dc][4 * g4], dv[dc][4 * g4 + 1], dv[dc][4 * g4 + 2], dv[dc][4 * g4 + 3]);
+      }
+  }
+}
+
+template <typename T, int D, int MODE>
+__global__ __launch_bounds__(256, 1) void k_bwd_dq(BwdParams p) {
+  constexpr int DS = D / 16, DC = D / 32;
+  extern __shared__ float red[];
+  int unit, rank;
+  if (!wgmap_get(p.map, blockIdx.x, unit, rank)) return;
+  const int lane = lane_id(), c = lane & 31, h = lane >> 5, w = wave_id();
+  const int bi = unit / p.hkv, kvh = unit % p.hkv;
+  const int I = p.causal ? (p.Tr - 1 - rank / p.G) : (rank / p.G);
+  const int head = kvh * p.G + rank % p.G;
+  const int QCB = p.Br / 32, NS = 4 / QCB;
+  const int qc = w % QCB, slot = w / QCB;
+  const int KC = p.Bc / 32;
+  const int n = p.n;
+  const int q0 = I * p.Br + 32 * qc;
+  const float cx = p.cx, kappa = p.kappa;
+
+  const size_t qbase = (size_t)(bi * p.hq + head) * n;
+  const size_t kvbase = (size_t)(bi * p.hkv + kvh) * n;
+  const T* Q = reinterpret_cast<const T*>(p.q) + qbase * D;
+  const T* DO = reinterpret_cast<const T*>(p.dout) + qbase * D;
+  const T* K = reinterpret_cast<const T*>(p.k) + kvbase * D;
+  const T* V = reinterpret_cast<const T*>(p.v) + kvbase * D;
+  const T* Kt = reinterpret_cast<const T*>(p.kt) + kvbase * D;   // [D][n] of this KV head
+  Frag<T> qb[DS], db[DS];
+#pragma unroll
+  for (int s = 0; s < DS; ++s) {
+    load_frag(qb[s], Q + (size_t)(q0 + c) * D + 16 * s + 8 * h);
+    load_frag(db[s], DO + (size_t)(q0 + c) * D + 16 * s + 8 * h);
+  }
+  const float tq = p.tau[qbase + q0 + c];
+  const float dq_delta = p.delta[qbase + q0 + c];
+  const int qrow = q0 + c;
+  f32x16 dq[DC];
+#pragma unroll
+  for (int dc = 0; dc < DC; ++dc) dq[dc] = f32x16{};
+
+  const uint32_t* roww = p.mask + ((size_t)(bi * p.hq + head) * p.Tr + I) * p.W;
+  int t = 0;
+  for (int wi = 0; wi < p.W; ++wi) {
+    uint32_t word = uniform_u32(roww[wi]);
+    while (word) {
+      const int J = wi * 32 + __builtin_ctz(word);
+      word &= word - 1;
+      for (int ks = 0; ks < KC; ++ks, ++t) {
+        if (t % NS != slot) continue;
+        const int key0 = J * p.Bc + 32 * ks;
+        if (p.causal && key0 > q0 + 31) continue;
+        Frag<T> ka[DS];
+#pragma unroll
+        for (int s = 0; s < DS; ++s) load_frag(ka[s], K + (size_t)(key0 + c) * D + 16 * s + 8 * h);
+        f32x16 S = f32x16{};
+#pragma unroll
+        for (int s = 0; s < DS; ++s) mma16(S, ka[s], qb[s]);   // S^T[key][q]
+        const bool diag = p.causal && key0 + 31 > q0;
+        f32x16 G;
+        bool any = false;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const bool valid = !diag || (key0 + acc_row(r, h) <= qrow);
+          const float tt = valid ? (cx * S[r] - tq) : -1.0f;
+          const float dm = fmaxf(tt, 0.f);
+          G[r] = Weight<MODE>::g(tt > 0.f ? dm : 0.f, kappa);
+          any = any || (tt > 0.f);
+        }
+        if (ballot(any) == 0) continue;
+        Frag<T> va[DS];
+#pragma unroll
+        for (int s = 0; s < DS; ++s) load_frag(va[s], V + (size_t)(key0 + c) * D + 16 * s + 8 * h);
+        f32x16 dP = f32x16{};
+#pragma unroll
+        for (int s = 0; s < DS; ++s) mma16(dP, va[s], db[s]);   // dP^T[key][q]
+        f32x16 dS;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dS[r] = G[r] * (dP[r] - dq_delta);
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          Frag<T> sf;
+          acc_frag(sf, dS, m);
+#pragma unroll
+          for (int dc = 0; dc < DC; ++dc) {
+            Frag<T> kt;
+            load_frag(kt, Kt + (size_t)(32 * dc + c) * n + key0 + 16 * m + 8 * h);
+            mma16(dq[dc], kt, sf);   // dQ^T[d][q] += K^T dS^T
+          }
+        }
+      }
+    }
+  }
+
+  float* buf = red + (size_t)qc * (DC * 16 * 64);
+  for (int sl = 1; sl < NS; ++sl) {
+    __syncthreads();
+    if (slot == sl) {
+#pragma unroll
+      for (int dc = 0; dc < DC; ++dc)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) buf[(dc * 16 + r) * 64 + lane] = dq[dc][r];
+    }
+    __syncthreads();
+    if (slot == 0) {
+#pragma unroll
+      for (int dc = 0; dc < DC; ++dc)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dq[dc][r] += buf[(dc * 16 + r) * 64 + lane];
+    }
+  }
+  if (slot == 0) {
+    T* dQ = reinterpret_cast<T*>(p.dq) + (qbase + q0 + c) * D;
+    const float sc = p.scale;
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d0 = 32 * dc + 8 * g4 + 4 * h;
+        store4(dQ + d0, sc * dq[dc][4 * g4], sc * dq[dc][4 * g4 + 1], sc * dq[dc][4 * g4 + 2],
+               sc * dq[dc][4 * g4 + 3]);
+      }
+  }
+}
+
+template <typename T, int D>
+static hipError_t launch_dkv_t(const BwdParams& p, int mode, hipStream_t s) {
+  const int KC = p.Bc / 32, DC = D / 32;
+  const size_t lds = (4 / KC > 1) ? (size_t)KC * 2 * DC * 16 * 64 * sizeof(float) : 0;
+  const int grid = wgmap_grid(p.map);
+  if (grid == 0) return hipSuccess;
+  if (mode == 1) hipLaunchKernelGGL((k_bwd_dkv<T, D, 1>), dim3(grid), dim3(256), lds, s, p);
+  else if (mode == 2) hipLaunchKernelGGL((k_bwd_dkv<T, D, 2>), dim3(grid), dim3(256), lds, s, p);
+  else hipLaunchKernelGGL((k_bwd_dkv<T, D, 0>), dim3(grid), dim3(256), lds, s, p);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+static hipError_t launch_dq_t(const BwdParams& p, int mode, hipStream_t s) {
+  const int QCB = p.Br / 32, DC = D / 32;
+  const size_t lds = (4 / QCB > 1) ? (size_t)QCB * DC * 16 * 64 * sizeof(float) : 0;
+  const int grid = wgmap_grid(p.map);
+  if (grid == 0) return hipSuccess;
+  if (mode == 1) hipLaunchKernelGGL((k_bwd_dq<T, D, 1>), dim3(grid), dim3(256), lds, s, p);
+  else if (mode == 2) hipLaunchKernelGGL((k_bwd_dq<T, D, 2>), dim3(grid), dim3(256), lds, s, p);
+  else hipLaunchKernelGGL((k_bwd_dq<T, D, 0>), dim3(grid), dim3(256), lds, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dkv(const BwdParams& p, int dtype, int D, int mode, hipStream_t s) {
+  if (dtype == 1) return D == 64 ? launch_dkv_t<__bf16, 64>(p, mode, s) : launch_dkv_t<__bf16, 128>(p, mode, s);
+  return D == 64 ? launch_dkv_t<float, 64>(p, mode, s) : launch_dkv_t<float, 128>(p, mode, s);
+}
+
+hipError_t launch_bwd_dq(const BwdParams& p, int dtype, int D, int mode, hipStream_t s) {
+  if (dtype == 1) return D == 64 ? launch_dq_t<__bf16, 64>(p, mode, s) : launch_dq_t<__bf16, 128>(p, mode, s);
+  return D == 64 ? launch_dq_t<float, 64>(p, mode, s) : launch_dq_t<float, 128>(p, mode, s);
+}
+
+}  // namespace entmax

@@ -1,0 +1,155 @@
+// Device building blocks shared by the alpha-entmax attention kernels (gfx950 / CDNA4).
+//
+// Tiles are 32x32 products on the matrix cores. In a 32x32 MFMA output, lane l
+// (c = l % 32, h = l / 32) holds accumulator register r at
+//     row R(r, h) = 8 (r / 4) + 4 h + (r % 4),   column c.
+// A contraction chunk of 16 is fed as one fragment per lane: lane (c, h) holds the
+// 8 consecutive contraction indices 8h .. 8h+7 of its row (A operand) or column
+// (B operand). For bf16 that is one v_mfma_f32_32x32x16_bf16; for fp32 it is eight
+// v_mfma_f32_32x32x2_f32 where the j-th takes elements j and 8+j.
+//
+// When an accumulator tile becomes the B operand of the next product (P, G or dS
+// contracted over its rows), registers 8m .. 8m+7 of lane (c, h) feed chunk m and
+// stand for rows 16m + sigma(8h + j), sigma(8h + j) = 8 (j / 4) + 4 h + (j % 4). The
+// matching A operand is read from a transposed copy whose 16-position groups are
+// stored in sigma order (the "permuted transpose" built by k_transpose_perm), so the
+// same lane again reads 8 consecutive elements.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace entmax {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int WAVE = 64;
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+
+// Row of accumulator register r for half-wave h in a 32x32 MFMA output.
+__device__ __forceinline__ constexpr int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
+
+// Position of row `row` (0..15 within a 16-group) in the permuted transposed layout
+// (sigma is an involution: it swaps the middle two quads).
+__host__ __device__ __forceinline__ constexpr int sigma16(int p) {
+  return (p & ~12) | ((p & 4) << 1) | ((p & 8) >> 1);
+}
+
+// ------------------------------------------------------------------------------------------
+// fragments
+// ------------------------------------------------------------------------------------------
+template <typename T> struct Frag;
+template <> struct Frag<__bf16> {
+  bf16x8 v;
+};
+template <> struct Frag<float> {
+  f32x4 a, b;
+};
+
+__device__ __forceinline__ void load_frag(Frag<__bf16>& f, const __bf16* p) {
+  f.v = *reinterpret_cast<const bf16x8*>(p);
+}
+__device__ __forceinline__ void load_frag(Frag<float>& f, const float* p) {
+  f.a = *reinterpret_cast<const f32x4*>(p);
+  f.b = *reinterpret_cast<const f32x4*>(p + 4);
+}
+__device__ __forceinline__ void zero_frag(Frag<__bf16>& f) {
+  f.v = bf16x8{};
+}
+__device__ __forceinline__ void zero_frag(Frag<float>& f) {
+  f.a = f32x4{};
+  f.b = f32x4{};
+}
+
+// Fragment from 8 fp32 values (bf16: round to nearest even).
+__device__ __forceinline__ void set_frag(Frag<__bf16>& f, float x0, float x1, float x2, float x3,
+                                         float x4, float x5, float x6, float x7) {
+  f.v[0] = (__bf16)x0; f.v[1] = (__bf16)x1; f.v[2] = (__bf16)x2; f.v[3] = (__bf16)x3;
+  f.v[4] = (__bf16)x4; f.v[5] = (__bf16)x5; f.v[6] = (__bf16)x6; f.v[7] = (__bf16)x7;
+}
+__device__ __forceinline__ void set_frag(Frag<float>& f, float x0, float x1, float x2, float x3,
+                                         float x4, float x5, float x6, float x7) {
+  f.a = f32x4{x0, x1, x2, x3};
+  f.b = f32x4{x4, x5, x6, x7};
+}
+// Fragment m (0 or 1) of an accumulator tile: registers 8m .. 8m+7.
+template <typename T>
+__device__ __forceinline__ void acc_frag(Frag<T>& f, const f32x16& acc, int m) {
+  const int o = 8 * m;
+  set_frag(f, acc[o + 0], acc[o + 1], acc[o + 2], acc[o + 3], acc[o + 4], acc[o + 5], acc[o + 6],
+           acc[o + 7]);
+}
+
+// acc += A_chunk * B_chunk over one contraction chunk of 16.
+__device__ __forceinline__ void mma16(f32x16& acc, const Frag<__bf16>& a, const Frag<__bf16>& b) {
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.v, b.v, acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma16(f32x16& acc, const Frag<float>& a, const Frag<float>& b) {
+  acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.a[0], b.a[0], acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.a[1], b.a[1], acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.a[2], b.a[2], acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.a[3], b.a[3], acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.b[0], b.b[0], acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.b[1], b.b[1], acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.b[2], b.b[2], acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.b[3], b.b[3], acc, 0, 0, 0);
+}
+
+// ------------------------------------------------------------------------------------------
+// element stores
+// ------------------------------------------------------------------------------------------
+// Store 4 consecutive values (fp32 in registers) at p.
+__device__ __forceinline__ void store4(__bf16* p, float a, float b, float c, float d) {
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+  bf16x4 v;
+  v[0] = (__bf16)a; v[1] = (__bf16)b; v[2] = (__bf16)c; v[3] = (__bf16)d;
+  *reinterpret_cast<bf16x4*>(p) = v;
+}
+__device__ __forceinline__ void store4(float* p, float a, float b, float c, float d) {
+  *reinterpret_cast<f32x4*>(p) = f32x4{a, b, c, d};
+}
+
+// ------------------------------------------------------------------------------------------
+// wave helpers
+// ------------------------------------------------------------------------------------------
+__device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
+__device__ __forceinline__ float xor32f(float x) { return __shfl_xor(x, 32); }
+__device__ __forceinline__ int xor32i(int x) { return __shfl_xor(x, 32); }
+__device__ __forceinline__ uint32_t uniform_u32(uint32_t x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ int uniform_i32(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+__device__ __forceinline__ float max16(const f32x16& a) {
+  float m0 = fmaxf(fmaxf(a[0], a[1]), a[2]);
+  float m1 = fmaxf(fmaxf(a[3], a[4]), a[5]);
+  float m2 = fmaxf(fmaxf(a[6], a[7]), a[8]);
+  float m3 = fmaxf(fmaxf(a[9], a[10]), a[11]);
+  float m4 = fmaxf(fmaxf(a[12], a[13]), a[14]);
+  return fmaxf(fmaxf(fmaxf(m0, m1), fmaxf(m2, m3)), fmaxf(m4, a[15]));
+}
+
+// ------------------------------------------------------------------------------------------
+// the alpha-entmax weight: p = d^kappa, g = d^(kappa - 1) for d = x - tau > 0
+// MODE 1: kappa = 1 (alpha = 2); MODE 2: kappa = 2 (alpha = 1.5); MODE 0: any kappa.
+// ------------------------------------------------------------------------------------------
+template <int MODE>
+struct Weight {
+  __device__ __forceinline__ static float p(float d, float kappa) {
+    if constexpr (MODE == 1) return d;
+    else if constexpr (MODE == 2) return d * d;
+    else return d > 0.f ? exp2f(kappa * log2f(d)) : 0.f;
+  }
+  __device__ __forceinline__ static float g(float d, float kappa) {
+    if constexpr (MODE == 1) return d > 0.f ? 1.f : 0.f;
+    else if constexpr (MODE == 2) return d;
+    else return d > 0.f ? exp2f((kappa - 1.f) * log2f(d)) : 0.f;
+  }
+};
+
+struct ProfileHook;  // host side
+
+}  // namespace entmax

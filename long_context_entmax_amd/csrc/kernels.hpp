@@ -1,0 +1,110 @@
+// Kernel parameter blocks and launchers (internal to the library).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace entmax {
+
+// Work-group to (unit, rank) map. A unit is one (batch, KV head); all of its work
+// groups land on the same XCD (work group i runs on XCD i % 8) so K/V blocks are
+// reused from that XCD's L2. rank 0 is the longest work item of the unit.
+struct WgMap {
+  int U;      // units
+  int R;      // ranks per unit
+  int xcd;    // 1: XCD-grouped order (U % 8 == 0), 0: flat order
+};
+
+__host__ __device__ inline int wgmap_grid(const WgMap& m) {
+  if (m.xcd) return 8 * ((m.U + 7) / 8) * m.R;
+  return m.U * m.R;
+}
+
+__device__ __forceinline__ bool wgmap_get(const WgMap& m, int bid, int& unit, int& rank) {
+  if (m.xcd) {
+    const int x = bid & 7, s = bid >> 3;
+    const int cnt = (m.U - x + 7) >> 3;
+    if (s >= cnt * m.R) return false;
+    unit = x + 8 * (s % cnt);
+    rank = s / cnt;
+  } else {
+    if (bid >= m.U * m.R) return false;
+    unit = bid % m.U;
+    rank = bid / m.U;
+  }
+  return true;
+}
+
+struct FwdParams {
+  const void* q;
+  const void* k;
+  const void* vt;        // permuted transpose of V: [b, hkv, D, n]
+  float* o;              // fp32 [b, hq, n, D]
+  float* tau;
+  uint32_t* mask;
+  float* aux;            // o~ [b, hq, n, D] fp32
+  int32_t* hist;         // optional [b, hq, n, B]
+  float* tau_h;          // optional [b, hq, n]
+  unsigned long long* stats;  // optional [32]
+  int b, hq, hkv, n, G;
+  int causal, Br, Bc, B, max_iters;
+  float cx;              // (alpha - 1) * scale
+  float alpha, kappa, tol;
+  int GP;                // query heads per work group
+  int RH;                // rows per head per work group
+  int RG;                // row groups per head = ceil(n / RH)
+  int nkb, NW32;         // 32-key sub-blocks, words of sub-block bits
+  int Tr, Tc, W;
+  WgMap map;
+};
+
+struct PrepParams {
+  // permuted transposes X [H, n, D] -> Xt [H, D, n]
+  const void* src[3];
+  void* dst[3];
+  int heads[3];
+  int ntrans;
+  int n, D;
+  // delta = sum_d dO * o~
+  const void* dout;
+  const float* aux;
+  float* delta;
+  int rows;              // b * hq * n (0: skip)
+  // mask transpose: mask [P, Tr, W] -> maskT [P, Tc, WT]
+  const uint32_t* mask;
+  uint32_t* maskT;
+  int planes, Tr, Tc, W, WT;
+};
+
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* dout;
+  const void* qt;        // permuted transposes
+  const void* dot;
+  const void* kt;
+  const float* tau;
+  const float* delta;
+  const uint32_t* mask;  // [b, hq, Tr, W]
+  const uint32_t* maskT; // [b, hq, Tc, WT]
+  void* dq;
+  void* dk;
+  void* dv;
+  int b, hq, hkv, n, G;
+  int causal, Br, Bc;
+  float cx, scale, kappa;
+  int Tr, Tc, W, WT;
+  WgMap map;
+};
+
+hipError_t launch_fwd(const FwdParams& p, int dtype, int D, int mode, hipStream_t s);
+hipError_t launch_transpose(const PrepParams& p, int dtype, hipStream_t s);
+hipError_t launch_bwd_prep(const PrepParams& p, int dtype, hipStream_t s);
+hipError_t launch_bwd_dkv(const BwdParams& p, int dtype, int D, int mode, hipStream_t s);
+hipError_t launch_bwd_dq(const BwdParams& p, int dtype, int D, int mode, hipStream_t s);
+
+// timing hooks (api.hip): called around every launch
+void prof_begin(const char* name, hipStream_t s);
+void prof_end(hipStream_t s);
+
+}  // namespace entmax

@@ -1,0 +1,109 @@
+"""Host-side checks of the C ABI: the library loads, exports every declared entry point,
+and rejects bad arguments before touching the GPU (these calls make no HIP call, so
+they run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import long_context_entmax_amd as lce
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "entmax_attn.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(entmax_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(lce.LIB_PATH):
+        pytest.fail("libentmax_attn.so is not built (python -m long_context_entmax_amd.build)")
+    return lce.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = _declared()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(lce.EXPORTS)
+
+
+def _desc(**kw):
+    base = dict(batch=1, heads_q=2, heads_kv=1, seqlen=256, head_dim=64, dtype=lce.ENTMAX_BF16,
+                alpha=1.5, causal=True, block=(64, 64), bins=16)
+    base.update(kw)
+    blk = base.pop("block")
+    return lce.make_desc(base["batch"], base["heads_q"], base["heads_kv"], base["seqlen"],
+                         base["head_dim"], base["dtype"], base["alpha"], base["causal"], blk,
+                         base["bins"], base.get("scale"), base.get("max_iters", 0), base.get("tol", 0.0))
+
+
+BAD = [
+    (dict(alpha=1.0), 3), (dict(alpha=float("nan")), 3), (dict(alpha=0.5), 3), (dict(alpha=17.0), 3),
+    (dict(heads_q=3, heads_kv=2), 2), (dict(seqlen=100), 2), (dict(seqlen=-64), 2),
+    (dict(head_dim=96), 4), (dict(block=(48, 64)), 4), (dict(block=(64, 256)), 4),
+    (dict(bins=12), 4), (dict(bins=32), 4), (dict(dtype=7), 4), (dict(seqlen=1 << 20), 4),
+    (dict(max_iters=16), 2), (dict(heads_kv=0), 2),
+]
+
+
+@pytest.mark.parametrize("kw,status", BAD, ids=[str(b[0]) for b in BAD])
+def test_argument_errors(L, kw, status):
+    d = _desc(**kw)
+    assert L.entmax_attn_fwd_workspace_bytes(ctypes.byref(d)) == 0
+    fake = ctypes.c_void_p(256)
+    st = L.entmax_attn_fwd(ctypes.byref(d), fake, fake, fake, fake, fake, fake, fake, None, None, None,
+                           fake, 1 << 30, None)
+    assert st == status, L.entmax_last_error()
+    assert len(L.entmax_last_error()) > 0
+    st = L.entmax_attn_bwd(ctypes.byref(d), fake, fake, fake, fake, fake, fake, fake, fake, fake, fake,
+                           fake, 1 << 30, None)
+    assert st == status
+
+
+def test_null_pointers_alignment_workspace(L):
+    d = _desc()
+    f = ctypes.c_void_p(4096)
+    assert L.entmax_attn_fwd(None, f, f, f, f, f, f, f, None, None, None, f, 1 << 30, None) == 1
+    assert L.entmax_attn_fwd(ctypes.byref(d), None, f, f, f, f, f, f, None, None, None, f, 1 << 30, None) == 1
+    mis = ctypes.c_void_p(4098)
+    assert L.entmax_attn_fwd(ctypes.byref(d), mis, f, f, f, f, f, f, None, None, None, f, 1 << 30, None) == 5
+    need = L.entmax_attn_fwd_workspace_bytes(ctypes.byref(d))
+    assert need > 0
+    assert L.entmax_attn_fwd(ctypes.byref(d), f, f, f, f, f, f, f, None, None, None, f, need - 1, None) == 6
+    assert L.entmax_attn_fwd(ctypes.byref(d), f, f, f, f, f, f, f, None, None, None, None, need, None) == 6
+    nb = L.entmax_attn_bwd_workspace_bytes(ctypes.byref(d))
+    assert L.entmax_attn_bwd(ctypes.byref(d), f, f, f, f, f, f, f, f, f, f, f, nb - 1, None) == 6
+    assert L.entmax_attn_bwd(ctypes.byref(d), f, f, f, None, f, f, f, f, f, f, f, nb, None) == 1
+
+
+def test_empty_problem_is_a_no_op(L):
+    for kw in (dict(batch=0), dict(heads_q=0, heads_kv=1), dict(seqlen=0)):
+        d = _desc(**kw)
+        assert L.entmax_attn_fwd(ctypes.byref(d), None, None, None, None, None, None, None, None, None,
+                                 None, None, 0, None) == 0
+        assert L.entmax_attn_bwd(ctypes.byref(d), None, None, None, None, None, None, None, None, None,
+                                 None, None, 0, None) == 0
+
+
+def test_sizes(L):
+    d = _desc(batch=2, heads_q=8, heads_kv=2, seqlen=4096, head_dim=64, block=(128, 64))
+    Tr, W = 4096 // 128, (4096 // 64 + 31) // 32
+    assert L.entmax_attn_mask_words(ctypes.byref(d)) == 2 * 8 * Tr * W
+    assert L.entmax_attn_aux_bytes(ctypes.byref(d)) == 2 * 8 * 4096 * 64 * 4
+    assert L.entmax_attn_fwd_workspace_bytes(ctypes.byref(d)) >= 2 * 2 * 4096 * 64 * 2
+    assert L.entmax_status_string(0) == b"ok"
+    assert L.entmax_status_string(7) == b"HIP runtime error"
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    q = torch.zeros(1, 1, 64, 64)
+    with pytest.raises(ValueError):
+        lce.fwd(q, q, q)

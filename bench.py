@@ -1,0 +1,235 @@
+"""Benchmark: alpha-entmax attention fwd+bwd step on one MI355X.
+
+A step is one forward and one backward of the whole hot path (histogram pass,
+refinement, output pass, backward preparation, dK/dV and dQ kernels) over one
+batch of synthetic inputs resident in HBM. The default workload is the 4K-token
+configuration (batch 4, 8 heads, n 4096, d 64, bf16, causal, alpha 1.5, 64x64
+blocks, B 16) with the centroid-cluster generator calibrated to ~90% block
+sparsity; ``--config C3|C4|C5`` and ``--alpha``/``--sparsity`` select the others.
+
+Prints one JSON line: value = effective TFLOP/s (dense-equivalent FLOPs of a causal
+attention fwd+bwd, 3.5 x 4 b h n^2 d / 2, divided by the measured step time),
+plus a roofline object for the dominant kernel (algorithmic MFMA FLOPs per launch
+over its HIP-event-timed average duration) and the CPU oracle timed on a bounded
+sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_FP32_TFLOPS = 157.3
+METRIC = "fwd+bwd ms/step & effective TFLOP/s vs block sparsity, α-entmax attn 4K–128K"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="C2")
+    ap.add_argument("--alpha", type=float, default=None)
+    ap.add_argument("--sparsity", type=float, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample time")
+    ap.add_argument("--profile-only", action="store_true",
+                    help="warmup + steps only (for rocprofv3 runs), still prints the JSON line")
+    return ap.parse_args()
+
+
+def src_digest() -> str:
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "long_context_entmax_amd", "csrc")
+    for f in sorted(os.listdir(d)):
+        if f.endswith((".hip", ".hpp")):
+            with open(os.path.join(d, f), "rb") as fh:
+                h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def dense_eq_flops(w) -> float:
+    f = 3.5 * 4.0 * w.batch * w.heads_q * float(w.seqlen) ** 2 * w.head_dim
+    return f * (0.5 if w.causal else 1.0)
+
+
+def valid_blocks(w) -> int:
+    Tr, Tc = w.seqlen // w.block_q, w.seqlen // w.block_k
+    if not w.causal:
+        return Tr * Tc
+    return sum(min(Tc, (I * w.block_q + w.block_q - 1) // w.block_k + 1) for I in range(Tr))
+
+
+def popcount_mask(mask) -> int:
+    import torch
+    m = mask.to(torch.int64) & 0xFFFFFFFF
+    cnt = torch.zeros_like(m)
+    for b in range(32):
+        cnt += (m >> b) & 1
+    return int(cnt.sum().item())
+
+
+def cpu_baseline(w, inp_cpu, target_s: float):
+    """Time the fp64 oracle (fwd + bwd) on whole query heads until ~target_s, extrapolate."""
+    import numpy as np
+    import oracle
+    threads = oracle.default_threads()
+    G = w.heads_q // w.heads_kv
+    heads_done = 0
+    t0 = time.time()
+    q = inp_cpu["q"]
+    for h in range(w.heads_q):
+        if heads_done > 0 and time.time() - t0 > target_s:
+            break
+        kh = h // G
+        qh = q[0, h].double().numpy()
+        kk = inp_cpu["k"][0, kh].double().numpy()
+        vv = inp_cpu["v"][0, kh].double().numpy()
+        do = inp_cpu["do"][0, h].double().numpy()
+        scale = 1.0 / math.sqrt(w.head_dim)
+        f = oracle.attn_fwd_head(qh, kk, vv, w.alpha, w.causal, w.n_bins, w.block_k, scale,
+                                 threads=threads)
+        r = oracle.attn_bwd_rows_head(qh, kk, vv, do, f["tau"], w.alpha, w.causal, scale,
+                                      threads=threads)
+        # the key-side backward of one query head's contribution (G = 1 share of its KV head)
+        oracle.attn_bwd_keys_group(qh[None], kk, vv, do[None], f["tau"][None], r["delta"][None],
+                                   w.alpha, w.causal, scale, threads=threads)
+        heads_done += 1
+    el = time.time() - t0
+    total_heads = w.batch * w.heads_q
+    s_per_step = el * total_heads / heads_done
+    return {
+        "value": dense_eq_flops(w) / s_per_step / 1e12,
+        "unit": "TFLOP/s (effective)",
+        "ms_per_step": s_per_step * 1e3,
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{heads_done} of {total_heads} query heads, full length, fwd+bwd, {el:.1f} s, "
+                  f"extrapolated linearly to all heads",
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 (multi-GPU "
+                                   "sharding is described, not implemented)"}))
+        sys.exit(2)
+    import torch
+    import synth
+    import long_context_entmax_amd as lce
+
+    w = synth.workload(args.config, alpha=args.alpha, sparsity=args.sparsity)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = synth.make_inputs(w, device=dev)
+    q, k, v, do = inp["q"], inp["k"], inp["v"], inp["do"]
+    blk = (w.block_q, w.block_k)
+    b, hq, n, d = q.shape
+    Tr, W = lce.mask_shape(n, blk)
+    outs = lce.FwdOut(torch.empty(q.shape, dtype=torch.float32, device=dev),
+                      torch.empty((b, hq, n), dtype=torch.float32, device=dev),
+                      torch.empty((b, hq, Tr, W), dtype=torch.int32, device=dev),
+                      torch.empty((b, hq, n, d), dtype=torch.float32, device=dev), None, None)
+    grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    desc = lce._desc_for(q, k, w.alpha, w.causal, blk, w.n_bins, None, 0, 0.0)
+    fws, bws = lce.workspace_bytes(desc)
+    wsf = torch.empty(max(fws, 256), dtype=torch.uint8, device=dev)
+    wsb = torch.empty(max(bws, 256), dtype=torch.uint8, device=dev)
+
+    def step(stats=None):
+        r = lce.fwd(q, k, v, w.alpha, w.causal, blk, w.n_bins, workspace=wsf, out=outs, stats=stats)
+        lce.bwd(q, k, v, do, r.tau, r.mask, r.aux, w.alpha, w.causal, blk, w.n_bins, workspace=wsb,
+                out=grads)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.time()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.time() - t0
+    ms = e0.elapsed_time(e1) / args.steps
+
+    # per-kernel HIP-event timing (same steps, separate loop) and method statistics
+    stats = torch.zeros(32, dtype=torch.int64, device=dev)
+    lce.profile(True)
+    lce.profile_read()
+    for _ in range(args.steps):
+        step(stats)
+    torch.cuda.synchronize()
+    ktimes = lce.profile_read()
+    lce.profile(False)
+    st = stats.cpu().tolist()
+    nnzb = popcount_mask(outs.mask)
+    nvb = valid_blocks(w) * b * hq
+    sparsity = 1.0 - nnzb / nvb
+    blockflop = 2.0 * w.block_q * w.block_k * d
+    subflop = 2.0 * 32 * 32 * d
+    per_step = lambda idx: st[idx] / args.steps
+    alg = {
+        "entmax_fwd": subflop * (per_step(20) + per_step(21)) + 3 * blockflop * nnzb,
+        "entmax_bwd_dkv": 4 * blockflop * nnzb,
+        "entmax_bwd_dq": 3 * blockflop * nnzb,
+    }
+    kern = {name: {"avg_ms": t / max(c, 1), "launches_per_step": c / args.steps}
+            for name, (t, c) in ktimes.items()}
+    dom = max(alg, key=lambda nm: kern.get(nm, {"avg_ms": 0})["avg_ms"])
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
+    achieved = alg[dom] / (kern[dom]["avg_ms"] * 1e-3) / 1e12
+    traffic = None
+    tfile = os.path.join(ROOT, "profiles", f"{dom}_{w.name}_traffic.json")
+    if os.path.exists(tfile):
+        with open(tfile) as f:
+            tj = json.load(f)
+        if tj.get("src_digest") == src_digest() and tj.get("workload") == w.name:
+            traffic = tj.get("bytes_per_launch")
+    passes = {str(p): st[p] for p in range(1, 17) if st[p]}
+    eff = dense_eq_flops(w) / (ms * 1e-3) / 1e12
+    line = {
+        "metric": METRIC,
+        "value": round(eff, 3),
+        "unit": "TFLOP/s (effective, dense-equivalent)",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded centroid-cluster generator, beta calibrated to the target block sparsity)",
+        "config": {
+            "workload": f"{w.name}: b{w.batch} hq{w.heads_q}/hkv{w.heads_kv} n{w.seqlen} d{w.head_dim} "
+                        f"{w.dtype} {'causal' if w.causal else 'full'} alpha {w.alpha} blocks "
+                        f"{w.block_q}x{w.block_k} B {w.n_bins}",
+            "target_block_sparsity": w.target_sparsity, "beta": w.beta,
+            "achieved_block_sparsity": round(sparsity, 4), "nonzero_blocks": nnzb, "valid_blocks": nvb,
+        },
+        "roofline": {
+            "kernel": dom, "bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
+            "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,
+            "algorithmic_flops_per_launch": alg[dom],
+        },
+        "kernels_ms": {kk: round(vv["avg_ms"], 4) for kk, vv in kern.items()},
+        "refine_passes_rows": passes,
+        "wall_s": round(wall, 3),
+    }
+    if not args.no_cpu_baseline and not args.profile_only:
+        inp_cpu = {kk: vv.cpu() for kk, vv in inp.items() if hasattr(vv, "cpu")}
+        line["cpu_baseline"] = cpu_baseline(w, inp_cpu, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

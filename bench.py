@@ -165,24 +165,31 @@ def main():
     wall = time.time() - t0
     ms = e0.elapsed_time(e1) / args.steps
 
-    # per-kernel HIP-event timing (same steps, separate loop) and method statistics
-    stats = torch.zeros(32, dtype=torch.int64, device=dev)
+    # per-kernel HIP-event timing (same steps, separate loop, events recorded on the
+    # stream each kernel is launched on)
     lce.profile(True)
     lce.profile_read()
     for _ in range(args.steps):
-        step(stats)
+        step()
     torch.cuda.synchronize()
     ktimes = lce.profile_read()
     lce.profile(False)
+    # method statistics from one extra, untimed step
+    stats = torch.zeros(32, dtype=torch.int64, device=dev)
+    step(stats)
+    torch.cuda.synchronize()
     st = stats.cpu().tolist()
     nnzb = popcount_mask(outs.mask)
     nvb = valid_blocks(w) * b * hq
     sparsity = 1.0 - nnzb / nvb
     blockflop = 2.0 * w.block_q * w.block_k * d
     subflop = 2.0 * 32 * 32 * d
-    per_step = lambda idx: st[idx] / args.steps
+    # algorithmic MFMA FLOPs per launch: one 32x32xd score product per sub-block the
+    # histogram pass scores and per refinement visit, a score and a P.V product per
+    # output visit, and per non-zero 64x64 block 4 products in dK/dV and 3 in dQ
     alg = {
-        "entmax_fwd": subflop * (per_step(20) + per_step(21)) + 3 * blockflop * nnzb,
+        "entmax_fwd_hist": subflop * st[20],
+        "entmax_fwd_refine_out": subflop * (st[21] + 2 * st[22]),
         "entmax_bwd_dkv": 4 * blockflop * nnzb,
         "entmax_bwd_dq": 3 * blockflop * nnzb,
     }
@@ -199,6 +206,8 @@ def main():
         if tj.get("src_digest") == src_digest() and tj.get("workload") == w.name:
             traffic = tj.get("bytes_per_launch")
     passes = {str(p): st[p] for p in range(1, 17) if st[p]}
+    sub_stats = {"hist_subblocks": st[20], "refine_visits": st[21], "output_visits": st[22],
+                 "candidate_subblocks": st[23]}
     eff = dense_eq_flops(w) / (ms * 1e-3) / 1e12
     line = {
         "metric": METRIC,
@@ -222,7 +231,10 @@ def main():
             "algorithmic_flops_per_launch": alg[dom],
         },
         "kernels_ms": {kk: round(vv["avg_ms"], 4) for kk, vv in kern.items()},
+        "kernel_tflops": {kk: round(alg[kk] / (kern[kk]["avg_ms"] * 1e-3) / 1e12, 2)
+                          for kk in alg if kk in kern},
         "refine_passes_rows": passes,
+        "subblock_stats": sub_stats,
         "wall_s": round(wall, 3),
     }
     if not args.no_cpu_baseline and not args.profile_only:

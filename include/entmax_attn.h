@@ -104,7 +104,8 @@ size_t entmax_attn_mask_words(const entmax_attn_desc *desc);
  * stats[p] for p = 1..max_iters counts query rows whose refinement stopped after p
  * passes, stats[max_iters + 1] rows that hit the cap; stats[20] key sub-blocks
  * (32 keys x 32 rows) scored by the histogram pass, stats[21] by refinement passes,
- * stats[22] by the output pass).
+ * stats[22] by the output pass with a non-zero weight, stats[23] sub-blocks that the
+ * histogram pass marked as candidates).
  * workspace: at least entmax_attn_fwd_workspace_bytes(desc) bytes, 256-byte aligned.
  */
 entmax_status entmax_attn_fwd(const entmax_attn_desc *desc,

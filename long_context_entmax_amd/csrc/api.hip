@@ -137,22 +137,29 @@ static entmax_status derive(const entmax_attn_desc* d, Derived& o) {
   o.nkb = o.n / 32;
   o.NW32 = (o.nkb + 31) / 32;
   o.es = o.dtype == ENTMAX_BF16 ? 2 : 4;
-  o.QW = o.D == 64 ? 64 : 32;
+  // forward work group: 8 waves x 32 rows over GP query heads of one KV head
+  o.QW = 32;
   o.GP = 1;
-  for (int gp : {4, 2}) {
-    if (o.G % gp == 0 && ((4 / gp) * o.QW) % o.Br == 0) {
+  for (int gp : {8, 4, 2}) {
+    if (o.G % gp == 0 && ((8 / gp) * o.QW) % o.Br == 0) {
       o.GP = gp;
       break;
     }
   }
-  o.RH = (4 / o.GP) * o.QW;
+  o.RH = (8 / o.GP) * o.QW;
   o.RG = (o.n + o.RH - 1) / o.RH;
   return ENTMAX_OK;
 }
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-static size_t fwd_ws(const Derived& o) { return align256((size_t)o.b * o.hkv * o.D * o.n * o.es); }
+// forward workspace: K and V fragment-major copies, then per (chunk, sub-block) maxima
+static size_t fwd_kv_bytes(const Derived& o) { return align256((size_t)o.b * o.hkv * o.D * o.n * o.es); }
+static size_t fwd_dmax_bytes(const Derived& o) { return align256((size_t)o.b * o.hq * (size_t)o.nkb * o.nkb * 4); }
+static size_t fwd_cand_bytes(const Derived& o) { return align256((size_t)o.b * o.hq * (size_t)o.nkb * o.NW32 * 4); }
+static size_t fwd_ws(const Derived& o) {
+  return 2 * fwd_kv_bytes(o) + fwd_dmax_bytes(o) + fwd_cand_bytes(o) + align256((size_t)o.b * o.hq * o.n * 4);
+}
 
 struct BwdLayout {
   size_t delta, maskT, qt, dot, kt, total;
@@ -230,19 +237,28 @@ entmax_status entmax_attn_fwd(const entmax_attn_desc* desc, const void* q, const
                 workspace_bytes);
   hipStream_t s = (hipStream_t)stream;
 
+  char* wsb = (char*)workspace;
   PrepParams tp{};
-  tp.src[0] = v;
-  tp.dst[0] = workspace;
+  tp.src[0] = k;
+  tp.dst[0] = wsb;
   tp.heads[0] = o.b * o.hkv;
-  tp.ntrans = 1;
+  tp.kind[0] = 1;
+  tp.src[1] = v;
+  tp.dst[1] = wsb + fwd_kv_bytes(o);
+  tp.heads[1] = o.b * o.hkv;
+  tp.kind[1] = 2;
+  tp.ntrans = 2;
   tp.n = o.n;
   tp.D = o.D;
   hipError_t e = launch_transpose(tp, o.dtype, s);
-  if (e != hipSuccess) return hip_fail(e, "transpose of V");
+  if (e != hipSuccess) return hip_fail(e, "fragment-major copies of K and V");
 
   FwdParams p{};
-  p.q = q; p.k = k; p.vt = workspace; p.o = (float*)o_; p.tau = tau; p.mask = block_mask; p.aux = (float*)aux;
+  p.q = q; p.kf = wsb; p.vf = wsb + fwd_kv_bytes(o); p.o = (float*)o_; p.tau = tau; p.mask = block_mask; p.aux = (float*)aux;
   p.hist = hist_counts; p.tau_h = tau_h; p.stats = (unsigned long long*)stats;
+  p.dmax = (float*)(wsb + 2 * fwd_kv_bytes(o));
+  p.cand = (uint32_t*)(wsb + 2 * fwd_kv_bytes(o) + fwd_dmax_bytes(o));
+  p.tauh_ws = (float*)(wsb + 2 * fwd_kv_bytes(o) + fwd_dmax_bytes(o) + fwd_cand_bytes(o));
   p.b = o.b; p.hq = o.hq; p.hkv = o.hkv; p.n = o.n; p.G = o.G;
   p.causal = o.causal; p.Br = o.Br; p.Bc = o.Bc; p.B = o.B; p.max_iters = o.max_iters;
   p.cx = (float)(((double)o.alpha - 1.0) * (double)o.scale);
@@ -250,9 +266,8 @@ entmax_status entmax_attn_fwd(const entmax_attn_desc* desc, const void* q, const
   p.GP = o.GP; p.RH = o.RH; p.RG = o.RG;
   p.nkb = o.nkb; p.NW32 = o.NW32; p.Tr = o.Tr; p.Tc = o.Tc; p.W = o.W;
   p.map = make_map(o.b * o.hkv, (o.G / o.GP) * o.RG);
-  prof_begin("entmax_fwd", s);
+  p.map2 = make_map(o.b * o.hkv, o.G * ((o.nkb + 3) / 4));
   e = launch_fwd(p, o.dtype, o.D, o.mode, s);
-  prof_end(s);
   if (e != hipSuccess) return hip_fail(e, "forward kernel");
   return ENTMAX_OK;
 }
@@ -282,6 +297,7 @@ entmax_status entmax_attn_bwd(const entmax_attn_desc* desc, const void* q, const
   pp.src[0] = q;    pp.dst[0] = ws + L.qt;  pp.heads[0] = o.b * o.hq;
   pp.src[1] = dout; pp.dst[1] = ws + L.dot; pp.heads[1] = o.b * o.hq;
   pp.src[2] = k;    pp.dst[2] = ws + L.kt;  pp.heads[2] = o.b * o.hkv;
+  pp.kind[0] = pp.kind[1] = pp.kind[2] = 0;
   pp.ntrans = 3;
   pp.n = o.n;
   pp.D = o.D;

@@ -66,6 +66,16 @@ __device__ __forceinline__ void zero_frag(Frag<float>& f) {
   f.b = f32x4{};
 }
 
+// Multiply a fragment by a power of two (exact unless it overflows or underflows).
+__device__ __forceinline__ void scale_frag(Frag<__bf16>& f, float sc) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) f.v[j] = (__bf16)((float)f.v[j] * sc);
+}
+__device__ __forceinline__ void scale_frag(Frag<float>& f, float sc) {
+  f.a *= sc;
+  f.b *= sc;
+}
+
 // Fragment from 8 fp32 values (bf16: round to nearest even).
 __device__ __forceinline__ void set_frag(Frag<__bf16>& f, float x0, float x1, float x2, float x3,
                                          float x4, float x5, float x6, float x7) {
@@ -118,18 +128,75 @@ __device__ __forceinline__ void store4(float* p, float a, float b, float c, floa
 // wave helpers
 // ------------------------------------------------------------------------------------------
 __device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
-__device__ __forceinline__ float xor32f(float x) { return __shfl_xor(x, 32); }
-__device__ __forceinline__ int xor32i(int x) { return __shfl_xor(x, 32); }
 __device__ __forceinline__ uint32_t uniform_u32(uint32_t x) { return __builtin_amdgcn_readfirstlane(x); }
 __device__ __forceinline__ int uniform_i32(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
+// Value of lane l ^ 32 (the other half-wave), without going through LDS.
+__device__ __forceinline__ float xor32f(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+}
+__device__ __forceinline__ int xor32i(int v) {
+  auto r = __builtin_amdgcn_permlane32_swap((uint32_t)v, (uint32_t)v, false, false);
+  return (int)((threadIdx.x & 32) ? r[0] : r[1]);
+}
+
+// Wave-wide max / min with DPP row operations (no LDS traffic); the result is uniform.
+#define ENTMAX_DPP(v, ctrl, rmask) \
+  __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), ctrl, rmask, 0xF, false))
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, ENTMAX_DPP(v, 0xB1, 0xF));    // quad_perm 1,0,3,2
+  v = fmaxf(v, ENTMAX_DPP(v, 0x4E, 0xF));    // quad_perm 2,3,0,1
+  v = fmaxf(v, ENTMAX_DPP(v, 0x141, 0xF));   // row_half_mirror
+  v = fmaxf(v, ENTMAX_DPP(v, 0x140, 0xF));   // row_mirror
+  v = fmaxf(v, ENTMAX_DPP(v, 0x142, 0xA));   // row_bcast15 into rows 1, 3
+  v = fmaxf(v, ENTMAX_DPP(v, 0x143, 0xC));   // row_bcast31 into rows 2, 3
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+__device__ __forceinline__ float wave_min(float v) {
+  v = fminf(v, ENTMAX_DPP(v, 0xB1, 0xF));
+  v = fminf(v, ENTMAX_DPP(v, 0x4E, 0xF));
+  v = fminf(v, ENTMAX_DPP(v, 0x141, 0xF));
+  v = fminf(v, ENTMAX_DPP(v, 0x140, 0xF));
+  v = fminf(v, ENTMAX_DPP(v, 0x142, 0xA));
+  v = fminf(v, ENTMAX_DPP(v, 0x143, 0xC));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+// floor(x) as int in one instruction (saturating: -inf -> INT_MIN, +inf -> INT_MAX).
+__device__ __forceinline__ int cvt_floor(float x) {
+  int r;
+  asm("v_cvt_flr_i32_f32 %0, %1" : "=v"(r) : "v"(x));
+  return r;
+}
+
+// max of three without canonicalising the inputs (no IEEE-mode NaN quieting)
+__device__ __forceinline__ float max3_raw(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
 __device__ __forceinline__ float max16(const f32x16& a) {
-  float m0 = fmaxf(fmaxf(a[0], a[1]), a[2]);
-  float m1 = fmaxf(fmaxf(a[3], a[4]), a[5]);
-  float m2 = fmaxf(fmaxf(a[6], a[7]), a[8]);
-  float m3 = fmaxf(fmaxf(a[9], a[10]), a[11]);
-  float m4 = fmaxf(fmaxf(a[12], a[13]), a[14]);
-  return fmaxf(fmaxf(fmaxf(m0, m1), fmaxf(m2, m3)), fmaxf(m4, a[15]));
+  const float m0 = max3_raw(a[0], a[1], a[2]);
+  const float m1 = max3_raw(a[3], a[4], a[5]);
+  const float m2 = max3_raw(a[6], a[7], a[8]);
+  const float m3 = max3_raw(a[9], a[10], a[11]);
+  const float m4 = max3_raw(a[12], a[13], a[14]);
+  return max3_raw(max3_raw(m0, m1, m2), max3_raw(m3, m4, a[15]), m0);
+}
+// Wave-wide max with DPP-fused v_max (one instruction per step; s_nop 1 covers the
+// VALU-write -> DPP-read hazard); the result is uniform.
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  asm volatile(
+      "s_nop 1\n v_max_f32_dpp %0, %0, %0 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n"
+      "s_nop 1\n v_max_f32_dpp %0, %0, %0 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n"
+      "s_nop 1\n v_max_f32_dpp %0, %0, %0 row_half_mirror row_mask:0xf bank_mask:0xf\n"
+      "s_nop 1\n v_max_f32_dpp %0, %0, %0 row_mirror row_mask:0xf bank_mask:0xf\n"
+      "s_nop 1\n v_max_f32_dpp %0, %0, %0 row_bcast:15 row_mask:0xa bank_mask:0xf\n"
+      "s_nop 1\n v_max_f32_dpp %0, %0, %0 row_bcast:31 row_mask:0xc bank_mask:0xf\n"
+      "s_nop 4"
+      : "+v"(v));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
 // ------------------------------------------------------------------------------------------

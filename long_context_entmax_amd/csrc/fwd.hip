@@ -1,32 +1,35 @@
-// Forward of alpha-entmax attention: one fused kernel per group of query rows.
+// Forward of alpha-entmax attention: a histogram kernel and a refinement/output kernel.
 //
 // Stages (AdaSplash-2 pages, page 1 section 2, page 3 section 2, page 5 section 2):
-//   1. histogram pass: every valid key block streams through once; each lane keeps
-//      an online max and a B-bin histogram of its scores on the anchored grid
-//      (bins [m/B, (m+1)/B), window = the B cells ending with the max's cell); a
-//      window that slides up drops the cells that fall off. tau_h, the root of the
-//      B-bin problem (counts at lower bin edges), satisfies tau* - 1/B < tau_h <= tau*
-//      (Proposition 1). The same pass marks the 32-key sub-blocks that hold a score
-//      within two bins below the running window: every score that can exceed the
-//      bracket's lower end lies in one of them.
-//   2. refinement passes over the marked sub-blocks only: a safeguarded hybrid root
-//      solver on f(tau) = sum_j [x_j - tau]_+^kappa - 1 from tau_h with bracket
-//      [tau_h, tau_h + 1/B]: Halley (alpha <= 1.5), Newton (1.5 < alpha <= 2), secant
-//      (alpha > 2, started by false position on the bracket ends), bisection whenever a
-//      step leaves the bracket (page 1 section 2.2, page 3 section 2.2).
-//   3. output pass over the marked sub-blocks: p = [x - tau]_+^kappa, o = P V,
-//      o~ = G V / sum G with g = [x - tau]_+^(kappa-1), and the exact block mask
-//      (bit-packed, 32 blocks per word; page 1 section 2.3). Sub-blocks without a
-//      non-zero weight skip the PV products.
+//   1. k_hist -- histogram pass: every valid key block streams through once; each lane
+//      keeps an online max and a B-bin histogram of its scores on the anchored grid
+//      (bins [m/B, (m+1)/B), window = the B cells ending with the max's cell); a window
+//      that slides up drops the cells that fall off. tau_h, the root of the B-bin
+//      problem (counts at lower bin edges), satisfies tau* - 1/B < tau_h <= tau*
+//      (Proposition 1). The same pass marks the 32-key sub-blocks that hold a score at
+//      most two bins below the running window (every score that can exceed the
+//      bracket's lower end lies in one of them) and records each marked sub-block's
+//      largest score per 32-row chunk.
+//   2. k_refine_out -- refinement passes: a safeguarded hybrid root solver on
+//      f(tau) = sum_j [x_j - tau]_+^kappa - 1 from tau_h with bracket [tau_h, tau_h + 1/B]:
+//      Halley (alpha <= 1.5), Newton (1.5 < alpha <= 2), secant (alpha > 2, started by
+//      false position on the bracket ends), bisection whenever a step leaves the bracket
+//      (page 1 section 2.2, page 3 section 2.2). Each pass visits only the marked
+//      sub-blocks whose recorded maximum exceeds the evaluation point. Then the output
+//      pass: p = [x - tau]_+^kappa, o = P V, o~ = G V / sum G with g = [x - tau]_+^(kappa-1),
+//      and the exact block mask (bit-packed, 32 blocks per word; page 1 section 2.3).
 //
-// Work decomposition (MI355X): a work group is 4 waves over up to 256 query rows that
-// share one KV head (GQA heads of a group, or consecutive row blocks of one head), so
-// the streamed K blocks are shared through L1/L2; each wave owns QW = 32*QC rows.
-// Scores are computed transposed (keys x queries) on 32x32 MFMA tiles so that a lane
-// owns one query (two lanes per query, 16 keys each per tile): the histogram state of a
-// query is private to its lane (its own LDS column, no atomic contention), and P and G
-// come out already in the B-operand layout of the PV product (V is read from its
-// permuted transpose).
+// MI355X decomposition. Scores are computed transposed (keys x queries) on 32x32 MFMA
+// tiles so that a lane owns one query (two lanes per query, 16 keys each per tile): the
+// histogram of a query is private to its lane (its own LDS column, no contention), and
+// P and G come out already in the B-operand layout of the PV product. K and V are read
+// from fragment-major copies, so each operand load of a wave is one contiguous run.
+// The histogram kernel streams K for 256 query rows that share one KV head (8 waves) and
+// keeps its register count low enough for four waves per SIMD, so one wave's MFMA latency
+// hides under the others' VALU work; the refinement/output kernel has a data-dependent
+// cost per wave and runs in small work groups of 4 waves for balance.
+#include <cmath>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -109,417 +112,470 @@ __device__ float tau_from_counts(const int (&cnt)[16], int T, int B, float kappa
 
 }  // namespace
 
-template <typename T, int D, int QC, int MODE>
-__global__ __launch_bounds__(256, 1) void k_fwd(FwdParams p) {
-  constexpr int DS = D / 16;   // contraction chunks over the head dimension
-  constexpr int DC = D / 32;   // 32-wide output chunks of the head dimension
-  constexpr int QW = 32 * QC;
-  extern __shared__ uint32_t lds[];
+constexpr int HIST_WAVES = 8;
+constexpr int OUT_WAVES = 4;
 
+template <typename T, int D>
+struct KvOps {
+  static constexpr int DS = D / 16;
+  static constexpr int DC = D / 32;
+  // K fragments of sub-block kb (A operand: lane c is key 32 kb + c)
+  __device__ __forceinline__ static void load_k(Frag<T> (&f)[DS], const T* Kf, int kb, int c, int h) {
+#pragma unroll
+    for (int s = 0; s < DS; ++s) load_frag(f[s], Kf + ((size_t)((kb * DS + s) * 2 + h) * 32 + c) * 8);
+  }
+  // S^T tile (keys x queries); keys after the query (causal) become -inf
+  __device__ __forceinline__ static f32x16 scores(const Frag<T> (&kc)[DS], const Frag<T> (&qf)[DS], int kb,
+                                                  int row0, int qrow, int h, bool causal) {
+    f32x16 acc = f32x16{};
+#pragma unroll
+    for (int s = 0; s < DS; ++s) mma16(acc, kc[s], qf[s]);
+    if (causal && kb * 32 + 31 > row0) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (kb * 32 + acc_row(r, h) > qrow) acc[r] = -INFINITY;
+    }
+    return acc;
+  }
+};
+
+// ================================================================================ k_hist
+template <typename T, int D, int MODE, bool QS>
+__global__ __launch_bounds__(512) void k_hist(FwdParams p) {
+  using Ops = KvOps<T, D>;
+  constexpr int DS = Ops::DS;
+  extern __shared__ uint32_t lds[];
   int unit, rank;
   if (!wgmap_get(p.map, blockIdx.x, unit, rank)) return;   // whole work group
 
-  const int lane = lane_id(), c = lane & 31, h = lane >> 5, w = wave_id();
-  const int nsub = p.G / p.GP;                 // head subgroups per KV head
+  const int lane = lane_id(), c = lane & 31, h = lane >> 5;
+  const int w = uniform_i32(wave_id());
+  const int nsub = p.G / p.GP;
   const int bi = unit / p.hkv, kvh = unit % p.hkv;
   const int rg = p.causal ? (p.RG - 1 - rank / nsub) : (rank / nsub);
   const int gsub = rank % nsub;
-  const int per = 4 / p.GP;                    // waves per head
+  const int per = HIST_WAVES / p.GP;           // waves per head
   const int head = kvh * p.G + gsub * p.GP + w / per;
-  const int row0 = rg * p.RH + (w % per) * QW;
-  const int n = p.n, B = p.B;
+  const int row0 = rg * p.RH + (w % per) * 32; // this wave's 32 rows
+  const int n = p.n, B = p.B, R2 = 2 * B;      // histogram ring of 2B cells per lane
+  const bool valid_rows = row0 < n;
+  const int qrow = row0 + c;
+  const size_t bh = (size_t)(bi * p.hq + head);
 
-  const T* Q = reinterpret_cast<const T*>(p.q) + ((size_t)(bi * p.hq + head) * n) * D;
-  const T* K = reinterpret_cast<const T*>(p.k) + ((size_t)(bi * p.hkv + kvh) * n) * D;
-  const T* Vt = reinterpret_cast<const T*>(p.vt) + ((size_t)(bi * p.hkv + kvh) * D) * n;
+  const T* Q = reinterpret_cast<const T*>(p.q) + bh * n * D;
+  const T* Kf = reinterpret_cast<const T*>(p.kf) + ((size_t)(bi * p.hkv + kvh) * n) * D;
+  uint32_t* hist = lds + (w * R2) * 64;        // [2B][64] of this wave
+  uint32_t* discard = lds + (HIST_WAVES * R2) * 64;
+  for (int i = lane; i < R2 * 64; i += 64) hist[i] = 0;
+  float* dmx = p.dmax + (bh * p.nkb + (row0 >> 5)) * p.nkb;
+  uint32_t* cw_out = p.cand + (bh * p.nkb + (row0 >> 5)) * p.NW32;
 
-  uint32_t* hist = lds + (w * QC * B) * 64;                   // [QC][B][64]
-  uint32_t* cand = lds + 4 * QC * B * 64 + w * p.NW32;        // [NW32]
-  uint32_t* exact = lds + 4 * QC * B * 64 + 4 * p.NW32 + w * QC * p.NW32;  // [QC][NW32]
-
-  for (int i = lane; i < QC * B * 64; i += 64) hist[i] = 0;
-  for (int i = lane; i < p.NW32; i += 64) cand[i] = 0;
-  for (int i = lane; i < QC * p.NW32; i += 64) exact[i] = 0;
-
-  bool cvalid[QC];
-#pragma unroll
-  for (int qc = 0; qc < QC; ++qc) cvalid[qc] = (row0 + 32 * qc) < n;
-  const int row_end = min(row0 + QW, n);        // rows of this wave: [row0, row_end)
-  const int kb_end = (row0 >= n) ? 0 : (p.causal ? min(p.nkb, (row_end - 1) / 32 + 1) : p.nkb);
-
-  // Q fragments (B operand of S^T = K Q^T): lane (c, h) holds row row0+32qc+c, d = 16s+8h..+7
-  Frag<T> qf[QC][DS];
-#pragma unroll
-  for (int qc = 0; qc < QC; ++qc)
-#pragma unroll
-    for (int s = 0; s < DS; ++s) {
-      if (cvalid[qc]) load_frag(qf[qc][s], Q + (size_t)(row0 + 32 * qc + c) * D + 16 * s + 8 * h);
-      else zero_frag(qf[qc][s]);
+  // clear the block-mask words of this work group's tiles (k_refine_out ORs bits in)
+  {
+    const int tiles_per_head = p.RH / p.Br;
+    const int total = p.GP * tiles_per_head * p.W;
+    for (int idx = threadIdx.x; idx < total; idx += blockDim.x) {
+      const int wi = idx % p.W, t = (idx / p.W) % tiles_per_head, hs = idx / (p.W * tiles_per_head);
+      const int trow0 = rg * p.RH + t * p.Br;
+      if (trow0 >= n) continue;
+      const int hg = kvh * p.G + gsub * p.GP + hs;
+      p.mask[((size_t)(bi * p.hq + hg) * p.Tr + trow0 / p.Br) * p.W + wi] = 0u;
     }
-
-  const float cx = p.cx;
-  const float cB = cx * (float)B;              // x * B = cB * s exactly (B is a power of two)
-
-  // ---------------------------------------------------------------- 1. histogram pass
-  float mB[QC];     // running max of x*B over this lane's scores
-  int Tt[QC];       // floor(mB): top cell of the window
-  bool have[QC];
-#pragma unroll
-  for (int qc = 0; qc < QC; ++qc) {
-    mB[qc] = -INFINITY;
-    Tt[qc] = 0;
-    have[qc] = false;
   }
+  if (!valid_rows) return;                     // no barrier follows: the wave may leave
+  const int kb_end = p.causal ? min(p.nkb, (row0 + 31) / 32 + 1) : p.nkb;
+
+  Frag<T> qf[DS];
+#pragma unroll
+  for (int s = 0; s < DS; ++s) load_frag(qf[s], Q + (size_t)qrow * D + 16 * s + 8 * h);
+  // x * B = cB * s exactly (B is a power of two). When cB is itself a power of two it is
+  // folded into Q (exact scaling), and the score tile is x * B directly.
+  const float cB = QS ? 1.0f : p.cx * (float)B;
+  if constexpr (QS) {
+    const float qsc = p.cx * (float)B;
+#pragma unroll
+    for (int s = 0; s < DS; ++s) scale_frag(qf[s], qsc);
+  }
+
+  // Two sub-blocks per step: both tiles update the running max first, then all their
+  // scores are counted against the updated window. This is exact: a score that would
+  // have been counted under the older window but lies below the newer one is exactly a
+  // score the window slide would drop later.
+  float mB = -INFINITY;   // running max of x*B over this lane's scores
+  int Tt = 0;             // its cell floor(mB): top of the lane's window
+  bool have = false;
   uint32_t cword = 0;
-  unsigned long long n_sweep = 0;
+  float dreg = -INFINITY; // lane j < 32 keeps the chunk max of sub-block 32*word + j
+  unsigned long long n_cand = 0;
 
-  Frag<T> kf[DS];
-  if (kb_end > 0) {
+  Frag<T> kf[DS], kf2[DS];
+  Ops::load_k(kf, Kf, 0, c, h);
+  if (kb_end > 1) Ops::load_k(kf2, Kf, 1, c, h);
+  for (int kb = 0; kb < kb_end; kb += 2) {
+    const bool two = kb + 1 < kb_end;
+    const f32x16 acc0 = Ops::scores(kf, qf, kb, row0, qrow, h, p.causal);
+    f32x16 acc1;
+    if (two) {
+      acc1 = Ops::scores(kf2, qf, kb + 1, row0, qrow, h, p.causal);
+    } else {
 #pragma unroll
-    for (int s = 0; s < DS; ++s) load_frag(kf[s], K + (size_t)(c) * D + 16 * s + 8 * h);
-  }
-  for (int kb = 0; kb < kb_end; ++kb) {
-    Frag<T> kc[DS];
-#pragma unroll
-    for (int s = 0; s < DS; ++s) kc[s] = kf[s];
-    if (kb + 1 < kb_end) {
-#pragma unroll
-      for (int s = 0; s < DS; ++s) load_frag(kf[s], K + (size_t)((kb + 1) * 32 + c) * D + 16 * s + 8 * h);
+      for (int r = 0; r < 16; ++r) acc1[r] = -INFINITY;
     }
-    f32x16 acc[QC];
-#pragma unroll
-    for (int qc = 0; qc < QC; ++qc) {
-      acc[qc] = f32x16{};
-#pragma unroll
-      for (int s = 0; s < DS; ++s) mma16(acc[qc], kc[s], qf[qc][s]);
-    }
-    bool act[QC];
-    float tmB[QC];
-#pragma unroll
-    for (int qc = 0; qc < QC; ++qc) {
-      act[qc] = false;
-      tmB[qc] = -INFINITY;
-      if (!cvalid[qc]) continue;
-      const int qrow = row0 + 32 * qc + c;
-      if (p.causal && kb * 32 + 31 > row0 + 32 * qc) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (kb * 32 + acc_row(r, h) > qrow) acc[qc][r] = -INFINITY;
+    if (kb + 2 < kb_end) Ops::load_k(kf, Kf, kb + 2, c, h);
+    if (kb + 3 < kb_end) Ops::load_k(kf2, Kf, kb + 3, c, h);
+    const float t0 = QS ? max16(acc0) : cB * max16(acc0);
+    const float t1 = QS ? max16(acc1) : cB * max16(acc1);
+    const float nmB = fmaxf(mB, fmaxf(t0, t1));
+    const bool fin = nmB > -INFINITY;
+    const int Tn = fin ? cvt_floor(nmB) : Tt;
+    // a tile is active for a lane when one of its scores lies at most two bins below
+    // the lane's window
+    const float thrB = (float)(Tn - B - 1);
+    const bool act0 = fin && t0 >= thrB;
+    const bool act1 = fin && t1 >= thrB;
+    const uint64_t b0 = ballot(act0), b1 = ballot(act1);
+    if ((b0 | b1) != 0) {
+      if (b0) {
+        const float cm = wave_max_dpp(t0);     // largest x*B of the 32 rows in this sub-block
+        if (lane == (kb & 31)) dreg = cm;
+        cword |= 1u << (kb & 31);
+        ++n_cand;
       }
-      tmB[qc] = cB * max16(acc[qc]);
-      const float nmB = fmaxf(mB[qc], tmB[qc]);
-      if (nmB > -INFINITY) {
-        const int Tn = (int)floorf(nmB);
-        act[qc] = tmB[qc] >= (float)(Tn - B - 1);
+      if (b1) {
+        const float cm = wave_max_dpp(t1);
+        if (lane == ((kb + 1) & 31)) dreg = cm;
+        cword |= 1u << ((kb + 1) & 31);
+        ++n_cand;
       }
-    }
-    bool anyact = false;
+      const bool act = act0 || act1;
+      // slide the window up: clear the cells of the bins that enter it (top first)
+      const int nz = (have && act) ? min(Tn - Tt, B) : 0;
+      for (int z = 0; ballot(z < nz) != 0; ++z)
+        if (z < nz) hist[((Tn - z) & (R2 - 1)) * 64 + lane] = 0;
+      if (act) {
+        mB = nmB;
+        Tt = Tn;
+        have = true;
+      }
+      // count every score: cells of bins more than B below the window fold into the
+      // cell of bin Tt + 1 (outside the window; cleared when the window reaches it);
+      // lanes with no active tile count into a discard column
+      const int lowm = Tt - R2 + 1;
+      uint32_t* basep = act ? (hist + lane) : (discard + lane);
 #pragma unroll
-    for (int qc = 0; qc < QC; ++qc) anyact = anyact || act[qc];
-    if (ballot(anyact) != 0) {
-      cword |= 1u << (kb & 31);
-      ++n_sweep;
+      for (int r = 0; r < 16; ++r) {
+        const int ta = max(cvt_floor(QS ? acc0[r] : cB * acc0[r]), lowm);
+        atomicAdd(basep + ((ta & (R2 - 1)) << 6), 1u);
+      }
+      if (two) {
 #pragma unroll
-      for (int qc = 0; qc < QC; ++qc) {
-        if (!cvalid[qc]) continue;
-        const float nmB = fmaxf(mB[qc], tmB[qc]);
-        const int Tn = act[qc] ? (int)floorf(nmB) : Tt[qc];
-        // slide the window up: clear the cells of bins Tt+1 .. Tn (they reuse dropped slots)
-        const int nz = (have[qc] && act[qc]) ? min(Tn - Tt[qc], B) : 0;
-        uint32_t* col = hist + (qc * B) * 64 + lane;
-        for (int z = 0; ballot(z < nz) != 0; ++z)
-          if (z < nz) col[((Tt[qc] + 1 + z) & (B - 1)) * 64] = 0;
-        if (act[qc]) {
-          mB[qc] = nmB;
-          Tt[qc] = Tn;
-          have[qc] = true;
-          const float low = (float)(Tn - B + 1);
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float xb = cB * acc[qc][r];
-            if (xb >= low) {
-              const int t = (int)floorf(xb);
-              atomicAdd(&col[(t & (B - 1)) * 64], 1u);
-            }
-          }
+        for (int r = 0; r < 16; ++r) {
+          const int tb = max(cvt_floor(QS ? acc1[r] : cB * acc1[r]), lowm);
+          atomicAdd(basep + ((tb & (R2 - 1)) << 6), 1u);
         }
       }
     }
-    if ((kb & 31) == 31 || kb == kb_end - 1) {
-      if (lane == 0) cand[kb >> 5] = cword;
+    // flush a finished word of sub-block bits and chunk maxima (kb is even: a word ends
+    // at kb + 1 == 31 mod 32, or at the last sub-block)
+    const int klast = two ? kb + 1 : kb;
+    if ((klast & 31) == 31 || klast == kb_end - 1) {
+      if (lane == 0) cw_out[klast >> 5] = cword;
+      const int wbase = klast & ~31;
+      if (lane < 32 && wbase + lane <= klast) dmx[wbase + lane] = dreg;
       cword = 0;
+      dreg = -INFINITY;
     }
   }
 
   // merge the two half-wave histograms of each query and solve the B-bin problem
-  float tau[QC], lo[QC], hi[QC];
+  const int To = xor32i(Tt);
+  const bool ho = xor32i(have ? 1 : 0) != 0;
+  const int Tf = (have && ho) ? max(Tt, To) : (have ? Tt : To);
+  int cnt[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    int mine = 0;
+    if (k < B) {
+      const int bin = Tf - B + 1 + k;
+      if (have && bin >= Tt - B + 1 && bin <= Tt) mine = (int)hist[(bin & (R2 - 1)) * 64 + lane];
+    }
+    cnt[k] = mine + xor32i(mine);
+  }
+  const float tau_h = tau_from_counts<MODE>(cnt, Tf, B, p.kappa);
+  if (h == 0) {
+    const size_t row = bh * n + qrow;
+    p.tauh_ws[row] = tau_h;
+    if (p.tau_h) p.tau_h[row] = tau_h;
+    if (p.hist) {
+      int32_t* dst = p.hist + row * B;
+      for (int k = 0; k < 16; ++k)
+        if (k < B) dst[k] = cnt[k];
+    }
+  }
+  if (p.stats && lane == 0) {
+    atomicAdd(&p.stats[20], (unsigned long long)kb_end);
+    atomicAdd(&p.stats[23], n_cand);
+  }
+}
+
+// ================================================================================ k_refine_out
+template <typename T, int D, int MODE>
+__global__ __launch_bounds__(256) void k_refine_out(FwdParams p) {
+  using Ops = KvOps<T, D>;
+  constexpr int DS = Ops::DS, DC = Ops::DC;
+  int unit, rank;
+  if (!wgmap_get(p.map2, blockIdx.x, unit, rank)) return;
+  const int lane = lane_id(), c = lane & 31, h = lane >> 5;
+  const int w = uniform_i32(wave_id());
+  const int bi = unit / p.hkv, kvh = unit % p.hkv;
+  const int RG2 = (p.nkb + OUT_WAVES - 1) / OUT_WAVES;   // groups of 4 chunks per head
+  const int grp = p.causal ? (RG2 - 1 - rank / p.G) : (rank / p.G);
+  const int head = kvh * p.G + rank % p.G;
+  const int row0 = (grp * OUT_WAVES + w) * 32;
+  const int n = p.n, B = p.B;
+  if (row0 >= n) return;
+  const int qrow = row0 + c;
+  const size_t bh = (size_t)(bi * p.hq + head);
+  const int kb_end = p.causal ? min(p.nkb, (row0 + 31) / 32 + 1) : p.nkb;
+  const int nwords = (kb_end + 31) >> 5;
+
+  const T* Q = reinterpret_cast<const T*>(p.q) + bh * n * D;
+  const T* Kf = reinterpret_cast<const T*>(p.kf) + ((size_t)(bi * p.hkv + kvh) * n) * D;
+  const T* Vf = reinterpret_cast<const T*>(p.vf) + ((size_t)(bi * p.hkv + kvh) * n) * D;
+  const float* dmx = p.dmax + (bh * p.nkb + (row0 >> 5)) * p.nkb;
+  const uint32_t* cwords = p.cand + (bh * p.nkb + (row0 >> 5)) * p.NW32;
+
+  Frag<T> qf[DS];
+#pragma unroll
+  for (int s = 0; s < DS; ++s) load_frag(qf[s], Q + (size_t)qrow * D + 16 * s + 8 * h);
+  const float cx = p.cx;
+  float tau = p.tauh_ws[bh * n + qrow];
   const float hB = 1.0f / (float)B;
-#pragma unroll
-  for (int qc = 0; qc < QC; ++qc) {
-    const int To = xor32i(Tt[qc]);
-    const bool ho = xor32i(have[qc] ? 1 : 0) != 0;
-    const int Tf = (have[qc] && ho) ? max(Tt[qc], To) : (have[qc] ? Tt[qc] : To);
-    int cnt[16];
-    const uint32_t* col = hist + (qc * B) * 64 + lane;
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      int mine = 0;
-      if (k < B) {
-        const int bin = Tf - B + 1 + k;
-        if (have[qc] && bin >= Tt[qc] - B + 1 && bin <= Tt[qc]) mine = (int)col[(bin & (B - 1)) * 64];
-      }
-      cnt[k] = mine + xor32i(mine);
-    }
-    tau[qc] = tau_from_counts<MODE>(cnt, Tf, B, p.kappa);
-    lo[qc] = tau[qc];
-    hi[qc] = tau[qc] + hB;
-    if (cvalid[qc] && h == 0) {
-      const size_t row = (size_t)(bi * p.hq + head) * n + row0 + 32 * qc + c;
-      if (p.tau_h) p.tau_h[row] = tau[qc];
-      if (p.hist) {
-        int32_t* dst = p.hist + row * B;
-        for (int k = 0; k < 16; ++k)
-          if (k < B) dst[k] = cnt[k];
-      }
-    }
-  }
+  float lo = tau, hi = tau + hB;
 
-  // ---------------------------------------------------------------- 2. refinement passes
-  // candidate sub-block iterator over this wave's bits (wave-uniform)
-  auto next_cand = [&](int from) -> int {
-    int wi = from >> 5;
-    if (wi >= p.NW32) return -1;
-    uint32_t word = uniform_u32(cand[wi]) & (~0u << (from & 31));
-    while (word == 0) {
-      if (++wi >= p.NW32) return -1;
-      word = uniform_u32(cand[wi]);
-    }
-    return (wi << 5) + __builtin_ctz(word);
+  // Walk over the sub-blocks a pass needs: candidate bits of the histogram pass, kept
+  // where the chunk max (read 32 sub-blocks at a time) exceeds the threshold.
+  struct Walk {
+    int wi;
+    uint32_t word;
   };
-  int ncand = 0;
-  for (int i = 0; i < p.NW32; ++i) ncand += __builtin_popcount(uniform_u32(cand[i]));
+  auto needed_word = [&](int wi, float thr) -> uint32_t {
+    const uint32_t cw = uniform_u32(cwords[wi]);
+    if (cw == 0) return 0u;
+    const int kbl = wi * 32 + (lane & 31);
+    const float dv = (kbl < kb_end) ? dmx[kbl] : -INFINITY;
+    return cw & (uint32_t)ballot(dv > thr);
+  };
+  auto walk_next = [&](Walk& wk, float thr) -> int {
+    while (wk.word == 0) {
+      if (++wk.wi >= nwords) return -1;
+      wk.word = needed_word(wk.wi, thr);
+    }
+    const int kb = wk.wi * 32 + __builtin_ctz(wk.word);
+    wk.word &= wk.word - 1;
+    return kb;
+  };
 
+  // ---------------------------------------------------------------- refinement passes
   const float kappa = p.kappa, alpha = p.alpha;
-  bool done[QC];
-  int rowpass[QC];
-  float tprev[QC], fprev[QC];
-#pragma unroll
-  for (int qc = 0; qc < QC; ++qc) {
-    done[qc] = !cvalid[qc];
-    rowpass[qc] = 0;
-    tprev[qc] = 0.f;
-    fprev[qc] = 0.f;
-  }
+  bool done = false;
+  int rowpass = 0;
+  float tprev = 0.f, fprev = 0.f;
   const bool secant = alpha > 2.0f;
   int npass = 0;
+  unsigned long long n_ref = 0;
+  Frag<T> kf[DS];
   while (npass < p.max_iters) {
-    bool pending = false;
-#pragma unroll
-    for (int qc = 0; qc < QC; ++qc) pending = pending || !done[qc];
-    if (ballot(pending) == 0) break;
+    if (ballot(!done) == 0) break;
     const bool first = (npass == 0);
-    float F0[QC], F1[QC], F2[QC], Fh[QC];
-#pragma unroll
-    for (int qc = 0; qc < QC; ++qc) F0[qc] = F1[qc] = F2[qc] = Fh[qc] = 0.f;
-    int kb = next_cand(0);
-    if (kb >= 0) {
-#pragma unroll
-      for (int s = 0; s < DS; ++s) load_frag(kf[s], K + (size_t)(kb * 32 + c) * D + 16 * s + 8 * h);
-    }
+    const float thr = wave_min(done ? INFINITY : tau) * (float)B;
+    float F0 = 0.f, F1 = 0.f, F2 = 0.f, Fh = 0.f, mrel = INFINITY;
+    Walk wk{-1, 0u};
+    int kb = walk_next(wk, thr);
+    if (kb >= 0) Ops::load_k(kf, Kf, kb, c, h);
     while (kb >= 0) {
       Frag<T> kc[DS];
 #pragma unroll
       for (int s = 0; s < DS; ++s) kc[s] = kf[s];
-      const int kn = next_cand(kb + 1);
-      if (kn >= 0) {
+      const int kn = walk_next(wk, thr);
+      if (kn >= 0) Ops::load_k(kf, Kf, kn, c, h);
+      ++n_ref;
+      const f32x16 acc = Ops::scores(kc, qf, kb, row0, qrow, h, p.causal);
+      const float th = hi;
 #pragma unroll
-        for (int s = 0; s < DS; ++s) load_frag(kf[s], K + (size_t)(kn * 32 + c) * D + 16 * s + 8 * h);
-      }
-#pragma unroll
-      for (int qc = 0; qc < QC; ++qc) {
-        if (!cvalid[qc]) continue;
-        f32x16 acc = f32x16{};
-#pragma unroll
-        for (int s = 0; s < DS; ++s) mma16(acc, kc[s], qf[qc][s]);
-        const int qrow = row0 + 32 * qc + c;
-        const bool diag = p.causal && kb * 32 + 31 > row0 + 32 * qc;
-        const float tq = tau[qc], th = hi[qc];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const bool valid = !diag || (kb * 32 + acc_row(r, h) <= qrow);
-          const float x = cx * acc[r];
-          const float t = valid ? (x - tq) : -1.0f;
-          if (t > 0.f) {
-            if constexpr (MODE == 2) {
-              F0[qc] += t * t;
-              F1[qc] += t;
-              F2[qc] += 1.0f;
-            } else if constexpr (MODE == 1) {
-              F0[qc] += t;
-              F1[qc] += 1.0f;
-            } else {
-              const float lt = log2f(t);
-              F0[qc] += exp2f(kappa * lt);
-              F1[qc] += exp2f((kappa - 1.0f) * lt);
-              F2[qc] += exp2f((kappa - 2.0f) * lt);
-            }
-          }
-          if constexpr (MODE == 0) {
-            if (secant && first) {
-              const float u = valid ? (x - th) : -1.0f;
-              if (u > 0.f) Fh[qc] += exp2f(kappa * log2f(u));
-            }
+      for (int r = 0; r < 16; ++r) {
+        const float t = cx * acc[r] - tau;           // -inf for masked keys
+        const bool in = t > 0.f;
+        const float dm = in ? t : 0.f;
+        if constexpr (MODE == 2) {
+          F0 += dm * dm;
+          F1 += dm;
+          F2 += in ? 1.0f : 0.0f;
+        } else if constexpr (MODE == 1) {
+          F0 += dm;
+          F1 += in ? 1.0f : 0.0f;
+        } else {
+          const float lt = log2f(dm);
+          F0 += in ? exp2f(kappa * lt) : 0.f;
+          F1 += in ? exp2f((kappa - 1.0f) * lt) : 0.f;
+          F2 += in ? exp2f((kappa - 2.0f) * lt) : 0.f;
+          if (secant && first) {
+            const float u = cx * acc[r] - th;
+            if (u > 0.f) Fh += exp2f(kappa * log2f(u));
           }
         }
+        if constexpr (MODE != 0) mrel = fminf(mrel, in ? t : INFINITY);
       }
       kb = kn;
     }
     ++npass;
-#pragma unroll
-    for (int qc = 0; qc < QC; ++qc) {
-      F0[qc] += xor32f(F0[qc]);
-      F1[qc] += xor32f(F1[qc]);
-      F2[qc] += xor32f(F2[qc]);
-      Fh[qc] += xor32f(Fh[qc]);
-      if (done[qc]) continue;
-      const float f = F0[qc] - 1.0f;
-      const float t0 = tau[qc];
-      if (f >= 0.f) lo[qc] = t0; else hi[qc] = t0;
-      if (first && f < 0.f) lo[qc] = t0 - hB;   // rounding lost the histogram bound
-      float tn;
-      if (alpha <= 1.5f) {
-        const float fp = -kappa * F1[qc];
-        const float fpp = kappa * (kappa - 1.0f) * F2[qc];
-        tn = t0 - 2.0f * f * fp / (2.0f * fp * fp - f * fpp);
-      } else if (alpha <= 2.0f) {
-        const float fp = -kappa * F1[qc];
-        tn = t0 - f / fp;
+    F0 += xor32f(F0);
+    F1 += xor32f(F1);
+    F2 += xor32f(F2);
+    Fh += xor32f(Fh);
+    mrel = fminf(mrel, xor32f(mrel));
+    if (!done) {
+      const float f = F0 - 1.0f;
+      const float t0 = tau;
+      if (f >= 0.f) lo = t0; else hi = t0;
+      if (first && f < 0.f) lo = t0 - hB;   // rounding lost the histogram bound
+      bool fin_row = false;
+      // alpha in {1.5, 2}: the root of the equation restricted to the support {x > t0}
+      // is exact when it keeps that support (it lies at or above t0 and at or below the
+      // support's smallest score): then stop without a confirming pass.
+      if constexpr (MODE == 1 || MODE == 2) {
+        const float cntS = (MODE == 2) ? F2 : F1;
+        if (cntS > 0.f && f >= 0.f) {
+          float u;
+          if constexpr (MODE == 2) {
+            const float disc = F1 * F1 - cntS * f;
+            u = disc >= 0.f ? f / (F1 + sqrtf(disc)) : INFINITY;
+          } else {
+            u = f / cntS;
+          }
+          if (u <= mrel) {
+            tau = t0 + u;
+            fin_row = true;
+          }
+        }
+      }
+      if (fin_row) {
+        done = true;
+        rowpass = npass;
       } else {
-        if (first) {
-          const float th = t0 + hB;
-          const float fh = Fh[qc] - 1.0f;
-          if (fh >= 0.f) lo[qc] = th; else hi[qc] = fminf(hi[qc], th);
-          tn = t0 - f * (th - t0) / (fh - f);
+        float tn;
+        if (alpha <= 1.5f) {
+          const float fp = -kappa * F1;
+          const float fpp = kappa * (kappa - 1.0f) * F2;
+          tn = t0 - 2.0f * f * fp / (2.0f * fp * fp - f * fpp);
+        } else if (alpha <= 2.0f) {
+          const float fp = -kappa * F1;
+          tn = t0 - f / fp;
         } else {
-          tn = t0 - f * (t0 - tprev[qc]) / (f - fprev[qc]);
+          if (first) {
+            const float th = t0 + hB;
+            const float fh = Fh - 1.0f;
+            if (fh >= 0.f) lo = th; else hi = fminf(hi, th);
+            tn = t0 - f * (th - t0) / (fh - f);
+          } else {
+            tn = t0 - f * (t0 - tprev) / (f - fprev);
+          }
+          tprev = t0;
+          fprev = f;
         }
-        tprev[qc] = t0;
-        fprev[qc] = f;
-      }
-      // converged when the solver's own step is below tolerance (tested before the
-      // bracket check: a vanishing step lands on a bracket end and must not be
-      // replaced by a bisection jump); otherwise keep the step inside (lo, hi)
-      const float tabs = p.tol * fmaxf(1.0f, fabsf(t0));
-      if (fabsf(tn - t0) <= tabs) {
-        done[qc] = true;
-        rowpass[qc] = npass;
-        tn = fminf(fmaxf(tn, lo[qc]), hi[qc]);
-      } else {
-        if (!(tn > lo[qc] && tn < hi[qc])) tn = 0.5f * (lo[qc] + hi[qc]);
-        if (hi[qc] - lo[qc] <= tabs) {
-          done[qc] = true;
-          rowpass[qc] = npass;
+        // converged when the solver's own step is below tolerance (tested before the
+        // bracket check: a vanishing step lands on a bracket end and must not be
+        // replaced by a bisection jump); otherwise keep the step inside (lo, hi)
+        const float tabs = p.tol * fmaxf(1.0f, fabsf(t0));
+        if (fabsf(tn - t0) <= tabs) {
+          done = true;
+          rowpass = npass;
+          tn = fminf(fmaxf(tn, lo), hi);
+        } else {
+          if (!(tn > lo && tn < hi)) tn = 0.5f * (lo + hi);
+          if (hi - lo <= tabs) {
+            done = true;
+            rowpass = npass;
+          }
         }
+        tau = tn;
       }
-      tau[qc] = tn;
     }
   }
 
-  // ---------------------------------------------------------------- 3. output pass
-  f32x16 oacc[QC][DC], gacc[QC][DC];
-  float sg[QC];
+  // ---------------------------------------------------------------- output pass
+  f32x16 oacc[DC], gacc[DC];
 #pragma unroll
-  for (int qc = 0; qc < QC; ++qc) {
-    sg[qc] = 0.f;
-#pragma unroll
-    for (int dc = 0; dc < DC; ++dc) {
-      oacc[qc][dc] = f32x16{};
-      gacc[qc][dc] = f32x16{};
-    }
+  for (int dc = 0; dc < DC; ++dc) {
+    oacc[dc] = f32x16{};
+    gacc[dc] = f32x16{};
   }
+  float sg = 0.f;
+  const float othr = wave_min(tau) * (float)B;
   unsigned long long n_out = 0;
+  // exact mask bits of this wave, OR-ed into the tile's words one word at a time
+  uint32_t* mrow = p.mask + (bh * p.Tr + row0 / p.Br) * p.W;
+  int mw = -1;
+  uint32_t mbits = 0;
   {
-    int kb = next_cand(0);
-    if (kb >= 0) {
-#pragma unroll
-      for (int s = 0; s < DS; ++s) load_frag(kf[s], K + (size_t)(kb * 32 + c) * D + 16 * s + 8 * h);
-    }
+    Walk wk{-1, 0u};
+    int kb = walk_next(wk, othr);
+    if (kb >= 0) Ops::load_k(kf, Kf, kb, c, h);
     while (kb >= 0) {
       Frag<T> kc[DS];
 #pragma unroll
       for (int s = 0; s < DS; ++s) kc[s] = kf[s];
-      const int kn = next_cand(kb + 1);
-      if (kn >= 0) {
+      const int kn = walk_next(wk, othr);
+      if (kn >= 0) Ops::load_k(kf, Kf, kn, c, h);
+      const f32x16 acc = Ops::scores(kc, qf, kb, row0, qrow, h, p.causal);
+      f32x16 pw, gw;
+      bool any = false;
 #pragma unroll
-        for (int s = 0; s < DS; ++s) load_frag(kf[s], K + (size_t)(kn * 32 + c) * D + 16 * s + 8 * h);
+      for (int r = 0; r < 16; ++r) {
+        const float t = cx * acc[r] - tau;
+        const bool in = t > 0.f;
+        const float dm = in ? t : 0.f;
+        pw[r] = Weight<MODE>::p(dm, kappa);
+        gw[r] = Weight<MODE>::g(dm, kappa);
+        sg += gw[r];
+        any = any || in;
       }
-      f32x16 pacc[QC], gw[QC];
-      bool nzq[QC];
-      bool anynz = false;
-#pragma unroll
-      for (int qc = 0; qc < QC; ++qc) {
-        nzq[qc] = false;
-        pacc[qc] = f32x16{};
-        gw[qc] = f32x16{};
-        if (!cvalid[qc]) continue;
-        f32x16 acc = f32x16{};
-#pragma unroll
-        for (int s = 0; s < DS; ++s) mma16(acc, kc[s], qf[qc][s]);
-        const int qrow = row0 + 32 * qc + c;
-        const bool diag = p.causal && kb * 32 + 31 > row0 + 32 * qc;
-        const float tq = tau[qc];
-        bool any = false;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const bool valid = !diag || (kb * 32 + acc_row(r, h) <= qrow);
-          const float t = valid ? (cx * acc[r] - tq) : -1.0f;
-          const float dm = fmaxf(t, 0.f);
-          pacc[qc][r] = Weight<MODE>::p(dm, kappa);
-          gw[qc][r] = Weight<MODE>::g(t > 0.f ? dm : 0.f, kappa);
-          sg[qc] += gw[qc][r];
-          any = any || (t > 0.f);
-        }
-        nzq[qc] = ballot(any) != 0;
-        anynz = anynz || nzq[qc];
-      }
-      if (anynz) {
+      if (ballot(any) != 0) {
         ++n_out;
-#pragma unroll
-        for (int qc = 0; qc < QC; ++qc)
-          if (nzq[qc] && lane == 0) exact[qc * p.NW32 + (kb >> 5)] |= 1u << (kb & 31);
+        const int J = (kb * 32) / p.Bc;          // key block of this sub-block
+        if ((J >> 5) != mw) {
+          if (mw >= 0 && lane == 0) atomicOr(mrow + mw, mbits);
+          mw = J >> 5;
+          mbits = 0;
+        }
+        mbits |= 1u << (J & 31);
         Frag<T> vf[DC][2];
 #pragma unroll
         for (int dc = 0; dc < DC; ++dc)
 #pragma unroll
           for (int m = 0; m < 2; ++m)
-            load_frag(vf[dc][m], Vt + (size_t)(32 * dc + c) * n + kb * 32 + 16 * m + 8 * h);
+            load_frag(vf[dc][m], Vf + ((size_t)(((kb * DC + dc) * 2 + m) * 2 + h) * 32 + c) * 8);
 #pragma unroll
-        for (int qc = 0; qc < QC; ++qc) {
-          if (!nzq[qc]) continue;
+        for (int m = 0; m < 2; ++m) {
+          Frag<T> pf, gf;
+          acc_frag(pf, pw, m);
+          acc_frag(gf, gw, m);
 #pragma unroll
-          for (int m = 0; m < 2; ++m) {
-            Frag<T> pf, gf;
-            acc_frag(pf, pacc[qc], m);
-            acc_frag(gf, gw[qc], m);
-#pragma unroll
-            for (int dc = 0; dc < DC; ++dc) {
-              mma16(oacc[qc][dc], vf[dc][m], pf);
-              mma16(gacc[qc][dc], vf[dc][m], gf);
-            }
+          for (int dc = 0; dc < DC; ++dc) {
+            mma16(oacc[dc], vf[dc][m], pf);
+            mma16(gacc[dc], vf[dc][m], gf);
           }
         }
       }
       kb = kn;
     }
   }
+  if (mw >= 0 && lane == 0) atomicOr(mrow + mw, mbits);
 
-  // ---------------------------------------------------------------- outputs of this wave
-#pragma unroll
-  for (int qc = 0; qc < QC; ++qc) {
-    if (!cvalid[qc]) continue;
-    const float sgt = sg[qc] + xor32f(sg[qc]);
+  {
+    const float sgt = sg + xor32f(sg);
     const float inv = sgt > 0.f ? 1.0f / sgt : 0.f;
-    const size_t row = (size_t)(bi * p.hq + head) * n + row0 + 32 * qc + c;
+    const size_t row = bh * n + qrow;
     float* orow = p.o + row * D;
     float* arow = p.aux + row * D;
 #pragma unroll
@@ -527,87 +583,64 @@ __global__ __launch_bounds__(256, 1) void k_fwd(FwdParams p) {
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const int d0 = 32 * dc + 8 * g4 + 4 * h;
-        const f32x16& oa = oacc[qc][dc];
-        const f32x16& ga = gacc[qc][dc];
+        const f32x16& oa = oacc[dc];
+        const f32x16& ga = gacc[dc];
         store4(orow + d0, oa[4 * g4 + 0], oa[4 * g4 + 1], oa[4 * g4 + 2], oa[4 * g4 + 3]);
         store4(arow + d0, ga[4 * g4 + 0] * inv, ga[4 * g4 + 1] * inv, ga[4 * g4 + 2] * inv,
                ga[4 * g4 + 3] * inv);
       }
-    if (h == 0) p.tau[row] = tau[qc];
+    if (h == 0) p.tau[row] = tau;
   }
   if (p.stats) {
     // rows by refinement passes (rows that hit the cap go to max_iters + 1)
     for (int ps = 1; ps <= p.max_iters + 1; ++ps) {
-      int cntp = 0;
-#pragma unroll
-      for (int qc = 0; qc < QC; ++qc) {
-        const int rp = done[qc] ? rowpass[qc] : p.max_iters + 1;
-        cntp += __popcll(ballot(cvalid[qc] && h == 0 && rp == ps));
-      }
+      const int rp = done ? rowpass : p.max_iters + 1;
+      const int cntp = __popcll(ballot(h == 0 && rp == ps));
       if (lane == 0 && cntp) atomicAdd(&p.stats[ps], (unsigned long long)cntp);
     }
     if (lane == 0) {
-      atomicAdd(&p.stats[20], (unsigned long long)kb_end * QC);
-      atomicAdd(&p.stats[21], (unsigned long long)ncand * npass * QC);
-      atomicAdd(&p.stats[22], n_out * QC);
+      atomicAdd(&p.stats[21], n_ref);
+      atomicAdd(&p.stats[22], n_out);
     }
-  }
-  (void)n_sweep;
-
-  // ---------------------------------------------------------------- block mask of the tiles
-  __syncthreads();
-  const int tiles_per_head = p.RH / p.Br;
-  const int KW = p.Bc / 32;                    // sub-blocks per key block
-  const int QCB = p.Br / 32;                   // 32-row chunks per tile
-  const int total = p.GP * tiles_per_head * p.W;
-  for (int idx = threadIdx.x; idx < total; idx += blockDim.x) {
-    const int wi = idx % p.W;
-    const int t = (idx / p.W) % tiles_per_head;
-    const int hs = idx / (p.W * tiles_per_head);
-    const int trow0 = rg * p.RH + t * p.Br;
-    if (trow0 >= n) continue;
-    uint32_t word = 0;
-    for (int bit = 0; bit < 32; ++bit) {
-      const int J = wi * 32 + bit;
-      if (J >= p.Tc) break;
-      uint32_t any = 0;
-      for (int u = 0; u < KW && !any; ++u) {
-        const int kbi = J * KW + u;
-        if ((kbi >> 5) >= p.NW32) break;
-        for (int ch = 0; ch < QCB && !any; ++ch) {
-          const int chunk = t * QCB + ch;       // 32-row chunk within this head's rows
-          const int ww = hs * per + chunk / QC; // wave holding it
-          const int qq = chunk % QC;
-          const uint32_t* ex = lds + 4 * QC * B * 64 + 4 * p.NW32 + ww * QC * p.NW32 + qq * p.NW32;
-          any |= (ex[kbi >> 5] >> (kbi & 31)) & 1u;
-        }
-      }
-      word |= any << bit;
-    }
-    const int hg = kvh * p.G + gsub * p.GP + hs;
-    const int I = trow0 / p.Br;
-    p.mask[((size_t)(bi * p.hq + hg) * p.Tr + I) * p.W + wi] = word;
   }
 }
 
-template <typename T, int D, int QC>
+template <typename T, int D>
+static void (*hist_kernel(bool qs, int mode))(FwdParams) {
+  if (qs) return mode == 1 ? k_hist<T, D, 1, true> : mode == 2 ? k_hist<T, D, 2, true> : k_hist<T, D, 0, true>;
+  return mode == 1 ? k_hist<T, D, 1, false> : mode == 2 ? k_hist<T, D, 2, false> : k_hist<T, D, 0, false>;
+}
+
+size_t fwd_lds_bytes(int B) { return (size_t)((HIST_WAVES + 1) * 2 * B * 64) * sizeof(uint32_t); }
+
+template <typename T, int D>
 static hipError_t launch_fwd_t(const FwdParams& p, int mode, hipStream_t s) {
-  const size_t lds = (size_t)(4 * QC * p.B * 64 + 4 * p.NW32 + 4 * QC * p.NW32) * sizeof(uint32_t);
+  const size_t lds = fwd_lds_bytes(p.B);
   const int grid = wgmap_grid(p.map);
+  const int grid2 = wgmap_grid(p.map2);
   if (grid == 0) return hipSuccess;
-  if (mode == 1) hipLaunchKernelGGL((k_fwd<T, D, QC, 1>), dim3(grid), dim3(256), lds, s, p);
-  else if (mode == 2) hipLaunchKernelGGL((k_fwd<T, D, QC, 2>), dim3(grid), dim3(256), lds, s, p);
-  else hipLaunchKernelGGL((k_fwd<T, D, QC, 0>), dim3(grid), dim3(256), lds, s, p);
+  // fold the score scale into Q when it is an exact power of two
+  const float cB = p.cx * (float)p.B;
+  int ex = 0;
+  const bool qs = std::frexp(cB, &ex) == 0.5f && ex >= -8 && ex <= 8;
+  void (*hist_fn)(FwdParams) = hist_kernel<T, D>(qs, mode);
+  hipError_t e = hipFuncSetAttribute((const void*)hist_fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  prof_begin("entmax_fwd_hist", s);
+  hipLaunchKernelGGL(hist_fn, dim3(grid), dim3(64 * HIST_WAVES), lds, s, p);
+  prof_end(s);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  prof_begin("entmax_fwd_refine_out", s);
+  if (mode == 1) hipLaunchKernelGGL((k_refine_out<T, D, 1>), dim3(grid2), dim3(64 * OUT_WAVES), 0, s, p);
+  else if (mode == 2) hipLaunchKernelGGL((k_refine_out<T, D, 2>), dim3(grid2), dim3(64 * OUT_WAVES), 0, s, p);
+  else hipLaunchKernelGGL((k_refine_out<T, D, 0>), dim3(grid2), dim3(64 * OUT_WAVES), 0, s, p);
+  prof_end(s);
   return hipGetLastError();
 }
 
 hipError_t launch_fwd(const FwdParams& p, int dtype, int D, int mode, hipStream_t s) {
-  if (dtype == 1) {
-    if (D == 64) return launch_fwd_t<__bf16, 64, 2>(p, mode, s);
-    return launch_fwd_t<__bf16, 128, 1>(p, mode, s);
-  }
-  if (D == 64) return launch_fwd_t<float, 64, 2>(p, mode, s);
-  return launch_fwd_t<float, 128, 1>(p, mode, s);
+  if (dtype == 1) return D == 64 ? launch_fwd_t<__bf16, 64>(p, mode, s) : launch_fwd_t<__bf16, 128>(p, mode, s);
+  return D == 64 ? launch_fwd_t<float, 64>(p, mode, s) : launch_fwd_t<float, 128>(p, mode, s);
 }
 
 }  // namespace entmax

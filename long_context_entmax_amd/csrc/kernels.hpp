@@ -37,7 +37,8 @@ __device__ __forceinline__ bool wgmap_get(const WgMap& m, int bid, int& unit, in
 struct FwdParams {
   const void* q;
   const void* k;
-  const void* vt;        // permuted transpose of V: [b, hkv, D, n]
+  const void* kf;        // K, fragment-major rows
+  const void* vf;        // V, fragment-major columns
   float* o;              // fp32 [b, hq, n, D]
   float* tau;
   uint32_t* mask;
@@ -45,6 +46,9 @@ struct FwdParams {
   int32_t* hist;         // optional [b, hq, n, B]
   float* tau_h;          // optional [b, hq, n]
   unsigned long long* stats;  // optional [32]
+  float* dmax;           // workspace: per (32-row chunk, 32-key sub-block) max of x*B
+  uint32_t* cand;        // workspace: candidate sub-block bits per 32-row chunk [b*hq][n/32][NW32]
+  float* tauh_ws;        // workspace: tau_h per row [b*hq*n]
   int b, hq, hkv, n, G;
   int causal, Br, Bc, B, max_iters;
   float cx;              // (alpha - 1) * scale
@@ -54,14 +58,17 @@ struct FwdParams {
   int RG;                // row groups per head = ceil(n / RH)
   int nkb, NW32;         // 32-key sub-blocks, words of sub-block bits
   int Tr, Tc, W;
-  WgMap map;
+  WgMap map;             // histogram kernel
+  WgMap map2;            // refinement/output kernel
 };
 
 struct PrepParams {
-  // permuted transposes X [H, n, D] -> Xt [H, D, n]
-  const void* src[3];
-  void* dst[3];
-  int heads[3];
+  // re-layouts of X [H, n, D]: kind 0 permuted transpose [H, D, n], 1 fragment-major
+  // rows, 2 fragment-major columns (see prep.hip)
+  const void* src[8];
+  void* dst[8];
+  int heads[8];
+  int kind[8];
   int ntrans;
   int n, D;
   // delta = sum_d dO * o~

@@ -1,4 +1,12 @@
 // Data-movement kernels around the attention kernels (HBM-bound, O(n d)):
+//   k_frag_rows       X [H, n, D] -> fragment-major copy for operands whose rows are
+//                     the 32 lanes: block b, chunk s, half h, lane c holds the 8 elements
+//                     X[32b + c][16s + 8h .. +7] at ((b*DS + s)*2 + h)*32 + c (in 8-element
+//                     units), so one wave's operand load is one contiguous run;
+//   k_frag_cols       X [H, n, D] -> fragment-major copy for operands whose lanes walk the
+//                     head dimension and whose contraction runs over rows: block b, 32-wide
+//                     d chunk dc, 16-row chunk m, half h, lane c holds
+//                     X[32b + 16m + sigma(8h + j)][32dc + c], j = 0..7;
 //   k_transpose_perm  X [H, n, D] -> Xt [H, D, n], positions inside each 16-group in sigma
 //                     order, so that a lane reads 8 consecutive elements as an MFMA operand
 //                     when the contraction runs over keys or queries;
@@ -27,6 +35,40 @@ __global__ __launch_bounds__(256) void k_transpose_perm(const T* __restrict__ sr
   for (int i = threadIdx.x; i < 64 * D; i += 256) {
     const int dd = i / 64, pos = i % 64;
     if (r0 + pos < n) d[(size_t)dd * n + pos] = tile[(pos & ~15) | sigma16(pos & 15)][dd];
+  }
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void k_frag_rows(const T* __restrict__ src, T* __restrict__ dst, int n) {
+  constexpr int DS = D / 16;
+  constexpr int V4 = 8 * sizeof(T) / 16;           // 16-byte vectors per 8-element fragment
+  const size_t hh = blockIdx.y;
+  const int units = (n / 32) * DS * 2 * 32;        // 8-element units per head
+  const int u = blockIdx.x * 256 + threadIdx.x;
+  if (u >= units) return;
+  const int c = u & 31, h = (u >> 5) & 1, s = (u >> 6) % DS, b = (u >> 6) / DS;
+  const uint4* sp = reinterpret_cast<const uint4*>(src + (hh * n + (size_t)b * 32 + c) * D + 16 * s + 8 * h);
+  uint4* dp = reinterpret_cast<uint4*>(dst + hh * (size_t)n * D + (size_t)u * 8);
+#pragma unroll
+  for (int j = 0; j < V4; ++j) dp[j] = sp[j];
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void k_frag_cols(const T* __restrict__ src, T* __restrict__ dst, int n) {
+  constexpr int DC = D / 32;
+  constexpr int PAD = (sizeof(T) == 2) ? 2 : 1;
+  __shared__ T tile[32][D + PAD];
+  const size_t hh = blockIdx.y;
+  const int b = blockIdx.x;                         // 32-row block
+  const T* sp = src + (hh * n + (size_t)b * 32) * D;
+  for (int i = threadIdx.x; i < 32 * D; i += 256) tile[i / D][i % D] = sp[i];
+  __syncthreads();
+  // units of this block: DC * 2 (m) * 2 (h) * 32 (c)
+  T* dp = dst + hh * (size_t)n * D + (size_t)b * 32 * D;
+  for (int u = threadIdx.x; u < DC * 128; u += 256) {
+    const int c = u & 31, h = (u >> 5) & 1, m = (u >> 6) & 1, dc = u >> 7;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) dp[(size_t)u * 8 + j] = tile[16 * m + sigma16(8 * h + j)][32 * dc + c];
   }
 }
 
@@ -68,22 +110,33 @@ __global__ __launch_bounds__(256) void k_mask_transpose(const uint32_t* __restri
 }
 
 template <typename T>
-static hipError_t transpose_one(const void* src, void* dst, int heads, int n, int D, hipStream_t s) {
+static hipError_t relayout_one(const void* src, void* dst, int heads, int n, int D, int kind, hipStream_t s) {
   if (heads == 0 || n == 0) return hipSuccess;
-  dim3 grid((n + 63) / 64, heads);
-  prof_begin("transpose_perm", s);
-  if (D == 64)
-    hipLaunchKernelGGL((k_transpose_perm<T, 64>), grid, dim3(256), 0, s, (const T*)src, (T*)dst, n);
-  else
-    hipLaunchKernelGGL((k_transpose_perm<T, 128>), grid, dim3(256), 0, s, (const T*)src, (T*)dst, n);
+  if (kind == 0) {            // permuted transpose [D][n]
+    dim3 grid((n + 63) / 64, heads);
+    prof_begin("transpose_perm", s);
+    if (D == 64) hipLaunchKernelGGL((k_transpose_perm<T, 64>), grid, dim3(256), 0, s, (const T*)src, (T*)dst, n);
+    else hipLaunchKernelGGL((k_transpose_perm<T, 128>), grid, dim3(256), 0, s, (const T*)src, (T*)dst, n);
+  } else if (kind == 1) {     // fragment-major rows
+    const int units = (n / 32) * (D / 16) * 64;
+    dim3 grid((units + 255) / 256, heads);
+    prof_begin("frag_rows", s);
+    if (D == 64) hipLaunchKernelGGL((k_frag_rows<T, 64>), grid, dim3(256), 0, s, (const T*)src, (T*)dst, n);
+    else hipLaunchKernelGGL((k_frag_rows<T, 128>), grid, dim3(256), 0, s, (const T*)src, (T*)dst, n);
+  } else {                    // fragment-major columns
+    dim3 grid(n / 32, heads);
+    prof_begin("frag_cols", s);
+    if (D == 64) hipLaunchKernelGGL((k_frag_cols<T, 64>), grid, dim3(256), 0, s, (const T*)src, (T*)dst, n);
+    else hipLaunchKernelGGL((k_frag_cols<T, 128>), grid, dim3(256), 0, s, (const T*)src, (T*)dst, n);
+  }
   prof_end(s);
   return hipGetLastError();
 }
 
 hipError_t launch_transpose(const PrepParams& p, int dtype, hipStream_t s) {
   for (int t = 0; t < p.ntrans; ++t) {
-    hipError_t e = (dtype == 1) ? transpose_one<__bf16>(p.src[t], p.dst[t], p.heads[t], p.n, p.D, s)
-                                : transpose_one<float>(p.src[t], p.dst[t], p.heads[t], p.n, p.D, s);
+    hipError_t e = (dtype == 1) ? relayout_one<__bf16>(p.src[t], p.dst[t], p.heads[t], p.n, p.D, p.kind[t], s)
+                                : relayout_one<float>(p.src[t], p.dst[t], p.heads[t], p.n, p.D, p.kind[t], s);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

@@ -44,6 +44,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample time")
     ap.add_argument("--profile-only", action="store_true",
                     help="warmup + steps only (for rocprofv3 runs), still prints the JSON line")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="after the steps, run 3 plain fp32 copies (x * 1) of this many MiB: the "
+                         "reference for scaling FETCH_SIZE / WRITE_SIZE counters to bytes")
     return ap.parse_args()
 
 
@@ -165,6 +168,15 @@ def main():
     wall = time.time() - t0
     ms = e0.elapsed_time(e1) / args.steps
 
+    if args.copy_probe_mib > 0:
+        nel = args.copy_probe_mib * (1 << 20) // 4
+        src = torch.ones(nel, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+
     # per-kernel HIP-event timing (same steps, separate loop, events recorded on the
     # stream each kernel is launched on)
     lce.profile(True)
@@ -198,13 +210,16 @@ def main():
     dom = max(alg, key=lambda nm: kern.get(nm, {"avg_ms": 0})["avg_ms"])
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
     achieved = alg[dom] / (kern[dom]["avg_ms"] * 1e-3) / 1e12
+    # HBM bytes per launch of the dominant kernel from the committed rocprofv3 counter
+    # summary of this workload (FETCH_SIZE + WRITE_SIZE scaled by a copy of known size);
+    # null when the kernel sources changed since the counters were taken
     traffic = None
-    tfile = os.path.join(ROOT, "profiles", f"{dom}_{w.name}_traffic.json")
+    tfile = os.path.join(ROOT, "profiles", f"entmax_attn_{w.name}_traffic.json")
     if os.path.exists(tfile):
         with open(tfile) as f:
             tj = json.load(f)
         if tj.get("src_digest") == src_digest() and tj.get("workload") == w.name:
-            traffic = tj.get("bytes_per_launch")
+            traffic = tj.get("kernels", {}).get(dom, {}).get("bytes_per_launch")
     passes = {str(p): st[p] for p in range(1, 17) if st[p]}
     sub_stats = {"hist_subblocks": st[20], "refine_visits": st[21], "output_visits": st[22],
                  "candidate_subblocks": st[23]}

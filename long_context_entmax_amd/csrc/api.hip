@@ -161,17 +161,25 @@ static size_t fwd_ws(const Derived& o) {
   return 2 * fwd_kv_bytes(o) + fwd_dmax_bytes(o) + fwd_cand_bytes(o) + align256((size_t)o.b * o.hq * o.n * 4);
 }
 
+// backward workspace: delta, transposed mask, then fragment-major copies of Q and dO
+// (rows and cols layouts), K (rows and cols) and V (rows)
 struct BwdLayout {
-  size_t delta, maskT, qt, dot, kt, total;
+  size_t delta, maskT, qr, qc, dor, doc, kr, kc, vr, total;
 };
 static BwdLayout bwd_ws(const Derived& o) {
   BwdLayout L;
   size_t off = 0;
+  const size_t qbytes = align256((size_t)o.b * o.hq * o.D * o.n * o.es);
+  const size_t kbytes = align256((size_t)o.b * o.hkv * o.D * o.n * o.es);
   L.delta = off; off += align256((size_t)o.b * o.hq * o.n * 4);
   L.maskT = off; off += align256((size_t)o.b * o.hq * o.Tc * o.WT * 4);
-  L.qt = off; off += align256((size_t)o.b * o.hq * o.D * o.n * o.es);
-  L.dot = off; off += align256((size_t)o.b * o.hq * o.D * o.n * o.es);
-  L.kt = off; off += align256((size_t)o.b * o.hkv * o.D * o.n * o.es);
+  L.qr = off; off += qbytes;
+  L.qc = off; off += qbytes;
+  L.dor = off; off += qbytes;
+  L.doc = off; off += qbytes;
+  L.kr = off; off += kbytes;
+  L.kc = off; off += kbytes;
+  L.vr = off; off += kbytes;
   L.total = off;
   return L;
 }
@@ -238,19 +246,11 @@ entmax_status entmax_attn_fwd(const entmax_attn_desc* desc, const void* q, const
   hipStream_t s = (hipStream_t)stream;
 
   char* wsb = (char*)workspace;
-  PrepParams tp{};
-  tp.src[0] = k;
-  tp.dst[0] = wsb;
-  tp.heads[0] = o.b * o.hkv;
-  tp.kind[0] = 1;
-  tp.src[1] = v;
-  tp.dst[1] = wsb + fwd_kv_bytes(o);
-  tp.heads[1] = o.b * o.hkv;
-  tp.kind[1] = 2;
-  tp.ntrans = 2;
-  tp.n = o.n;
-  tp.D = o.D;
-  hipError_t e = launch_transpose(tp, o.dtype, s);
+  hipError_t e = launch_relayout(Relayout{k, wsb, nullptr, nullptr, nullptr, o.b * o.hkv, "frag_rows"}, o.dtype,
+                                 o.n, o.D, s);
+  if (e == hipSuccess)
+    e = launch_relayout(Relayout{v, nullptr, wsb + fwd_kv_bytes(o), nullptr, nullptr, o.b * o.hkv, "frag_cols"},
+                        o.dtype, o.n, o.D, s);
   if (e != hipSuccess) return hip_fail(e, "fragment-major copies of K and V");
 
   FwdParams p{};
@@ -293,28 +293,25 @@ entmax_status entmax_attn_bwd(const entmax_attn_desc* desc, const void* q, const
   hipStream_t s = (hipStream_t)stream;
   char* ws = (char*)workspace;
 
-  PrepParams pp{};
-  pp.src[0] = q;    pp.dst[0] = ws + L.qt;  pp.heads[0] = o.b * o.hq;
-  pp.src[1] = dout; pp.dst[1] = ws + L.dot; pp.heads[1] = o.b * o.hq;
-  pp.src[2] = k;    pp.dst[2] = ws + L.kt;  pp.heads[2] = o.b * o.hkv;
-  pp.kind[0] = pp.kind[1] = pp.kind[2] = 0;
-  pp.ntrans = 3;
-  pp.n = o.n;
-  pp.D = o.D;
-  pp.dout = dout;
-  pp.aux = (const float*)aux;
-  pp.delta = (float*)(ws + L.delta);
-  pp.rows = o.b * o.hq * o.n;
-  pp.mask = block_mask;
-  pp.maskT = (uint32_t*)(ws + L.maskT);
-  pp.planes = o.b * o.hq;
-  pp.Tr = o.Tr; pp.Tc = o.Tc; pp.W = o.W; pp.WT = o.WT;
-  hipError_t e = launch_bwd_prep(pp, o.dtype, s);
+  const int hq_all = o.b * o.hq, hkv_all = o.b * o.hkv;
+  hipError_t e = launch_relayout(Relayout{q, ws + L.qr, ws + L.qc, nullptr, nullptr, hq_all, "relayout_q"},
+                                 o.dtype, o.n, o.D, s);
+  if (e == hipSuccess)
+    e = launch_relayout(Relayout{dout, ws + L.dor, ws + L.doc, (const float*)aux, (float*)(ws + L.delta), hq_all,
+                                 "relayout_do_delta"}, o.dtype, o.n, o.D, s);
+  if (e == hipSuccess)
+    e = launch_relayout(Relayout{k, ws + L.kr, ws + L.kc, nullptr, nullptr, hkv_all, "relayout_k"}, o.dtype, o.n,
+                        o.D, s);
+  if (e == hipSuccess)
+    e = launch_relayout(Relayout{v, ws + L.vr, nullptr, nullptr, nullptr, hkv_all, "relayout_v"}, o.dtype, o.n,
+                        o.D, s);
+  if (e == hipSuccess)
+    e = launch_mask_transpose(block_mask, (uint32_t*)(ws + L.maskT), hq_all, o.Tr, o.Tc, o.W, o.WT, s);
   if (e != hipSuccess) return hip_fail(e, "backward preparation");
 
   BwdParams p{};
-  p.q = q; p.k = k; p.v = v; p.dout = dout;
-  p.qt = ws + L.qt; p.dot = ws + L.dot; p.kt = ws + L.kt;
+  p.qr = ws + L.qr; p.qc = ws + L.qc; p.dor = ws + L.dor; p.doc = ws + L.doc;
+  p.kr = ws + L.kr; p.kc = ws + L.kc; p.vr = ws + L.vr;
   p.tau = tau; p.delta = (const float*)(ws + L.delta);
   p.mask = block_mask; p.maskT = (const uint32_t*)(ws + L.maskT);
   p.dq = dq; p.dk = dk; p.dv = dv;

@@ -9,8 +9,13 @@
 //   dS_ij = g_ij (dP_ij - delta_i),  dq_i = scale sum_j dS_ij k_j,
 //   dk_j  = scale sum_i dS_ij q_i,   dv_j = sum_i p_ij dO_i.
 //
+// Every MFMA operand is read from a fragment-major copy (rows: lanes walk rows, 8
+// consecutive head-dimension elements per lane; cols: lanes walk the head dimension, 8
+// rows per lane in accumulator order), so a wave's operand load is one contiguous 1 KB
+// run at a wave-uniform base plus lane * 16 bytes.
+//
 // k_bwd_dkv: one work group per (batch, KV head, key block J). Wave w owns the 32-key
-// sub-block w % KC of J and every (NS)-th item of the list (query head of the GQA group,
+// sub-block w % KC of J and every NS-th item of the list (query head of the GQA group,
 // query tile with bit J set, 32-row chunk); K and V of the sub-block stay in registers,
 // dK and dV accumulate in registers and the waves that share a sub-block add their sums
 // in LDS in a fixed order (deterministic, no atomics).
@@ -21,13 +26,26 @@
 
 namespace entmax {
 
+namespace {
+
+// offset (in elements) of a wave's operand fragment in a fragment-major copy
+__device__ __forceinline__ size_t rows_off(int blk32, int s, int DS, int lane) {
+  return ((size_t)(blk32 * DS + s) * 64 + lane) * 8;
+}
+__device__ __forceinline__ size_t cols_off(int blk32, int dc, int m, int DC, int lane) {
+  return ((size_t)((blk32 * DC + dc) * 2 + m) * 64 + lane) * 8;
+}
+
+}  // namespace
+
 template <typename T, int D, int MODE>
-__global__ __launch_bounds__(256, 1) void k_bwd_dkv(BwdParams p) {
+__global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void k_bwd_dkv(BwdParams p) {
   constexpr int DS = D / 16, DC = D / 32;
   extern __shared__ float red[];
   int unit, rank;
   if (!wgmap_get(p.map, blockIdx.x, unit, rank)) return;
-  const int lane = lane_id(), c = lane & 31, h = lane >> 5, w = wave_id();
+  const int lane = lane_id(), c = lane & 31, h = lane >> 5;
+  const int w = uniform_i32(wave_id());
   const int bi = unit / p.hkv, kvh = unit % p.hkv;
   const int J = rank;
   const int KC = p.Bc / 32, NS = 4 / KC;
@@ -37,14 +55,14 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dkv(BwdParams p) {
   const int QCB = p.Br / 32;
   const float cx = p.cx, kappa = p.kappa;
 
-  const size_t kvbase = (size_t)(bi * p.hkv + kvh) * n;
-  const T* K = reinterpret_cast<const T*>(p.k) + kvbase * D;
-  const T* V = reinterpret_cast<const T*>(p.v) + kvbase * D;
+  const size_t kvoff = (size_t)(bi * p.hkv + kvh) * n * D;
+  const T* Kr = reinterpret_cast<const T*>(p.kr) + kvoff;
+  const T* Vr = reinterpret_cast<const T*>(p.vr) + kvoff;
   Frag<T> kb[DS], vb[DS];
 #pragma unroll
   for (int s = 0; s < DS; ++s) {
-    load_frag(kb[s], K + (size_t)(key0 + c) * D + 16 * s + 8 * h);
-    load_frag(vb[s], V + (size_t)(key0 + c) * D + 16 * s + 8 * h);
+    load_frag(kb[s], Kr + rows_off(key0 >> 5, s, DS, lane));
+    load_frag(vb[s], Vr + rows_off(key0 >> 5, s, DS, lane));
   }
   f32x16 dk[DC], dv[DC];
 #pragma unroll
@@ -56,58 +74,76 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dkv(BwdParams p) {
   int t = 0;
   for (int g = 0; g < p.G; ++g) {
     const int head = kvh * p.G + g;
-    const size_t qbase = (size_t)(bi * p.hq + head) * n;
-    const T* Q = reinterpret_cast<const T*>(p.q) + qbase * D;
-    const T* DO = reinterpret_cast<const T*>(p.dout) + qbase * D;
-    const T* Qt = reinterpret_cast<const T*>(p.qt) + qbase * D;     // [D][n] of this head
-    const T* DOt = reinterpret_cast<const T*>(p.dot) + qbase * D;
-    const float* tau = p.tau + qbase;
-    const float* delta = p.delta + qbase;
+    const size_t qrow0 = (size_t)(bi * p.hq + head) * n;
+    const T* Qr = reinterpret_cast<const T*>(p.qr) + qrow0 * D;
+    const T* DOr = reinterpret_cast<const T*>(p.dor) + qrow0 * D;
+    const T* Qc = reinterpret_cast<const T*>(p.qc) + qrow0 * D;
+    const T* DOc = reinterpret_cast<const T*>(p.doc) + qrow0 * D;
+    const float* tau = p.tau + qrow0;
+    const float* delta = p.delta + qrow0;
     const uint32_t* colw = p.maskT + ((size_t)(bi * p.hq + head) * p.Tc + J) * p.WT;
     for (int wi = 0; wi < p.WT; ++wi) {
       uint32_t word = uniform_u32(colw[wi]);
       while (word) {
         const int I = wi * 32 + __builtin_ctz(word);
         word &= word - 1;
-        for (int qc = 0; qc < QCB; ++qc, ++t) {
-          if (t % NS != slot) continue;
+        for (int qc = 0; qc < QCB; ++qc) {
+          const bool mine = (t++ % NS) == slot;
           const int q0 = I * p.Br + 32 * qc;
-          if (p.causal && key0 > q0 + 31) continue;     // sub-tile above the diagonal
-          Frag<T> qa[DS];
+          if (!mine || (p.causal && key0 > q0 + 31)) continue;   // sub-tile above the diagonal
+          const int qb = q0 >> 5;
+          Frag<T> qa[DS], da[DS], qt[2][DC], dt[2][DC];
 #pragma unroll
-          for (int s = 0; s < DS; ++s) load_frag(qa[s], Q + (size_t)(q0 + c) * D + 16 * s + 8 * h);
-          f32x16 S = f32x16{};
-#pragma unroll
-          for (int s = 0; s < DS; ++s) mma16(S, qa[s], kb[s]);   // S[q][key]
-          f32x4 tv[4], dv4[4];
+          for (int s = 0; s < DS; ++s) {
+            load_frag(qa[s], Qr + rows_off(qb, s, DS, lane));
+            load_frag(da[s], DOr + rows_off(qb, s, DS, lane));
+          }
+          f32x4 tv[4], dl[4];
 #pragma unroll
           for (int g4 = 0; g4 < 4; ++g4) {
             tv[g4] = *reinterpret_cast<const f32x4*>(tau + q0 + 8 * g4 + 4 * h);
-            dv4[g4] = *reinterpret_cast<const f32x4*>(delta + q0 + 8 * g4 + 4 * h);
+            dl[g4] = *reinterpret_cast<const f32x4*>(delta + q0 + 8 * g4 + 4 * h);
           }
+#pragma unroll
+          for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int dc = 0; dc < DC; ++dc) {
+              load_frag(qt[m][dc], Qc + cols_off(qb, dc, m, DC, lane));
+              load_frag(dt[m][dc], DOc + cols_off(qb, dc, m, DC, lane));
+            }
+          f32x16 S = f32x16{};
+#pragma unroll
+          for (int s = 0; s < DS; ++s) mma16(S, qa[s], kb[s]);   // S[q][key]
+          // P and G; rows 8(r/4) + 4h + r%4 of the chunk, key c of the sub-block
           const bool diag = p.causal && key0 + 31 > q0;
           f32x16 P, G;
-          bool any = false;
+          float mx = 0.f;
+          if (diag) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int qrow = q0 + acc_row(r, h);
-            const bool valid = !diag || (key0 + c <= qrow);
-            const float tt = valid ? (cx * S[r] - tv[r >> 2][r & 3]) : -1.0f;
-            const float dm = fmaxf(tt, 0.f);
-            P[r] = Weight<MODE>::p(dm, kappa);
-            G[r] = Weight<MODE>::g(tt > 0.f ? dm : 0.f, kappa);
-            any = any || (tt > 0.f);
+            for (int r = 0; r < 16; ++r) {
+              float tt = cx * S[r] - tv[r >> 2][r & 3];
+              tt = (key0 + c <= q0 + acc_row(r, h)) ? tt : -1.0f;
+              const float dm = fmaxf(tt, 0.f);
+              P[r] = Weight<MODE>::p(dm, kappa);
+              G[r] = Weight<MODE>::g(dm, kappa);
+              mx = fmaxf(mx, dm);
+            }
+          } else {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const float dm = fmaxf(cx * S[r] - tv[r >> 2][r & 3], 0.f);
+              P[r] = Weight<MODE>::p(dm, kappa);
+              G[r] = Weight<MODE>::g(dm, kappa);
+              mx = fmaxf(mx, dm);
+            }
           }
-          if (ballot(any) == 0) continue;
-          Frag<T> da[DS];
-#pragma unroll
-          for (int s = 0; s < DS; ++s) load_frag(da[s], DO + (size_t)(q0 + c) * D + 16 * s + 8 * h);
+          if (ballot(mx > 0.f) == 0) continue;
           f32x16 dP = f32x16{};
 #pragma unroll
           for (int s = 0; s < DS; ++s) mma16(dP, da[s], vb[s]);  // dP[q][key]
           f32x16 dS;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) dS[r] = G[r] * (dP[r] - dv4[r >> 2][r & 3]);
+          for (int r = 0; r < 16; ++r) dS[r] = G[r] * (dP[r] - dl[r >> 2][r & 3]);
 #pragma unroll
           for (int m = 0; m < 2; ++m) {
             Frag<T> pf, sf;
@@ -115,11 +151,8 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dkv(BwdParams p) {
             acc_frag(sf, dS, m);
 #pragma unroll
             for (int dc = 0; dc < DC; ++dc) {
-              Frag<T> qt, dt;
-              load_frag(qt, Qt + (size_t)(32 * dc + c) * n + q0 + 16 * m + 8 * h);
-              load_frag(dt, DOt + (size_t)(32 * dc + c) * n + q0 + 16 * m + 8 * h);
-              mma16(dv[dc], dt, pf);   // dV^T[d][key] += dO^T P
-              mma16(dk[dc], qt, sf);   // dK^T[d][key] += Q^T dS
+              mma16(dv[dc], dt[m][dc], pf);   // dV^T[d][key] += dO^T P
+              mma16(dk[dc], qt[m][dc], sf);   // dK^T[d][key] += Q^T dS
             }
           }
         }
@@ -152,8 +185,9 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dkv(BwdParams p) {
     }
   }
   if (slot == 0) {
-    T* dK = reinterpret_cast<T*>(p.dk) + (kvbase + key0 + c) * D;
-    T* dV = reinterpret_cast<T*>(p.dv) + (kvbase + key0 + c) * D;
+    const size_t rowoff = ((size_t)(bi * p.hkv + kvh) * n + key0 + c) * D;
+    T* dK = reinterpret_cast<T*>(p.dk) + rowoff;
+    T* dV = reinterpret_cast<T*>(p.dv) + rowoff;
     const float sc = p.scale;
 #pragma unroll
     for (int dc = 0; dc < DC; ++dc)
@@ -168,12 +202,13 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dkv(BwdParams p) {
 }
 
 template <typename T, int D, int MODE>
-__global__ __launch_bounds__(256, 1) void k_bwd_dq(BwdParams p) {
+__global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void k_bwd_dq(BwdParams p) {
   constexpr int DS = D / 16, DC = D / 32;
   extern __shared__ float red[];
   int unit, rank;
   if (!wgmap_get(p.map, blockIdx.x, unit, rank)) return;
-  const int lane = lane_id(), c = lane & 31, h = lane >> 5, w = wave_id();
+  const int lane = lane_id(), c = lane & 31, h = lane >> 5;
+  const int w = uniform_i32(wave_id());
   const int bi = unit / p.hkv, kvh = unit % p.hkv;
   const int I = p.causal ? (p.Tr - 1 - rank / p.G) : (rank / p.G);
   const int head = kvh * p.G + rank % p.G;
@@ -184,22 +219,19 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dq(BwdParams p) {
   const int q0 = I * p.Br + 32 * qc;
   const float cx = p.cx, kappa = p.kappa;
 
-  const size_t qbase = (size_t)(bi * p.hq + head) * n;
-  const size_t kvbase = (size_t)(bi * p.hkv + kvh) * n;
-  const T* Q = reinterpret_cast<const T*>(p.q) + qbase * D;
-  const T* DO = reinterpret_cast<const T*>(p.dout) + qbase * D;
-  const T* K = reinterpret_cast<const T*>(p.k) + kvbase * D;
-  const T* V = reinterpret_cast<const T*>(p.v) + kvbase * D;
-  const T* Kt = reinterpret_cast<const T*>(p.kt) + kvbase * D;   // [D][n] of this KV head
+  const size_t qrow0 = (size_t)(bi * p.hq + head) * n;
+  const size_t kvoff = (size_t)(bi * p.hkv + kvh) * n * D;
+  const T* Kr = reinterpret_cast<const T*>(p.kr) + kvoff;
+  const T* Vr = reinterpret_cast<const T*>(p.vr) + kvoff;
+  const T* Kc = reinterpret_cast<const T*>(p.kc) + kvoff;
   Frag<T> qb[DS], db[DS];
 #pragma unroll
   for (int s = 0; s < DS; ++s) {
-    load_frag(qb[s], Q + (size_t)(q0 + c) * D + 16 * s + 8 * h);
-    load_frag(db[s], DO + (size_t)(q0 + c) * D + 16 * s + 8 * h);
+    load_frag(qb[s], reinterpret_cast<const T*>(p.qr) + qrow0 * D + rows_off(q0 >> 5, s, DS, lane));
+    load_frag(db[s], reinterpret_cast<const T*>(p.dor) + qrow0 * D + rows_off(q0 >> 5, s, DS, lane));
   }
-  const float tq = p.tau[qbase + q0 + c];
-  const float dq_delta = p.delta[qbase + q0 + c];
-  const int qrow = q0 + c;
+  const float tq = p.tau[qrow0 + q0 + c];
+  const float dq_delta = p.delta[qrow0 + q0 + c];
   f32x16 dq[DC];
 #pragma unroll
   for (int dc = 0; dc < DC; ++dc) dq[dc] = f32x16{};
@@ -211,31 +243,45 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dq(BwdParams p) {
     while (word) {
       const int J = wi * 32 + __builtin_ctz(word);
       word &= word - 1;
-      for (int ks = 0; ks < KC; ++ks, ++t) {
-        if (t % NS != slot) continue;
+      for (int ks = 0; ks < KC; ++ks) {
+        const bool mine = (t++ % NS) == slot;
         const int key0 = J * p.Bc + 32 * ks;
-        if (p.causal && key0 > q0 + 31) continue;
-        Frag<T> ka[DS];
+        if (!mine || (p.causal && key0 > q0 + 31)) continue;
+        const int kbk = key0 >> 5;
+        Frag<T> ka[DS], va[DS], kt[2][DC];
 #pragma unroll
-        for (int s = 0; s < DS; ++s) load_frag(ka[s], K + (size_t)(key0 + c) * D + 16 * s + 8 * h);
+        for (int s = 0; s < DS; ++s) {
+          load_frag(ka[s], Kr + rows_off(kbk, s, DS, lane));
+          load_frag(va[s], Vr + rows_off(kbk, s, DS, lane));
+        }
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+          for (int dc = 0; dc < DC; ++dc) load_frag(kt[m][dc], Kc + cols_off(kbk, dc, m, DC, lane));
         f32x16 S = f32x16{};
 #pragma unroll
         for (int s = 0; s < DS; ++s) mma16(S, ka[s], qb[s]);   // S^T[key][q]
         const bool diag = p.causal && key0 + 31 > q0;
         f32x16 G;
-        bool any = false;
+        float mx = 0.f;
+        if (diag) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const bool valid = !diag || (key0 + acc_row(r, h) <= qrow);
-          const float tt = valid ? (cx * S[r] - tq) : -1.0f;
-          const float dm = fmaxf(tt, 0.f);
-          G[r] = Weight<MODE>::g(tt > 0.f ? dm : 0.f, kappa);
-          any = any || (tt > 0.f);
+          for (int r = 0; r < 16; ++r) {
+            float tt = cx * S[r] - tq;
+            tt = (key0 + acc_row(r, h) <= q0 + c) ? tt : -1.0f;
+            const float dm = fmaxf(tt, 0.f);
+            G[r] = Weight<MODE>::g(dm, kappa);
+            mx = fmaxf(mx, dm);
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float dm = fmaxf(cx * S[r] - tq, 0.f);
+            G[r] = Weight<MODE>::g(dm, kappa);
+            mx = fmaxf(mx, dm);
+          }
         }
-        if (ballot(any) == 0) continue;
-        Frag<T> va[DS];
-#pragma unroll
-        for (int s = 0; s < DS; ++s) load_frag(va[s], V + (size_t)(key0 + c) * D + 16 * s + 8 * h);
+        if (ballot(mx > 0.f) == 0) continue;
         f32x16 dP = f32x16{};
 #pragma unroll
         for (int s = 0; s < DS; ++s) mma16(dP, va[s], db[s]);   // dP^T[key][q]
@@ -247,11 +293,7 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dq(BwdParams p) {
           Frag<T> sf;
           acc_frag(sf, dS, m);
 #pragma unroll
-          for (int dc = 0; dc < DC; ++dc) {
-            Frag<T> kt;
-            load_frag(kt, Kt + (size_t)(32 * dc + c) * n + key0 + 16 * m + 8 * h);
-            mma16(dq[dc], kt, sf);   // dQ^T[d][q] += K^T dS^T
-          }
+          for (int dc = 0; dc < DC; ++dc) mma16(dq[dc], kt[m][dc], sf);   // dQ^T[d][q] += K^T dS^T
         }
       }
     }
@@ -275,7 +317,7 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dq(BwdParams p) {
     }
   }
   if (slot == 0) {
-    T* dQ = reinterpret_cast<T*>(p.dq) + (qbase + q0 + c) * D;
+    T* dQ = reinterpret_cast<T*>(p.dq) + (qrow0 + q0 + c) * D;
     const float sc = p.scale;
 #pragma unroll
     for (int dc = 0; dc < DC; ++dc)

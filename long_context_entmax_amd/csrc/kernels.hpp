@@ -62,34 +62,26 @@ struct FwdParams {
   WgMap map2;            // refinement/output kernel
 };
 
-struct PrepParams {
-  // re-layouts of X [H, n, D]: kind 0 permuted transpose [H, D, n], 1 fragment-major
-  // rows, 2 fragment-major columns (see prep.hip)
-  const void* src[8];
-  void* dst[8];
-  int heads[8];
-  int kind[8];
-  int ntrans;
-  int n, D;
-  // delta = sum_d dO * o~
-  const void* dout;
-  const float* aux;
-  float* delta;
-  int rows;              // b * hq * n (0: skip)
-  // mask transpose: mask [P, Tr, W] -> maskT [P, Tc, WT]
-  const uint32_t* mask;
-  uint32_t* maskT;
-  int planes, Tr, Tc, W, WT;
+// one re-layout of X [heads, n, D] (prep.hip): any of the fragment-major row copy,
+// the fragment-major column copy and delta = X . aux per row (X = dO, aux = o~)
+struct Relayout {
+  const void* src;
+  void* rows;            // nullable
+  void* cols;            // nullable
+  const float* aux;      // with delta
+  float* delta;          // nullable
+  int heads;
+  const char* name;      // timing label
 };
 
 struct BwdParams {
-  const void* q;
-  const void* k;
-  const void* v;
-  const void* dout;
-  const void* qt;        // permuted transposes
-  const void* dot;
-  const void* kt;
+  const void* qr;        // fragment-major copies (rows / cols layouts of prep.hip)
+  const void* qc;
+  const void* dor;
+  const void* doc;
+  const void* kr;
+  const void* kc;
+  const void* vr;
   const float* tau;
   const float* delta;
   const uint32_t* mask;  // [b, hq, Tr, W]
@@ -105,8 +97,9 @@ struct BwdParams {
 };
 
 hipError_t launch_fwd(const FwdParams& p, int dtype, int D, int mode, hipStream_t s);
-hipError_t launch_transpose(const PrepParams& p, int dtype, hipStream_t s);
-hipError_t launch_bwd_prep(const PrepParams& p, int dtype, hipStream_t s);
+hipError_t launch_relayout(const Relayout& r, int dtype, int n, int D, hipStream_t s);
+hipError_t launch_mask_transpose(const uint32_t* mask, uint32_t* maskT, int planes, int Tr, int Tc, int W,
+                                 int WT, hipStream_t s);
 hipError_t launch_bwd_dkv(const BwdParams& p, int dtype, int D, int mode, hipStream_t s);
 hipError_t launch_bwd_dq(const BwdParams& p, int dtype, int D, int mode, hipStream_t s);
 

@@ -169,6 +169,12 @@ __device__ __forceinline__ int cvt_floor(float x) {
   asm("v_cvt_flr_i32_f32 %0, %1" : "=v"(r) : "v"(x));
   return r;
 }
+// float -> unsigned with truncation; negative inputs (and NaN) give 0
+__device__ __forceinline__ uint32_t cvt_u32_sat(float x) {
+  uint32_t r;
+  asm("v_cvt_u32_f32 %0, %1" : "=v"(r) : "v"(x));
+  return r;
+}
 
 // max of three without canonicalising the inputs (no IEEE-mode NaN quieting)
 __device__ __forceinline__ float max3_raw(float a, float b, float c) {

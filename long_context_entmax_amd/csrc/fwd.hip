@@ -112,6 +112,9 @@ __device__ float tau_from_counts(const int (&cnt)[16], int T, int B, float kappa
 
 }  // namespace
 
+#ifndef HIST_OCC64
+#define HIST_OCC64 4
+#endif
 constexpr int HIST_WAVES = 8;
 constexpr int OUT_WAVES = 4;
 
@@ -119,15 +122,19 @@ template <typename T, int D>
 struct KvOps {
   static constexpr int DS = D / 16;
   static constexpr int DC = D / 32;
-  // K fragments of sub-block kb (A operand: lane c is key 32 kb + c)
+  // K fragments of sub-block kb (A operand: lane c is key 32 kb + c): one contiguous
+  // 1 KB run per fragment at a wave-uniform base plus lane * 8 elements
   __device__ __forceinline__ static void load_k(Frag<T> (&f)[DS], const T* Kf, int kb, int c, int h) {
+    const T* kp = Kf + (size_t)kb * (DS * 512);
+    const int lo = (h * 32 + c) * 8;
 #pragma unroll
-    for (int s = 0; s < DS; ++s) load_frag(f[s], Kf + ((size_t)((kb * DS + s) * 2 + h) * 32 + c) * 8);
+    for (int s = 0; s < DS; ++s) load_frag(f[s], kp + s * 512 + lo);
   }
-  // S^T tile (keys x queries); keys after the query (causal) become -inf
+  // S^T tile (keys x queries) added to acc0; keys after the query (causal) become -inf
   __device__ __forceinline__ static f32x16 scores(const Frag<T> (&kc)[DS], const Frag<T> (&qf)[DS], int kb,
-                                                  int row0, int qrow, int h, bool causal) {
-    f32x16 acc = f32x16{};
+                                                  int row0, int qrow, int h, bool causal,
+                                                  const f32x16& acc0 = f32x16{}) {
+    f32x16 acc = acc0;
 #pragma unroll
     for (int s = 0; s < DS; ++s) mma16(acc, kc[s], qf[s]);
     if (causal && kb * 32 + 31 > row0) {
@@ -141,7 +148,7 @@ struct KvOps {
 
 // ================================================================================ k_hist
 template <typename T, int D, int MODE, bool QS>
-__global__ __launch_bounds__(512) void k_hist(FwdParams p) {
+__global__ __launch_bounds__(512, ((D == 64 && sizeof(T) == 2) ? HIST_OCC64 : 2)) void k_hist(FwdParams p) {
   using Ops = KvOps<T, D>;
   constexpr int DS = Ops::DS;
   extern __shared__ uint32_t lds[];
@@ -157,16 +164,15 @@ __global__ __launch_bounds__(512) void k_hist(FwdParams p) {
   const int per = HIST_WAVES / p.GP;           // waves per head
   const int head = kvh * p.G + gsub * p.GP + w / per;
   const int row0 = rg * p.RH + (w % per) * 32; // this wave's 32 rows
-  const int n = p.n, B = p.B, R2 = 2 * B;      // histogram ring of 2B cells per lane
+  const int n = p.n, B = p.B;                  // histogram window of B cells + 2 trash cells per lane
   const bool valid_rows = row0 < n;
   const int qrow = row0 + c;
   const size_t bh = (size_t)(bi * p.hq + head);
 
   const T* Q = reinterpret_cast<const T*>(p.q) + bh * n * D;
   const T* Kf = reinterpret_cast<const T*>(p.kf) + ((size_t)(bi * p.hkv + kvh) * n) * D;
-  uint32_t* hist = lds + (w * R2) * 64;        // [2B][64] of this wave
-  uint32_t* discard = lds + (HIST_WAVES * R2) * 64;
-  for (int i = lane; i < R2 * 64; i += 64) hist[i] = 0;
+  uint32_t* hist = lds + (w * (B + 2)) * 64;   // [B + 2][64] of this wave
+  for (int i = lane; i < (B + 2) * 64; i += 64) hist[i] = 0;
   float* dmx = p.dmax + (bh * p.nkb + (row0 >> 5)) * p.nkb;
   uint32_t* cw_out = p.cand + (bh * p.nkb + (row0 >> 5)) * p.NW32;
 
@@ -197,13 +203,25 @@ __global__ __launch_bounds__(512) void k_hist(FwdParams p) {
     for (int s = 0; s < DS; ++s) scale_frag(qf[s], qsc);
   }
 
+  // Window of a lane: bins Tt-B+1 .. Tt of its running max cell Tt, held in cells 1..B
+  // (cell j <-> bin base + j with base = Tt - B); cell 0 takes every lower score, and
+  // cell B+1 the lane's max when rounding of x*B - base lands exactly on B+1. A score's
+  // cell is cvt_u32(x*B - base): the conversion saturates negative values to 0.
+  // With the scale folded into Q the offset -base enters the score product as its
+  // initial accumulator, so a score costs a conversion, an address and an LDS add.
+  //
   // Two sub-blocks per step: both tiles update the running max first, then all their
   // scores are counted against the updated window. This is exact: a score that would
   // have been counted under the older window but lies below the newer one is exactly a
   // score the window slide would drop later.
   float mB = -INFINITY;   // running max of x*B over this lane's scores
   int Tt = 0;             // its cell floor(mB): top of the lane's window
+  int base = -B;          // Tt - B
   bool have = false;
+  f32x16 negb;            // -base in every register (initial accumulator)
+#pragma unroll
+  for (int r = 0; r < 16; ++r) negb[r] = (float)B;
+  uint32_t* const hl = hist + lane;          // this lane's column: cell j at hl[64 j]
   uint32_t cword = 0;
   float dreg = -INFINITY; // lane j < 32 keeps the chunk max of sub-block 32*word + j
   unsigned long long n_cand = 0;
@@ -213,18 +231,21 @@ __global__ __launch_bounds__(512) void k_hist(FwdParams p) {
   if (kb_end > 1) Ops::load_k(kf2, Kf, 1, c, h);
   for (int kb = 0; kb < kb_end; kb += 2) {
     const bool two = kb + 1 < kb_end;
-    const f32x16 acc0 = Ops::scores(kf, qf, kb, row0, qrow, h, p.causal);
+    f32x16 acc0 = QS ? Ops::scores(kf, qf, kb, row0, qrow, h, p.causal, negb)
+                     : Ops::scores(kf, qf, kb, row0, qrow, h, p.causal);
     f32x16 acc1;
     if (two) {
-      acc1 = Ops::scores(kf2, qf, kb + 1, row0, qrow, h, p.causal);
+      acc1 = QS ? Ops::scores(kf2, qf, kb + 1, row0, qrow, h, p.causal, negb)
+                : Ops::scores(kf2, qf, kb + 1, row0, qrow, h, p.causal);
     } else {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc1[r] = -INFINITY;
     }
     if (kb + 2 < kb_end) Ops::load_k(kf, Kf, kb + 2, c, h);
     if (kb + 3 < kb_end) Ops::load_k(kf2, Kf, kb + 3, c, h);
-    const float t0 = QS ? max16(acc0) : cB * max16(acc0);
-    const float t1 = QS ? max16(acc1) : cB * max16(acc1);
+    const float bF = (float)base;
+    const float t0 = QS ? max16(acc0) + bF : cB * max16(acc0);   // largest x*B of each tile
+    const float t1 = QS ? max16(acc1) + bF : cB * max16(acc1);
     const float nmB = fmaxf(mB, fmaxf(t0, t1));
     const bool fin = nmB > -INFINITY;
     const int Tn = fin ? cvt_floor(nmB) : Tt;
@@ -248,30 +269,47 @@ __global__ __launch_bounds__(512) void k_hist(FwdParams p) {
         ++n_cand;
       }
       const bool act = act0 || act1;
-      // slide the window up: clear the cells of the bins that enter it (top first)
-      const int nz = (have && act) ? min(Tn - Tt, B) : 0;
-      for (int z = 0; ballot(z < nz) != 0; ++z)
-        if (z < nz) hist[((Tn - z) & (R2 - 1)) * 64 + lane] = 0;
+      // slide a window up: cell k takes cell k + shift, the top cells start empty
+      const bool slide = act && (!have || Tn > Tt);
+      if (ballot(slide) != 0) {
+        const int shift = slide ? (have ? Tn - Tt : B + 1) : 0;
+        for (int k = 1; k <= B; ++k) {
+          if (slide) {
+            const int from = k + shift;
+            hist[k * 64 + lane] = from <= B ? hist[from * 64 + lane] : 0u;
+          }
+        }
+        const int nbase = slide ? Tn - B : base;
+        if constexpr (QS) {
+          const float corr = (float)(nbase - base);  // exact: small integers
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            acc0[r] -= corr;
+            acc1[r] -= corr;
+            negb[r] = (float)(-nbase);
+          }
+        }
+        base = nbase;
+      }
       if (act) {
         mB = nmB;
         Tt = Tn;
         have = true;
       }
-      // count every score: cells of bins more than B below the window fold into the
-      // cell of bin Tt + 1 (outside the window; cleared when the window reaches it);
-      // lanes with no active tile count into a discard column
-      const int lowm = Tt - R2 + 1;
-      uint32_t* basep = act ? (hist + lane) : (discard + lane);
+      // count every score of both tiles (lanes with no active tile land in cell 0)
+      const float nbF = -(float)base;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int ta = max(cvt_floor(QS ? acc0[r] : cB * acc0[r]), lowm);
-        atomicAdd(basep + ((ta & (R2 - 1)) << 6), 1u);
+        const float y = QS ? acc0[r] : fmaf(cB, acc0[r], nbF);
+        const uint32_t cell = cvt_u32_sat(y);
+        atomicAdd(hl + (cell << 6), 1u);
       }
       if (two) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int tb = max(cvt_floor(QS ? acc1[r] : cB * acc1[r]), lowm);
-          atomicAdd(basep + ((tb & (R2 - 1)) << 6), 1u);
+          const float y = QS ? acc1[r] : fmaf(cB, acc1[r], nbF);
+          const uint32_t cell = cvt_u32_sat(y);
+          atomicAdd(hl + (cell << 6), 1u);
         }
       }
     }
@@ -297,7 +335,7 @@ __global__ __launch_bounds__(512) void k_hist(FwdParams p) {
     int mine = 0;
     if (k < B) {
       const int bin = Tf - B + 1 + k;
-      if (have && bin >= Tt - B + 1 && bin <= Tt) mine = (int)hist[(bin & (R2 - 1)) * 64 + lane];
+      if (have && bin >= Tt - B + 1 && bin <= Tt) mine = (int)hist[(bin - base) * 64 + lane];
     }
     cnt[k] = mine + xor32i(mine);
   }
@@ -611,7 +649,7 @@ static void (*hist_kernel(bool qs, int mode))(FwdParams) {
   return mode == 1 ? k_hist<T, D, 1, false> : mode == 2 ? k_hist<T, D, 2, false> : k_hist<T, D, 0, false>;
 }
 
-size_t fwd_lds_bytes(int B) { return (size_t)((HIST_WAVES + 1) * 2 * B * 64) * sizeof(uint32_t); }
+size_t fwd_lds_bytes(int B) { return (size_t)(HIST_WAVES * (B + 2) * 64) * sizeof(uint32_t); }
 
 template <typename T, int D>
 static hipError_t launch_fwd_t(const FwdParams& p, int mode, hipStream_t s) {

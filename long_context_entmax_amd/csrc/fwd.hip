@@ -27,7 +27,10 @@
 // The histogram kernel streams K for 256 query rows that share one KV head (8 waves) and
 // keeps its register count low enough for four waves per SIMD, so one wave's MFMA latency
 // hides under the others' VALU work; the refinement/output kernel has a data-dependent
-// cost per wave and runs in small work groups of 4 waves for balance.
+// cost per wave and runs in small work groups of 4 waves for balance. When the score
+// scale (alpha-1) * scale is a power of two it is folded into Q (exact), and the offset
+// each pass subtracts from the scores (the histogram window base, or tau) enters the
+// score product as its initial accumulator.
 #include <cmath>
 
 #include "common.hpp"
@@ -357,21 +360,25 @@ __global__ __launch_bounds__(512, ((D == 64 && sizeof(T) == 2) ? HIST_OCC64 : 2)
 }
 
 // ================================================================================ k_refine_out
-template <typename T, int D, int MODE>
-__global__ __launch_bounds__(256) void k_refine_out(FwdParams p) {
+// Work groups of OUT_WAVES waves over consecutive 32-row chunks of one query head, one
+// chunk per wave; a wave's cost depends on its rows' candidates and passes, so small
+// groups keep the machine balanced.
+template <typename T, int D, int MODE, bool QS>
+__global__ __launch_bounds__(64 * OUT_WAVES, 2) void k_refine_out(FwdParams p) {
   using Ops = KvOps<T, D>;
   constexpr int DS = Ops::DS, DC = Ops::DC;
   int unit, rank;
-  if (!wgmap_get(p.map2, blockIdx.x, unit, rank)) return;
+  if (!wgmap_get(p.map2, blockIdx.x, unit, rank)) return;   // whole work group
   const int lane = lane_id(), c = lane & 31, h = lane >> 5;
   const int w = uniform_i32(wave_id());
   const int bi = unit / p.hkv, kvh = unit % p.hkv;
-  const int RG2 = (p.nkb + OUT_WAVES - 1) / OUT_WAVES;   // groups of 4 chunks per head
-  const int grp = p.causal ? (RG2 - 1 - rank / p.G) : (rank / p.G);
   const int head = kvh * p.G + rank % p.G;
-  const int row0 = (grp * OUT_WAVES + w) * 32;
+  const int ngrp = (p.nkb + OUT_WAVES - 1) / OUT_WAVES;
+  const int grp = p.causal ? (ngrp - 1 - rank / p.G) : (rank / p.G);
+  const int chunk = grp * OUT_WAVES + w;
+  if (chunk >= p.nkb) return;            // no barrier follows: the wave may leave
+  const int row0 = chunk * 32;
   const int n = p.n, B = p.B;
-  if (row0 >= n) return;
   const int qrow = row0 + c;
   const size_t bh = (size_t)(bi * p.hq + head);
   const int kb_end = p.causal ? min(p.nkb, (row0 + 31) / 32 + 1) : p.nkb;
@@ -380,19 +387,25 @@ __global__ __launch_bounds__(256) void k_refine_out(FwdParams p) {
   const T* Q = reinterpret_cast<const T*>(p.q) + bh * n * D;
   const T* Kf = reinterpret_cast<const T*>(p.kf) + ((size_t)(bi * p.hkv + kvh) * n) * D;
   const T* Vf = reinterpret_cast<const T*>(p.vf) + ((size_t)(bi * p.hkv + kvh) * n) * D;
-  const float* dmx = p.dmax + (bh * p.nkb + (row0 >> 5)) * p.nkb;
-  const uint32_t* cwords = p.cand + (bh * p.nkb + (row0 >> 5)) * p.NW32;
+  const float* dmx = p.dmax + (bh * p.nkb + chunk) * p.nkb;
+  const uint32_t* cwords = p.cand + (bh * p.nkb + chunk) * p.NW32;
 
   Frag<T> qf[DS];
 #pragma unroll
   for (int s = 0; s < DS; ++s) load_frag(qf[s], Q + (size_t)qrow * D + 16 * s + 8 * h);
+  // with QS the score scale is a power of two folded into Q (exact) and -tau enters the
+  // score product as its initial accumulator, so the tile holds x - tau directly
+  if constexpr (QS) {
+#pragma unroll
+    for (int s = 0; s < DS; ++s) scale_frag(qf[s], p.cx);
+  }
   const float cx = p.cx;
   float tau = p.tauh_ws[bh * n + qrow];
   const float hB = 1.0f / (float)B;
   float lo = tau, hi = tau + hB;
 
   // Walk over the sub-blocks a pass needs: candidate bits of the histogram pass, kept
-  // where the chunk max (read 32 sub-blocks at a time) exceeds the threshold.
+  // where the recorded chunk max exceeds the threshold (read 32 at a time).
   struct Walk {
     int wi;
     uint32_t word;
@@ -413,8 +426,22 @@ __global__ __launch_bounds__(256) void k_refine_out(FwdParams p) {
     wk.word &= wk.word - 1;
     return kb;
   };
+  f32x16 negt;
+  auto tile = [&](const Frag<T> (&kc)[DS], int kb) -> f32x16 {   // x - tau; -inf if masked
+    if constexpr (QS) {
+      return Ops::scores(kc, qf, kb, row0, qrow, h, p.causal, negt);
+    } else {
+      f32x16 acc = Ops::scores(kc, qf, kb, row0, qrow, h, p.causal);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[r] = fmaf(cx, acc[r], -tau);
+      return acc;
+    }
+  };
 
   // ---------------------------------------------------------------- refinement passes
+  // per-row sums: v0 = sum d^kappa, v1 = sum d^(kappa-1), v2 = support size (alpha 1.5, 2)
+  // or sum d^(kappa-2), v3 = sum (x - hi)_+^kappa (secant start), v4 = smallest positive
+  // gap x - tau (alpha 1.5, 2)
   const float kappa = p.kappa, alpha = p.alpha;
   bool done = false;
   int rowpass = 0;
@@ -427,7 +454,11 @@ __global__ __launch_bounds__(256) void k_refine_out(FwdParams p) {
     if (ballot(!done) == 0) break;
     const bool first = (npass == 0);
     const float thr = wave_min(done ? INFINITY : tau) * (float)B;
-    float F0 = 0.f, F1 = 0.f, F2 = 0.f, Fh = 0.f, mrel = INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) negt[r] = -tau;
+    float F0 = 0.f, F1 = 0.f, F2 = 0.f, Fh = 0.f;
+    int cnt = 0;
+    uint32_t mrelb = 0xFFFFFFFFu;        // positive floats order like their bits
     Walk wk{-1, 0u};
     int kb = walk_next(wk, thr);
     if (kb >= 0) Ops::load_k(kf, Kf, kb, c, h);
@@ -438,60 +469,68 @@ __global__ __launch_bounds__(256) void k_refine_out(FwdParams p) {
       const int kn = walk_next(wk, thr);
       if (kn >= 0) Ops::load_k(kf, Kf, kn, c, h);
       ++n_ref;
-      const f32x16 acc = Ops::scores(kc, qf, kb, row0, qrow, h, p.causal);
-      const float th = hi;
+      const f32x16 t = tile(kc, kb);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float t = cx * acc[r] - tau;           // -inf for masked keys
-        const bool in = t > 0.f;
-        const float dm = in ? t : 0.f;
+        const float tt = t[r];
         if constexpr (MODE == 2) {
-          F0 += dm * dm;
+          const float dm = fmaxf(tt, 0.f);
+          F0 = fmaf(dm, dm, F0);
           F1 += dm;
-          F2 += in ? 1.0f : 0.0f;
+          cnt += (tt > 0.f) ? 1 : 0;
+          mrelb = min(mrelb, __float_as_uint(tt));
         } else if constexpr (MODE == 1) {
-          F0 += dm;
-          F1 += in ? 1.0f : 0.0f;
+          F0 += fmaxf(tt, 0.f);
+          cnt += (tt > 0.f) ? 1 : 0;
+          mrelb = min(mrelb, __float_as_uint(tt));
         } else {
-          const float lt = log2f(dm);
+          const bool in = tt > 0.f;
+          const float lt = log2f(in ? tt : 1.0f);
           F0 += in ? exp2f(kappa * lt) : 0.f;
           F1 += in ? exp2f((kappa - 1.0f) * lt) : 0.f;
           F2 += in ? exp2f((kappa - 2.0f) * lt) : 0.f;
           if (secant && first) {
-            const float u = cx * acc[r] - th;
-            if (u > 0.f) Fh += exp2f(kappa * log2f(u));
+            const float u = tt - hB;       // x - hi on the first pass (hi = tau + 1/B)
+            Fh += u > 0.f ? exp2f(kappa * log2f(u)) : 0.f;
           }
         }
-        if constexpr (MODE != 0) mrel = fminf(mrel, in ? t : INFINITY);
       }
       kb = kn;
     }
     ++npass;
-    F0 += xor32f(F0);
-    F1 += xor32f(F1);
-    F2 += xor32f(F2);
-    Fh += xor32f(Fh);
-    mrel = fminf(mrel, xor32f(mrel));
+    // combine the two half-lanes of a row
+    float tot[5];
+    tot[0] = F0 + xor32f(F0);
+    tot[1] = F1 + xor32f(F1);
+    if constexpr (MODE == 0) {
+      tot[2] = F2 + xor32f(F2);
+      tot[4] = INFINITY;
+    } else {
+      tot[2] = (float)(cnt + xor32i(cnt));
+      const uint32_t mb = min(mrelb, (uint32_t)xor32i((int)mrelb));
+      tot[4] = mb < 0x7F800000u ? __uint_as_float(mb) : INFINITY;
+    }
+    tot[3] = Fh + xor32f(Fh);
     if (!done) {
-      const float f = F0 - 1.0f;
+      const float f = tot[0] - 1.0f;
       const float t0 = tau;
       if (f >= 0.f) lo = t0; else hi = t0;
       if (first && f < 0.f) lo = t0 - hB;   // rounding lost the histogram bound
       bool fin_row = false;
       // alpha in {1.5, 2}: the root of the equation restricted to the support {x > t0}
-      // is exact when it keeps that support (it lies at or above t0 and at or below the
-      // support's smallest score): then stop without a confirming pass.
+      // is exact when it keeps that support (it lies at or above t0 and no further than
+      // the support's smallest gap): then stop without a confirming pass
       if constexpr (MODE == 1 || MODE == 2) {
-        const float cntS = (MODE == 2) ? F2 : F1;
+        const float cntS = tot[2];
         if (cntS > 0.f && f >= 0.f) {
           float u;
           if constexpr (MODE == 2) {
-            const float disc = F1 * F1 - cntS * f;
-            u = disc >= 0.f ? f / (F1 + sqrtf(disc)) : INFINITY;
+            const float disc = tot[1] * tot[1] - cntS * f;
+            u = disc >= 0.f ? f / (tot[1] + sqrtf(disc)) : INFINITY;
           } else {
             u = f / cntS;
           }
-          if (u <= mrel) {
+          if (u <= tot[4]) {
             tau = t0 + u;
             fin_row = true;
           }
@@ -502,24 +541,32 @@ __global__ __launch_bounds__(256) void k_refine_out(FwdParams p) {
         rowpass = npass;
       } else {
         float tn;
-        if (alpha <= 1.5f) {
-          const float fp = -kappa * F1;
-          const float fpp = kappa * (kappa - 1.0f) * F2;
+        if constexpr (MODE == 2) {
+          // Halley on f = sum d^2 - 1: f' = -2 sum d, f'' = 2 |support|
+          const float fp = -2.0f * tot[1];
+          const float fpp = 2.0f * tot[2];
           tn = t0 - 2.0f * f * fp / (2.0f * fp * fp - f * fpp);
-        } else if (alpha <= 2.0f) {
-          const float fp = -kappa * F1;
-          tn = t0 - f / fp;
+        } else if constexpr (MODE == 1) {
+          tn = tot[2] > 0.f ? t0 + f / tot[2] : 0.5f * (lo + hi);   // Newton, f' = -|support|
         } else {
-          if (first) {
-            const float th = t0 + hB;
-            const float fh = Fh - 1.0f;
-            if (fh >= 0.f) lo = th; else hi = fminf(hi, th);
-            tn = t0 - f * (th - t0) / (fh - f);
+          const float fp = -kappa * tot[1];
+          if (alpha <= 1.5f) {
+            const float fpp = kappa * (kappa - 1.0f) * tot[2];
+            tn = t0 - 2.0f * f * fp / (2.0f * fp * fp - f * fpp);
+          } else if (alpha <= 2.0f) {
+            tn = t0 - f / fp;
           } else {
-            tn = t0 - f * (t0 - tprev) / (f - fprev);
+            if (first) {
+              const float thi = t0 + hB;
+              const float fh = tot[3] - 1.0f;
+              if (fh >= 0.f) lo = thi; else hi = fminf(hi, thi);
+              tn = t0 - f * (thi - t0) / (fh - f);
+            } else {
+              tn = t0 - f * (t0 - tprev) / (f - fprev);
+            }
+            tprev = t0;
+            fprev = f;
           }
-          tprev = t0;
-          fprev = f;
         }
         // converged when the solver's own step is below tolerance (tested before the
         // bracket check: a vanishing step lands on a bracket end and must not be
@@ -550,6 +597,8 @@ __global__ __launch_bounds__(256) void k_refine_out(FwdParams p) {
   }
   float sg = 0.f;
   const float othr = wave_min(tau) * (float)B;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) negt[r] = -tau;
   unsigned long long n_out = 0;
   // exact mask bits of this wave, OR-ed into the tile's words one word at a time
   uint32_t* mrow = p.mask + (bh * p.Tr + row0 / p.Br) * p.W;
@@ -565,20 +614,18 @@ __global__ __launch_bounds__(256) void k_refine_out(FwdParams p) {
       for (int s = 0; s < DS; ++s) kc[s] = kf[s];
       const int kn = walk_next(wk, othr);
       if (kn >= 0) Ops::load_k(kf, Kf, kn, c, h);
-      const f32x16 acc = Ops::scores(kc, qf, kb, row0, qrow, h, p.causal);
+      const f32x16 t = tile(kc, kb);
       f32x16 pw, gw;
-      bool any = false;
+      float mx = 0.f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float t = cx * acc[r] - tau;
-        const bool in = t > 0.f;
-        const float dm = in ? t : 0.f;
+        const float dm = fmaxf(t[r], 0.f);
         pw[r] = Weight<MODE>::p(dm, kappa);
         gw[r] = Weight<MODE>::g(dm, kappa);
         sg += gw[r];
-        any = any || in;
+        mx = fmaxf(mx, dm);
       }
-      if (ballot(any) != 0) {
+      if (ballot(mx > 0.f) != 0) {
         ++n_out;
         const int J = (kb * 32) / p.Bc;          // key block of this sub-block
         if ((J >> 5) != mw) {
@@ -588,11 +635,11 @@ __global__ __launch_bounds__(256) void k_refine_out(FwdParams p) {
         }
         mbits |= 1u << (J & 31);
         Frag<T> vf[DC][2];
+        const T* vp = Vf + (size_t)kb * (DC * 1024);
 #pragma unroll
         for (int dc = 0; dc < DC; ++dc)
 #pragma unroll
-          for (int m = 0; m < 2; ++m)
-            load_frag(vf[dc][m], Vf + ((size_t)(((kb * DC + dc) * 2 + m) * 2 + h) * 32 + c) * 8);
+          for (int m = 0; m < 2; ++m) load_frag(vf[dc][m], vp + (dc * 2 + m) * 512 + lane * 8);
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
           Frag<T> pf, gf;
@@ -630,11 +677,13 @@ __global__ __launch_bounds__(256) void k_refine_out(FwdParams p) {
     if (h == 0) p.tau[row] = tau;
   }
   if (p.stats) {
-    // rows by refinement passes (rows that hit the cap go to max_iters + 1)
-    for (int ps = 1; ps <= p.max_iters + 1; ++ps) {
-      const int rp = done ? rowpass : p.max_iters + 1;
-      const int cntp = __popcll(ballot(h == 0 && rp == ps));
-      if (lane == 0 && cntp) atomicAdd(&p.stats[ps], (unsigned long long)cntp);
+    {
+      // rows by refinement passes (rows that hit the cap go to max_iters + 1)
+      for (int ps = 1; ps <= p.max_iters + 1; ++ps) {
+        const int rp = done ? rowpass : p.max_iters + 1;
+        const int cntp = __popcll(ballot(h == 0 && rp == ps));
+        if (lane == 0 && cntp) atomicAdd(&p.stats[ps], (unsigned long long)cntp);
+      }
     }
     if (lane == 0) {
       atomicAdd(&p.stats[21], n_ref);
@@ -647,6 +696,15 @@ template <typename T, int D>
 static void (*hist_kernel(bool qs, int mode))(FwdParams) {
   if (qs) return mode == 1 ? k_hist<T, D, 1, true> : mode == 2 ? k_hist<T, D, 2, true> : k_hist<T, D, 0, true>;
   return mode == 1 ? k_hist<T, D, 1, false> : mode == 2 ? k_hist<T, D, 2, false> : k_hist<T, D, 0, false>;
+}
+
+template <typename T, int D>
+static void (*out_kernel(bool qs, int mode))(FwdParams) {
+  if (qs)
+    return mode == 1 ? k_refine_out<T, D, 1, true> : mode == 2 ? k_refine_out<T, D, 2, true>
+                                                               : k_refine_out<T, D, 0, true>;
+  return mode == 1 ? k_refine_out<T, D, 1, false> : mode == 2 ? k_refine_out<T, D, 2, false>
+                                                              : k_refine_out<T, D, 0, false>;
 }
 
 size_t fwd_lds_bytes(int B) { return (size_t)(HIST_WAVES * (B + 2) * 64) * sizeof(uint32_t); }
@@ -668,10 +726,10 @@ static hipError_t launch_fwd_t(const FwdParams& p, int mode, hipStream_t s) {
   hipLaunchKernelGGL(hist_fn, dim3(grid), dim3(64 * HIST_WAVES), lds, s, p);
   prof_end(s);
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  // (at head_dim 128 the extra accumulator block of the folded form would spill)
+  void (*out_fn)(FwdParams) = out_kernel<T, D>(qs && D == 64, mode);
   prof_begin("entmax_fwd_refine_out", s);
-  if (mode == 1) hipLaunchKernelGGL((k_refine_out<T, D, 1>), dim3(grid2), dim3(64 * OUT_WAVES), 0, s, p);
-  else if (mode == 2) hipLaunchKernelGGL((k_refine_out<T, D, 2>), dim3(grid2), dim3(64 * OUT_WAVES), 0, s, p);
-  else hipLaunchKernelGGL((k_refine_out<T, D, 0>), dim3(grid2), dim3(64 * OUT_WAVES), 0, s, p);
+  hipLaunchKernelGGL(out_fn, dim3(grid2), dim3(64 * OUT_WAVES), 0, s, p);
   prof_end(s);
   return hipGetLastError();
 }

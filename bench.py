@@ -83,30 +83,29 @@ def popcount_mask(mask) -> int:
 
 def cpu_baseline(w, inp_cpu, target_s: float):
     """Time the fp64 oracle (fwd + bwd) on whole query heads until ~target_s, extrapolate."""
-    import numpy as np
     import oracle
     threads = oracle.default_threads()
     G = w.heads_q // w.heads_kv
+    scale = 1.0 / math.sqrt(w.head_dim)
     heads_done = 0
     t0 = time.time()
-    q = inp_cpu["q"]
-    for h in range(w.heads_q):
-        if heads_done > 0 and time.time() - t0 > target_s:
-            break
-        kh = h // G
-        qh = q[0, h].double().numpy()
-        kk = inp_cpu["k"][0, kh].double().numpy()
-        vv = inp_cpu["v"][0, kh].double().numpy()
-        do = inp_cpu["do"][0, h].double().numpy()
-        scale = 1.0 / math.sqrt(w.head_dim)
-        f = oracle.attn_fwd_head(qh, kk, vv, w.alpha, w.causal, w.n_bins, w.block_k, scale,
-                                 threads=threads)
-        r = oracle.attn_bwd_rows_head(qh, kk, vv, do, f["tau"], w.alpha, w.causal, scale,
-                                      threads=threads)
-        # the key-side backward of one query head's contribution (G = 1 share of its KV head)
-        oracle.attn_bwd_keys_group(qh[None], kk, vv, do[None], f["tau"][None], r["delta"][None],
-                                   w.alpha, w.causal, scale, threads=threads)
-        heads_done += 1
+    for bi in range(w.batch):
+        for h in range(w.heads_q):
+            if heads_done > 0 and time.time() - t0 > target_s:
+                break
+            kh = h // G
+            qh = inp_cpu["q"][bi, h].double().numpy()
+            kk = inp_cpu["k"][bi, kh].double().numpy()
+            vv = inp_cpu["v"][bi, kh].double().numpy()
+            do = inp_cpu["do"][bi, h].double().numpy()
+            f = oracle.attn_fwd_head(qh, kk, vv, w.alpha, w.causal, w.n_bins, w.block_k, scale,
+                                     threads=threads)
+            r = oracle.attn_bwd_rows_head(qh, kk, vv, do, f["tau"], w.alpha, w.causal, scale,
+                                          threads=threads)
+            # the key-side backward of this query head's share of its KV head
+            oracle.attn_bwd_keys_group(qh[None], kk, vv, do[None], f["tau"][None], r["delta"][None],
+                                       w.alpha, w.causal, scale, threads=threads)
+            heads_done += 1
     el = time.time() - t0
     total_heads = w.batch * w.heads_q
     s_per_step = el * total_heads / heads_done

@@ -77,7 +77,8 @@ typedef struct {
     int32_t block_k;      /* Bc, keys of a mask block: 32, 64 or 128; seqlen % Bc == 0 */
     int32_t n_bins;       /* B, histogram bins: 2, 4, 8 or 16 (bin width 1/B on the x-scale) */
     float scale;          /* score scale; 0 means 1/sqrt(head_dim) */
-    int32_t max_iters;    /* cap on refinement passes; 0 means 8 (15 if alpha > 2); at most 15 */
+    int32_t max_iters;    /* cap on refinement passes; 0 means 8 for alpha <= 1.5, 12 for
+                             1.5 < alpha <= 2, 15 for alpha > 2; at most 15 */
     float tol;            /* stop when |step| <= tol * max(1, |tau|); 0 means 2^-20 */
 } entmax_attn_desc;
 

@@ -118,7 +118,9 @@ static entmax_status derive(const entmax_attn_desc* d, Derived& o) {
     return fail(ENTMAX_ERR_UNSUPPORTED, "n_bins %d: must be 2, 4, 8 or 16", o.B);
   if (d->causal != 0 && d->causal != 1) return fail(ENTMAX_ERR_SHAPE, "causal must be 0 or 1");
   o.causal = d->causal;
-  o.max_iters = d->max_iters == 0 ? (d->alpha > 2.0f ? 15 : 8) : d->max_iters;
+  // default pass caps: Halley (alpha <= 1.5) converges in a few passes; Newton from
+  // below shrinks a large support about by half per pass; the secant needs the most
+  o.max_iters = d->max_iters != 0 ? d->max_iters : d->alpha > 2.0f ? 15 : d->alpha > 1.5f ? 12 : 8;
   if (o.max_iters < 1 || o.max_iters > 15)
     return fail(ENTMAX_ERR_SHAPE, "max_iters %d: must be 0 (default) or 1..15", d->max_iters);
   if (!(d->scale >= 0.0f) || !isfinite(d->scale)) return fail(ENTMAX_ERR_SHAPE, "scale must be >= 0 and finite");

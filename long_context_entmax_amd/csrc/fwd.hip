@@ -11,7 +11,7 @@
 //      bracket's lower end lies in one of them) and records each marked sub-block's
 //      largest score per 32-row chunk.
 //   2. k_refine_out -- refinement passes: a safeguarded hybrid root solver on
-//      f(tau) = sum_j [x_j - tau]_+^kappa - 1 from tau_h with bracket [tau_h, tau_h + 1/B]:
+//      f(tau) = sum_j [x_j - tau]_+^kappa - 1 in the bracket [tau_h, tau_h + 1/B]:
 //      Halley (alpha <= 1.5), Newton (1.5 < alpha <= 2), secant (alpha > 2, started by
 //      false position on the bracket ends), bisection whenever a step leaves the bracket
 //      (page 1 section 2.2, page 3 section 2.2). Each pass visits only the marked
@@ -400,9 +400,14 @@ __global__ __launch_bounds__(64 * OUT_WAVES, 2) void k_refine_out(FwdParams p) {
     for (int s = 0; s < DS; ++s) scale_frag(qf[s], p.cx);
   }
   const float cx = p.cx;
-  float tau = p.tauh_ws[bh * n + qrow];
+  // Bracket [tau_h, tau_h + 1/B] (with a margin of 1/(16B) below tau_h for fp32 rounding of
+  // the B-bin solve); the first evaluation is a quarter of the way into it. Starting above
+  // tau_h leaves out the sub-blocks whose scores all lie in the bottom quarter, and on the
+  // workloads' rows it also takes fewer passes than starting at tau_h.
+  const float tau_h = p.tauh_ws[bh * n + qrow];
   const float hB = 1.0f / (float)B;
-  float lo = tau, hi = tau + hB;
+  float lo = tau_h - 0.0625f * hB, hi = tau_h + hB;
+  float tau = tau_h + 0.25f * hB;
 
   // Walk over the sub-blocks a pass needs: candidate bits of the histogram pass, kept
   // where the recorded chunk max exceeds the threshold (read 32 at a time).
@@ -457,6 +462,7 @@ __global__ __launch_bounds__(64 * OUT_WAVES, 2) void k_refine_out(FwdParams p) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) negt[r] = -tau;
     float F0 = 0.f, F1 = 0.f, F2 = 0.f, Fh = 0.f;
+    const float thi = hi - tau;          // secant start: f at the bracket's upper end
     int cnt = 0;
     uint32_t mrelb = 0xFFFFFFFFu;        // positive floats order like their bits
     Walk wk{-1, 0u};
@@ -490,7 +496,7 @@ __global__ __launch_bounds__(64 * OUT_WAVES, 2) void k_refine_out(FwdParams p) {
           F1 += in ? exp2f((kappa - 1.0f) * lt) : 0.f;
           F2 += in ? exp2f((kappa - 2.0f) * lt) : 0.f;
           if (secant && first) {
-            const float u = tt - hB;       // x - hi on the first pass (hi = tau + 1/B)
+            const float u = tt - thi;      // x - hi
             Fh += u > 0.f ? exp2f(kappa * log2f(u)) : 0.f;
           }
         }
@@ -515,7 +521,6 @@ __global__ __launch_bounds__(64 * OUT_WAVES, 2) void k_refine_out(FwdParams p) {
       const float f = tot[0] - 1.0f;
       const float t0 = tau;
       if (f >= 0.f) lo = t0; else hi = t0;
-      if (first && f < 0.f) lo = t0 - hB;   // rounding lost the histogram bound
       bool fin_row = false;
       // alpha in {1.5, 2}: the root of the equation restricted to the support {x > t0}
       // is exact when it keeps that support (it lies at or above t0 and no further than
@@ -557,10 +562,10 @@ __global__ __launch_bounds__(64 * OUT_WAVES, 2) void k_refine_out(FwdParams p) {
             tn = t0 - f / fp;
           } else {
             if (first) {
-              const float thi = t0 + hB;
+              const float th = t0 + thi;   // the bracket's upper end at the start of the pass
               const float fh = tot[3] - 1.0f;
-              if (fh >= 0.f) lo = thi; else hi = fminf(hi, thi);
-              tn = t0 - f * (thi - t0) / (fh - f);
+              if (fh >= 0.f) lo = fmaxf(lo, th); else hi = fminf(hi, th);
+              tn = t0 - f * (th - t0) / (fh - f);
             } else {
               tn = t0 - f * (t0 - tprev) / (f - fprev);
             }

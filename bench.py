@@ -40,6 +40,12 @@ def parse():
     ap.add_argument("--config", default="C2")
     ap.add_argument("--alpha", type=float, default=None)
     ap.add_argument("--sparsity", type=float, default=None)
+    ap.add_argument("--tau-init", choices=("hist", "bracket"), default="hist",
+                    help="refinement start: the histogram bound (the method) or the plain "
+                         "[x_max - 1, x_max - n^(1-alpha)] bracket (ablation)")
+    ap.add_argument("--tau-error", action="store_true",
+                    help="instead of timing, print the mean |tau_p - tau*| after p = 1..15 "
+                         "refinement passes for both starts (tau* = the converged tau)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample time")
     ap.add_argument("--profile-only", action="store_true",
@@ -120,6 +126,36 @@ def cpu_baseline(w, inp_cpu, target_s: float):
     }
 
 
+def tau_error_study(lce, w, q, k, v, blk, wsf):
+    """Mean absolute error of tau per refinement pass, histogram start vs plain bracket
+    (the study of the pages' Fig. 3, page 5 section 4). tau* is the histogram-started solve
+    with the largest pass cap; the bracket-started solve at that cap is reported beside it."""
+    import torch
+    b, hq, n, d = q.shape
+
+    def run(t_init, iters):
+        r = lce.fwd(q, k, v, w.alpha, w.causal, blk, w.n_bins, max_iters=iters, workspace=wsf,
+                    return_hist=True, tau_init=t_init)
+        torch.cuda.synchronize()
+        return r.tau.double().cpu(), r.tau_h.double().cpu()
+
+    ref, tau_h = run(0, 15)
+    out = {"study": "tau_mean_abs_error_per_pass", "workload": w.name, "alpha": w.alpha,
+           "n_bins": w.n_bins, "rows": b * hq * n}
+    start = tau_h + 0.25 / w.n_bins
+    out["histogram"] = {"tau_h": (tau_h - ref).abs().mean().item(),
+                        "start": (start - ref).abs().mean().item(), "passes": []}
+    tb15, xm1 = run(1, 15)
+    out["bracket"] = {"start": (xm1 - ref).abs().mean().item(), "passes": [],
+                      "cap15_vs_ref_max": (tb15 - ref).abs().max().item()}
+    for it in range(1, 16):
+        th, _ = run(0, it)
+        tb, _ = run(1, it)
+        out["histogram"]["passes"].append((th - ref).abs().mean().item())
+        out["bracket"]["passes"].append((tb - ref).abs().mean().item())
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -143,13 +179,19 @@ def main():
                       torch.empty((b, hq, Tr, W), dtype=torch.int32, device=dev),
                       torch.empty((b, hq, n, d), dtype=torch.float32, device=dev), None, None)
     grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
-    desc = lce._desc_for(q, k, w.alpha, w.causal, blk, w.n_bins, None, 0, 0.0)
+    tau_init = 0 if args.tau_init == "hist" else 1
+    desc = lce._desc_for(q, k, w.alpha, w.causal, blk, w.n_bins, None, 0, 0.0, tau_init)
     fws, bws = lce.workspace_bytes(desc)
     wsf = torch.empty(max(fws, 256), dtype=torch.uint8, device=dev)
     wsb = torch.empty(max(bws, 256), dtype=torch.uint8, device=dev)
 
+    if args.tau_error:
+        print(json.dumps(tau_error_study(lce, w, q, k, v, blk, wsf)), flush=True)
+        return
+
     def step(stats=None):
-        r = lce.fwd(q, k, v, w.alpha, w.causal, blk, w.n_bins, workspace=wsf, out=outs, stats=stats)
+        r = lce.fwd(q, k, v, w.alpha, w.causal, blk, w.n_bins, workspace=wsf, out=outs, stats=stats,
+                    tau_init=tau_init)
         lce.bwd(q, k, v, do, r.tau, r.mask, r.aux, w.alpha, w.causal, blk, w.n_bins, workspace=wsb,
                 out=grads)
 
@@ -236,6 +278,7 @@ def main():
             "workload": f"{w.name}: b{w.batch} hq{w.heads_q}/hkv{w.heads_kv} n{w.seqlen} d{w.head_dim} "
                         f"{w.dtype} {'causal' if w.causal else 'full'} alpha {w.alpha} blocks "
                         f"{w.block_q}x{w.block_k} B {w.n_bins}",
+            "tau_start": "histogram" if tau_init == 0 else "plain bracket (ablation)",
             "target_block_sparsity": w.target_sparsity, "beta": w.beta,
             "achieved_block_sparsity": round(sparsity, 4), "nonzero_blocks": nnzb, "valid_blocks": nvb,
         },

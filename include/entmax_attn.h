@@ -80,6 +80,12 @@ typedef struct {
     int32_t max_iters;    /* cap on refinement passes; 0 means 8 for alpha <= 1.5, 12 for
                              1.5 < alpha <= 2, 15 for alpha > 2; at most 15 */
     float tol;            /* stop when |step| <= tol * max(1, |tau|); 0 means 2^-20 */
+    int32_t tau_init;     /* start of the refinement: 0 = the histogram bound tau_h and the
+                             bracket [tau_h, tau_h + 1/B] (page 1 section 2.1-2.2, page 3
+                             section 2.1-2.2); 1 = no histogram, the plain bracket
+                             [x_max - 1, x_max - n_valid^(1-alpha)] from its lower end (the
+                             start the pages measure the histogram against, page 5 section 4),
+                             for ablation; max_iters 0 then means 15 */
 } entmax_attn_desc;
 
 /* Supported: head_dim 64 or 128 (bf16 and fp32); seqlen <= 2^19 (and a multiple of both blocks). */

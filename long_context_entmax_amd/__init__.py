@@ -39,7 +39,7 @@ class Desc(ctypes.Structure):
         ("seqlen", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32),
         ("alpha", ctypes.c_float), ("causal", ctypes.c_int32), ("block_q", ctypes.c_int32),
         ("block_k", ctypes.c_int32), ("n_bins", ctypes.c_int32), ("scale", ctypes.c_float),
-        ("max_iters", ctypes.c_int32), ("tol", ctypes.c_float),
+        ("max_iters", ctypes.c_int32), ("tol", ctypes.c_float), ("tau_init", ctypes.c_int32),
     ]
 
 
@@ -95,9 +95,11 @@ def _check(status: int) -> None:
 
 def make_desc(batch: int, heads_q: int, heads_kv: int, seqlen: int, head_dim: int, dtype: int,
               alpha: float, causal: bool, block: Tuple[int, int], bins: int,
-              scale: Optional[float] = None, max_iters: int = 0, tol: float = 0.0) -> Desc:
+              scale: Optional[float] = None, max_iters: int = 0, tol: float = 0.0,
+              tau_init: int = 0) -> Desc:
     return Desc(batch, heads_q, heads_kv, seqlen, head_dim, dtype, float(alpha), int(bool(causal)),
-                int(block[0]), int(block[1]), int(bins), float(scale or 0.0), int(max_iters), float(tol))
+                int(block[0]), int(block[1]), int(bins), float(scale or 0.0), int(max_iters), float(tol),
+                int(tau_init))
 
 
 def _torch():
@@ -105,7 +107,7 @@ def _torch():
     return torch
 
 
-def _desc_for(q, k, alpha, causal, block, bins, scale, max_iters, tol) -> Desc:
+def _desc_for(q, k, alpha, causal, block, bins, scale, max_iters, tol, tau_init: int = 0) -> Desc:
     torch = _torch()
     if q.dim() != 4 or k.dim() != 4:
         raise ValueError("q and k must be [batch, heads, seqlen, head_dim]")
@@ -116,7 +118,8 @@ def _desc_for(q, k, alpha, causal, block, bins, scale, max_iters, tol) -> Desc:
     else:
         raise ValueError(f"unsupported dtype {q.dtype}")
     b, hq, n, d = q.shape
-    return make_desc(b, hq, k.shape[1], n, d, dt, alpha, causal, block, bins, scale, max_iters, tol)
+    return make_desc(b, hq, k.shape[1], n, d, dt, alpha, causal, block, bins, scale, max_iters, tol,
+                     tau_init)
 
 
 def _ptr(t) -> Optional[int]:
@@ -148,16 +151,17 @@ FwdOut = namedtuple("FwdOut", "o tau mask aux hist tau_h")
 
 def fwd(q, k, v, alpha: float = 1.5, causal: bool = True, block=(64, 64), bins: int = 16,
         scale: Optional[float] = None, max_iters: int = 0, tol: float = 0.0,
-        return_hist: bool = False, stats=None, workspace=None, out=None) -> FwdOut:
+        return_hist: bool = False, stats=None, workspace=None, out=None, tau_init: int = 0) -> FwdOut:
     """alpha-entmax attention forward. Returns (o, tau, mask, aux, hist, tau_h); o is float32.
 
     hist/tau_h are the histogram stage's counts [b,hq,n,B] and lower bound [b,hq,n]
     (None unless return_hist). ``stats``: optional int64 CUDA tensor [32] (accumulated).
-    ``out``: optional FwdOut of preallocated tensors to write into.
+    ``out``: optional FwdOut of preallocated tensors to write into. ``tau_init``: 0 starts
+    the refinement from the histogram bound, 1 from the plain bracket below the row max.
     """
     torch = _torch()
     _require_gpu(q, k, v)
-    desc = _desc_for(q, k, alpha, causal, block, bins, scale, max_iters, tol)
+    desc = _desc_for(q, k, alpha, causal, block, bins, scale, max_iters, tol, tau_init)
     L = lib()
     b, hq, n, d = q.shape
     dev = q.device

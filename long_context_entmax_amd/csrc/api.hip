@@ -82,7 +82,7 @@ void prof_end(hipStream_t s) {
 // argument checks and derived sizes
 // ------------------------------------------------------------------------------------------
 struct Derived {
-  int b, hq, hkv, n, D, G, dtype, causal, Br, Bc, B, max_iters;
+  int b, hq, hkv, n, D, G, dtype, causal, Br, Bc, B, max_iters, tau_init;
   float alpha, scale, tol, kappa;
   int mode;               // 1: alpha = 2, 2: alpha = 1.5, 0: other
   int Tr, Tc, W, WT, nkb, NW32;
@@ -120,7 +120,14 @@ static entmax_status derive(const entmax_attn_desc* d, Derived& o) {
   o.causal = d->causal;
   // default pass caps: Halley (alpha <= 1.5) converges in a few passes; Newton from
   // below shrinks a large support about by half per pass; the secant needs the most
-  o.max_iters = d->max_iters != 0 ? d->max_iters : d->alpha > 2.0f ? 15 : d->alpha > 1.5f ? 12 : 8;
+  if (d->tau_init != 0 && d->tau_init != 1)
+    return fail(ENTMAX_ERR_UNSUPPORTED, "tau_init %d: must be 0 (histogram) or 1 (plain bracket)", d->tau_init);
+  o.tau_init = d->tau_init;
+  o.max_iters = d->max_iters != 0       ? d->max_iters
+                : (o.tau_init == 1)    ? 15
+                : d->alpha > 2.0f      ? 15
+                : d->alpha > 1.5f      ? 12
+                                       : 8;
   if (o.max_iters < 1 || o.max_iters > 15)
     return fail(ENTMAX_ERR_SHAPE, "max_iters %d: must be 0 (default) or 1..15", d->max_iters);
   if (!(d->scale >= 0.0f) || !isfinite(d->scale)) return fail(ENTMAX_ERR_SHAPE, "scale must be >= 0 and finite");
@@ -263,6 +270,7 @@ entmax_status entmax_attn_fwd(const entmax_attn_desc* desc, const void* q, const
   p.tauh_ws = (float*)(wsb + 2 * fwd_kv_bytes(o) + fwd_dmax_bytes(o) + fwd_cand_bytes(o));
   p.b = o.b; p.hq = o.hq; p.hkv = o.hkv; p.n = o.n; p.G = o.G;
   p.causal = o.causal; p.Br = o.Br; p.Bc = o.Bc; p.B = o.B; p.max_iters = o.max_iters;
+  p.tau_init = o.tau_init;
   p.cx = (float)(((double)o.alpha - 1.0) * (double)o.scale);
   p.alpha = o.alpha; p.kappa = o.kappa; p.tol = o.tol;
   p.GP = o.GP; p.RH = o.RH; p.RG = o.RG;

@@ -273,7 +273,7 @@ __global__ __launch_bounds__(512, ((D == 64 && sizeof(T) == 2) ? HIST_OCC64 : 2)
       }
       const bool act = act0 || act1;
       // slide a window up: cell k takes cell k + shift, the top cells start empty
-      const bool slide = act && (!have || Tn > Tt);
+      const bool slide = act && (!have || Tn > Tt) && p.tau_init == 0;
       if (ballot(slide) != 0) {
         const int shift = slide ? (have ? Tn - Tt : B + 1) : 0;
         for (int k = 1; k <= B; ++k) {
@@ -301,6 +301,7 @@ __global__ __launch_bounds__(512, ((D == 64 && sizeof(T) == 2) ? HIST_OCC64 : 2)
       }
       // count every score of both tiles (lanes with no active tile land in cell 0)
       const float nbF = -(float)base;
+      if (p.tau_init == 0) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float y = QS ? acc0[r] : fmaf(cB, acc0[r], nbF);
@@ -314,6 +315,7 @@ __global__ __launch_bounds__(512, ((D == 64 && sizeof(T) == 2) ? HIST_OCC64 : 2)
           const uint32_t cell = cvt_u32_sat(y);
           atomicAdd(hl + (cell << 6), 1u);
         }
+      }
       }
     }
     // flush a finished word of sub-block bits and chunk maxima (kb is even: a word ends
@@ -342,15 +344,18 @@ __global__ __launch_bounds__(512, ((D == 64 && sizeof(T) == 2) ? HIST_OCC64 : 2)
     }
     cnt[k] = mine + xor32i(mine);
   }
-  const float tau_h = tau_from_counts<MODE>(cnt, Tf, B, p.kappa);
+  // bracket mode: the refinement starts from the row max (x_max, handed over in place of
+  // tau_h); the test output tau_h is then its lower end x_max - 1 and the counts are 0
+  const float xmax = fmaxf(mB, xor32f(mB)) / (float)B;
+  const float tau_h = p.tau_init == 0 ? tau_from_counts<MODE>(cnt, Tf, B, p.kappa) : xmax - 1.0f;
   if (h == 0) {
     const size_t row = bh * n + qrow;
-    p.tauh_ws[row] = tau_h;
+    p.tauh_ws[row] = p.tau_init == 0 ? tau_h : xmax;
     if (p.tau_h) p.tau_h[row] = tau_h;
     if (p.hist) {
       int32_t* dst = p.hist + row * B;
       for (int k = 0; k < 16; ++k)
-        if (k < B) dst[k] = cnt[k];
+        if (k < B) dst[k] = p.tau_init == 0 ? cnt[k] : 0;
     }
   }
   if (p.stats && lane == 0) {
@@ -404,10 +409,21 @@ __global__ __launch_bounds__(64 * OUT_WAVES, 2) void k_refine_out(FwdParams p) {
   // the B-bin solve); the first evaluation is a quarter of the way into it. Starting above
   // tau_h leaves out the sub-blocks whose scores all lie in the bottom quarter, and on the
   // workloads' rows it also takes fewer passes than starting at tau_h.
-  const float tau_h = p.tauh_ws[bh * n + qrow];
   const float hB = 1.0f / (float)B;
-  float lo = tau_h - 0.0625f * hB, hi = tau_h + hB;
-  float tau = tau_h + 0.25f * hB;
+  float lo, hi, tau;
+  if (p.tau_init == 0) {
+    const float tau_h = p.tauh_ws[bh * n + qrow];
+    lo = tau_h - 0.0625f * hB;
+    hi = tau_h + hB;
+    tau = tau_h + 0.25f * hB;
+  } else {
+    // plain bracket [x_max - 1, x_max - n_valid^(1-alpha)], started at its lower end
+    const float xm = p.tauh_ws[bh * n + qrow];
+    const float nv = p.causal ? (float)(qrow + 1) : (float)n;
+    lo = xm - 1.0f;
+    hi = xm - exp2f((1.0f - p.alpha) * log2f(nv));
+    tau = lo;
+  }
 
   // Walk over the sub-blocks a pass needs: candidate bits of the histogram pass, kept
   // where the recorded chunk max exceeds the threshold (read 32 at a time).

@@ -60,6 +60,7 @@ struct FwdParams {
   int Tr, Tc, W;
   WgMap map;             // histogram kernel
   WgMap map2;            // refinement/output kernel
+  int tau_init;          // 0: histogram bound; 1: plain bracket from the row max (no histogram)
 };
 
 // one re-layout of X [heads, n, D] (prep.hip): any of the fragment-major row copy,

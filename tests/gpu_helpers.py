@@ -20,11 +20,12 @@ def to64(t: torch.Tensor) -> np.ndarray:
     return t.detach().float().cpu().numpy().astype(np.float64)
 
 
-def run_gpu(inp: dict, w: synth.Workload, with_bwd: bool = True, stats=None):
+def run_gpu(inp: dict, w: synth.Workload, with_bwd: bool = True, stats=None, tau_init: int = 0):
     d = dev()
     q, k, v = inp["q"].to(d), inp["k"].to(d), inp["v"].to(d)
     blk = (w.block_q, w.block_k)
-    r = lce.fwd(q, k, v, w.alpha, w.causal, blk, w.n_bins, return_hist=True, stats=stats)
+    r = lce.fwd(q, k, v, w.alpha, w.causal, blk, w.n_bins, return_hist=True, stats=stats,
+                tau_init=tau_init)
     out = {"o": r.o, "tau": r.tau, "mask": r.mask, "aux": r.aux, "hist": r.hist, "tau_h": r.tau_h}
     if with_bwd:
         do = inp["do"].to(d)

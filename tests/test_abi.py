@@ -26,6 +26,23 @@ def L():
     return lce.lib()
 
 
+def test_desc_fields_match_header():
+    """The binding's Desc has the header struct's fields, in order and with 4-byte types."""
+    src = open(HEADER).read()
+    body = re.search(r"typedef struct \{(.*?)\} entmax_attn_desc;", src, flags=re.S).group(1)
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    names = []
+    for decl in body.split(";"):
+        decl = decl.strip()
+        if not decl:
+            continue
+        typ, _, rest = decl.partition(" ")
+        assert typ in ("int32_t", "float"), decl
+        names += [x.strip() for x in rest.split(",")]
+    assert names == [f[0] for f in lce.Desc._fields_]
+    assert ctypes.sizeof(lce.Desc) == 4 * len(names)
+
+
 def test_exports_every_declared_symbol(L):
     names = _declared()
     assert len(names) >= 10
@@ -41,7 +58,8 @@ def _desc(**kw):
     blk = base.pop("block")
     return lce.make_desc(base["batch"], base["heads_q"], base["heads_kv"], base["seqlen"],
                          base["head_dim"], base["dtype"], base["alpha"], base["causal"], blk,
-                         base["bins"], base.get("scale"), base.get("max_iters", 0), base.get("tol", 0.0))
+                         base["bins"], base.get("scale"), base.get("max_iters", 0), base.get("tol", 0.0),
+                         base.get("tau_init", 0))
 
 
 BAD = [
@@ -49,7 +67,7 @@ BAD = [
     (dict(heads_q=3, heads_kv=2), 2), (dict(seqlen=100), 2), (dict(seqlen=-64), 2),
     (dict(head_dim=96), 4), (dict(block=(48, 64)), 4), (dict(block=(64, 256)), 4),
     (dict(bins=12), 4), (dict(bins=32), 4), (dict(dtype=7), 4), (dict(seqlen=1 << 20), 4),
-    (dict(max_iters=16), 2), (dict(heads_kv=0), 2),
+    (dict(max_iters=16), 2), (dict(heads_kv=0), 2), (dict(tau_init=2), 4), (dict(tau_init=-1), 4),
 ]
 
 

@@ -90,6 +90,30 @@ def test_bf16_random_shapes(case):
         assert err < 2e-2, (name, err)
 
 
+BRACKET_CASES = [CASES[0], CASES[1], CASES[3], CASES[4], CASES[6]]
+
+
+@pytest.mark.parametrize("case", BRACKET_CASES, ids=[str(c) for c in BRACKET_CASES])
+def test_plain_bracket_start(case):
+    """Starting the refinement from [x_max - 1, x_max - n^(1-alpha)] without the histogram
+    (the ablation) reaches the same tau, output and gradients."""
+    b, hq, hkv, n, d, alpha, causal, Br, Bc, B, qs = case
+    print(f"[case] bracket start {case}", flush=True)
+    w = synth.Workload("t", b, hq, hkv, n, d, "bf16", alpha, causal, Br, Bc, B, "normal",
+                       extra={"qk_scale": qs}, seed=hash(case) & 0xFFFF)
+    inp = synth.make_inputs(w)
+    ref = _oracle(inp, w)
+    g = run_gpu(inp, w, tau_init=1)
+    assert np.abs(g["tau"].numpy() - ref["tau"]).max() < 1e-3
+    assert np.abs(g["o"].float().numpy() - ref["o"]).max() < 1e-2
+    # the reported lower end is x_max - 1 <= tau*, and no counts are produced
+    assert np.all(g["tau_h"].numpy() <= ref["tau"] + 1e-4)
+    assert int(np.abs(g["hist"].numpy()).sum()) == 0
+    for name in ("dq", "dk", "dv"):
+        err = rel_fro(g[name].float().numpy().astype(np.float64), ref[name])
+        assert err < 2e-2, (name, err)
+
+
 def test_fp32_random_causal_gqa():
     w = synth.Workload("t", 1, 4, 2, 128, 64, "f32", 1.5, True, 32, 32, 16, "tiny", seed=5)
     inp = synth.make_inputs(w)

@@ -43,6 +43,9 @@ def parse():
     ap.add_argument("--tau-init", choices=("hist", "bracket"), default="hist",
                     help="refinement start: the histogram bound (the method) or the plain "
                          "[x_max - 1, x_max - n^(1-alpha)] bracket (ablation)")
+    ap.add_argument("--nape", action="store_true",
+                    help="NAPE heads: the first half of the query heads without position "
+                         "encoding, the second half ALiBi (per-head slopes of the scores)")
     ap.add_argument("--tau-error", action="store_true",
                     help="instead of timing, print the mean |tau_p - tau*| after p = 1..15 "
                          "refinement passes for both starts (tau* = the converged tau)")
@@ -180,6 +183,7 @@ def main():
                       torch.empty((b, hq, n, d), dtype=torch.float32, device=dev), None, None)
     grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
     tau_init = 0 if args.tau_init == "hist" else 1
+    slopes = (torch.tensor(lce.nape_slopes(hq), dtype=torch.float32, device=dev) if args.nape else None)
     desc = lce._desc_for(q, k, w.alpha, w.causal, blk, w.n_bins, None, 0, 0.0, tau_init)
     fws, bws = lce.workspace_bytes(desc)
     wsf = torch.empty(max(fws, 256), dtype=torch.uint8, device=dev)
@@ -191,9 +195,9 @@ def main():
 
     def step(stats=None):
         r = lce.fwd(q, k, v, w.alpha, w.causal, blk, w.n_bins, workspace=wsf, out=outs, stats=stats,
-                    tau_init=tau_init)
+                    tau_init=tau_init, slopes=slopes)
         lce.bwd(q, k, v, do, r.tau, r.mask, r.aux, w.alpha, w.causal, blk, w.n_bins, workspace=wsb,
-                out=grads)
+                out=grads, slopes=slopes)
 
     for _ in range(args.warmup):
         step()
@@ -279,6 +283,7 @@ def main():
                         f"{w.dtype} {'causal' if w.causal else 'full'} alpha {w.alpha} blocks "
                         f"{w.block_q}x{w.block_k} B {w.n_bins}",
             "tau_start": "histogram" if tau_init == 0 else "plain bracket (ablation)",
+            "position_bias": "NAPE (half the heads ALiBi)" if args.nape else "none",
             "target_block_sparsity": w.target_sparsity, "beta": w.beta,
             "achieved_block_sparsity": round(sparsity, 4), "nonzero_blocks": nnzb, "valid_blocks": nvb,
         },

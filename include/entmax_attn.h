@@ -32,6 +32,13 @@
  *   aux                    forward-to-backward context, entmax_attn_aux_bytes() bytes,
  *                          opaque to the caller (pass the forward's aux to the backward).
  * Grouped-query attention: query head h reads KV head h / (heads_q / heads_kv).
+ *   slopes                 [heads_q] float32, optional (NULL = no position bias):
+ *                          query head h adds -slopes[h] * |i - j| to s_ij before the
+ *                          transform (ALiBi; slope 0 = a head without position encoding,
+ *                          so NAPE -- half the heads without encoding, half ALiBi, pages 2
+ *                          section 4 and 1 section 4.2 -- is one slopes array). Under the
+ *                          causal mask |i - j| = i - j. Forward and backward must get the
+ *                          same slopes.
  *
  * Ownership and execution: the caller allocates every buffer (device memory)
  * and the workspace; the library keeps no pointer after a call returns and
@@ -106,7 +113,8 @@ size_t entmax_attn_mask_words(const entmax_attn_desc *desc);
  * the candidate key blocks find tau; a last pass over the blocks that hold a
  * non-zero weight forms o, aux and the exact block mask.
  * Required: q, k, v, o, tau, block_mask, aux (16-byte aligned; tau and mask 4-byte).
- * Optional (NULL to skip): hist_counts and tau_h (the histogram stage's output,
+ * Optional (NULL to skip): slopes (position bias, 4-byte aligned, device memory);
+ * hist_counts and tau_h (the histogram stage's output,
  * a test hook), stats (device uint64[32], accumulated, never cleared by the library:
  * stats[p] for p = 1..max_iters counts query rows whose refinement stopped after p
  * passes, stats[max_iters + 1] rows that hit the cap; stats[20] key sub-blocks
@@ -116,7 +124,7 @@ size_t entmax_attn_mask_words(const entmax_attn_desc *desc);
  * workspace: at least entmax_attn_fwd_workspace_bytes(desc) bytes, 256-byte aligned.
  */
 entmax_status entmax_attn_fwd(const entmax_attn_desc *desc,
-                              const void *q, const void *k, const void *v,
+                              const void *q, const void *k, const void *v, const float *slopes,
                               void *o, float *tau, uint32_t *block_mask, void *aux,
                               int32_t *hist_counts, float *tau_h, uint64_t *stats,
                               void *workspace, size_t workspace_bytes, void *stream);
@@ -128,13 +136,15 @@ entmax_status entmax_attn_fwd(const entmax_attn_desc *desc,
  *   dS_ij = g_ij (dP_ij - delta_i),  dq_i = scale sum_j dS_ij k_j,
  *   dk_j = scale sum_i dS_ij q_i,    dv_j = sum_i p_ij dO_i  (summed over the GQA group).
  * Only key blocks set in block_mask are visited. tau, block_mask and aux must come from
- * entmax_attn_fwd with the same desc and inputs. dq, dk, dv are overwritten.
+ * entmax_attn_fwd with the same desc, inputs and slopes (the bias enters x, not the
+ * gradient formulas; NULL = none). dq, dk, dv are overwritten.
  * Alignment: every tensor 16 bytes (tau included), block_mask 4 bytes.
  * workspace: at least entmax_attn_bwd_workspace_bytes(desc) bytes, 256-byte aligned.
  */
 entmax_status entmax_attn_bwd(const entmax_attn_desc *desc,
                               const void *q, const void *k, const void *v, const void *dout,
-                              const float *tau, const uint32_t *block_mask, const void *aux,
+                              const float *slopes, const float *tau, const uint32_t *block_mask,
+                              const void *aux,
                               void *dq, void *dk, void *dv,
                               void *workspace, size_t workspace_bytes, void *stream);
 

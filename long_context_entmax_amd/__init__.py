@@ -11,6 +11,8 @@ built, every call raises.
     o = entmax_attention(q, k, v, alpha=1.5)          # autograd-aware
 
 Shapes: q, do [b, hq, n, d]; k, v [b, hkv, n, d]; dtype float32 or bfloat16.
+``slopes`` (optional, float32 [hq] on the device): per-head position-bias slopes; head h
+adds -slopes[h] |i - j| to its scores (``nape_slopes`` gives the NAPE heads).
 """
 from __future__ import annotations
 
@@ -72,9 +74,9 @@ def lib() -> ctypes.CDLL:
             getattr(L, f).restype = _sz
             getattr(L, f).argtypes = [_DP]
         L.entmax_attn_fwd.restype = ctypes.c_int
-        L.entmax_attn_fwd.argtypes = [_DP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+        L.entmax_attn_fwd.argtypes = [_DP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
         L.entmax_attn_bwd.restype = ctypes.c_int
-        L.entmax_attn_bwd.argtypes = [_DP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+        L.entmax_attn_bwd.argtypes = [_DP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
         L.entmax_status_string.restype = ctypes.c_char_p
         L.entmax_status_string.argtypes = [ctypes.c_int]
         L.entmax_last_error.restype = ctypes.c_char_p
@@ -131,6 +133,14 @@ def _stream(dev) -> int:
     return torch.cuda.current_stream(dev).cuda_stream
 
 
+def _check_slopes(slopes, hq: int) -> None:
+    if slopes is None:
+        return
+    torch = _torch()
+    if slopes.dtype != torch.float32 or slopes.numel() != hq:
+        raise ValueError(f"slopes must be float32 with one value per query head ({hq})")
+
+
 def _require_gpu(*ts) -> None:
     for t in ts:
         if t is None:
@@ -149,9 +159,21 @@ def mask_shape(n: int, block: Tuple[int, int]) -> Tuple[int, int]:
 FwdOut = namedtuple("FwdOut", "o tau mask aux hist tau_h")
 
 
+def nape_slopes(heads: int):
+    """Slopes of NAPE heads as a list: the first half of the heads without position encoding
+    (slope 0), the second half ALiBi with the geometric slopes 2^(-8 k / H') of H' = heads/2
+    ALiBi heads, k = 1..H'. The pages name the split (half and half, page 2 section 4) but not
+    which half or the slopes; this is the reading taken."""
+    if heads < 2 or heads % 2:
+        raise ValueError("NAPE needs an even number of heads")
+    hp = heads // 2
+    return [0.0] * hp + [2.0 ** (-8.0 * kk / hp) for kk in range(1, hp + 1)]
+
+
 def fwd(q, k, v, alpha: float = 1.5, causal: bool = True, block=(64, 64), bins: int = 16,
         scale: Optional[float] = None, max_iters: int = 0, tol: float = 0.0,
-        return_hist: bool = False, stats=None, workspace=None, out=None, tau_init: int = 0) -> FwdOut:
+        return_hist: bool = False, stats=None, workspace=None, out=None, tau_init: int = 0,
+        slopes=None) -> FwdOut:
     """alpha-entmax attention forward. Returns (o, tau, mask, aux, hist, tau_h); o is float32.
 
     hist/tau_h are the histogram stage's counts [b,hq,n,B] and lower bound [b,hq,n]
@@ -160,7 +182,8 @@ def fwd(q, k, v, alpha: float = 1.5, causal: bool = True, block=(64, 64), bins: 
     the refinement from the histogram bound, 1 from the plain bracket below the row max.
     """
     torch = _torch()
-    _require_gpu(q, k, v)
+    _require_gpu(q, k, v, slopes)
+    _check_slopes(slopes, q.shape[1])
     desc = _desc_for(q, k, alpha, causal, block, bins, scale, max_iters, tol, tau_init)
     L = lib()
     b, hq, n, d = q.shape
@@ -178,17 +201,19 @@ def fwd(q, k, v, alpha: float = 1.5, causal: bool = True, block=(64, 64), bins: 
     nbytes = L.entmax_attn_fwd_workspace_bytes(ctypes.byref(desc))
     if workspace is None or workspace.numel() < nbytes:
         workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
-    _check(L.entmax_attn_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(tau),
+    _check(L.entmax_attn_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(slopes), _ptr(o), _ptr(tau),
                              _ptr(mask), _ptr(aux), _ptr(hist), _ptr(tau_h), _ptr(stats),
                              _ptr(workspace), workspace.numel(), _stream(dev)))
     return FwdOut(o, tau, mask, aux, hist, tau_h)
 
 
 def bwd(q, k, v, do, tau, mask, aux, alpha: float = 1.5, causal: bool = True, block=(64, 64),
-        bins: int = 16, scale: Optional[float] = None, workspace=None, out=None):
-    """alpha-entmax attention backward: (dq, dk, dv) given the forward's tau, mask, aux."""
+        bins: int = 16, scale: Optional[float] = None, workspace=None, out=None, slopes=None):
+    """alpha-entmax attention backward: (dq, dk, dv) given the forward's tau, mask, aux
+    (and the forward's slopes)."""
     torch = _torch()
-    _require_gpu(q, k, v, do, tau, mask, aux)
+    _require_gpu(q, k, v, do, tau, mask, aux, slopes)
+    _check_slopes(slopes, q.shape[1])
     desc = _desc_for(q, k, alpha, causal, block, bins, scale, 0, 0.0)
     L = lib()
     dev = q.device
@@ -199,7 +224,7 @@ def bwd(q, k, v, do, tau, mask, aux, alpha: float = 1.5, causal: bool = True, bl
     nbytes = L.entmax_attn_bwd_workspace_bytes(ctypes.byref(desc))
     if workspace is None or workspace.numel() < nbytes:
         workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
-    _check(L.entmax_attn_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(tau),
+    _check(L.entmax_attn_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(slopes), _ptr(tau),
                              _ptr(mask), _ptr(aux), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
                              workspace.numel(), _stream(dev)))
     return dq, dk, dv
@@ -229,18 +254,19 @@ def _make_function():
 
     class EntmaxAttentionFn(torch.autograd.Function):
         @staticmethod
-        def forward(ctx, q, k, v, alpha, causal, block, bins, scale):
-            r = fwd(q, k, v, alpha, causal, block, bins, scale)
+        def forward(ctx, q, k, v, alpha, causal, block, bins, scale, slopes):
+            r = fwd(q, k, v, alpha, causal, block, bins, scale, slopes=slopes)
             ctx.save_for_backward(q, k, v, r.tau, r.mask, r.aux)
-            ctx.cfg = (alpha, causal, block, bins, scale)
+            ctx.cfg = (alpha, causal, block, bins, scale, slopes)
             return r.o.to(q.dtype)
 
         @staticmethod
         def backward(ctx, do):
             q, k, v, tau, mask, aux = ctx.saved_tensors
-            alpha, causal, block, bins, scale = ctx.cfg
-            dq, dk, dv = bwd(q, k, v, do.contiguous(), tau, mask, aux, alpha, causal, block, bins, scale)
-            return dq, dk, dv, None, None, None, None, None
+            alpha, causal, block, bins, scale, slopes = ctx.cfg
+            dq, dk, dv = bwd(q, k, v, do.contiguous(), tau, mask, aux, alpha, causal, block, bins, scale,
+                             slopes=slopes)
+            return dq, dk, dv, None, None, None, None, None, None
 
     return EntmaxAttentionFn
 
@@ -249,9 +275,9 @@ _fn = None
 
 
 def entmax_attention(q, k, v, alpha: float = 1.5, causal: bool = True, block=(64, 64), bins: int = 16,
-                     scale: Optional[float] = None):
+                     scale: Optional[float] = None, slopes=None):
     """Differentiable alpha-entmax attention (forward and backward in the HIP library)."""
     global _fn
     if _fn is None:
         _fn = _make_function()
-    return _fn.apply(q, k, v, alpha, causal, tuple(block), bins, scale)
+    return _fn.apply(q, k, v, alpha, causal, tuple(block), bins, scale, slopes)

@@ -234,7 +234,8 @@ size_t entmax_attn_mask_words(const entmax_attn_desc* desc) {
 }
 
 entmax_status entmax_attn_fwd(const entmax_attn_desc* desc, const void* q, const void* k, const void* v,
-                              void* o_, float* tau, uint32_t* block_mask, void* aux, int32_t* hist_counts,
+                              const float* slopes, void* o_, float* tau, uint32_t* block_mask, void* aux,
+                              int32_t* hist_counts,
                               float* tau_h, uint64_t* stats, void* workspace, size_t workspace_bytes,
                               void* stream) {
   Derived o;
@@ -246,8 +247,8 @@ entmax_status entmax_attn_fwd(const entmax_attn_desc* desc, const void* q, const
     return fail(ENTMAX_ERR_NULL, "q, k, v, o, tau, block_mask and aux are required");
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o_, 16) || !aligned(aux, 16) ||
       !aligned(tau, 4) || !aligned(block_mask, 4) || (hist_counts && !aligned(hist_counts, 4)) ||
-      (tau_h && !aligned(tau_h, 4)) || (stats && !aligned(stats, 8)))
-    return fail(ENTMAX_ERR_ALIGN, "q, k, v, o, aux need 16-byte alignment; tau, mask, counts 4-byte");
+      (tau_h && !aligned(tau_h, 4)) || (stats && !aligned(stats, 8)) || (slopes && !aligned(slopes, 4)))
+    return fail(ENTMAX_ERR_ALIGN, "q, k, v, o, aux need 16-byte alignment; tau, mask, counts, slopes 4-byte");
   const size_t need = fwd_ws(o);
   if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
     return fail(ENTMAX_ERR_WORKSPACE, "forward workspace: need %zu bytes, 256-byte aligned (got %zu)", need,
@@ -271,6 +272,7 @@ entmax_status entmax_attn_fwd(const entmax_attn_desc* desc, const void* q, const
   p.b = o.b; p.hq = o.hq; p.hkv = o.hkv; p.n = o.n; p.G = o.G;
   p.causal = o.causal; p.Br = o.Br; p.Bc = o.Bc; p.B = o.B; p.max_iters = o.max_iters;
   p.tau_init = o.tau_init;
+  p.slopes = slopes;
   p.cx = (float)(((double)o.alpha - 1.0) * (double)o.scale);
   p.alpha = o.alpha; p.kappa = o.kappa; p.tol = o.tol;
   p.GP = o.GP; p.RH = o.RH; p.RG = o.RG;
@@ -283,7 +285,8 @@ entmax_status entmax_attn_fwd(const entmax_attn_desc* desc, const void* q, const
 }
 
 entmax_status entmax_attn_bwd(const entmax_attn_desc* desc, const void* q, const void* k, const void* v,
-                              const void* dout, const float* tau, const uint32_t* block_mask, const void* aux,
+                              const void* dout, const float* slopes, const float* tau,
+                              const uint32_t* block_mask, const void* aux,
                               void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
                               void* stream) {
   Derived o;
@@ -294,8 +297,8 @@ entmax_status entmax_attn_bwd(const entmax_attn_desc* desc, const void* q, const
     return fail(ENTMAX_ERR_NULL, "q, k, v, dout, tau, block_mask, aux, dq, dk and dv are required");
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(dout, 16) || !aligned(aux, 16) ||
       !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(tau, 16) ||
-      !aligned(block_mask, 4))
-    return fail(ENTMAX_ERR_ALIGN, "tensors need 16-byte alignment (block_mask 4-byte)");
+      !aligned(block_mask, 4) || (slopes && !aligned(slopes, 4)))
+    return fail(ENTMAX_ERR_ALIGN, "tensors need 16-byte alignment (block_mask, slopes 4-byte)");
   const BwdLayout L = bwd_ws(o);
   if (!workspace || workspace_bytes < L.total || !aligned(workspace, 256))
     return fail(ENTMAX_ERR_WORKSPACE, "backward workspace: need %zu bytes, 256-byte aligned (got %zu)", L.total,
@@ -329,6 +332,7 @@ entmax_status entmax_attn_bwd(const entmax_attn_desc* desc, const void* q, const
   p.causal = o.causal; p.Br = o.Br; p.Bc = o.Bc;
   p.cx = (float)(((double)o.alpha - 1.0) * (double)o.scale);
   p.scale = o.scale; p.kappa = o.kappa;
+  p.am1 = o.alpha - 1.0f; p.slopes = slopes;
   p.Tr = o.Tr; p.Tc = o.Tc; p.W = o.W; p.WT = o.WT;
 
   p.map = make_map(o.b * o.hkv, o.Tc);

@@ -38,7 +38,7 @@ __device__ __forceinline__ size_t cols_off(int blk32, int dc, int m, int DC, int
 
 }  // namespace
 
-template <typename T, int D, int MODE>
+template <typename T, int D, int MODE, bool BIAS>
 __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void k_bwd_dkv(BwdParams p) {
   constexpr int DS = D / 16, DC = D / 32;
   extern __shared__ float red[];
@@ -81,6 +81,7 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void k_bwd_dkv(BwdParams p)
     const T* DOc = reinterpret_cast<const T*>(p.doc) + qrow0 * D;
     const float* tau = p.tau + qrow0;
     const float* delta = p.delta + qrow0;
+    const float cm = BIAS ? p.slopes[head] * p.am1 : 0.0f;   // position bias on the x-scale
     const uint32_t* colw = p.maskT + ((size_t)(bi * p.hq + head) * p.Tc + J) * p.WT;
     for (int wi = 0; wi < p.WT; ++wi) {
       uint32_t word = uniform_u32(colw[wi]);
@@ -114,6 +115,15 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void k_bwd_dkv(BwdParams p)
           f32x16 S = f32x16{};
 #pragma unroll
           for (int s = 0; s < DS; ++s) mma16(S, qa[s], kb[s]);   // S[q][key]
+          // -tau of each entry's row (and the position bias): x - tau = cx S + off
+          f32x16 off;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) off[r] = -tv[r >> 2][r & 3];
+          if (BIAS && cm != 0.0f) {
+            const f32x16 bb = bias16<1>(0.0f, cm, (float)(q0 + 4 * h - key0 - c), p.causal);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) off[r] += bb[r];
+          }
           // P and G; rows 8(r/4) + 4h + r%4 of the chunk, key c of the sub-block
           const bool diag = p.causal && key0 + 31 > q0;
           f32x16 P, G;
@@ -121,7 +131,7 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void k_bwd_dkv(BwdParams p)
           if (diag) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-              float tt = cx * S[r] - tv[r >> 2][r & 3];
+              float tt = fmaf(cx, S[r], off[r]);
               tt = (key0 + c <= q0 + acc_row(r, h)) ? tt : -1.0f;
               const float dm = fmaxf(tt, 0.f);
               P[r] = Weight<MODE>::p(dm, kappa);
@@ -131,7 +141,7 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void k_bwd_dkv(BwdParams p)
           } else {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-              const float dm = fmaxf(cx * S[r] - tv[r >> 2][r & 3], 0.f);
+              const float dm = fmaxf(fmaf(cx, S[r], off[r]), 0.f);
               P[r] = Weight<MODE>::p(dm, kappa);
               G[r] = Weight<MODE>::g(dm, kappa);
               mx = fmaxf(mx, dm);
@@ -201,7 +211,7 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void k_bwd_dkv(BwdParams p)
   }
 }
 
-template <typename T, int D, int MODE>
+template <typename T, int D, int MODE, bool BIAS>
 __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void k_bwd_dq(BwdParams p) {
   constexpr int DS = D / 16, DC = D / 32;
   extern __shared__ float red[];
@@ -231,6 +241,7 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void k_bwd_dq(BwdParams p) 
     load_frag(db[s], reinterpret_cast<const T*>(p.dor) + qrow0 * D + rows_off(q0 >> 5, s, DS, lane));
   }
   const float tq = p.tau[qrow0 + q0 + c];
+  const float cm = BIAS ? p.slopes[head] * p.am1 : 0.0f;   // position bias on the x-scale
   const float dq_delta = p.delta[qrow0 + q0 + c];
   f32x16 dq[DC];
 #pragma unroll
@@ -261,13 +272,21 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void k_bwd_dq(BwdParams p) 
         f32x16 S = f32x16{};
 #pragma unroll
         for (int s = 0; s < DS; ++s) mma16(S, ka[s], qb[s]);   // S^T[key][q]
+        // x - tau = cx S + off (the row's -tau and the position bias)
+        f32x16 off;
+        if (BIAS && cm != 0.0f) {
+          off = bias16<-1>(-tq, cm, (float)(q0 + c - key0 - 4 * h), p.causal);
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) off[r] = -tq;
+        }
         const bool diag = p.causal && key0 + 31 > q0;
         f32x16 G;
         float mx = 0.f;
         if (diag) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            float tt = cx * S[r] - tq;
+            float tt = fmaf(cx, S[r], off[r]);
             tt = (key0 + acc_row(r, h) <= q0 + c) ? tt : -1.0f;
             const float dm = fmaxf(tt, 0.f);
             G[r] = Weight<MODE>::g(dm, kappa);
@@ -276,7 +295,7 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void k_bwd_dq(BwdParams p) 
         } else {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const float dm = fmaxf(cx * S[r] - tq, 0.f);
+            const float dm = fmaxf(fmaf(cx, S[r], off[r]), 0.f);
             G[r] = Weight<MODE>::g(dm, kappa);
             mx = fmaxf(mx, dm);
           }
@@ -336,9 +355,12 @@ static hipError_t launch_dkv_t(const BwdParams& p, int mode, hipStream_t s) {
   const size_t lds = (4 / KC > 1) ? (size_t)KC * 2 * DC * 16 * 64 * sizeof(float) : 0;
   const int grid = wgmap_grid(p.map);
   if (grid == 0) return hipSuccess;
-  if (mode == 1) hipLaunchKernelGGL((k_bwd_dkv<T, D, 1>), dim3(grid), dim3(256), lds, s, p);
-  else if (mode == 2) hipLaunchKernelGGL((k_bwd_dkv<T, D, 2>), dim3(grid), dim3(256), lds, s, p);
-  else hipLaunchKernelGGL((k_bwd_dkv<T, D, 0>), dim3(grid), dim3(256), lds, s, p);
+  void (*fn)(BwdParams);
+  if (p.slopes)
+    fn = mode == 1 ? k_bwd_dkv<T, D, 1, true> : mode == 2 ? k_bwd_dkv<T, D, 2, true> : k_bwd_dkv<T, D, 0, true>;
+  else
+    fn = mode == 1 ? k_bwd_dkv<T, D, 1, false> : mode == 2 ? k_bwd_dkv<T, D, 2, false> : k_bwd_dkv<T, D, 0, false>;
+  hipLaunchKernelGGL(fn, dim3(grid), dim3(256), lds, s, p);
   return hipGetLastError();
 }
 
@@ -348,9 +370,12 @@ static hipError_t launch_dq_t(const BwdParams& p, int mode, hipStream_t s) {
   const size_t lds = (4 / QCB > 1) ? (size_t)QCB * DC * 16 * 64 * sizeof(float) : 0;
   const int grid = wgmap_grid(p.map);
   if (grid == 0) return hipSuccess;
-  if (mode == 1) hipLaunchKernelGGL((k_bwd_dq<T, D, 1>), dim3(grid), dim3(256), lds, s, p);
-  else if (mode == 2) hipLaunchKernelGGL((k_bwd_dq<T, D, 2>), dim3(grid), dim3(256), lds, s, p);
-  else hipLaunchKernelGGL((k_bwd_dq<T, D, 0>), dim3(grid), dim3(256), lds, s, p);
+  void (*fn)(BwdParams);
+  if (p.slopes)
+    fn = mode == 1 ? k_bwd_dq<T, D, 1, true> : mode == 2 ? k_bwd_dq<T, D, 2, true> : k_bwd_dq<T, D, 0, true>;
+  else
+    fn = mode == 1 ? k_bwd_dq<T, D, 1, false> : mode == 2 ? k_bwd_dq<T, D, 2, false> : k_bwd_dq<T, D, 0, false>;
+  hipLaunchKernelGGL(fn, dim3(grid), dim3(256), lds, s, p);
   return hipGetLastError();
 }
 

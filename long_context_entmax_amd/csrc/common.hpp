@@ -34,6 +34,40 @@ __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
 // Row of accumulator register r for half-wave h in a 32x32 MFMA output.
 __device__ __forceinline__ constexpr int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
 
+// Additive position bias of a lane's 16 accumulator entries, plus v0: returns
+// v0 - cm * |i - j| where the entries' query-key distances are
+// i - j = d0 + SGN * (8 (r / 4) + r % 4), the row offsets of a 32x32 accumulator
+// (SGN = +1 when the accumulator rows are queries, -1 when they are keys). Under the
+// causal mask |i - j| = i - j on every valid entry; the caller masks the others.
+template <int SGN>
+__device__ __forceinline__ f32x16 bias16(float v0, float cm, float d0, bool causal) {
+  f32x16 b;
+  if (causal) {
+    const float a = fmaf(-cm, d0, v0);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) b[r] = fmaf((float)(-SGN * (8 * (r >> 2) + (r & 3))), cm, a);
+  } else {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) b[r] = fmaf(-cm, fabsf(d0 + (float)(SGN * (8 * (r >> 2) + (r & 3)))), v0);
+  }
+  return b;
+}
+
+// acc[r] = mul * acc[r] + v0 - cm |i - j| entry by entry (distances as in bias16)
+template <int SGN>
+__device__ __forceinline__ void scale_add_bias16(f32x16& acc, float mul, float v0, float cm, float d0,
+                                                 bool causal) {
+  if (causal) {
+    const float a = fmaf(-cm, d0, v0);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = fmaf(mul, acc[r], fmaf((float)(-SGN * (8 * (r >> 2) + (r & 3))), cm, a));
+  } else {
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      acc[r] = fmaf(mul, acc[r], fmaf(-cm, fabsf(d0 + (float)(SGN * (8 * (r >> 2) + (r & 3)))), v0));
+  }
+}
+
 // Position of row `row` (0..15 within a 16-group) in the permuted transposed layout
 // (sigma is an involution: it swaps the middle two quads).
 __host__ __device__ __forceinline__ constexpr int sigma16(int p) {

@@ -150,7 +150,7 @@ struct KvOps {
 };
 
 // ================================================================================ k_hist
-template <typename T, int D, int MODE, bool QS>
+template <typename T, int D, int MODE, bool QS, bool BIAS>
 __global__ __launch_bounds__(512, ((D == 64 && sizeof(T) == 2) ? HIST_OCC64 : 2)) void k_hist(FwdParams p) {
   using Ops = KvOps<T, D>;
   constexpr int DS = Ops::DS;
@@ -174,6 +174,8 @@ __global__ __launch_bounds__(512, ((D == 64 && sizeof(T) == 2) ? HIST_OCC64 : 2)
 
   const T* Q = reinterpret_cast<const T*>(p.q) + bh * n * D;
   const T* Kf = reinterpret_cast<const T*>(p.kf) + ((size_t)(bi * p.hkv + kvh) * n) * D;
+  // position bias of this head on the x*B scale: x*B gains -cmB |i - j|
+  const float cmB = BIAS ? p.slopes[head] * (p.alpha - 1.0f) * (float)B : 0.0f;
   uint32_t* hist = lds + (w * (B + 2)) * 64;   // [B + 2][64] of this wave
   for (int i = lane; i < (B + 2) * 64; i += 64) hist[i] = 0;
   float* dmx = p.dmax + (bh * p.nkb + (row0 >> 5)) * p.nkb;
@@ -198,7 +200,8 @@ __global__ __launch_bounds__(512, ((D == 64 && sizeof(T) == 2) ? HIST_OCC64 : 2)
 #pragma unroll
   for (int s = 0; s < DS; ++s) load_frag(qf[s], Q + (size_t)qrow * D + 16 * s + 8 * h);
   // x * B = cB * s exactly (B is a power of two). When cB is itself a power of two it is
-  // folded into Q (exact scaling), and the score tile is x * B directly.
+  // folded into Q (exact scaling), and the score tile is x * B directly. Either way a tile
+  // is held as x * B - base (base: the window's offset below).
   const float cB = QS ? 1.0f : p.cx * (float)B;
   if constexpr (QS) {
     const float qsc = p.cx * (float)B;
@@ -230,25 +233,48 @@ __global__ __launch_bounds__(512, ((D == 64 && sizeof(T) == 2) ? HIST_OCC64 : 2)
   unsigned long long n_cand = 0;
 
   Frag<T> kf[DS], kf2[DS];
-  Ops::load_k(kf, Kf, 0, c, h);
-  if (kb_end > 1) Ops::load_k(kf2, Kf, 1, c, h);
-  for (int kb = 0; kb < kb_end; kb += 2) {
+  // Sub-blocks go by aligned pairs (2m, 2m + 1) from the last pair down to the first: under
+  // the causal mask the keys next to the diagonal come first, so with a position bias (and
+  // in any recency-weighted data) the running max settles early and the far, lower tiles
+  // find the window already in place (fewer slides, fewer active tiles).
+  const int last_pair = (kb_end - 1) >> 1;
+  Ops::load_k(kf, Kf, 2 * last_pair, c, h);
+  if (2 * last_pair + 1 < kb_end) Ops::load_k(kf2, Kf, 2 * last_pair + 1, c, h);
+  // x * B - base of sub-block kbb (with the head's position bias)
+  auto tile = [&](const Frag<T> (&kc)[DS], int kbb) -> f32x16 {
+    if constexpr (BIAS) {
+      const float d0 = (float)(qrow - 32 * kbb - 4 * h);
+      if constexpr (QS)
+        return Ops::scores(kc, qf, kbb, row0, qrow, h, p.causal, bias16<-1>(-(float)base, cmB, d0, p.causal));
+      f32x16 a = Ops::scores(kc, qf, kbb, row0, qrow, h, p.causal);
+      scale_add_bias16<-1>(a, cB, -(float)base, cmB, d0, p.causal);
+      return a;
+    } else {
+      if constexpr (QS) return Ops::scores(kc, qf, kbb, row0, qrow, h, p.causal, negb);
+      f32x16 a = Ops::scores(kc, qf, kbb, row0, qrow, h, p.causal);
+      const float nb = -(float)base;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) a[r] = fmaf(cB, a[r], nb);
+      return a;
+    }
+  };
+  for (int kb = 2 * last_pair; kb >= 0; kb -= 2) {
     const bool two = kb + 1 < kb_end;
-    f32x16 acc0 = QS ? Ops::scores(kf, qf, kb, row0, qrow, h, p.causal, negb)
-                     : Ops::scores(kf, qf, kb, row0, qrow, h, p.causal);
+    f32x16 acc0 = tile(kf, kb);
     f32x16 acc1;
     if (two) {
-      acc1 = QS ? Ops::scores(kf2, qf, kb + 1, row0, qrow, h, p.causal, negb)
-                : Ops::scores(kf2, qf, kb + 1, row0, qrow, h, p.causal);
+      acc1 = tile(kf2, kb + 1);
     } else {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc1[r] = -INFINITY;
     }
-    if (kb + 2 < kb_end) Ops::load_k(kf, Kf, kb + 2, c, h);
-    if (kb + 3 < kb_end) Ops::load_k(kf2, Kf, kb + 3, c, h);
+    if (kb >= 2) {                      // every pair below the last one is whole
+      Ops::load_k(kf, Kf, kb - 2, c, h);
+      Ops::load_k(kf2, Kf, kb - 1, c, h);
+    }
     const float bF = (float)base;
-    const float t0 = QS ? max16(acc0) + bF : cB * max16(acc0);   // largest x*B of each tile
-    const float t1 = QS ? max16(acc1) + bF : cB * max16(acc1);
+    const float t0 = max16(acc0) + bF;   // largest x*B of each tile
+    const float t1 = max16(acc1) + bF;
     const float nmB = fmaxf(mB, fmaxf(t0, t1));
     const bool fin = nmB > -INFINITY;
     const int Tn = fin ? cvt_floor(nmB) : Tt;
@@ -283,14 +309,12 @@ __global__ __launch_bounds__(512, ((D == 64 && sizeof(T) == 2) ? HIST_OCC64 : 2)
           }
         }
         const int nbase = slide ? Tn - B : base;
-        if constexpr (QS) {
-          const float corr = (float)(nbase - base);  // exact: small integers
+        const float corr = (float)(nbase - base);  // small integers
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            acc0[r] -= corr;
-            acc1[r] -= corr;
-            negb[r] = (float)(-nbase);
-          }
+        for (int r = 0; r < 16; ++r) {
+          acc0[r] -= corr;
+          acc1[r] -= corr;
+          negb[r] = (float)(-nbase);
         }
         base = nbase;
       }
@@ -300,31 +324,26 @@ __global__ __launch_bounds__(512, ((D == 64 && sizeof(T) == 2) ? HIST_OCC64 : 2)
         have = true;
       }
       // count every score of both tiles (lanes with no active tile land in cell 0)
-      const float nbF = -(float)base;
       if (p.tau_init == 0) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float y = QS ? acc0[r] : fmaf(cB, acc0[r], nbF);
-        const uint32_t cell = cvt_u32_sat(y);
-        atomicAdd(hl + (cell << 6), 1u);
-      }
-      if (two) {
-#pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float y = QS ? acc1[r] : fmaf(cB, acc1[r], nbF);
-          const uint32_t cell = cvt_u32_sat(y);
+          const uint32_t cell = cvt_u32_sat(acc0[r]);
           atomicAdd(hl + (cell << 6), 1u);
         }
-      }
+        if (two) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const uint32_t cell = cvt_u32_sat(acc1[r]);
+            atomicAdd(hl + (cell << 6), 1u);
+          }
+        }
       }
     }
-    // flush a finished word of sub-block bits and chunk maxima (kb is even: a word ends
-    // at kb + 1 == 31 mod 32, or at the last sub-block)
-    const int klast = two ? kb + 1 : kb;
-    if ((klast & 31) == 31 || klast == kb_end - 1) {
-      if (lane == 0) cw_out[klast >> 5] = cword;
-      const int wbase = klast & ~31;
-      if (lane < 32 && wbase + lane <= klast) dmx[wbase + lane] = dreg;
+    // flush a finished word of sub-block bits and chunk maxima (pairs never straddle a
+    // word; the word is complete once its lowest sub-block, kb == 0 mod 32, is done)
+    if ((kb & 31) == 0) {
+      if (lane == 0) cw_out[kb >> 5] = cword;
+      if (lane < 32 && kb + lane < kb_end) dmx[kb + lane] = dreg;
       cword = 0;
       dreg = -INFINITY;
     }
@@ -368,7 +387,7 @@ __global__ __launch_bounds__(512, ((D == 64 && sizeof(T) == 2) ? HIST_OCC64 : 2)
 // Work groups of OUT_WAVES waves over consecutive 32-row chunks of one query head, one
 // chunk per wave; a wave's cost depends on its rows' candidates and passes, so small
 // groups keep the machine balanced.
-template <typename T, int D, int MODE, bool QS>
+template <typename T, int D, int MODE, bool QS, bool BIAS>
 __global__ __launch_bounds__(64 * OUT_WAVES, 2) void k_refine_out(FwdParams p) {
   using Ops = KvOps<T, D>;
   constexpr int DS = Ops::DS, DC = Ops::DC;
@@ -448,8 +467,17 @@ __global__ __launch_bounds__(64 * OUT_WAVES, 2) void k_refine_out(FwdParams p) {
     return kb;
   };
   f32x16 negt;
+  // position bias of this head on the x-scale: x gains -cm |i - j|
+  const float cm = BIAS ? p.slopes[head] * (p.alpha - 1.0f) : 0.0f;
   auto tile = [&](const Frag<T> (&kc)[DS], int kb) -> f32x16 {   // x - tau; -inf if masked
-    if constexpr (QS) {
+    if constexpr (BIAS) {
+      const float d0 = (float)(qrow - 32 * kb - 4 * h);
+      if constexpr (QS)
+        return Ops::scores(kc, qf, kb, row0, qrow, h, p.causal, bias16<-1>(-tau, cm, d0, p.causal));
+      f32x16 acc = Ops::scores(kc, qf, kb, row0, qrow, h, p.causal);
+      scale_add_bias16<-1>(acc, cx, -tau, cm, d0, p.causal);
+      return acc;
+    } else if constexpr (QS) {
       return Ops::scores(kc, qf, kb, row0, qrow, h, p.causal, negt);
     } else {
       f32x16 acc = Ops::scores(kc, qf, kb, row0, qrow, h, p.causal);
@@ -714,18 +742,33 @@ __global__ __launch_bounds__(64 * OUT_WAVES, 2) void k_refine_out(FwdParams p) {
 }
 
 template <typename T, int D>
-static void (*hist_kernel(bool qs, int mode))(FwdParams) {
-  if (qs) return mode == 1 ? k_hist<T, D, 1, true> : mode == 2 ? k_hist<T, D, 2, true> : k_hist<T, D, 0, true>;
-  return mode == 1 ? k_hist<T, D, 1, false> : mode == 2 ? k_hist<T, D, 2, false> : k_hist<T, D, 0, false>;
+static void (*hist_kernel(bool qs, bool bias, int mode))(FwdParams) {
+  if (bias) {
+    if (qs) return mode == 1 ? k_hist<T, D, 1, true, true> : mode == 2 ? k_hist<T, D, 2, true, true>
+                                                                     : k_hist<T, D, 0, true, true>;
+    return mode == 1 ? k_hist<T, D, 1, false, true> : mode == 2 ? k_hist<T, D, 2, false, true>
+                                                                : k_hist<T, D, 0, false, true>;
+  }
+  if (qs) return mode == 1 ? k_hist<T, D, 1, true, false> : mode == 2 ? k_hist<T, D, 2, true, false>
+                                                                    : k_hist<T, D, 0, true, false>;
+  return mode == 1 ? k_hist<T, D, 1, false, false> : mode == 2 ? k_hist<T, D, 2, false, false>
+                                                               : k_hist<T, D, 0, false, false>;
 }
 
 template <typename T, int D>
-static void (*out_kernel(bool qs, int mode))(FwdParams) {
+static void (*out_kernel(bool qs, bool bias, int mode))(FwdParams) {
+  if (bias) {
+    if (qs)
+      return mode == 1 ? k_refine_out<T, D, 1, true, true> : mode == 2 ? k_refine_out<T, D, 2, true, true>
+                                                                       : k_refine_out<T, D, 0, true, true>;
+    return mode == 1 ? k_refine_out<T, D, 1, false, true> : mode == 2 ? k_refine_out<T, D, 2, false, true>
+                                                                      : k_refine_out<T, D, 0, false, true>;
+  }
   if (qs)
-    return mode == 1 ? k_refine_out<T, D, 1, true> : mode == 2 ? k_refine_out<T, D, 2, true>
-                                                               : k_refine_out<T, D, 0, true>;
-  return mode == 1 ? k_refine_out<T, D, 1, false> : mode == 2 ? k_refine_out<T, D, 2, false>
-                                                              : k_refine_out<T, D, 0, false>;
+    return mode == 1 ? k_refine_out<T, D, 1, true, false> : mode == 2 ? k_refine_out<T, D, 2, true, false>
+                                                                      : k_refine_out<T, D, 0, true, false>;
+  return mode == 1 ? k_refine_out<T, D, 1, false, false> : mode == 2 ? k_refine_out<T, D, 2, false, false>
+                                                                     : k_refine_out<T, D, 0, false, false>;
 }
 
 size_t fwd_lds_bytes(int B) { return (size_t)(HIST_WAVES * (B + 2) * 64) * sizeof(uint32_t); }
@@ -740,7 +783,8 @@ static hipError_t launch_fwd_t(const FwdParams& p, int mode, hipStream_t s) {
   const float cB = p.cx * (float)p.B;
   int ex = 0;
   const bool qs = std::frexp(cB, &ex) == 0.5f && ex >= -8 && ex <= 8;
-  void (*hist_fn)(FwdParams) = hist_kernel<T, D>(qs, mode);
+  const bool bias = p.slopes != nullptr;
+  void (*hist_fn)(FwdParams) = hist_kernel<T, D>(qs, bias, mode);
   hipError_t e = hipFuncSetAttribute((const void*)hist_fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   prof_begin("entmax_fwd_hist", s);
@@ -748,7 +792,7 @@ static hipError_t launch_fwd_t(const FwdParams& p, int mode, hipStream_t s) {
   prof_end(s);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // (at head_dim 128 the extra accumulator block of the folded form would spill)
-  void (*out_fn)(FwdParams) = out_kernel<T, D>(qs && D == 64, mode);
+  void (*out_fn)(FwdParams) = out_kernel<T, D>(qs && D == 64, bias, mode);
   prof_begin("entmax_fwd_refine_out", s);
   hipLaunchKernelGGL(out_fn, dim3(grid2), dim3(64 * OUT_WAVES), 0, s, p);
   prof_end(s);

@@ -61,6 +61,7 @@ struct FwdParams {
   WgMap map;             // histogram kernel
   WgMap map2;            // refinement/output kernel
   int tau_init;          // 0: histogram bound; 1: plain bracket from the row max (no histogram)
+  const float* slopes;   // optional [hq]: position-bias slope m of each query head (scores - m |i - j|)
 };
 
 // one re-layout of X [heads, n, D] (prep.hip): any of the fragment-major row copy,
@@ -93,6 +94,8 @@ struct BwdParams {
   int b, hq, hkv, n, G;
   int causal, Br, Bc;
   float cx, scale, kappa;
+  float am1;             // alpha - 1 (scales the position bias onto the x-scale)
+  const float* slopes;   // optional [hq] position-bias slopes
   int Tr, Tc, W, WT;
   WgMap map;
 };

@@ -55,16 +55,16 @@ def _load():
         lib.oracle_attn_fwd_rows.restype = None
         lib.oracle_attn_fwd_rows.argtypes = [
             ctypes.c_long, ctypes.c_long, _dp, _dp, _dp, ctypes.c_double, ctypes.c_double,
-            ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_long, ctypes.c_long,
+            ctypes.c_double, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_long, ctypes.c_long,
             _dp, _dp, _dp, _ip, _lp, _up, _dp, _dp]
         lib.oracle_attn_bwd_rows.restype = None
         lib.oracle_attn_bwd_rows.argtypes = [
             ctypes.c_long, ctypes.c_long, _dp, _dp, _dp, _dp, _dp, ctypes.c_double,
-            ctypes.c_double, ctypes.c_int, ctypes.c_long, ctypes.c_long, _dp, _dp]
+            ctypes.c_double, ctypes.c_double, ctypes.c_int, ctypes.c_long, ctypes.c_long, _dp, _dp]
         lib.oracle_attn_bwd_keys.restype = None
         lib.oracle_attn_bwd_keys.argtypes = [
             ctypes.c_long, ctypes.c_long, ctypes.c_long, _dp, _dp, _dp, _dp, _dp, _dp,
-            ctypes.c_double, ctypes.c_double, ctypes.c_int, ctypes.c_long, ctypes.c_long,
+            ctypes.c_double, ctypes.c_double, _dp, ctypes.c_int, ctypes.c_long, ctypes.c_long,
             _dp, _dp]
         _lib = lib
     return _lib
@@ -126,10 +126,11 @@ def tau_from_hist(counts, T: int, B: int, alpha: float) -> float:
 # ---------------------------------------------------------------------------------------------
 
 def attn_fwd_head(q, k, v, alpha: float, causal: bool, B: int, Bc: int, scale: float,
-                  rows=None, threads: int | None = None) -> dict:
+                  rows=None, threads: int | None = None, slope: float = 0.0) -> dict:
     """Dense forward of one query head. q: [n, d]; k, v: [n, d] of its KV head.
 
     ``rows``: None for all rows, or an iterable of row indices (sampled rows).
+    ``slope``: the head's position-bias slope m (scores get -m |i - j|; 0 = none).
     Returns per requested row: o [r, d], tau, tau_h, counts [r, B], T, rowbits [r, W],
     xgap, psum, and ``rows`` (the row indices).
     """
@@ -166,7 +167,7 @@ def attn_fwd_head(q, k, v, alpha: float, causal: bool, B: int, Bc: int, scale: f
         r0, r1 = int(rows_arr[u]), int(rows_arr[u]) + (w - u)
         lib.oracle_attn_fwd_rows(
             n, d, _ptr(q, _dp), _ptr(k, _dp), _ptr(v, _dp), float(alpha), float(scale),
-            int(bool(causal)), int(B), int(Bc), r0, r1,
+            float(slope), int(bool(causal)), int(B), int(Bc), r0, r1,
             _ptr(out["o"][u:w], _dp), _ptr(out["tau"][u:w], _dp), _ptr(out["tau_h"][u:w], _dp),
             _ptr(out["counts"][u:w], _ip), _ptr(out["T"][u:w], _lp),
             _ptr(out["rowbits"][u:w], _up), _ptr(out["xgap"][u:w], _dp),
@@ -188,7 +189,7 @@ def block_mask(rowbits: np.ndarray, Br: int) -> np.ndarray:
 
 
 def attn_bwd_rows_head(q, k, v, dout, tau, alpha: float, causal: bool, scale: float,
-                       rows=None, threads: int | None = None) -> dict:
+                       rows=None, threads: int | None = None, slope: float = 0.0) -> dict:
     """Per-row backward of one query head: dq [r, d] and delta [r] for the given rows.
 
     ``tau`` holds the forward tau of exactly these rows (same order as ``rows``).
@@ -209,7 +210,7 @@ def attn_bwd_rows_head(q, k, v, dout, tau, alpha: float, causal: bool, scale: fl
             r = int(rows_arr[t])
             lib.oracle_attn_bwd_rows(n, d, _ptr(q, _dp), _ptr(k, _dp), _ptr(v, _dp),
                                      _ptr(dout, _dp), _ptr(tau[t:t + 1], _dp), float(alpha),
-                                     float(scale), int(bool(causal)), r, r + 1,
+                                     float(scale), float(slope), int(bool(causal)), r, r + 1,
                                      _ptr(dq[t:t + 1], _dp), _ptr(delta[t:t + 1], _dp))
 
     with ThreadPoolExecutor(max_workers=nthr) as ex:
@@ -218,17 +219,20 @@ def attn_bwd_rows_head(q, k, v, dout, tau, alpha: float, causal: bool, scale: fl
 
 
 def attn_bwd_keys_group(q_group, k, v, dout_group, tau_group, delta_group, alpha: float,
-                        causal: bool, scale: float, keys=None, threads: int | None = None) -> dict:
+                        causal: bool, scale: float, keys=None, threads: int | None = None,
+                        slopes=None) -> dict:
     """Per-key backward of one KV head: dk, dv for the given keys (default: all).
 
     q_group, dout_group: [G, n, d] of the KV head's query heads; tau_group,
-    delta_group: [G, n] (all rows of those heads).
+    delta_group: [G, n] (all rows of those heads); slopes: [G] position-bias slopes of
+    those heads, or None.
     """
     lib = _load()
     qg, dog = _f64(q_group), _f64(dout_group)
     tg, dg = _f64(tau_group), _f64(delta_group)
     k, v = _f64(k), _f64(v)
     G, n, d = qg.shape
+    sl = None if slopes is None else _f64(slopes).ravel()
     keys_arr = np.arange(n, dtype=np.int64) if keys is None else np.asarray(keys, dtype=np.int64)
     m = keys_arr.size
     dk = np.zeros((m, d))
@@ -241,7 +245,8 @@ def attn_bwd_keys_group(q_group, k, v, dout_group, tau_group, delta_group, alpha
             j = int(keys_arr[t])
             lib.oracle_attn_bwd_keys(n, d, G, _ptr(qg, _dp), _ptr(k, _dp), _ptr(v, _dp),
                                      _ptr(dog, _dp), _ptr(tg, _dp), _ptr(dg, _dp), float(alpha),
-                                     float(scale), int(bool(causal)), j, j + 1,
+                                     float(scale), None if sl is None else _ptr(sl, _dp),
+                                     int(bool(causal)), j, j + 1,
                                      _ptr(dk[t:t + 1], _dp), _ptr(dv[t:t + 1], _dp))
 
     with ThreadPoolExecutor(max_workers=nthr) as ex:
@@ -250,10 +255,12 @@ def attn_bwd_keys_group(q_group, k, v, dout_group, tau_group, delta_group, alpha
 
 
 def attn_full(q, k, v, dout, alpha: float, causal: bool, B: int, Br: int, Bc: int,
-              scale: float | None = None, threads: int | None = None, backward: bool = True) -> dict:
+              scale: float | None = None, threads: int | None = None, backward: bool = True,
+              slopes=None) -> dict:
     """Dense forward (and backward) of a whole problem.
 
     q, dout: [b, hq, n, d]; k, v: [b, hkv, n, d] (any array-like; widened to fp64).
+    slopes: None, or [hq] position-bias slopes (head h scores get -slopes[h] |i - j|).
     Returns o, tau, tau_h, counts, T, mask [b, hq, Tr, W], xgap, psum and, with
     ``backward``, dq, dk, dv, delta.
     """
@@ -265,6 +272,7 @@ def attn_full(q, k, v, dout, alpha: float, causal: bool, B: int, Br: int, Bc: in
         scale = 1.0 / np.sqrt(d)
     Tr = (n + Br - 1) // Br
     W = (n + 32 * Bc - 1) // (32 * Bc)
+    sl = np.zeros(hq) if slopes is None else _f64(slopes).ravel()
     res = {
         "o": np.zeros_like(q), "tau": np.zeros((b, hq, n)), "tau_h": np.zeros((b, hq, n)),
         "counts": np.zeros((b, hq, n, B), dtype=np.int32), "T": np.zeros((b, hq, n), dtype=np.int64),
@@ -274,7 +282,7 @@ def attn_full(q, k, v, dout, alpha: float, causal: bool, B: int, Br: int, Bc: in
     for bi in range(b):
         for h in range(hq):
             f = attn_fwd_head(q[bi, h], k[bi, h // G], v[bi, h // G], alpha, causal, B, Bc, scale,
-                              threads=threads)
+                              threads=threads, slope=sl[h])
             res["o"][bi, h] = f["o"]
             for key in ("tau", "tau_h", "counts", "T", "xgap", "psum"):
                 res[key][bi, h] = f[key]
@@ -288,14 +296,15 @@ def attn_full(q, k, v, dout, alpha: float, causal: bool, B: int, Br: int, Bc: in
         for bi in range(b):
             for h in range(hq):
                 r = attn_bwd_rows_head(q[bi, h], k[bi, h // G], v[bi, h // G], do[bi, h],
-                                       res["tau"][bi, h], alpha, causal, scale, threads=threads)
+                                       res["tau"][bi, h], alpha, causal, scale, threads=threads,
+                                       slope=sl[h])
                 res["dq"][bi, h] = r["dq"]
                 res["delta"][bi, h] = r["delta"]
             for kh in range(hkv):
                 hs = slice(kh * G, (kh + 1) * G)
                 kk = attn_bwd_keys_group(q[bi, hs], k[bi, kh], v[bi, kh], do[bi, hs],
                                          res["tau"][bi, hs], res["delta"][bi, hs], alpha, causal,
-                                         scale, threads=threads)
+                                         scale, threads=threads, slopes=sl[hs])
                 res["dk"][bi, kh] = kk["dk"]
                 res["dv"][bi, kh] = kk["dv"]
     return res

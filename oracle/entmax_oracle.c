@@ -27,6 +27,15 @@
  * kappa = 1/(alpha-1). This is the standard alpha-entmax (Peters, Niculae,
  * Martins 2019) written on the x-scale, where tau* lies in
  * [x_max - 1, x_max - n^(1-alpha)], a window of width at most 1.
+ *
+ * Position bias (NAPE heads: half of the heads without position encoding, half
+ * with ALiBi; page 2 section 4, page 1 section 4.2): a head with slope m adds
+ * -m |i - j| to every score s_ij before the transform, so
+ *   x_ij = (alpha - 1) (scale q_i . k_j - m |i - j|),
+ * and m = 0 is a head without position encoding. Under the causal mask
+ * |i - j| = i - j. Everything downstream (tau, histogram, mask, gradients) sees
+ * the biased scores; the bias does not depend on q or k, so the gradient
+ * formulas keep their form.
  */
 #include <math.h>
 #include <stdint.h>
@@ -134,22 +143,28 @@ double oracle_tau_from_hist(const int32_t *counts, int64_t T, int B, double alph
     return lo;
 }
 
-/* scores of row i against keys 0..nv-1 on the x-scale */
-static void row_x(long d, const double *qi, const double *k, long nv, double alpha,
-                  double scale, double *x)
+/* biased score of query i and key j: scale q_i . k_j - slope |i - j| */
+static double score(long d, const double *qi, const double *kj, double scale, double slope,
+                    long i, long j)
 {
-    for (long j = 0; j < nv; ++j) {
-        double s = 0.0;
-        for (long c = 0; c < d; ++c)
-            s += qi[c] * k[j * d + c];
-        x[j] = (alpha - 1.0) * (scale * s);
-    }
+    double s = 0.0;
+    for (long c = 0; c < d; ++c)
+        s += qi[c] * kj[c];
+    return scale * s - slope * fabs((double)(i - j));
+}
+
+/* scores of row i against keys 0..nv-1 on the x-scale */
+static void row_x(long d, long i, const double *qi, const double *k, long nv, double alpha,
+                  double scale, double slope, double *x)
+{
+    for (long j = 0; j < nv; ++j)
+        x[j] = (alpha - 1.0) * score(d, qi, k + j * d, scale, slope, i, j);
 }
 
 /*
  * Dense forward for rows [r0, r1) of one query head (arrays are [n, d] row-major).
  * For each row i, with valid keys j < nv (nv = i+1 if causal, else n):
- *   x_j = (alpha-1) scale q_i.k_j ; tau_i = root of f (bisection above);
+ *   x_j = (alpha-1) (scale q_i.k_j - slope |i-j|) ; tau_i = root of f (bisection above);
  *   p_j = [x_j - tau_i]_+^kappa (no renormalisation) ; o_i = sum_j p_j v_j;
  *   histogram counts and T of the row, tau_h from the B-bin problem;
  *   rowbits: bit J of the row's W = ceil(n/Bc) words (LSB first, 32 per word)
@@ -159,7 +174,7 @@ static void row_x(long d, const double *qi, const double *k, long nv, double alp
  * Any output pointer may be NULL except o and tau.
  */
 void oracle_attn_fwd_rows(long n, long d, const double *q, const double *k, const double *v,
-                          double alpha, double scale, int causal, int B, int Bc,
+                          double alpha, double scale, double slope, int causal, int B, int Bc,
                           long r0, long r1, double *o, double *tau, double *tau_h,
                           int32_t *counts, int64_t *T, uint32_t *rowbits, double *xgap,
                           double *psum)
@@ -169,7 +184,7 @@ void oracle_attn_fwd_rows(long n, long d, const double *q, const double *k, cons
     double *x = (double *)malloc(sizeof(double) * (size_t)n);
     for (long i = r0; i < r1; ++i) {
         long nv = causal ? i + 1 : n;
-        row_x(d, q + i * d, k, nv, alpha, scale, x);
+        row_x(d, i, q + i * d, k, nv, alpha, scale, slope, x);
         double t = oracle_entmax_tau(x, nv, alpha);
         tau[i - r0] = t;
         double *oi = o + (i - r0) * d;
@@ -218,7 +233,7 @@ void oracle_attn_fwd_rows(long n, long d, const double *q, const double *k, cons
  */
 void oracle_attn_bwd_rows(long n, long d, const double *q, const double *k, const double *v,
                           const double *dout, const double *tau, double alpha, double scale,
-                          int causal, long r0, long r1, double *dq, double *delta)
+                          double slope, int causal, long r0, long r1, double *dq, double *delta)
 {
     double kappa = 1.0 / (alpha - 1.0);
     double *x = (double *)malloc(sizeof(double) * (size_t)n);
@@ -226,7 +241,7 @@ void oracle_attn_bwd_rows(long n, long d, const double *q, const double *k, cons
     double *g = (double *)malloc(sizeof(double) * (size_t)n);
     for (long i = r0; i < r1; ++i) {
         long nv = causal ? i + 1 : n;
-        row_x(d, q + i * d, k, nv, alpha, scale, x);
+        row_x(d, i, q + i * d, k, nv, alpha, scale, slope, x);
         double t = tau[i - r0];
         double sg = 0.0, sgdp = 0.0;
         for (long j = 0; j < nv; ++j) {
@@ -261,13 +276,15 @@ void oracle_attn_bwd_rows(long n, long d, const double *q, const double *k, cons
  * Backward, per key, for keys [j0, j1) of one KV head shared by G query heads
  * (grouped-query attention: the KV head's gradients sum over its query heads).
  * q, dout: [G, n, d]; tau, delta: [G, n] (forward tau and the delta of
- * oracle_attn_bwd_rows). For each key j, over heads g and valid rows i:
+ * oracle_attn_bwd_rows); slopes: [G] position-bias slopes of those heads, or NULL
+ * for none. For each key j, over heads g and valid rows i:
  *   dk_j = scale * sum dS_ij q_i,   dv_j = sum p_ij dO_i.
  */
 void oracle_attn_bwd_keys(long n, long d, long G, const double *q, const double *k,
                           const double *v, const double *dout, const double *tau,
-                          const double *delta, double alpha, double scale, int causal,
-                          long j0, long j1, double *dk, double *dv)
+                          const double *delta, double alpha, double scale,
+                          const double *slopes, int causal, long j0, long j1, double *dk,
+                          double *dv)
 {
     double kappa = 1.0 / (alpha - 1.0);
     for (long j = j0; j < j1; ++j) {
@@ -278,11 +295,10 @@ void oracle_attn_bwd_keys(long n, long d, long G, const double *q, const double 
         }
         for (long gh = 0; gh < G; ++gh) {
             const double *qg = q + gh * n * d, *dog = dout + gh * n * d;
+            double slope = slopes ? slopes[gh] : 0.0;
             for (long i = causal ? j : 0; i < n; ++i) {
-                double s = 0.0;
-                for (long c = 0; c < d; ++c)
-                    s += qg[i * d + c] * k[j * d + c];
-                double diff = (alpha - 1.0) * (scale * s) - tau[gh * n + i];
+                double x = (alpha - 1.0) * score(d, qg + i * d, k + j * d, scale, slope, i, j);
+                double diff = x - tau[gh * n + i];
                 if (!(diff > 0.0))
                     continue;
                 double p = pow(diff, kappa);

@@ -20,16 +20,19 @@ def to64(t: torch.Tensor) -> np.ndarray:
     return t.detach().float().cpu().numpy().astype(np.float64)
 
 
-def run_gpu(inp: dict, w: synth.Workload, with_bwd: bool = True, stats=None, tau_init: int = 0):
+def run_gpu(inp: dict, w: synth.Workload, with_bwd: bool = True, stats=None, tau_init: int = 0,
+            slopes=None):
     d = dev()
     q, k, v = inp["q"].to(d), inp["k"].to(d), inp["v"].to(d)
     blk = (w.block_q, w.block_k)
+    sl = None if slopes is None else torch.tensor(list(slopes), dtype=torch.float32, device=d)
     r = lce.fwd(q, k, v, w.alpha, w.causal, blk, w.n_bins, return_hist=True, stats=stats,
-                tau_init=tau_init)
+                tau_init=tau_init, slopes=sl)
     out = {"o": r.o, "tau": r.tau, "mask": r.mask, "aux": r.aux, "hist": r.hist, "tau_h": r.tau_h}
     if with_bwd:
         do = inp["do"].to(d)
-        dq, dk, dv = lce.bwd(q, k, v, do, r.tau, r.mask, r.aux, w.alpha, w.causal, blk, w.n_bins)
+        dq, dk, dv = lce.bwd(q, k, v, do, r.tau, r.mask, r.aux, w.alpha, w.causal, blk, w.n_bins,
+                             slopes=sl)
         out.update(dq=dq, dk=dk, dv=dv)
     torch.cuda.synchronize()
     return {kk: (vv.cpu() if isinstance(vv, torch.Tensor) else vv) for kk, vv in out.items()}
@@ -43,10 +46,15 @@ def mask_bits(mask_i32: np.ndarray) -> np.ndarray:
     return mask_i32.astype(np.int64) & 0xFFFFFFFF
 
 
-def scores_x(q64, k64, alpha, scale, G):
-    """x = (alpha-1) scale q k^T per query head, fp64: [b, hq, n, n]."""
+def scores_x(q64, k64, alpha, scale, G, slopes=None):
+    """x = (alpha-1) (scale q k^T - slope |i - j|) per query head, fp64: [b, hq, n, n]."""
     kk = np.repeat(k64, G, axis=1)
-    return (alpha - 1.0) * (scale * np.einsum("bhid,bhjd->bhij", q64, kk))
+    s = scale * np.einsum("bhid,bhjd->bhij", q64, kk)
+    if slopes is not None:
+        n = s.shape[-1]
+        dist = np.abs(np.arange(n)[:, None] - np.arange(n)[None, :]).astype(np.float64)
+        s = s - np.asarray(slopes, dtype=np.float64)[None, :, None, None] * dist[None, None]
+    return (alpha - 1.0) * s
 
 
 def mask_mismatch_is_ambiguous(gpu_mask, ref_mask, x, tau_ref, w, band):

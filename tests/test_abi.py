@@ -76,38 +76,46 @@ def test_argument_errors(L, kw, status):
     d = _desc(**kw)
     assert L.entmax_attn_fwd_workspace_bytes(ctypes.byref(d)) == 0
     fake = ctypes.c_void_p(256)
-    st = L.entmax_attn_fwd(ctypes.byref(d), fake, fake, fake, fake, fake, fake, fake, None, None, None,
-                           fake, 1 << 30, None)
+    st = L.entmax_attn_fwd(ctypes.byref(d), fake, fake, fake, None, fake, fake, fake, fake, None, None,
+                           None, fake, 1 << 30, None)
     assert st == status, L.entmax_last_error()
     assert len(L.entmax_last_error()) > 0
-    st = L.entmax_attn_bwd(ctypes.byref(d), fake, fake, fake, fake, fake, fake, fake, fake, fake, fake,
-                           fake, 1 << 30, None)
+    st = L.entmax_attn_bwd(ctypes.byref(d), fake, fake, fake, fake, None, fake, fake, fake, fake, fake,
+                           fake, fake, 1 << 30, None)
     assert st == status
 
 
 def test_null_pointers_alignment_workspace(L):
     d = _desc()
     f = ctypes.c_void_p(4096)
-    assert L.entmax_attn_fwd(None, f, f, f, f, f, f, f, None, None, None, f, 1 << 30, None) == 1
-    assert L.entmax_attn_fwd(ctypes.byref(d), None, f, f, f, f, f, f, None, None, None, f, 1 << 30, None) == 1
+    assert L.entmax_attn_fwd(None, f, f, f, None, f, f, f, f, None, None, None, f, 1 << 30, None) == 1
+    assert L.entmax_attn_fwd(ctypes.byref(d), None, f, f, None, f, f, f, f, None, None, None, f, 1 << 30,
+                             None) == 1
     mis = ctypes.c_void_p(4098)
-    assert L.entmax_attn_fwd(ctypes.byref(d), mis, f, f, f, f, f, f, None, None, None, f, 1 << 30, None) == 5
+    assert L.entmax_attn_fwd(ctypes.byref(d), mis, f, f, None, f, f, f, f, None, None, None, f, 1 << 30,
+                             None) == 5
+    # slopes need 4-byte alignment
+    assert L.entmax_attn_fwd(ctypes.byref(d), f, f, f, mis, f, f, f, f, None, None, None, f, 1 << 30,
+                             None) == 5
     need = L.entmax_attn_fwd_workspace_bytes(ctypes.byref(d))
     assert need > 0
-    assert L.entmax_attn_fwd(ctypes.byref(d), f, f, f, f, f, f, f, None, None, None, f, need - 1, None) == 6
-    assert L.entmax_attn_fwd(ctypes.byref(d), f, f, f, f, f, f, f, None, None, None, None, need, None) == 6
+    assert L.entmax_attn_fwd(ctypes.byref(d), f, f, f, None, f, f, f, f, None, None, None, f, need - 1,
+                             None) == 6
+    assert L.entmax_attn_fwd(ctypes.byref(d), f, f, f, None, f, f, f, f, None, None, None, None, need,
+                             None) == 6
     nb = L.entmax_attn_bwd_workspace_bytes(ctypes.byref(d))
-    assert L.entmax_attn_bwd(ctypes.byref(d), f, f, f, f, f, f, f, f, f, f, f, nb - 1, None) == 6
-    assert L.entmax_attn_bwd(ctypes.byref(d), f, f, f, None, f, f, f, f, f, f, f, nb, None) == 1
+    assert L.entmax_attn_bwd(ctypes.byref(d), f, f, f, f, None, f, f, f, f, f, f, f, nb - 1, None) == 6
+    assert L.entmax_attn_bwd(ctypes.byref(d), f, f, f, None, None, f, f, f, f, f, f, f, nb, None) == 1
+    assert L.entmax_attn_bwd(ctypes.byref(d), f, f, f, f, mis, f, f, f, f, f, f, f, nb, None) == 5
 
 
 def test_empty_problem_is_a_no_op(L):
     for kw in (dict(batch=0), dict(heads_q=0, heads_kv=1), dict(seqlen=0)):
         d = _desc(**kw)
         assert L.entmax_attn_fwd(ctypes.byref(d), None, None, None, None, None, None, None, None, None,
-                                 None, None, 0, None) == 0
+                                 None, None, None, 0, None) == 0
         assert L.entmax_attn_bwd(ctypes.byref(d), None, None, None, None, None, None, None, None, None,
-                                 None, None, 0, None) == 0
+                                 None, None, None, 0, None) == 0
 
 
 def test_sizes(L):

@@ -20,9 +20,9 @@ from tests.gpu_helpers import (mask_bits, mask_mismatch_is_ambiguous, rel_fro, r
 pytestmark = pytest.mark.gpu
 
 
-def _oracle(inp, w):
+def _oracle(inp, w, slopes=None):
     return oracle.attn_full(to64(inp["q"]), to64(inp["k"]), to64(inp["v"]), to64(inp["do"]), w.alpha,
-                            w.causal, w.n_bins, w.block_q, w.block_k)
+                            w.causal, w.n_bins, w.block_q, w.block_k, slopes=slopes)
 
 
 def _check_prop1(g, ref, B):
@@ -112,6 +112,80 @@ def test_plain_bracket_start(case):
     for name in ("dq", "dk", "dv"):
         err = rel_fro(g[name].float().numpy().astype(np.float64), ref[name])
         assert err < 2e-2, (name, err)
+
+
+BIAS_CASES = [
+    # (b, hq, hkv, n, d, alpha, causal, Br, Bc, B, qk_scale)
+    (1, 4, 2, 256, 64, 1.5, True, 64, 64, 16, 1.0),
+    (1, 2, 1, 192, 64, 2.0, True, 64, 64, 16, 1.5),
+    (2, 4, 2, 128, 64, 1.5, False, 32, 64, 8, 1.0),
+    (1, 2, 2, 256, 128, 1.5, True, 64, 64, 8, 1.0),
+    (1, 4, 4, 256, 64, 1.25, True, 64, 32, 16, 0.8),
+    (1, 2, 1, 96, 64, 3.0, False, 32, 32, 8, 1.0),
+    (1, 4, 2, 384, 128, 2.0, True, 128, 64, 16, 1.2),
+]
+
+
+def _bias_slopes(hq):
+    """NAPE-style split with strong slopes: heads < hq/2 unbiased, then 1/2, 1/4, ..."""
+    return [0.0] * (hq // 2) + [2.0 ** -(t + 1) for t in range(hq - hq // 2)]
+
+
+@pytest.mark.parametrize("case", BIAS_CASES, ids=[str(c) for c in BIAS_CASES])
+def test_position_bias(case):
+    """Per-head position bias (NAPE heads: half without encoding, half ALiBi)."""
+    b, hq, hkv, n, d, alpha, causal, Br, Bc, B, qs = case
+    slopes = _bias_slopes(hq)
+    print(f"[case] bias {case} slopes {slopes}", flush=True)
+    # alpha > 2: g = (x - tau)^(1/(alpha-1) - 1) is unbounded at the threshold, so a score
+    # within 1e-4 of tau makes the gradient ill-conditioned; such inputs are skipped by seed
+    for t in range(20):
+        w = synth.Workload("t", b, hq, hkv, n, d, "bf16", alpha, causal, Br, Bc, B, "normal",
+                           extra={"qk_scale": qs}, seed=(hash(case) + 7 + 1000 * t) & 0xFFFF)
+        inp = synth.make_inputs(w)
+        ref = _oracle(inp, w, slopes)
+        if alpha <= 2.0 or ref["xgap"].min() > 1e-4:
+            break
+    g = run_gpu(inp, w, slopes=slopes)
+    assert np.abs(g["tau"].numpy() - ref["tau"]).max() < 1e-3
+    assert np.abs(g["o"].float().numpy() - ref["o"]).max() < 1e-2
+    _check_prop1(g, ref, B)
+    x = scores_x(to64(inp["q"]), to64(inp["k"]), alpha, 1.0 / math.sqrt(d), hq // hkv, slopes)
+    assert mask_mismatch_is_ambiguous(g["mask"].numpy(), ref["mask"], x, ref["tau"], w, 1e-3)
+    for name in ("dq", "dk", "dv"):
+        err = rel_fro(g[name].float().numpy().astype(np.float64), ref[name])
+        assert err < 2e-2, (name, err)
+
+
+def test_position_bias_fp32_bit_exact():
+    """The tiny fp32 configuration with slope 1/16: every biased score is exact in fp32
+    (x B = score B / 2 - |i - j| / 2), so counts and the block mask match bit for bit."""
+    w = synth.workload("C1")
+    slopes = [0.0625]
+    print(f"[case] C1 bias {slopes}", flush=True)
+    inp = synth.make_inputs(w)
+    ref = _oracle(inp, w, slopes)
+    assert ref["xgap"].min() > 1e-6, "test construction: a score sits on the threshold"
+    g = run_gpu(inp, w, slopes=slopes)
+    np.testing.assert_array_equal(g["hist"].numpy(), ref["counts"])
+    _check_prop1(g, ref, w.n_bins)
+    assert np.abs(g["tau"].numpy() - ref["tau"]).max() < 1e-5
+    np.testing.assert_array_equal(mask_bits(g["mask"].numpy()), ref["mask"].astype(np.int64))
+    assert np.abs(g["o"].numpy() - ref["o"]).max() < 1e-4
+    for name in ("dq", "dk", "dv"):
+        err = rel_fro(g[name].numpy().astype(np.float64), ref[name])
+        assert err < 1e-4, (name, err)
+
+
+def test_zero_slopes_match_no_bias():
+    """All-zero slopes take the bias kernels and must reproduce the unbiased run."""
+    w = synth.Workload("t", 1, 4, 2, 256, 64, "bf16", 1.5, True, 64, 64, 16, "normal", seed=11)
+    print("[case] zero slopes", flush=True)
+    inp = synth.make_inputs(w)
+    a = run_gpu(inp, w)
+    z = run_gpu(inp, w, slopes=[0.0] * 4)
+    for kk in ("o", "tau", "mask", "hist", "tau_h", "dq", "dk", "dv"):
+        assert torch.equal(a[kk], z[kk]), kk
 
 
 def test_fp32_random_causal_gqa():

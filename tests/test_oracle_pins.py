@@ -403,3 +403,124 @@ def test_backward_softmax_limit():
         r = oracle.attn_bwd_rows_head(q, k, v, do, f["tau"], alpha, False, scale)
         errs.append(np.abs(r["dq"] - dq_soft).max())
     assert errs[1] < 0.25 * errs[0] and errs[2] < 0.25 * errs[1]
+
+
+# ------------------------------------------------------------------------------------------------
+# position bias (NAPE heads: half without position encoding, half ALiBi; page 2 section 4)
+# ------------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_position_bias_hand_derived(causal):
+    """q = 0 leaves only the bias: x_ij = -m |i - j| at alpha = 2 (sparsemax).
+
+    Derived by hand for m = 0.05. Causal row i >= 5: the support is the k nearest keys
+    with k (k - 1) < 2/m = 40, so k = 6 and tau = -(1 + m k (k - 1)/2)/k = -1.75/6,
+    p_ij = 0.29167, 0.24167, ..., 0.04167 for i - j = 0..5. Full (non-causal) interior
+    row: the support |i - j| <= 4 gives tau = -(1 + m r (r - 1))/(2r - 1) = -2/9 with r = 5,
+    and the excluded keys at distance 5 have x = -0.25 <= tau.
+    """
+    n, m = 32, 0.05
+    q = np.zeros((n, n))
+    k = np.ones((n, n))
+    v = np.eye(n)                      # o_i is the weight row p_i
+    f = oracle.attn_fwd_head(q, k, v, 2.0, causal, 16, 32, 1.0, slope=m)
+    if causal:
+        rows, tau = range(5, n), -1.75 / 6
+    else:
+        rows, tau = range(4, n - 4), -2.0 / 9.0
+    for i in rows:
+        assert abs(f["tau"][i] - tau) < 1e-12
+        dist = np.abs(i - np.arange(n))
+        want = np.maximum(-m * dist - tau, 0.0)
+        if causal:
+            want[i + 1:] = 0.0
+        np.testing.assert_allclose(f["o"][i], want, atol=1e-12)
+    if causal:
+        np.testing.assert_allclose(f["o"][10][5:11], [0.25 / 6 + 0.05 * t for t in range(6)], atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_position_bias_closed_forms(causal):
+    """Random q, k with a slope: the sort-based closed forms on the biased scores."""
+    rng = np.random.default_rng(33)
+    n, d = 80, 16
+    q, k, v = _rand_problem(rng, n, d, 1.5)
+    scale = 1.0 / math.sqrt(d)
+    for alpha, ref, m in ((2.0, sparsemax_closed_form, 0.07), (1.5, entmax15_closed_form, 0.3)):
+        f = oracle.attn_fwd_head(q, k, v, alpha, causal, 16, 32, scale, slope=m)
+        f0 = oracle.attn_fwd_head(q, k, v, alpha, causal, 16, 32, scale)
+        for i in range(n):
+            nv = i + 1 if causal else n
+            s = scale * (q[i] @ k[:nv].T) - m * np.abs(i - np.arange(nv))
+            p, t = ref(s)
+            assert abs(f["tau"][i] - t) < 1e-10
+            np.testing.assert_allclose(f["o"][i], p @ v[:nv], atol=1e-10)
+        # the bias moves the weight towards the diagonal
+        assert np.mean(f["xgap"]) != np.mean(f0["xgap"])
+
+
+def _loss_bias(q, k, v, do, alpha, causal, scale, m):
+    f = oracle.attn_fwd_head(q, k, v, alpha, causal, 16, 32, scale, threads=1, slope=m)
+    return float((f["o"] * do).sum()), f
+
+
+@pytest.mark.parametrize("alpha", [1.5, 2.0, 3.0])
+@pytest.mark.parametrize("causal", [False, True])
+def test_position_bias_gradients_finite_differences(alpha, causal):
+    """Analytic backward with a slope vs central differences of L = sum(O * dO)."""
+    n, d, m = 10, 4, 0.35
+    scale = 1.0 / math.sqrt(d)
+    seed = 0
+    while True:
+        rng = np.random.default_rng(2000 * seed + int(alpha * 10) + causal)
+        q, k, v = _rand_problem(rng, n, d, 1.2)
+        do = rng.standard_normal((n, d))
+        L0, f = _loss_bias(q, k, v, do, alpha, causal, scale, m)
+        if f["xgap"].min() > 1e-3 and seed < 50:
+            break
+        seed += 1
+    r = oracle.attn_bwd_rows_head(q, k, v, do, f["tau"], alpha, causal, scale, threads=1, slope=m)
+    kk = oracle.attn_bwd_keys_group(q[None], k, v, do[None], f["tau"][None], r["delta"][None],
+                                    alpha, causal, scale, threads=1, slopes=[m])
+    eps = 1e-5
+    for name, arr, grad in (("q", q, r["dq"]), ("k", k, kk["dk"]), ("v", v, kk["dv"])):
+        num = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            a1, a2 = arr.copy(), arr.copy()
+            a1[idx] += eps
+            a2[idx] -= eps
+            args1 = {"q": q, "k": k, "v": v}
+            args2 = {"q": q, "k": k, "v": v}
+            args1[name], args2[name] = a1, a2
+            L1, _ = _loss_bias(args1["q"], args1["k"], args1["v"], do, alpha, causal, scale, m)
+            L2, _ = _loss_bias(args2["q"], args2["k"], args2["v"], do, alpha, causal, scale, m)
+            num[idx] = (L1 - L2) / (2 * eps)
+        err = np.linalg.norm(num - grad) / max(np.linalg.norm(num), 1e-12)
+        assert err < 1e-5, (name, err)
+
+
+def test_position_bias_gqa_heads_sum():
+    """A KV head's dK/dV with per-head slopes is the sum of its heads' single-head results."""
+    rng = np.random.default_rng(12)
+    b, hq, hkv, n, d = 1, 4, 2, 48, 8
+    q = rng.standard_normal((b, hq, n, d)) * 1.5
+    k = rng.standard_normal((b, hkv, n, d)) * 1.5
+    v = rng.standard_normal((b, hkv, n, d))
+    do = rng.standard_normal((b, hq, n, d))
+    slopes = np.array([0.0, 0.25, 0.0, 0.0625])
+    res = oracle.attn_full(q, k, v, do, 1.5, True, 16, 32, 32, threads=4, slopes=slopes)
+    G = hq // hkv
+    scale = 1.0 / math.sqrt(d)
+    for kh in range(hkv):
+        dk = np.zeros((n, d))
+        dv = np.zeros((n, d))
+        for g in range(G):
+            h = kh * G + g
+            one = oracle.attn_bwd_keys_group(q[0, h][None], k[0, kh], v[0, kh], do[0, h][None],
+                                             res["tau"][0, h][None], res["delta"][0, h][None],
+                                             1.5, True, scale, slopes=[slopes[h]])
+            dk += one["dk"]
+            dv += one["dv"]
+        np.testing.assert_allclose(res["dk"][0, kh], dk, atol=1e-12)
+        np.testing.assert_allclose(res["dv"][0, kh], dv, atol=1e-12)
+        np.testing.assert_allclose(res["dk"][0, kh].sum(0), 0.0, atol=1e-9)

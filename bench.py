@@ -16,6 +16,7 @@ sample of the same workload.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import math
@@ -46,6 +47,9 @@ def parse():
     ap.add_argument("--nape", action="store_true",
                     help="NAPE heads: the first half of the query heads without position "
                          "encoding, the second half ALiBi (per-head slopes of the scores)")
+    ap.add_argument("--decode", action="store_true",
+                    help="time one decode step (a new query row per head against the workload's "
+                         "K/V as a cache) instead of the training step")
     ap.add_argument("--tau-error", action="store_true",
                     help="instead of timing, print the mean |tau_p - tau*| after p = 1..15 "
                          "refinement passes for both starts (tau* = the converged tau)")
@@ -159,6 +163,59 @@ def tau_error_study(lce, w, q, k, v, blk, wsf):
     return out
 
 
+def decode_bench(args, lce, w, inp, dev):
+    """One decode step per iteration: q = the workload's query row n-1, the workload's K and V
+    as the cache. Roofline of the score kernel: HBM bytes = the K cache read once plus the
+    fp32 score row written."""
+    import torch
+    n = w.seqlen
+    q = inp["q"][:, :, n - 1].contiguous()
+    k, v = inp["k"], inp["v"]
+    slopes = (torch.tensor(lce.nape_slopes(w.heads_q), dtype=torch.float32, device=dev)
+              if args.nape else None)
+    desc = lce.make_desc(w.batch, w.heads_q, w.heads_kv, n, w.head_dim,
+                         lce.ENTMAX_BF16 if w.dtype == "bf16" else lce.ENTMAX_F32, w.alpha, True,
+                         (32, 32), w.n_bins)
+    ws = torch.empty(lce.lib().entmax_attn_decode_workspace_bytes(ctypes.byref(desc)),
+                     dtype=torch.uint8, device=dev)
+    step = lambda: lce.decode(q, k, v, w.alpha, w.n_bins, slopes=slopes, workspace=ws)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    lce.profile(True)
+    lce.profile_read()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    kt = lce.profile_read()
+    lce.profile(False)
+    kern = {name: t / max(c, 1) for name, (t, c) in kt.items()}
+    es = 2 if w.dtype == "bf16" else 4
+    kbytes = w.batch * w.heads_kv * n * w.head_dim * es + w.batch * w.heads_q * n * 4
+    achieved = kbytes / (kern["dec_scores"] * 1e-3) / 1e9
+    line = {
+        "metric": "decode_tokens_per_s", "value": round(w.batch / (ms * 1e-3), 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "vs_baseline": None, "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic (the workload's K/V as the cache, its query row n-1)",
+        "config": {"workload": f"decode against {w.name}: b{w.batch} hq{w.heads_q}/hkv{w.heads_kv} "
+                               f"cache {n} d{w.head_dim} alpha {w.alpha} B {w.n_bins}",
+                   "position_bias": "NAPE" if args.nape else "none"},
+        "roofline": {"kernel": "dec_scores", "bound": "hbm", "achieved": round(achieved, 1),
+                     "peak": 8000.0, "unit": "GB/s", "frac": round(achieved / 8000.0, 4),
+                     "traffic": None, "algorithmic_bytes_per_launch": kbytes},
+        "kernels_ms": {kk: round(vv, 4) for kk, vv in kern.items()},
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -172,7 +229,10 @@ def main():
     w = synth.workload(args.config, alpha=args.alpha, sparsity=args.sparsity)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    inp = synth.make_inputs(w, device=dev)
+    inp = synth.make_inputs(w, device=dev, need_grad_inputs=not args.decode)
+    if args.decode:
+        decode_bench(args, lce, w, inp, dev)
+        return
     q, k, v, do = inp["q"], inp["k"], inp["v"], inp["do"]
     blk = (w.block_q, w.block_k)
     b, hq, n, d = q.shape

@@ -148,6 +148,35 @@ entmax_status entmax_attn_bwd(const entmax_attn_desc *desc,
                               void *dq, void *dk, void *dv,
                               void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * Decode: one new query row per (sequence, query head) against a KV cache, forward only
+ * (the pages leave inference to future work, page 3 section 5; DashAttention decodes
+ * incrementally on the same primitives, page 4). The query follows the cached keys, so
+ * keys 0..len_b-1 of sequence b are all valid and, with a position bias, key j sits at
+ * distance len_b - 1 - j. The threshold is found as in the forward: the B-bin histogram
+ * of the row's scores gives tau_h (Proposition 1), the same hybrid solver refines it, and
+ * o = sum_j p_j v_j. The result equals the last row of a causal forward over the cache.
+ *
+ * desc: batch, heads_q, heads_kv (heads_q / heads_kv <= 16), seqlen = cache capacity n_ctx
+ *       (1..2^19, any value), head_dim, dtype, alpha, n_bins, scale, max_iters, tol and
+ *       tau_init as for the forward; causal, block_q and block_k are not used.
+ * q        [batch, heads_q, head_dim] dtype             k_cache, v_cache [batch, heads_kv, n_ctx, head_dim] dtype
+ * lengths  [batch] int32, device, optional (NULL = n_ctx): valid keys of each sequence,
+ *          values are clamped to 1..n_ctx
+ * slopes   [heads_q] float32, device, optional: position bias as in the forward
+ * o        [batch, heads_q, head_dim] float32            tau, tau_h [batch, heads_q] float32
+ * hist_counts [batch, heads_q, n_bins] int32, optional; tau_h optional
+ * Alignment: q, k_cache, v_cache, o 16 bytes; tau, lengths, slopes, tau_h, counts 4 bytes.
+ * workspace: at least entmax_attn_decode_workspace_bytes(desc) bytes, 256-byte aligned
+ * (the score rows, fp32 [batch, heads_q, n_ctx], and per-split partial results).
+ */
+size_t entmax_attn_decode_workspace_bytes(const entmax_attn_desc *desc);
+entmax_status entmax_attn_decode(const entmax_attn_desc *desc,
+                                 const void *q, const void *k_cache, const void *v_cache,
+                                 const int32_t *lengths, const float *slopes,
+                                 float *o, float *tau, int32_t *hist_counts, float *tau_h,
+                                 void *workspace, size_t workspace_bytes, void *stream);
+
 const char *entmax_status_string(entmax_status s);
 const char *entmax_last_error(void);
 

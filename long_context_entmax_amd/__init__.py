@@ -56,7 +56,8 @@ _DP = ctypes.POINTER(Desc)
 
 EXPORTS = [
     "entmax_attn_fwd_workspace_bytes", "entmax_attn_bwd_workspace_bytes", "entmax_attn_aux_bytes",
-    "entmax_attn_mask_words", "entmax_attn_fwd", "entmax_attn_bwd", "entmax_status_string",
+    "entmax_attn_mask_words", "entmax_attn_fwd", "entmax_attn_bwd", "entmax_attn_decode_workspace_bytes",
+    "entmax_attn_decode", "entmax_status_string",
     "entmax_last_error", "entmax_attn_profile", "entmax_attn_profile_read",
 ]
 
@@ -77,6 +78,10 @@ def lib() -> ctypes.CDLL:
         L.entmax_attn_fwd.argtypes = [_DP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
         L.entmax_attn_bwd.restype = ctypes.c_int
         L.entmax_attn_bwd.argtypes = [_DP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+        L.entmax_attn_decode_workspace_bytes.restype = _sz
+        L.entmax_attn_decode_workspace_bytes.argtypes = [_DP]
+        L.entmax_attn_decode.restype = ctypes.c_int
+        L.entmax_attn_decode.argtypes = [_DP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
         L.entmax_status_string.restype = ctypes.c_char_p
         L.entmax_status_string.argtypes = [ctypes.c_int]
         L.entmax_last_error.restype = ctypes.c_char_p
@@ -228,6 +233,46 @@ def bwd(q, k, v, do, tau, mask, aux, alpha: float = 1.5, causal: bool = True, bl
                              _ptr(mask), _ptr(aux), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
                              workspace.numel(), _stream(dev)))
     return dq, dk, dv
+
+
+DecodeOut = namedtuple("DecodeOut", "o tau hist tau_h")
+
+
+def decode(q, k_cache, v_cache, alpha: float = 1.5, bins: int = 16, scale: Optional[float] = None,
+           lengths=None, slopes=None, max_iters: int = 0, tol: float = 0.0, tau_init: int = 0,
+           return_hist: bool = False, workspace=None) -> DecodeOut:
+    """One decode step: q [b, hq, d] against the caches k_cache, v_cache [b, hkv, n_ctx, d].
+
+    ``lengths``: optional int32 [b] device tensor of valid cache lengths (default n_ctx).
+    Returns o [b, hq, d] (float32), tau [b, hq] and, with ``return_hist``, the histogram
+    counts [b, hq, bins] and tau_h [b, hq]. Equals the last row of a causal forward.
+    """
+    torch = _torch()
+    _require_gpu(q, k_cache, v_cache, lengths, slopes)
+    if q.dim() != 3 or k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("q must be [b, hq, d] and the caches [b, hkv, n_ctx, d]")
+    b, hq, d = q.shape
+    if k_cache.shape[0] != b or k_cache.shape[3] != d or q.dtype != k_cache.dtype:
+        raise ValueError("q and the caches disagree in batch, head_dim or dtype")
+    if lengths is not None and (lengths.dtype != torch.int32 or lengths.numel() != b):
+        raise ValueError("lengths must be int32 with one value per sequence")
+    _check_slopes(slopes, hq)
+    dt = ENTMAX_BF16 if q.dtype == torch.bfloat16 else ENTMAX_F32
+    desc = make_desc(b, hq, k_cache.shape[1], k_cache.shape[2], d, dt, alpha, True, (32, 32), bins,
+                     scale, max_iters, tol, tau_init)
+    L = lib()
+    dev = q.device
+    o = torch.empty((b, hq, d), dtype=torch.float32, device=dev)
+    tau = torch.empty((b, hq), dtype=torch.float32, device=dev)
+    hist = torch.empty((b, hq, bins), dtype=torch.int32, device=dev) if return_hist else None
+    tau_h = torch.empty((b, hq), dtype=torch.float32, device=dev) if return_hist else None
+    nbytes = L.entmax_attn_decode_workspace_bytes(ctypes.byref(desc))
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+    _check(L.entmax_attn_decode(ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(lengths),
+                                _ptr(slopes), _ptr(o), _ptr(tau), _ptr(hist), _ptr(tau_h), _ptr(workspace),
+                                workspace.numel(), _stream(dev)))
+    return DecodeOut(o, tau, hist, tau_h)
 
 
 def workspace_bytes(desc: Desc) -> Tuple[int, int]:

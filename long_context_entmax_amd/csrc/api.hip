@@ -93,7 +93,8 @@ struct Derived {
 
 static bool pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 
-static entmax_status derive(const entmax_attn_desc* d, Derived& o) {
+// decode: blocks and the causal flag are not used, seqlen is the cache capacity (any value)
+static entmax_status derive(const entmax_attn_desc* d, Derived& o, bool decode = false) {
   if (!d) return fail(ENTMAX_ERR_NULL, "desc is NULL");
   o.b = d->batch; o.hq = d->heads_q; o.hkv = d->heads_kv; o.n = d->seqlen; o.D = d->head_dim;
   if (o.b < 0 || o.hq < 0 || o.hkv < 0 || o.n < 0 || o.D <= 0)
@@ -107,17 +108,20 @@ static entmax_status derive(const entmax_attn_desc* d, Derived& o) {
   if (d->dtype != ENTMAX_F32 && d->dtype != ENTMAX_BF16)
     return fail(ENTMAX_ERR_UNSUPPORTED, "dtype %d is not F32 (0) or BF16 (1)", d->dtype);
   if (o.D != 64 && o.D != 128) return fail(ENTMAX_ERR_UNSUPPORTED, "head_dim %d: only 64 and 128", o.D);
-  o.Br = d->block_q; o.Bc = d->block_k;
+  o.Br = decode ? 32 : d->block_q;
+  o.Bc = decode ? 32 : d->block_k;
   if (!(o.Br == 32 || o.Br == 64 || o.Br == 128) || !(o.Bc == 32 || o.Bc == 64 || o.Bc == 128))
     return fail(ENTMAX_ERR_UNSUPPORTED, "blocks %dx%d: each must be 32, 64 or 128", o.Br, o.Bc);
-  if (o.n % o.Br != 0 || o.n % o.Bc != 0)
+  if (!decode && (o.n % o.Br != 0 || o.n % o.Bc != 0))
     return fail(ENTMAX_ERR_SHAPE, "seqlen %d is not a multiple of the blocks %dx%d", o.n, o.Br, o.Bc);
+  if (decode && o.hkv > 0 && o.hq / o.hkv > 16)
+    return fail(ENTMAX_ERR_UNSUPPORTED, "decode: heads_q / heads_kv = %d > 16", o.hq / o.hkv);
   if (o.n > (1 << 19)) return fail(ENTMAX_ERR_UNSUPPORTED, "seqlen %d > 524288", o.n);
   o.B = d->n_bins;
   if (!pow2(o.B) || o.B < 2 || o.B > 16)
     return fail(ENTMAX_ERR_UNSUPPORTED, "n_bins %d: must be 2, 4, 8 or 16", o.B);
-  if (d->causal != 0 && d->causal != 1) return fail(ENTMAX_ERR_SHAPE, "causal must be 0 or 1");
-  o.causal = d->causal;
+  if (!decode && d->causal != 0 && d->causal != 1) return fail(ENTMAX_ERR_SHAPE, "causal must be 0 or 1");
+  o.causal = decode ? 1 : d->causal;
   // default pass caps: Halley (alpha <= 1.5) converges in a few passes; Newton from
   // below shrinks a large support about by half per pass; the secant needs the most
   if (d->tau_init != 0 && d->tau_init != 1)
@@ -346,6 +350,62 @@ entmax_status entmax_attn_bwd(const entmax_attn_desc* desc, const void* q, const
   e = launch_bwd_dq(p, o.dtype, o.D, o.mode, s);
   prof_end(s);
   if (e != hipSuccess) return hip_fail(e, "dQ kernel");
+  return ENTMAX_OK;
+}
+
+struct DecLayout {
+  size_t xs, smax, opart, total;
+  int nsplit, ldx;
+};
+
+static DecLayout dec_ws(const Derived& o) {
+  DecLayout L;
+  L.nsplit = (o.n + DEC_SPLIT - 1) / DEC_SPLIT;
+  const size_t rows = (size_t)o.b * o.hq;
+  L.xs = 0;
+  L.ldx = (o.n + 3) & ~3;
+  L.smax = align256(rows * L.ldx * sizeof(float));
+  L.opart = L.smax + align256(rows * L.nsplit * sizeof(float));
+  L.total = L.opart + align256((size_t)L.nsplit * rows * o.D * sizeof(float));
+  return L;
+}
+
+size_t entmax_attn_decode_workspace_bytes(const entmax_attn_desc* desc) {
+  Derived o;
+  if (derive(desc, o, true) != ENTMAX_OK) return 0;
+  return dec_ws(o).total;
+}
+
+entmax_status entmax_attn_decode(const entmax_attn_desc* desc, const void* q, const void* k_cache,
+                                 const void* v_cache, const int32_t* lengths, const float* slopes, float* o_,
+                                 float* tau, int32_t* hist_counts, float* tau_h, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  Derived o;
+  entmax_status st = derive(desc, o, true);
+  if (st != ENTMAX_OK) return st;
+  if ((size_t)o.b * o.hq == 0) return ENTMAX_OK;
+  if (o.n == 0) return fail(ENTMAX_ERR_SHAPE, "decode needs a cache of at least one key (seqlen 0)");
+  if (!q || !k_cache || !v_cache || !o_ || !tau)
+    return fail(ENTMAX_ERR_NULL, "q, k_cache, v_cache, o and tau are required");
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(o_, 16) || !aligned(tau, 4) ||
+      (lengths && !aligned(lengths, 4)) || (slopes && !aligned(slopes, 4)) ||
+      (hist_counts && !aligned(hist_counts, 4)) || (tau_h && !aligned(tau_h, 4)))
+    return fail(ENTMAX_ERR_ALIGN, "q, k_cache, v_cache, o need 16-byte alignment; the others 4-byte");
+  const DecLayout L = dec_ws(o);
+  if (!workspace || workspace_bytes < L.total || !aligned(workspace, 256))
+    return fail(ENTMAX_ERR_WORKSPACE, "decode workspace: need %zu bytes, 256-byte aligned (got %zu)", L.total,
+                workspace_bytes);
+  char* ws = (char*)workspace;
+  DecParams p{};
+  p.q = q; p.k = k_cache; p.v = v_cache; p.lengths = lengths; p.slopes = slopes;
+  p.o = o_; p.tau = tau; p.hist = hist_counts; p.tau_h = tau_h;
+  p.xs = (float*)(ws + L.xs); p.smax = (float*)(ws + L.smax); p.opart = (float*)(ws + L.opart);
+  p.b = o.b; p.hq = o.hq; p.hkv = o.hkv; p.G = o.G; p.n = o.n; p.B = o.B;
+  p.max_iters = o.max_iters; p.tau_init = o.tau_init; p.nsplit = L.nsplit; p.ldx = L.ldx;
+  p.cx = (float)(((double)o.alpha - 1.0) * (double)o.scale);
+  p.am1 = o.alpha - 1.0f; p.alpha = o.alpha; p.kappa = o.kappa; p.tol = o.tol;
+  const hipError_t e = launch_decode(p, o.dtype, o.D, o.mode, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "decode kernels");
   return ENTMAX_OK;
 }
 

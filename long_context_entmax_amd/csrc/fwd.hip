@@ -35,85 +35,10 @@
 
 #include "common.hpp"
 #include "kernels.hpp"
+#include "solver.hpp"
 
 namespace entmax {
 
-namespace {
-
-// tau_h from merged counts c[0..B-1] (bin k has lower edge l_k = (T - B + 1 + k)/B).
-// Works relative to l_top = T/B with u_k = l_k - l_top = (k - B + 1)/B exactly.
-template <int MODE>
-__device__ float tau_from_counts(const int (&cnt)[16], int T, int B, float kappa) {
-  const float invB = 1.0f / (float)B;
-  const float ltop = (float)T * invB;
-  float v = -1.0f;
-  if constexpr (MODE == 1) {
-    // sum_k c_k (u_k - v)_+ = 1: scan bins from the top, v = (S1 - 1)/S0
-    float S0 = 0.f, S1 = 0.f;
-    bool found = false;
-#pragma unroll
-    for (int kk = 15; kk >= 0; --kk) {
-      if (kk < B && !found) {
-        const int k = kk;
-        const float u = (float)(k - B + 1) * invB;
-        S0 += (float)cnt[k];
-        S1 += (float)cnt[k] * u;
-        if (S0 > 0.f) {
-          const float vv = (S1 - 1.0f) / S0;
-          const float lower = (k > 0) ? u - invB : -INFINITY;
-          if (vv >= lower) {
-            v = vv;
-            found = true;
-          }
-        }
-      }
-    }
-  } else if constexpr (MODE == 2) {
-    // sum_k c_k (u_k - v)_+^2 = 1 on the top bins: v = mu - sqrt((1 - sum c (u - mu)^2)/S0)
-    float S0 = 0.f, S1 = 0.f, S2 = 0.f;
-    bool found = false;
-#pragma unroll
-    for (int kk = 15; kk >= 0; --kk) {
-      if (kk < B && !found) {
-        const int k = kk;
-        const float u = (float)(k - B + 1) * invB;
-        const float cf = (float)cnt[k];
-        S0 += cf;
-        S1 += cf * u;
-        S2 += cf * u * u;
-        if (S0 > 0.f) {
-          const float mu = S1 / S0;
-          const float ss = fmaxf(S2 - S1 * mu, 0.f);
-          const float vv = mu - sqrtf(fmaxf(1.0f - ss, 0.f) / S0);
-          const float lower = (k > 0) ? u - invB : -INFINITY;
-          if (vv >= lower) {
-            v = vv;
-            found = true;
-          }
-        }
-      }
-    }
-  } else {
-    // any kappa: bisection on [-1, 0]; keep the end where the B-bin mass is >= 1
-    float lo = -1.0f, hi = 0.0f;
-    for (int it = 0; it < 32; ++it) {
-      const float mid = 0.5f * (lo + hi);
-      float s = 0.f;
-#pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        if (k < B && cnt[k] > 0) {
-          const float t = (float)(k - B + 1) * invB - mid;
-          if (t > 0.f) s += (float)cnt[k] * exp2f(kappa * log2f(t));
-        }
-      }
-      if (s >= 1.0f) lo = mid; else hi = mid;
-    }
-    v = lo;
-  }
-  return ltop + v;
-}
-
-}  // namespace
 
 #ifndef HIST_OCC64
 #define HIST_OCC64 4
@@ -424,25 +349,11 @@ __global__ __launch_bounds__(64 * OUT_WAVES, 2) void k_refine_out(FwdParams p) {
     for (int s = 0; s < DS; ++s) scale_frag(qf[s], p.cx);
   }
   const float cx = p.cx;
-  // Bracket [tau_h, tau_h + 1/B] (with a margin of 1/(16B) below tau_h for fp32 rounding of
-  // the B-bin solve); the first evaluation is a quarter of the way into it. Starting above
-  // tau_h leaves out the sub-blocks whose scores all lie in the bottom quarter, and on the
-  // workloads' rows it also takes fewer passes than starting at tau_h.
-  const float hB = 1.0f / (float)B;
-  float lo, hi, tau;
-  if (p.tau_init == 0) {
-    const float tau_h = p.tauh_ws[bh * n + qrow];
-    lo = tau_h - 0.0625f * hB;
-    hi = tau_h + hB;
-    tau = tau_h + 0.25f * hB;
-  } else {
-    // plain bracket [x_max - 1, x_max - n_valid^(1-alpha)], started at its lower end
-    const float xm = p.tauh_ws[bh * n + qrow];
-    const float nv = p.causal ? (float)(qrow + 1) : (float)n;
-    lo = xm - 1.0f;
-    hi = xm - exp2f((1.0f - p.alpha) * log2f(nv));
-    tau = lo;
-  }
+  // solver state: the bracket from tau_h (or the plain bracket below the row max)
+  const float nv = p.causal ? (float)(qrow + 1) : (float)n;
+  RowState st = p.tau_init == 0 ? RowState::from_hist(p.tauh_ws[bh * n + qrow], B)
+                                : RowState::from_max(p.tauh_ws[bh * n + qrow], nv, p.alpha);
+  float& tau = st.tau;
 
   // Walk over the sub-blocks a pass needs: candidate bits of the histogram pass, kept
   // where the recorded chunk max exceeds the threshold (read 32 at a time).
@@ -492,23 +403,18 @@ __global__ __launch_bounds__(64 * OUT_WAVES, 2) void k_refine_out(FwdParams p) {
   // or sum d^(kappa-2), v3 = sum (x - hi)_+^kappa (secant start), v4 = smallest positive
   // gap x - tau (alpha 1.5, 2)
   const float kappa = p.kappa, alpha = p.alpha;
-  bool done = false;
-  int rowpass = 0;
-  float tprev = 0.f, fprev = 0.f;
   const bool secant = alpha > 2.0f;
   int npass = 0;
   unsigned long long n_ref = 0;
   Frag<T> kf[DS];
   while (npass < p.max_iters) {
-    if (ballot(!done) == 0) break;
+    if (ballot(!st.done) == 0) break;
     const bool first = (npass == 0);
-    const float thr = wave_min(done ? INFINITY : tau) * (float)B;
+    const float thr = wave_min(st.done ? INFINITY : tau) * (float)B;
 #pragma unroll
     for (int r = 0; r < 16; ++r) negt[r] = -tau;
-    float F0 = 0.f, F1 = 0.f, F2 = 0.f, Fh = 0.f;
-    const float thi = hi - tau;          // secant start: f at the bracket's upper end
-    int cnt = 0;
-    uint32_t mrelb = 0xFFFFFFFFu;        // positive floats order like their bits
+    PassSums sums;
+    const float thi = st.hi - st.tau;    // secant start: f at the bracket's upper end
     Walk wk{-1, 0u};
     int kb = walk_next(wk, thr);
     if (kb >= 0) Ops::load_k(kf, Kf, kb, c, h);
@@ -521,120 +427,24 @@ __global__ __launch_bounds__(64 * OUT_WAVES, 2) void k_refine_out(FwdParams p) {
       ++n_ref;
       const f32x16 t = tile(kc, kb);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float tt = t[r];
-        if constexpr (MODE == 2) {
-          const float dm = fmaxf(tt, 0.f);
-          F0 = fmaf(dm, dm, F0);
-          F1 += dm;
-          cnt += (tt > 0.f) ? 1 : 0;
-          mrelb = min(mrelb, __float_as_uint(tt));
-        } else if constexpr (MODE == 1) {
-          F0 += fmaxf(tt, 0.f);
-          cnt += (tt > 0.f) ? 1 : 0;
-          mrelb = min(mrelb, __float_as_uint(tt));
-        } else {
-          const bool in = tt > 0.f;
-          const float lt = log2f(in ? tt : 1.0f);
-          F0 += in ? exp2f(kappa * lt) : 0.f;
-          F1 += in ? exp2f((kappa - 1.0f) * lt) : 0.f;
-          F2 += in ? exp2f((kappa - 2.0f) * lt) : 0.f;
-          if (secant && first) {
-            const float u = tt - thi;      // x - hi
-            Fh += u > 0.f ? exp2f(kappa * log2f(u)) : 0.f;
-          }
-        }
-      }
+      for (int r = 0; r < 16; ++r) sums.add<MODE>(t[r], thi, secant && first, kappa);
       kb = kn;
     }
     ++npass;
     // combine the two half-lanes of a row
     float tot[5];
-    tot[0] = F0 + xor32f(F0);
-    tot[1] = F1 + xor32f(F1);
+    tot[0] = sums.F0 + xor32f(sums.F0);
+    tot[1] = sums.F1 + xor32f(sums.F1);
     if constexpr (MODE == 0) {
-      tot[2] = F2 + xor32f(F2);
+      tot[2] = sums.F2 + xor32f(sums.F2);
       tot[4] = INFINITY;
     } else {
-      tot[2] = (float)(cnt + xor32i(cnt));
-      const uint32_t mb = min(mrelb, (uint32_t)xor32i((int)mrelb));
+      tot[2] = (float)(sums.cnt + xor32i(sums.cnt));
+      const uint32_t mb = min(sums.mrelb, (uint32_t)xor32i((int)sums.mrelb));
       tot[4] = mb < 0x7F800000u ? __uint_as_float(mb) : INFINITY;
     }
-    tot[3] = Fh + xor32f(Fh);
-    if (!done) {
-      const float f = tot[0] - 1.0f;
-      const float t0 = tau;
-      if (f >= 0.f) lo = t0; else hi = t0;
-      bool fin_row = false;
-      // alpha in {1.5, 2}: the root of the equation restricted to the support {x > t0}
-      // is exact when it keeps that support (it lies at or above t0 and no further than
-      // the support's smallest gap): then stop without a confirming pass
-      if constexpr (MODE == 1 || MODE == 2) {
-        const float cntS = tot[2];
-        if (cntS > 0.f && f >= 0.f) {
-          float u;
-          if constexpr (MODE == 2) {
-            const float disc = tot[1] * tot[1] - cntS * f;
-            u = disc >= 0.f ? f / (tot[1] + sqrtf(disc)) : INFINITY;
-          } else {
-            u = f / cntS;
-          }
-          if (u <= tot[4]) {
-            tau = t0 + u;
-            fin_row = true;
-          }
-        }
-      }
-      if (fin_row) {
-        done = true;
-        rowpass = npass;
-      } else {
-        float tn;
-        if constexpr (MODE == 2) {
-          // Halley on f = sum d^2 - 1: f' = -2 sum d, f'' = 2 |support|
-          const float fp = -2.0f * tot[1];
-          const float fpp = 2.0f * tot[2];
-          tn = t0 - 2.0f * f * fp / (2.0f * fp * fp - f * fpp);
-        } else if constexpr (MODE == 1) {
-          tn = tot[2] > 0.f ? t0 + f / tot[2] : 0.5f * (lo + hi);   // Newton, f' = -|support|
-        } else {
-          const float fp = -kappa * tot[1];
-          if (alpha <= 1.5f) {
-            const float fpp = kappa * (kappa - 1.0f) * tot[2];
-            tn = t0 - 2.0f * f * fp / (2.0f * fp * fp - f * fpp);
-          } else if (alpha <= 2.0f) {
-            tn = t0 - f / fp;
-          } else {
-            if (first) {
-              const float th = t0 + thi;   // the bracket's upper end at the start of the pass
-              const float fh = tot[3] - 1.0f;
-              if (fh >= 0.f) lo = fmaxf(lo, th); else hi = fminf(hi, th);
-              tn = t0 - f * (th - t0) / (fh - f);
-            } else {
-              tn = t0 - f * (t0 - tprev) / (f - fprev);
-            }
-            tprev = t0;
-            fprev = f;
-          }
-        }
-        // converged when the solver's own step is below tolerance (tested before the
-        // bracket check: a vanishing step lands on a bracket end and must not be
-        // replaced by a bisection jump); otherwise keep the step inside (lo, hi)
-        const float tabs = p.tol * fmaxf(1.0f, fabsf(t0));
-        if (fabsf(tn - t0) <= tabs) {
-          done = true;
-          rowpass = npass;
-          tn = fminf(fmaxf(tn, lo), hi);
-        } else {
-          if (!(tn > lo && tn < hi)) tn = 0.5f * (lo + hi);
-          if (hi - lo <= tabs) {
-            done = true;
-            rowpass = npass;
-          }
-        }
-        tau = tn;
-      }
-    }
+    tot[3] = sums.Fh + xor32f(sums.Fh);
+    if (!st.done) st.update<MODE>(tot, npass, first, thi, kappa, alpha, p.tol);
   }
 
   // ---------------------------------------------------------------- output pass
@@ -729,7 +539,7 @@ __global__ __launch_bounds__(64 * OUT_WAVES, 2) void k_refine_out(FwdParams p) {
     {
       // rows by refinement passes (rows that hit the cap go to max_iters + 1)
       for (int ps = 1; ps <= p.max_iters + 1; ++ps) {
-        const int rp = done ? rowpass : p.max_iters + 1;
+        const int rp = st.done ? st.rowpass : p.max_iters + 1;
         const int cntp = __popcll(ballot(h == 0 && rp == ps));
         if (lane == 0 && cntp) atomicAdd(&p.stats[ps], (unsigned long long)cntp);
       }

@@ -100,7 +100,29 @@ struct BwdParams {
   WgMap map;
 };
 
+// decode (decode.hip): keys per work group of the score and output kernels
+constexpr int DEC_SPLIT = 2048;
+
+struct DecParams {
+  const void* q;         // [b, hq, D]
+  const void* k;         // [b, hkv, n, D] cache
+  const void* v;
+  const int32_t* lengths;  // optional [b]
+  const float* slopes;   // optional [hq]
+  float* o;              // [b, hq, D] fp32
+  float* tau;            // [b, hq]
+  int32_t* hist;         // optional [b, hq, B]
+  float* tau_h;          // optional [b, hq]
+  float* xs;             // workspace: scores [b, hq, n] fp32
+  float* smax;           // workspace: per-slice max [b, hq, nsplit]
+  float* opart;          // workspace: per-slice partial o [nsplit, b, hq, D]
+  int b, hq, hkv, G, n, B, max_iters, tau_init, nsplit;
+  int ldx;               // row stride of xs: n rounded up to a multiple of 4
+  float cx, am1, alpha, kappa, tol;
+};
+
 hipError_t launch_fwd(const FwdParams& p, int dtype, int D, int mode, hipStream_t s);
+hipError_t launch_decode(const DecParams& p, int dtype, int D, int mode, hipStream_t s);
 hipError_t launch_relayout(const Relayout& r, int dtype, int n, int D, hipStream_t s);
 hipError_t launch_mask_transpose(const uint32_t* mask, uint32_t* maskT, int planes, int Tr, int Tc, int W,
                                  int WT, hipStream_t s);

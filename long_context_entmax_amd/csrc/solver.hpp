@@ -1,0 +1,229 @@
+// The per-row threshold solver shared by the prefill and decode forwards (AdaSplash-2
+// pages, page 1 sections 2.1-2.2, page 3 sections 2.1-2.2): tau_h from the B-bin histogram
+// (Proposition 1: tau* - 1/B < tau_h <= tau*), then a safeguarded hybrid root solver on
+// f(tau) = sum_j [x_j - tau]_+^kappa - 1 -- Halley (alpha <= 1.5), Newton (1.5 < alpha <= 2),
+// secant started by false position (alpha > 2), bisection whenever a step leaves the
+// bracket. A pass over a row's scores accumulates PassSums; RowState::update takes the
+// row's totals and moves tau.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace entmax {
+
+// tau_h from merged counts c[0..B-1] (bin k has lower edge l_k = (T - B + 1 + k)/B).
+// Works relative to l_top = T/B with u_k = l_k - l_top = (k - B + 1)/B exactly.
+template <int MODE>
+__device__ float tau_from_counts(const int (&cnt)[16], int T, int B, float kappa) {
+  const float invB = 1.0f / (float)B;
+  const float ltop = (float)T * invB;
+  float v = -1.0f;
+  if constexpr (MODE == 1) {
+    // sum_k c_k (u_k - v)_+ = 1: scan bins from the top, v = (S1 - 1)/S0
+    float S0 = 0.f, S1 = 0.f;
+    bool found = false;
+#pragma unroll
+    for (int kk = 15; kk >= 0; --kk) {
+      if (kk < B && !found) {
+        const int k = kk;
+        const float u = (float)(k - B + 1) * invB;
+        S0 += (float)cnt[k];
+        S1 += (float)cnt[k] * u;
+        if (S0 > 0.f) {
+          const float vv = (S1 - 1.0f) / S0;
+          const float lower = (k > 0) ? u - invB : -INFINITY;
+          if (vv >= lower) {
+            v = vv;
+            found = true;
+          }
+        }
+      }
+    }
+  } else if constexpr (MODE == 2) {
+    // sum_k c_k (u_k - v)_+^2 = 1 on the top bins: v = mu - sqrt((1 - sum c (u - mu)^2)/S0)
+    float S0 = 0.f, S1 = 0.f, S2 = 0.f;
+    bool found = false;
+#pragma unroll
+    for (int kk = 15; kk >= 0; --kk) {
+      if (kk < B && !found) {
+        const int k = kk;
+        const float u = (float)(k - B + 1) * invB;
+        const float cf = (float)cnt[k];
+        S0 += cf;
+        S1 += cf * u;
+        S2 += cf * u * u;
+        if (S0 > 0.f) {
+          const float mu = S1 / S0;
+          const float ss = fmaxf(S2 - S1 * mu, 0.f);
+          const float vv = mu - sqrtf(fmaxf(1.0f - ss, 0.f) / S0);
+          const float lower = (k > 0) ? u - invB : -INFINITY;
+          if (vv >= lower) {
+            v = vv;
+            found = true;
+          }
+        }
+      }
+    }
+  } else {
+    // any kappa: bisection on [-1, 0]; keep the end where the B-bin mass is >= 1
+    float lo = -1.0f, hi = 0.0f;
+    for (int it = 0; it < 32; ++it) {
+      const float mid = 0.5f * (lo + hi);
+      float s = 0.f;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        if (k < B && cnt[k] > 0) {
+          const float t = (float)(k - B + 1) * invB - mid;
+          if (t > 0.f) s += (float)cnt[k] * exp2f(kappa * log2f(t));
+        }
+      }
+      if (s >= 1.0f) lo = mid; else hi = mid;
+    }
+    v = lo;
+  }
+  return ltop + v;
+}
+
+
+// Per-score sums of one pass at the evaluation point tau, fed with tt = x - tau:
+// F0 = sum d^kappa, F1 = sum d^(kappa-1), F2 = sum d^(kappa-2) (general alpha), cnt = |support|
+// and mrelb = bits of the smallest positive gap (alpha 1.5, 2; positive floats order like
+// their bits), Fh = sum (x - hi)_+^kappa on the first pass of the secant (thi = hi - tau).
+struct PassSums {
+  float F0 = 0.f, F1 = 0.f, F2 = 0.f, Fh = 0.f;
+  int cnt = 0;
+  uint32_t mrelb = 0xFFFFFFFFu;
+
+  template <int MODE>
+  __device__ __forceinline__ void add(float tt, float thi, bool sec_first, float kappa) {
+    if constexpr (MODE == 2) {
+      const float dm = fmaxf(tt, 0.f);
+      F0 = fmaf(dm, dm, F0);
+      F1 += dm;
+      cnt += (tt > 0.f) ? 1 : 0;
+      mrelb = min(mrelb, __float_as_uint(tt));
+    } else if constexpr (MODE == 1) {
+      F0 += fmaxf(tt, 0.f);
+      cnt += (tt > 0.f) ? 1 : 0;
+      mrelb = min(mrelb, __float_as_uint(tt));
+    } else {
+      const bool in = tt > 0.f;
+      const float lt = log2f(in ? tt : 1.0f);
+      F0 += in ? exp2f(kappa * lt) : 0.f;
+      F1 += in ? exp2f((kappa - 1.0f) * lt) : 0.f;
+      F2 += in ? exp2f((kappa - 2.0f) * lt) : 0.f;
+      if (sec_first) {
+        const float u = tt - thi;      // x - hi
+        Fh += u > 0.f ? exp2f(kappa * log2f(u)) : 0.f;
+      }
+    }
+  }
+};
+
+// Solver state of one row: bracket [lo, hi] holding tau*, the evaluation point tau, the
+// previous secant iterate, and whether (after how many passes) the row has converged.
+struct RowState {
+  float lo, hi, tau;
+  float tprev = 0.f, fprev = 0.f;
+  bool done = false;
+  int rowpass = 0;
+
+  // Bracket [tau_h, tau_h + 1/B] (with a margin of 1/(16B) below tau_h for fp32 rounding of
+  // the B-bin solve); the first evaluation is a quarter of the way into it. Starting above
+  // tau_h leaves out the sub-blocks whose scores all lie in the bottom quarter, and on the
+  // workloads' rows it also takes fewer passes than starting at tau_h.
+  __device__ __forceinline__ static RowState from_hist(float tau_h, int B) {
+    const float hB = 1.0f / (float)B;
+    RowState s;
+    s.lo = tau_h - 0.0625f * hB;
+    s.hi = tau_h + hB;
+    s.tau = tau_h + 0.25f * hB;
+    return s;
+  }
+  // the plain bracket [x_max - 1, x_max - n_valid^(1-alpha)], started at its lower end
+  __device__ __forceinline__ static RowState from_max(float xmax, float nvalid, float alpha) {
+    RowState s;
+    s.lo = xmax - 1.0f;
+    s.hi = xmax - exp2f((1.0f - alpha) * log2f(nvalid));
+    s.tau = s.lo;
+    return s;
+  }
+
+  // One solver step from a pass's row totals: tot[0] = F0, tot[1] = F1, tot[2] = |support|
+  // (alpha 1.5, 2) or F2, tot[3] = Fh, tot[4] = smallest positive gap (alpha 1.5, 2) or inf.
+  // npass counts the passes done, including this one; thi = hi - tau of the first pass.
+  template <int MODE>
+  __device__ __forceinline__ void update(const float (&tot)[5], int npass, bool first, float thi, float kappa,
+                                         float alpha, float tol) {
+    const float f = tot[0] - 1.0f;
+    const float t0 = tau;
+    if (f >= 0.f) lo = t0; else hi = t0;
+    // alpha in {1.5, 2}: the root of the equation restricted to the support {x > t0}
+    // is exact when it keeps that support (it lies at or above t0 and no further than
+    // the support's smallest gap): then stop without a confirming pass
+    if constexpr (MODE == 1 || MODE == 2) {
+      const float cntS = tot[2];
+      if (cntS > 0.f && f >= 0.f) {
+        float u;
+        if constexpr (MODE == 2) {
+          const float disc = tot[1] * tot[1] - cntS * f;
+          u = disc >= 0.f ? f / (tot[1] + sqrtf(disc)) : INFINITY;
+        } else {
+          u = f / cntS;
+        }
+        if (u <= tot[4]) {
+          tau = t0 + u;
+          done = true;
+          rowpass = npass;
+          return;
+        }
+      }
+    }
+    float tn;
+    if constexpr (MODE == 2) {
+      // Halley on f = sum d^2 - 1: f' = -2 sum d, f'' = 2 |support|
+      const float fp = -2.0f * tot[1];
+      const float fpp = 2.0f * tot[2];
+      tn = t0 - 2.0f * f * fp / (2.0f * fp * fp - f * fpp);
+    } else if constexpr (MODE == 1) {
+      tn = tot[2] > 0.f ? t0 + f / tot[2] : 0.5f * (lo + hi);   // Newton, f' = -|support|
+    } else {
+      const float fp = -kappa * tot[1];
+      if (alpha <= 1.5f) {
+        const float fpp = kappa * (kappa - 1.0f) * tot[2];
+        tn = t0 - 2.0f * f * fp / (2.0f * fp * fp - f * fpp);
+      } else if (alpha <= 2.0f) {
+        tn = t0 - f / fp;
+      } else {
+        if (first) {
+          const float th = t0 + thi;   // the bracket's upper end at the start of the pass
+          const float fh = tot[3] - 1.0f;
+          if (fh >= 0.f) lo = fmaxf(lo, th); else hi = fminf(hi, th);
+          tn = t0 - f * (th - t0) / (fh - f);
+        } else {
+          tn = t0 - f * (t0 - tprev) / (f - fprev);
+        }
+        tprev = t0;
+        fprev = f;
+      }
+    }
+    // converged when the solver's own step is below tolerance (tested before the
+    // bracket check: a vanishing step lands on a bracket end and must not be
+    // replaced by a bisection jump); otherwise keep the step inside (lo, hi)
+    const float tabs = tol * fmaxf(1.0f, fabsf(t0));
+    if (fabsf(tn - t0) <= tabs) {
+      done = true;
+      rowpass = npass;
+      tn = fminf(fmaxf(tn, lo), hi);
+    } else {
+      if (!(tn > lo && tn < hi)) tn = 0.5f * (lo + hi);
+      if (hi - lo <= tabs) {
+        done = true;
+        rowpass = npass;
+      }
+    }
+    tau = tn;
+  }
+};
+
+}  // namespace entmax

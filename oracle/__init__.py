@@ -308,3 +308,38 @@ def attn_full(q, k, v, dout, alpha: float, causal: bool, B: int, Br: int, Bc: in
                 res["dk"][bi, kh] = kk["dk"]
                 res["dv"][bi, kh] = kk["dv"]
     return res
+
+
+def attn_decode(q, k_cache, v_cache, lengths, alpha: float, B: int, scale: float | None = None,
+                slopes=None, heads=None, threads: int | None = None) -> dict:
+    """Decode step: query row q[b, h] against keys 0..lengths[b]-1 of its KV head's cache.
+
+    The new token follows the cache, so this is row L-1 of a causal forward over the first
+    L cached keys with the query placed there (the same per-row computation as
+    ``attn_fwd_head``). q: [b, hq, d]; caches [b, hkv, n_ctx, d]; lengths: [b] or None.
+    ``heads``: None for all (b, h) pairs, or a list of them. Returns o [b, hq, d], tau,
+    tau_h [b, hq], counts [b, hq, B] (pairs not computed stay 0).
+    """
+    q = _f64(q)
+    kc, vc = _f64(k_cache), _f64(v_cache)
+    b, hq, d = q.shape
+    hkv, n = kc.shape[1], kc.shape[2]
+    G = hq // hkv
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    sl = np.zeros(hq) if slopes is None else _f64(slopes).ravel()
+    lens = [n] * b if lengths is None else [min(max(int(x), 1), n) for x in lengths]
+    pairs = [(bi, h) for bi in range(b) for h in range(hq)] if heads is None else list(heads)
+    out = {"o": np.zeros((b, hq, d)), "tau": np.zeros((b, hq)), "tau_h": np.zeros((b, hq)),
+           "counts": np.zeros((b, hq, B), dtype=np.int32)}
+    for bi, h in pairs:
+        L = lens[bi]
+        qf = np.zeros((L, d))
+        qf[L - 1] = q[bi, h]
+        f = attn_fwd_head(qf, kc[bi, h // G, :L], vc[bi, h // G, :L], alpha, True, B, 32, scale,
+                          rows=[L - 1], threads=threads, slope=sl[h])
+        out["o"][bi, h] = f["o"][0]
+        out["tau"][bi, h] = f["tau"][0]
+        out["tau_h"][bi, h] = f["tau_h"][0]
+        out["counts"][bi, h] = f["counts"][0]
+    return out

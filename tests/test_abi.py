@@ -133,3 +133,27 @@ def test_binding_refuses_cpu_tensors():
     q = torch.zeros(1, 1, 64, 64)
     with pytest.raises(ValueError):
         lce.fwd(q, q, q)
+
+
+def test_decode_arguments(L):
+    """Decode: seqlen is a cache capacity (no block multiple), group size at most 16,
+    required pointers, alignment and workspace size."""
+    d = _desc(seqlen=1000, heads_q=4, heads_kv=2)
+    nb = L.entmax_attn_decode_workspace_bytes(ctypes.byref(d))
+    assert nb > 0
+    assert L.entmax_attn_fwd_workspace_bytes(ctypes.byref(d)) == 0     # not a forward shape
+    f = ctypes.c_void_p(4096)
+    mis = ctypes.c_void_p(4098)
+    dec = L.entmax_attn_decode
+    assert dec(ctypes.byref(d), None, f, f, None, None, f, f, None, None, f, nb, None) == 1
+    assert dec(ctypes.byref(d), f, f, f, None, None, None, f, None, None, f, nb, None) == 1
+    assert dec(ctypes.byref(d), f, mis, f, None, None, f, f, None, None, f, nb, None) == 5
+    assert dec(ctypes.byref(d), f, f, f, mis, None, f, f, None, None, f, nb, None) == 5
+    assert dec(ctypes.byref(d), f, f, f, None, None, f, f, None, None, f, nb - 1, None) == 6
+    big = _desc(seqlen=1000, heads_q=32, heads_kv=1)
+    assert L.entmax_attn_decode_workspace_bytes(ctypes.byref(big)) == 0
+    assert dec(ctypes.byref(big), f, f, f, None, None, f, f, None, None, f, 1 << 30, None) == 4
+    empty = _desc(seqlen=0)
+    assert dec(ctypes.byref(empty), f, f, f, None, None, f, f, None, None, f, 1 << 30, None) == 2
+    assert dec(ctypes.byref(_desc(batch=0)), None, None, None, None, None, None, None, None, None,
+               None, 0, None) == 0

@@ -524,3 +524,33 @@ def test_position_bias_gqa_heads_sum():
         np.testing.assert_allclose(res["dk"][0, kh], dk, atol=1e-12)
         np.testing.assert_allclose(res["dv"][0, kh], dv, atol=1e-12)
         np.testing.assert_allclose(res["dk"][0, kh].sum(0), 0.0, atol=1e-9)
+
+
+# ------------------------------------------------------------------------------------------------
+# decode (one new query row against a cache)
+# ------------------------------------------------------------------------------------------------
+
+def test_decode_single_key_and_hand_derived_row():
+    """A one-key cache gives tau = x_0 - 1 and o = v_0; with q = 0 and slope m = 0.05 the
+    decode row is the hand-derived causal sparsemax row (support: the 6 newest keys,
+    tau = -1.75/6; the key at distance t gets 0.29167 - 0.05 t)."""
+    rng = np.random.default_rng(5)
+    d = 8
+    q = rng.standard_normal((1, 2, d))
+    kc = rng.standard_normal((1, 1, 40, d))
+    vc = rng.standard_normal((1, 1, 40, d))
+    r = oracle.attn_decode(q, kc, vc, [1], 1.5, 16, scale=0.5)
+    for h in range(2):
+        x0 = 0.5 * 0.5 * (q[0, h] @ kc[0, 0, 0])
+        assert abs(r["tau"][0, h] - (x0 - 1.0)) < 1e-12
+        np.testing.assert_allclose(r["o"][0, h], vc[0, 0, 0], atol=1e-12)
+    n = 24
+    q0 = np.zeros((1, 1, n))
+    kc = np.ones((1, 1, n, n))
+    vc = np.eye(n)[None, None]
+    r = oracle.attn_decode(q0, kc, vc, [20], 2.0, 16, scale=1.0, slopes=[0.05])
+    assert abs(r["tau"][0, 0] - (-1.75 / 6)) < 1e-12
+    want = np.zeros(n)
+    for t in range(6):
+        want[19 - t] = 1.75 / 6 - 0.05 * t
+    np.testing.assert_allclose(r["o"][0, 0], want, atol=1e-12)

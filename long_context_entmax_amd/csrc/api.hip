@@ -354,19 +354,32 @@ entmax_status entmax_attn_bwd(const entmax_attn_desc* desc, const void* q, const
 }
 
 struct DecLayout {
-  size_t xs, smax, opart, total;
-  int nsplit, ldx;
+  size_t xs, smax, hcnt, opart, total;
+  int split, osplit, nsplit, nsplit_o, ldx;
 };
+
+// slice size: the largest power of two in [lo, hi] that still gives about 1024 work groups
+// over the (slice, KV head) grid, so short caches and few heads still fill the chip
+static int dec_slice(long long keys_all_heads, int lo, int hi) {
+  int s = hi;
+  while (s > lo && keys_all_heads / s < 1024) s >>= 1;
+  return s;
+}
 
 static DecLayout dec_ws(const Derived& o) {
   DecLayout L;
-  L.nsplit = (o.n + DEC_SPLIT - 1) / DEC_SPLIT;
+  const long long keys = (long long)o.n * o.b * o.hkv;
+  L.split = dec_slice(keys, 256, DEC_SPLIT_MAX);
+  L.osplit = dec_slice(keys, 128, 512);
+  L.nsplit = (o.n + L.split - 1) / L.split;
+  L.nsplit_o = (o.n + L.osplit - 1) / L.osplit;
   const size_t rows = (size_t)o.b * o.hq;
   L.xs = 0;
   L.ldx = (o.n + 3) & ~3;
   L.smax = align256(rows * L.ldx * sizeof(float));
-  L.opart = L.smax + align256(rows * L.nsplit * sizeof(float));
-  L.total = L.opart + align256((size_t)L.nsplit * rows * o.D * sizeof(float));
+  L.hcnt = L.smax + align256(rows * L.nsplit * sizeof(float));
+  L.opart = L.hcnt + align256(rows * L.nsplit * 16 * sizeof(int32_t));
+  L.total = L.opart + align256((size_t)L.nsplit_o * rows * o.D * sizeof(float));
   return L;
 }
 
@@ -399,9 +412,10 @@ entmax_status entmax_attn_decode(const entmax_attn_desc* desc, const void* q, co
   DecParams p{};
   p.q = q; p.k = k_cache; p.v = v_cache; p.lengths = lengths; p.slopes = slopes;
   p.o = o_; p.tau = tau; p.hist = hist_counts; p.tau_h = tau_h;
-  p.xs = (float*)(ws + L.xs); p.smax = (float*)(ws + L.smax); p.opart = (float*)(ws + L.opart);
+  p.xs = (float*)(ws + L.xs); p.smax = (float*)(ws + L.smax); p.hcnt = (int32_t*)(ws + L.hcnt); p.opart = (float*)(ws + L.opart);
   p.b = o.b; p.hq = o.hq; p.hkv = o.hkv; p.G = o.G; p.n = o.n; p.B = o.B;
-  p.max_iters = o.max_iters; p.tau_init = o.tau_init; p.nsplit = L.nsplit; p.ldx = L.ldx;
+  p.max_iters = o.max_iters; p.tau_init = o.tau_init; p.nsplit = L.nsplit; p.nsplit_o = L.nsplit_o;
+  p.split = L.split; p.osplit = L.osplit; p.ldx = L.ldx;
   p.cx = (float)(((double)o.alpha - 1.0) * (double)o.scale);
   p.am1 = o.alpha - 1.0f; p.alpha = o.alpha; p.kappa = o.kappa; p.tol = o.tol;
   const hipError_t e = launch_decode(p, o.dtype, o.D, o.mode, (hipStream_t)stream);

@@ -100,8 +100,8 @@ struct BwdParams {
   WgMap map;
 };
 
-// decode (decode.hip): keys per work group of the score and output kernels
-constexpr int DEC_SPLIT = 2048;
+// decode (decode.hip): the largest key slice of a score / histogram work group
+constexpr int DEC_SPLIT_MAX = 2048;
 
 struct DecParams {
   const void* q;         // [b, hq, D]
@@ -115,8 +115,10 @@ struct DecParams {
   float* tau_h;          // optional [b, hq]
   float* xs;             // workspace: scores [b, hq, n] fp32
   float* smax;           // workspace: per-slice max [b, hq, nsplit]
-  float* opart;          // workspace: per-slice partial o [nsplit, b, hq, D]
-  int b, hq, hkv, G, n, B, max_iters, tau_init, nsplit;
+  int32_t* hcnt;         // workspace: per-slice histogram counts [b, hq, nsplit, 16]
+  float* opart;          // workspace: per-output-slice partial o [nsplit_o, b, hq, D]
+  int b, hq, hkv, G, n, B, max_iters, tau_init, nsplit, nsplit_o;
+  int split, osplit;     // keys per slice of the score/histogram and of the output kernels
   int ldx;               // row stride of xs: n rounded up to a multiple of 4
   float cx, am1, alpha, kappa, tol;
 };

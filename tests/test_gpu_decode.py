@@ -57,6 +57,9 @@ DEC_CASES = [
     (1, 4, 1, 5000, 64, 3.0, 8, None, False, 1.0),
     (1, 16, 1, 2500, 64, 1.5, 4, [2049], True, 1.0),
     (2, 2, 1, 2048, 128, 1.5, 16, [2048, 2047], False, 0.8),
+    # nearly flat scores: most keys stay refinement candidates, more than a work group keeps
+    # on chip, so the passes rescan the stored row
+    (1, 2, 1, 30000, 64, 1.5, 16, None, False, 0.05),
 ]
 
 

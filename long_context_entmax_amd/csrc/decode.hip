@@ -7,9 +7,9 @@
 //
 // MI355X decomposition. One query row is too little work for a wave to stream a long cache
 // by itself, so the keys are split in slices (p.split keys), one work group per (slice, KV
-// head), and the score row itself is kept: at 4 bytes per key and query head it is 1/32 to
-// 1/64 of the K bytes it is computed from, so the histogram and every refinement pass read
-// the fp32 scores instead of recomputing them from K.
+// head), and the score row itself is kept: 4 bytes per key and query head against 2 d bytes
+// of bf16 K per key and KV head, so the histogram and every refinement pass read the fp32
+// scores instead of recomputing them from K.
 //   1. k_dec_scores  (slice, KV head): x for the G query heads of the KV head on MFMA (the
 //      G query rows padded to 32), stored, plus the slice's max per row.
 //   2. k_dec_hist    (slice, query row): the slice's counts on the row's anchored B-bin grid.

@@ -199,10 +199,11 @@ static BwdLayout bwd_ws(const Derived& o) {
 
 static bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
-static WgMap make_map(int U, int R) {
+static WgMap make_map(int U, int R, int fold = 0) {
   WgMap m;
   m.U = U;
   m.R = R;
+  m.fold = fold;
   m.xcd = (U > 0 && U % 8 == 0) ? 1 : 0;
   return m;
 }
@@ -281,7 +282,16 @@ entmax_status entmax_attn_fwd(const entmax_attn_desc* desc, const void* q, const
   p.alpha = o.alpha; p.kappa = o.kappa; p.tol = o.tol;
   p.GP = o.GP; p.RH = o.RH; p.RG = o.RG;
   p.nkb = o.nkb; p.NW32 = o.NW32; p.Tr = o.Tr; p.Tc = o.Tc; p.W = o.W;
+  // Causal rows differ in length. When the whole histogram grid is resident at once (two
+  // 8-wave groups per CU at head_dim 64 in bf16), pair long and short groups on a CU;
+  // otherwise longest first is the better order.
   p.map = make_map(o.b * o.hkv, (o.G / o.GP) * o.RG);
+  {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
+      p.map.fold = o.causal && o.D == 64 && o.dtype == ENTMAX_BF16 && wgmap_grid(p.map) <= 2 * cus;
+  }
   p.map2 = make_map(o.b * o.hkv, o.G * ((o.nkb + 3) / 4));
   e = launch_fwd(p, o.dtype, o.D, o.mode, s);
   if (e != hipSuccess) return hip_fail(e, "forward kernel");

@@ -12,6 +12,9 @@ struct WgMap {
   int U;      // units
   int R;      // ranks per unit
   int xcd;    // 1: XCD-grouped order (U % 8 == 0), 0: flat order
+  int fold;   // 1: the second half of the ranks in reverse (shortest first), so work groups
+              // dispatched half a grid apart -- which share a CU when two fit -- pair long
+              // with short items
 };
 
 __host__ __device__ inline int wgmap_grid(const WgMap& m) {
@@ -30,6 +33,10 @@ __device__ __forceinline__ bool wgmap_get(const WgMap& m, int bid, int& unit, in
     if (bid >= m.U * m.R) return false;
     unit = bid % m.U;
     rank = bid / m.U;
+  }
+  if (m.fold) {
+    const int h = (m.R + 1) >> 1;
+    if (rank >= h) rank = m.R - 1 - (rank - h);
   }
   return true;
 }

@@ -261,11 +261,13 @@ entmax_status entmax_attn_fwd(const entmax_attn_desc* desc, const void* q, const
   hipStream_t s = (hipStream_t)stream;
 
   char* wsb = (char*)workspace;
-  hipError_t e = launch_relayout(Relayout{k, wsb, nullptr, nullptr, nullptr, o.b * o.hkv, "frag_rows"}, o.dtype,
-                                 o.n, o.D, s);
-  if (e == hipSuccess)
-    e = launch_relayout(Relayout{v, nullptr, wsb + fwd_kv_bytes(o), nullptr, nullptr, o.b * o.hkv, "frag_cols"},
-                        o.dtype, o.n, o.D, s);
+  // fragment-major copies: K in the row layout, V in the column layout (one launch)
+  PrepBatch pb{};
+  pb.job[0] = Relayout{k, wsb, nullptr, nullptr, nullptr, o.b * o.hkv, "k"};
+  pb.job[1] = Relayout{v, nullptr, wsb + fwd_kv_bytes(o), nullptr, nullptr, o.b * o.hkv, "v"};
+  pb.njobs = 2;
+  pb.n = o.n;
+  hipError_t e = launch_prep(pb, o.dtype, o.D, "fwd_prep", s);
   if (e != hipSuccess) return hip_fail(e, "fragment-major copies of K and V");
 
   FwdParams p{};
@@ -321,19 +323,19 @@ entmax_status entmax_attn_bwd(const entmax_attn_desc* desc, const void* q, const
   char* ws = (char*)workspace;
 
   const int hq_all = o.b * o.hq, hkv_all = o.b * o.hkv;
-  hipError_t e = launch_relayout(Relayout{q, ws + L.qr, ws + L.qc, nullptr, nullptr, hq_all, "relayout_q"},
-                                 o.dtype, o.n, o.D, s);
-  if (e == hipSuccess)
-    e = launch_relayout(Relayout{dout, ws + L.dor, ws + L.doc, (const float*)aux, (float*)(ws + L.delta), hq_all,
-                                 "relayout_do_delta"}, o.dtype, o.n, o.D, s);
-  if (e == hipSuccess)
-    e = launch_relayout(Relayout{k, ws + L.kr, ws + L.kc, nullptr, nullptr, hkv_all, "relayout_k"}, o.dtype, o.n,
-                        o.D, s);
-  if (e == hipSuccess)
-    e = launch_relayout(Relayout{v, ws + L.vr, nullptr, nullptr, nullptr, hkv_all, "relayout_v"}, o.dtype, o.n,
-                        o.D, s);
-  if (e == hipSuccess)
-    e = launch_mask_transpose(block_mask, (uint32_t*)(ws + L.maskT), hq_all, o.Tr, o.Tc, o.W, o.WT, s);
+  // one launch: fragment-major copies of Q and dO (both layouts, with delta = dO . o~),
+  // K (both layouts) and V (row layout), and the transposed block mask
+  PrepBatch pb{};
+  pb.job[0] = Relayout{dout, ws + L.dor, ws + L.doc, (const float*)aux, (float*)(ws + L.delta), hq_all, "do"};
+  pb.job[1] = Relayout{q, ws + L.qr, ws + L.qc, nullptr, nullptr, hq_all, "q"};
+  pb.job[2] = Relayout{k, ws + L.kr, ws + L.kc, nullptr, nullptr, hkv_all, "k"};
+  pb.job[3] = Relayout{v, ws + L.vr, nullptr, nullptr, nullptr, hkv_all, "v"};
+  pb.njobs = 4;
+  pb.n = o.n;
+  pb.mask = block_mask;
+  pb.maskT = (uint32_t*)(ws + L.maskT);
+  pb.planes = hq_all; pb.Tr = o.Tr; pb.Tc = o.Tc; pb.W = o.W; pb.WT = o.WT;
+  hipError_t e = launch_prep(pb, o.dtype, o.D, "bwd_prep", s);
   if (e != hipSuccess) return hip_fail(e, "backward preparation");
 
   BwdParams p{};

@@ -83,6 +83,17 @@ struct Relayout {
   const char* name;      // timing label
 };
 
+// several re-layout jobs and an optional mask transpose in one launch (prep.hip)
+struct PrepBatch {
+  Relayout job[4];
+  int njobs;
+  int start[5];          // first work group of each job (filled by the launcher)
+  int n;                 // rows per head of every job
+  const uint32_t* mask;  // nullable: mask [planes, Tr, W] to transpose into maskT
+  uint32_t* maskT;
+  int planes, Tr, Tc, W, WT;
+};
+
 struct BwdParams {
   const void* qr;        // fragment-major copies (rows / cols layouts of prep.hip)
   const void* qc;
@@ -133,6 +144,7 @@ struct DecParams {
 hipError_t launch_fwd(const FwdParams& p, int dtype, int D, int mode, hipStream_t s);
 hipError_t launch_decode(const DecParams& p, int dtype, int D, int mode, hipStream_t s);
 hipError_t launch_relayout(const Relayout& r, int dtype, int n, int D, hipStream_t s);
+hipError_t launch_prep(const PrepBatch& b, int dtype, int D, const char* name, hipStream_t s);
 hipError_t launch_mask_transpose(const uint32_t* mask, uint32_t* maskT, int planes, int Tr, int Tc, int W,
                                  int WT, hipStream_t s);
 hipError_t launch_bwd_dkv(const BwdParams& p, int dtype, int D, int mode, hipStream_t s);

@@ -15,22 +15,29 @@
 //         and aux = o~ from the forward.
 // k_mask_transpose: block mask [P, Tr, W] -> column-major copy [P, Tc, WT] (bit I of the
 //   words of key block J), one 32x32 bit block per wave through 32 ballots.
+// k_prep runs several of these jobs in one launch (one range of work groups per job), so
+// the small copies before the backward do not each pay a launch and a drain.
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace entmax {
 
 template <typename T, int D>
-__global__ __launch_bounds__(256) void k_relayout(const T* __restrict__ src, T* __restrict__ rows,
-                                                  T* __restrict__ cols, const float* __restrict__ aux,
-                                                  float* __restrict__ delta, int n) {
+struct RelayoutTile {
+  static constexpr int PAD = 16 / (int)sizeof(T);   // keeps 16-byte alignment of LDS rows
+  static constexpr int LD = D + PAD;
+  static constexpr int LDS_ELEMS = 32 * LD;
+};
+
+// one 32-row tile (block blk of head hh) of a re-layout job; tile: LDS of LDS_ELEMS elements
+template <typename T, int D>
+__device__ __forceinline__ void relayout_tile(const T* __restrict__ src, T* __restrict__ rows,
+                                              T* __restrict__ cols, const float* __restrict__ aux,
+                                              float* __restrict__ delta, int n, int blk, size_t hh,
+                                              T* tile) {
   constexpr int DS = D / 16, DC = D / 32;
-  constexpr int PAD = 16 / (int)sizeof(T);       // keeps 16-byte alignment of LDS rows
-  constexpr int LD = D + PAD;
+  constexpr int LD = RelayoutTile<T, D>::LD;
   constexpr int VEC = 16 / (int)sizeof(T);       // elements per 16-byte vector
-  __shared__ __align__(16) T tile[32 * LD];
-  const size_t hh = blockIdx.y;
-  const int blk = blockIdx.x;                    // 32-row block
   const T* sp = src + (hh * n + (size_t)blk * 32) * D;
   for (int i = threadIdx.x; i < 32 * D / VEC; i += 256) {
     const int r = (i * VEC) / D, cc = (i * VEC) % D;
@@ -72,12 +79,19 @@ __global__ __launch_bounds__(256) void k_relayout(const T* __restrict__ src, T* 
   }
 }
 
+template <typename T, int D>
+__global__ __launch_bounds__(256) void k_relayout(const T* __restrict__ src, T* __restrict__ rows,
+                                                  T* __restrict__ cols, const float* __restrict__ aux,
+                                                  float* __restrict__ delta, int n) {
+  __shared__ __align__(16) T tile[RelayoutTile<T, D>::LDS_ELEMS];
+  relayout_tile<T, D>(src, rows, cols, aux, delta, n, blockIdx.x, blockIdx.y, tile);
+}
+
 // One wave per (plane, 32 query tiles, 32 key blocks): lane l < 32 holds the mask word of
 // tile I0 + l; ballot over bit b gives the column word of key block J0 + b.
-__global__ __launch_bounds__(256) void k_mask_transpose(const uint32_t* __restrict__ mask,
-                                                        uint32_t* __restrict__ maskT, int planes,
-                                                        int Tr, int Tc, int W, int WT) {
-  const long long wave = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+__device__ __forceinline__ void mask_transpose_wave(const uint32_t* __restrict__ mask,
+                                                    uint32_t* __restrict__ maskT, int planes, int Tr,
+                                                    int Tc, int W, int WT, long long wave) {
   const long long total = (long long)planes * W * WT;
   if (wave >= total) return;                        // whole wave
   const int lane = threadIdx.x & 63;
@@ -94,6 +108,32 @@ __global__ __launch_bounds__(256) void k_mask_transpose(const uint32_t* __restri
   }
   const int J = wj * 32 + lane;
   if (lane < 32 && J < Tc) maskT[((size_t)pl * Tc + J) * WT + wt] = mine;
+}
+
+__global__ __launch_bounds__(256) void k_mask_transpose(const uint32_t* __restrict__ mask,
+                                                        uint32_t* __restrict__ maskT, int planes,
+                                                        int Tr, int Tc, int W, int WT) {
+  mask_transpose_wave(mask, maskT, planes, Tr, Tc, W, WT, (long long)blockIdx.x * 4 + (threadIdx.x >> 6));
+}
+
+// Several re-layout jobs and an optional mask transpose in one launch: work groups
+// [start[j], start[j + 1]) run job j (one 32-row tile each), the rest the transpose (four
+// waves each).
+template <typename T, int D>
+__global__ __launch_bounds__(256) void k_prep(PrepBatch b) {
+  __shared__ __align__(16) T tile[RelayoutTile<T, D>::LDS_ELEMS];
+  const int bid = blockIdx.x;
+  for (int j = 0; j < b.njobs; ++j) {
+    if (bid < b.start[j + 1]) {
+      const Relayout& r = b.job[j];
+      const int local = bid - b.start[j], nb = b.n / 32;
+      relayout_tile<T, D>((const T*)r.src, (T*)r.rows, (T*)r.cols, r.aux, r.delta, b.n, local % nb,
+                          (size_t)(local / nb), tile);
+      return;
+    }
+  }
+  mask_transpose_wave(b.mask, b.maskT, b.planes, b.Tr, b.Tc, b.W, b.WT,
+                      (long long)(bid - b.start[b.njobs]) * 4 + (threadIdx.x >> 6));
 }
 
 template <typename T>
@@ -113,6 +153,27 @@ static hipError_t relayout_t(const Relayout& r, int n, int D, hipStream_t s) {
 
 hipError_t launch_relayout(const Relayout& r, int dtype, int n, int D, hipStream_t s) {
   return dtype == 1 ? relayout_t<__bf16>(r, n, D, s) : relayout_t<float>(r, n, D, s);
+}
+
+template <typename T>
+static hipError_t prep_t(PrepBatch b, int D, const char* name, hipStream_t s) {
+  int grid = 0;
+  for (int j = 0; j < b.njobs; ++j) {
+    b.start[j] = grid;
+    grid += b.job[j].heads * (b.n / 32);
+  }
+  b.start[b.njobs] = grid;
+  if (b.mask) grid += (int)(((long long)b.planes * b.W * b.WT + 3) / 4);
+  if (grid == 0) return hipSuccess;
+  prof_begin(name, s);
+  if (D == 64) hipLaunchKernelGGL((k_prep<T, 64>), dim3(grid), dim3(256), 0, s, b);
+  else hipLaunchKernelGGL((k_prep<T, 128>), dim3(grid), dim3(256), 0, s, b);
+  prof_end(s);
+  return hipGetLastError();
+}
+
+hipError_t launch_prep(const PrepBatch& b, int dtype, int D, const char* name, hipStream_t s) {
+  return dtype == 1 ? prep_t<__bf16>(b, D, name, s) : prep_t<float>(b, D, name, s);
 }
 
 hipError_t launch_mask_transpose(const uint32_t* mask, uint32_t* maskT, int planes, int Tr, int Tc, int W,

@@ -32,6 +32,7 @@
 // each pass subtracts from the scores (the histogram window base, or tau) enters the
 // score product as its initial accumulator.
 #include <cmath>
+#include <type_traits>
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -44,6 +45,7 @@ namespace entmax {
 #define HIST_OCC64 4
 #endif
 constexpr int HIST_WAVES = 8;
+constexpr int ALPHA2_POINTS = 4;   // evaluation points per refinement pass at alpha = 2
 constexpr int OUT_WAVES = 4;
 
 template <typename T, int D>
@@ -351,8 +353,10 @@ __global__ __launch_bounds__(64 * OUT_WAVES, 2) void k_refine_out(FwdParams p) {
   const float cx = p.cx;
   // solver state: the bracket from tau_h (or the plain bracket below the row max)
   const float nv = p.causal ? (float)(qrow + 1) : (float)n;
-  RowState st = p.tau_init == 0 ? RowState::from_hist(p.tauh_ws[bh * n + qrow], B)
-                                : RowState::from_max(p.tauh_ws[bh * n + qrow], nv, p.alpha);
+  // (alpha = 2: several evaluation points per pass, see MultiState)
+  using State = std::conditional_t<MODE == 1, MultiState<ALPHA2_POINTS>, RowState>;
+  State st = p.tau_init == 0 ? State::from_hist(p.tauh_ws[bh * n + qrow], B)
+                             : State::from_max(p.tauh_ws[bh * n + qrow], nv, p.alpha);
   float& tau = st.tau;
 
   // Walk over the sub-blocks a pass needs: candidate bits of the histogram pass, kept
@@ -414,6 +418,7 @@ __global__ __launch_bounds__(64 * OUT_WAVES, 2) void k_refine_out(FwdParams p) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) negt[r] = -tau;
     PassSums sums;
+    MultiSums<ALPHA2_POINTS> msums;
     const float thi = st.hi - st.tau;    // secant start: f at the bracket's upper end
     Walk wk{-1, 0u};
     int kb = walk_next(wk, thr);
@@ -426,25 +431,41 @@ __global__ __launch_bounds__(64 * OUT_WAVES, 2) void k_refine_out(FwdParams p) {
       if (kn >= 0) Ops::load_k(kf, Kf, kn, c, h);
       ++n_ref;
       const f32x16 t = tile(kc, kb);
+      if constexpr (MODE == 1) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sums.add<MODE>(t[r], thi, secant && first, kappa);
+        for (int r = 0; r < 16; ++r) msums.add(t[r], st.off);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sums.add<MODE>(t[r], thi, secant && first, kappa);
+      }
       kb = kn;
     }
     ++npass;
-    // combine the two half-lanes of a row
-    float tot[5];
-    tot[0] = sums.F0 + xor32f(sums.F0);
-    tot[1] = sums.F1 + xor32f(sums.F1);
-    if constexpr (MODE == 0) {
-      tot[2] = sums.F2 + xor32f(sums.F2);
-      tot[4] = INFINITY;
+    if constexpr (MODE == 1) {
+      float Ft[ALPHA2_POINTS];
+      int Nt[ALPHA2_POINTS];
+#pragma unroll
+      for (int k = 0; k < ALPHA2_POINTS; ++k) {
+        Ft[k] = msums.F[k] + xor32f(msums.F[k]);
+        Nt[k] = msums.N[k] + xor32i(msums.N[k]);
+      }
+      if (!st.done) st.update(Ft, Nt, npass, p.tol);
     } else {
-      tot[2] = (float)(sums.cnt + xor32i(sums.cnt));
-      const uint32_t mb = min(sums.mrelb, (uint32_t)xor32i((int)sums.mrelb));
-      tot[4] = mb < 0x7F800000u ? __uint_as_float(mb) : INFINITY;
+      // combine the two half-lanes of a row
+      float tot[5];
+      tot[0] = sums.F0 + xor32f(sums.F0);
+      tot[1] = sums.F1 + xor32f(sums.F1);
+      if constexpr (MODE == 0) {
+        tot[2] = sums.F2 + xor32f(sums.F2);
+        tot[4] = INFINITY;
+      } else {
+        tot[2] = (float)(sums.cnt + xor32i(sums.cnt));
+        const uint32_t mb = min(sums.mrelb, (uint32_t)xor32i((int)sums.mrelb));
+        tot[4] = mb < 0x7F800000u ? __uint_as_float(mb) : INFINITY;
+      }
+      tot[3] = sums.Fh + xor32f(sums.Fh);
+      if (!st.done) st.template update<MODE>(tot, npass, first, thi, kappa, alpha, p.tol);
     }
-    tot[3] = sums.Fh + xor32f(sums.Fh);
-    if (!st.done) st.update<MODE>(tot, npass, first, thi, kappa, alpha, p.tol);
   }
 
   // ---------------------------------------------------------------- output pass

@@ -226,4 +226,127 @@ struct RowState {
   }
 };
 
+
+// alpha = 2 in the forward's refinement: f(tau) = sum (x - tau)_+ - 1 is piecewise linear
+// and convex, and Newton from below (the pages' solver for 1.5 < alpha <= 2) shrinks the
+// error only about by half per pass when many scores sit just below the root. A pass costs
+// one sweep over the candidate keys whatever is evaluated on them, so each pass here
+// evaluates f and the support count at NP points at once: the Newton point from the best
+// lower end (at or below the root) and NP - 1 points between it and the chord root through
+// the bracket ends (at or above the root, by convexity). The bracket then shrinks to the
+// two points around the root, and the next Newton point starts from its lower end. The
+// root is exact when no score lies between the lower end and the next point above it and
+// the Newton step stays inside that gap (the support does not change on it).
+template <int NP>
+struct MultiState {
+  float lo, hi;          // bracket: f(lo) >= 0 > f(hi) (f at the initial ends may be unknown)
+  float flo = 0.f, fhi = 0.f;
+  int nlo = 0;           // support count at lo (0: f(lo) unknown)
+  bool fhi_known = false;
+  float tau;             // lowest evaluation point of the next pass; the root once done
+  float off[NP];         // evaluation points tau + off[k], off[0] = 0
+  bool done = false;
+  int rowpass = 0;
+
+  __device__ __forceinline__ void spread(float t0, float top) {
+    tau = t0;
+#pragma unroll
+    for (int k = 0; k < NP; ++k) off[k] = (top - t0) * (float)k / (float)NP;
+  }
+  // histogram start: bracket [tau_h - 1/(16B), tau_h + 1/B], first points close above tau_h
+  // (at alpha = 2 tau_h is within a few hundredths of a bin of the root on the workloads)
+  __device__ __forceinline__ static MultiState from_hist(float tau_h, int B) {
+    const float hB = 1.0f / (float)B;
+    MultiState s;
+    s.lo = tau_h - 0.0625f * hB;
+    s.hi = tau_h + hB;
+    s.tau = tau_h + 0.02f * hB;
+    const float first[4] = {0.0f, 0.03f, 0.08f, 0.23f};
+#pragma unroll
+    for (int k = 0; k < NP; ++k) s.off[k] = first[k < 4 ? k : 3] * hB;
+    return s;
+  }
+  __device__ __forceinline__ static MultiState from_max(float xmax, float nvalid, float alpha) {
+    MultiState s;
+    s.lo = xmax - 1.0f;
+    s.hi = xmax - exp2f((1.0f - alpha) * log2f(nvalid));
+    s.spread(s.lo, s.hi);
+    return s;
+  }
+
+  // F[k] = sum (x - tau - off[k])_+ and N[k] = support count at point k, over the row
+  __device__ __forceinline__ void update(const float (&F)[NP], const int (&N)[NP], int npass, float tol) {
+    int klo = -1;
+#pragma unroll
+    for (int k = 0; k < NP; ++k)
+      if (F[k] - 1.0f >= 0.0f) klo = k;          // f decreases: a prefix of the points
+    if (klo >= 0) {
+      lo = tau + off[klo];
+      flo = F[klo] - 1.0f;
+      nlo = N[klo];
+    }
+    int nnext = -1;
+    float tnext = hi;
+    if (klo + 1 < NP) {
+      tnext = tau + off[klo + 1];
+      hi = tnext;
+      fhi = F[klo + 1] - 1.0f;
+      fhi_known = true;
+      nnext = N[klo + 1];
+    }
+    const float tabs = tol * fmaxf(1.0f, fabsf(lo));
+    if (nlo > 0) {
+      const float u = flo / (float)nlo;
+      // exact: the support is the same at lo and at the next point, and the root lies before it
+      if (nnext == nlo && lo + u <= tnext) {
+        tau = lo + u;
+        done = true;
+        rowpass = npass;
+        return;
+      }
+      const float t0 = fminf(lo + u, hi);        // Newton from the lower end: at or below the root
+      float top = fhi_known ? lo + flo * (hi - lo) / (flo - fhi) : hi;   // chord: at or above
+      top = fminf(fmaxf(top, t0), hi);
+      if (top - t0 <= tabs || hi - lo <= tabs) {
+        tau = t0;
+        done = true;
+        rowpass = npass;
+        return;
+      }
+      spread(t0, top);
+    } else {
+      // no point with f >= 0 yet: the root lies in [lo, lowest point); spread over it
+      if (hi - lo <= tabs) {
+        tau = lo;
+        done = true;
+        rowpass = npass;
+        return;
+      }
+      spread(lo, hi);
+    }
+  }
+};
+
+template <int NP>
+struct MultiSums {
+  float F[NP];
+  int N[NP];
+  __device__ __forceinline__ MultiSums() {
+#pragma unroll
+    for (int k = 0; k < NP; ++k) {
+      F[k] = 0.f;
+      N[k] = 0;
+    }
+  }
+  // tt = x - tau (the lowest point)
+  __device__ __forceinline__ void add(float tt, const float (&off)[NP]) {
+#pragma unroll
+    for (int k = 0; k < NP; ++k) {
+      const float d = k == 0 ? tt : tt - off[k];
+      F[k] += fmaxf(d, 0.f);
+      N[k] += d > 0.f ? 1 : 0;
+    }
+  }
+};
+
 }  // namespace entmax

@@ -150,16 +150,18 @@ static entmax_status derive(const entmax_attn_desc* d, Derived& o, bool decode =
   o.nkb = o.n / 32;
   o.NW32 = (o.nkb + 31) / 32;
   o.es = o.dtype == ENTMAX_BF16 ? 2 : 4;
-  // forward work group: 8 waves x 32 rows over GP query heads of one KV head
+  // histogram work group: HW waves x 32 rows over GP query heads of one KV head (HW = 4 at
+  // head_dim 128 in bf16, else 8; the kernels check that they were built for the same shape)
   o.QW = 32;
+  const int HW = (o.D == 128 && d->dtype == ENTMAX_BF16) ? 4 : 8;
   o.GP = 1;
   for (int gp : {8, 4, 2}) {
-    if (o.G % gp == 0 && ((8 / gp) * o.QW) % o.Br == 0) {
+    if (gp <= HW && o.G % gp == 0 && ((HW / gp) * o.QW) % o.Br == 0) {
       o.GP = gp;
       break;
     }
   }
-  o.RH = (8 / o.GP) * o.QW;
+  o.RH = (HW / o.GP) * o.QW;
   o.RG = (o.n + o.RH - 1) / o.RH;
   return ENTMAX_OK;
 }

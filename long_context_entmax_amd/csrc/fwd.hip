@@ -44,7 +44,14 @@ namespace entmax {
 #ifndef HIST_OCC64
 #define HIST_OCC64 4
 #endif
-constexpr int HIST_WAVES = 8;
+// Waves per histogram work group and the waves per SIMD the register budget allows: eight
+// 32-row waves at head_dim 64 (four per SIMD in bf16, 128 registers); four at head_dim 128
+// in bf16, where a wave needs more than 128 registers, so that three groups (three waves per
+// SIMD) share a CU instead of one eight-wave group.
+template <typename T, int D>
+constexpr int hist_waves() { return (D == 128 && sizeof(T) == 2) ? 4 : 8; }
+template <typename T, int D>
+constexpr int hist_occ() { return (D == 64 && sizeof(T) == 2) ? HIST_OCC64 : (D == 128 && sizeof(T) == 2) ? 3 : 2; }
 constexpr int ALPHA2_POINTS = 4;   // evaluation points per refinement pass at alpha = 2
 constexpr int OUT_WAVES = 4;
 
@@ -78,7 +85,7 @@ struct KvOps {
 
 // ================================================================================ k_hist
 template <typename T, int D, int MODE, bool QS, bool BIAS>
-__global__ __launch_bounds__(512, ((D == 64 && sizeof(T) == 2) ? HIST_OCC64 : 2)) void k_hist(FwdParams p) {
+__global__ __launch_bounds__((64 * hist_waves<T, D>()), (hist_occ<T, D>())) void k_hist(FwdParams p) {
   using Ops = KvOps<T, D>;
   constexpr int DS = Ops::DS;
   extern __shared__ uint32_t lds[];
@@ -91,7 +98,8 @@ __global__ __launch_bounds__(512, ((D == 64 && sizeof(T) == 2) ? HIST_OCC64 : 2)
   const int bi = unit / p.hkv, kvh = unit % p.hkv;
   const int rg = p.causal ? (p.RG - 1 - rank / nsub) : (rank / nsub);
   const int gsub = rank % nsub;
-  const int per = HIST_WAVES / p.GP;           // waves per head
+  constexpr int HW = hist_waves<T, D>();
+  const int per = HW / p.GP;                   // waves per head
   const int head = kvh * p.G + gsub * p.GP + w / per;
   const int row0 = rg * p.RH + (w % per) * 32; // this wave's 32 rows
   const int n = p.n, B = p.B;                  // histogram window of B cells + 2 trash cells per lane
@@ -602,11 +610,13 @@ static void (*out_kernel(bool qs, bool bias, int mode))(FwdParams) {
                                                                      : k_refine_out<T, D, 0, false, false>;
 }
 
-size_t fwd_lds_bytes(int B) { return (size_t)(HIST_WAVES * (B + 2) * 64) * sizeof(uint32_t); }
+static size_t fwd_lds_bytes(int B, int waves) { return (size_t)(waves * (B + 2) * 64) * sizeof(uint32_t); }
 
 template <typename T, int D>
 static hipError_t launch_fwd_t(const FwdParams& p, int mode, hipStream_t s) {
-  const size_t lds = fwd_lds_bytes(p.B);
+  const size_t lds = fwd_lds_bytes(p.B, hist_waves<T, D>());
+  // the work decomposition (rows per head and work group) is sized for this group shape
+  if (p.RH != (hist_waves<T, D>() / p.GP) * 32) return hipErrorInvalidConfiguration;
   const int grid = wgmap_grid(p.map);
   const int grid2 = wgmap_grid(p.map2);
   if (grid == 0) return hipSuccess;
@@ -619,7 +629,7 @@ static hipError_t launch_fwd_t(const FwdParams& p, int mode, hipStream_t s) {
   hipError_t e = hipFuncSetAttribute((const void*)hist_fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   prof_begin("entmax_fwd_hist", s);
-  hipLaunchKernelGGL(hist_fn, dim3(grid), dim3(64 * HIST_WAVES), lds, s, p);
+  hipLaunchKernelGGL(hist_fn, dim3(grid), dim3(64 * hist_waves<T, D>()), lds, s, p);
   prof_end(s);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // (at head_dim 128 the extra accumulator block of the folded form would spill)

@@ -149,7 +149,9 @@ def tau_error_study(lce, w, q, k, v, blk, wsf):
     ref, tau_h = run(0, 15)
     out = {"study": "tau_mean_abs_error_per_pass", "workload": w.name, "alpha": w.alpha,
            "n_bins": w.n_bins, "rows": b * hq * n}
-    start = tau_h + 0.25 / w.n_bins
+    # the refinement's first evaluation point: a quarter bin above tau_h, at alpha = 2 the
+    # lowest of its four points (0.02 bin above tau_h)
+    start = tau_h + (0.02 if w.alpha == 2.0 else 0.25) / w.n_bins
     out["histogram"] = {"tau_h": (tau_h - ref).abs().mean().item(),
                         "start": (start - ref).abs().mean().item(), "passes": []}
     tb15, xm1 = run(1, 15)

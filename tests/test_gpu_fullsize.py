@@ -46,7 +46,7 @@ def _bits_of_tile(row_bits: np.ndarray) -> np.ndarray:
     return np.bitwise_or.reduce(row_bits, axis=0)
 
 
-def _run(cfg):
+def _run(cfg, slopes=None):
     w = synth.workload(cfg)
     d = dev()
     inp = synth.make_inputs(w, device=d)
@@ -58,9 +58,10 @@ def _run(cfg):
     fws, bws = lce.workspace_bytes(desc)
     wsf = torch.empty(max(fws, 256), dtype=torch.uint8, device=d)
     wsb = torch.empty(max(bws, 256), dtype=torch.uint8, device=d)
-    r = lce.fwd(q, k, v, w.alpha, w.causal, blk, w.n_bins, workspace=wsf, return_hist=True)
+    sl = None if slopes is None else torch.tensor(slopes, dtype=torch.float32, device=d)
+    r = lce.fwd(q, k, v, w.alpha, w.causal, blk, w.n_bins, workspace=wsf, return_hist=True, slopes=sl)
     dq, dk, dv = lce.bwd(q, k, v, do, r.tau, r.mask, r.aux, w.alpha, w.causal, blk, w.n_bins,
-                         workspace=wsb)
+                         workspace=wsb, slopes=sl)
     torch.cuda.synchronize()
     return w, inp, r, (dq, dk, dv)
 
@@ -216,3 +217,37 @@ def test_fullsize_gradient_sums(cfg):
               f"sum dV vs sum dO rel {err_v:.2e}", flush=True)
         assert err_k <= 2.0 ** -6
         assert err_v <= 1e-2
+
+
+@pytest.mark.parametrize("cfg", ["C3", "C4"])
+def test_fullsize_nape_sampled_tiles(cfg):
+    """NAPE heads at full size (half the heads ALiBi with nape_slopes): whole sampled query
+    tiles of an unbiased and a biased head against the oracle with the same slopes."""
+    w0 = synth.workload(cfg)
+    slopes = lce.nape_slopes(w0.heads_q)
+    w, inp, r, (dq, dk, dv) = _run(cfg, slopes)
+    rng = np.random.default_rng(77)
+    G = w.heads_q // w.heads_kv
+    scale = 1.0 / math.sqrt(w.head_dim)
+    Br, Bc, B = w.block_q, w.block_k, w.n_bins
+    bi = 0
+    for h in (0, w.heads_q - 1):
+        kh = h // G
+        q64 = to64(inp["q"][bi, h]); k64 = to64(inp["k"][bi, kh]); v64 = to64(inp["v"][bi, kh])
+        do64 = to64(inp["do"][bi, h])
+        tiles = _sample_tiles(w, rng)
+        rows = np.concatenate([np.arange(I * Br, (I + 1) * Br) for I in tiles])
+        ref = oracle.attn_fwd_head(q64, k64, v64, w.alpha, w.causal, B, Bc, scale, rows=rows,
+                                   slope=slopes[h])
+        rb = oracle.attn_bwd_rows_head(q64, k64, v64, do64, ref["tau"], w.alpha, w.causal, scale,
+                                       rows=ref["rows"], slope=slopes[h])
+        rows = ref["rows"]
+        dtau = np.abs(to64(r.tau[bi, h])[rows] - ref["tau"]).max()
+        do_ = np.abs(to64(r.o[bi, h])[rows] - ref["o"]).max()
+        rdq = rel_fro(to64(dq[bi, h])[rows], rb["dq"])
+        tau_h_g = to64(r.tau_h[bi, h])[rows]
+        print(f"[fullsize] {cfg} NAPE h{h} slope {slopes[h]:.4g} tiles {tiles}: max|dtau| {dtau:.2e} "
+              f"max|dO| {do_:.2e} dq rel {rdq:.2e}", flush=True)
+        assert np.all(tau_h_g <= ref["tau"] + 1e-4)
+        assert np.all(tau_h_g > ref["tau"] - 1.0 / B - 1e-4)
+        assert dtau <= TAU_TOL and do_ <= O_TOL and rdq <= G_TOL

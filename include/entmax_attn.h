@@ -86,7 +86,9 @@ typedef struct {
     float scale;          /* score scale; 0 means 1/sqrt(head_dim) */
     int32_t max_iters;    /* cap on refinement passes; 0 means 8 for alpha <= 1.5, 12 for
                              1.5 < alpha <= 2, 15 for alpha > 2; at most 15 */
-    float tol;            /* stop when |step| <= tol * max(1, |tau|); 0 means 2^-20 */
+    float tol;            /* alpha 1.5 and 2: stop when |step| <= tol * max(1, |tau|); 0 means
+                             2^-20. Other alpha stop when |sum p - 1| <= 1e-4 at the
+                             evaluated tau (tol unused there) */
     int32_t tau_init;     /* start of the refinement: 0 = the histogram bound tau_h and the
                              bracket [tau_h, tau_h + 1/B] (page 1 section 2.1-2.2, page 3
                              section 2.1-2.2); 1 = no histogram, the plain bracket

@@ -173,7 +173,7 @@ static size_t fwd_kv_bytes(const Derived& o) { return align256((size_t)o.b * o.h
 static size_t fwd_dmax_bytes(const Derived& o) { return align256((size_t)o.b * o.hq * (size_t)o.nkb * o.nkb * 4); }
 static size_t fwd_cand_bytes(const Derived& o) { return align256((size_t)o.b * o.hq * (size_t)o.nkb * o.NW32 * 4); }
 static size_t fwd_ws(const Derived& o) {
-  return 2 * fwd_kv_bytes(o) + fwd_dmax_bytes(o) + fwd_cand_bytes(o) + align256((size_t)o.b * o.hq * o.n * 4);
+  return 2 * fwd_kv_bytes(o) + fwd_dmax_bytes(o) + fwd_cand_bytes(o) + align256((size_t)o.b * o.hq * o.n * 8);
 }
 
 // backward workspace: delta, transposed mask, then fragment-major copies of Q and dO
@@ -277,7 +277,7 @@ entmax_status entmax_attn_fwd(const entmax_attn_desc* desc, const void* q, const
   p.hist = hist_counts; p.tau_h = tau_h; p.stats = (unsigned long long*)stats;
   p.dmax = (float*)(wsb + 2 * fwd_kv_bytes(o));
   p.cand = (uint32_t*)(wsb + 2 * fwd_kv_bytes(o) + fwd_dmax_bytes(o));
-  p.tauh_ws = (float*)(wsb + 2 * fwd_kv_bytes(o) + fwd_dmax_bytes(o) + fwd_cand_bytes(o));
+  p.tauh_ws = (float2*)(wsb + 2 * fwd_kv_bytes(o) + fwd_dmax_bytes(o) + fwd_cand_bytes(o));
   p.b = o.b; p.hq = o.hq; p.hkv = o.hkv; p.n = o.n; p.G = o.G;
   p.causal = o.causal; p.Br = o.Br; p.Bc = o.Bc; p.B = o.B; p.max_iters = o.max_iters;
   p.tau_init = o.tau_init;

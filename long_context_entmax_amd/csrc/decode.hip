@@ -243,7 +243,8 @@ __global__ __launch_bounds__(DEC_TAU_THREADS) void k_dec_tau(DecParams p) {
 #pragma unroll
     for (int k = 0; k < 16; ++k) cnt[k] = k < B ? cnt_tot[k] : 0;
     tau_h = tau_from_counts<MODE>(cnt, T, B, kappa);
-    st = RowState::from_hist(tau_h, B);
+    st = MODE == 0 ? RowState::from_hist_bounded(tau_h, B, m, (float)L, alpha)
+                   : RowState::from_hist(tau_h, B);
   } else {
 #pragma unroll
     for (int k = 0; k < 16; ++k) cnt[k] = 0;

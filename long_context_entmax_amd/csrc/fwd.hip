@@ -298,13 +298,13 @@ __global__ __launch_bounds__((64 * hist_waves<T, D>()), (hist_occ<T, D>())) void
     }
     cnt[k] = mine + xor32i(mine);
   }
-  // bracket mode: the refinement starts from the row max (x_max, handed over in place of
-  // tau_h); the test output tau_h is then its lower end x_max - 1 and the counts are 0
+  // the refinement gets tau_h and the row max; in bracket mode it starts from the row max
+  // alone, the test output tau_h is then its lower end x_max - 1 and the counts are 0
   const float xmax = fmaxf(mB, xor32f(mB)) / (float)B;
   const float tau_h = p.tau_init == 0 ? tau_from_counts<MODE>(cnt, Tf, B, p.kappa) : xmax - 1.0f;
   if (h == 0) {
     const size_t row = bh * n + qrow;
-    p.tauh_ws[row] = p.tau_init == 0 ? tau_h : xmax;
+    p.tauh_ws[row] = make_float2(tau_h, xmax);
     if (p.tau_h) p.tau_h[row] = tau_h;
     if (p.hist) {
       int32_t* dst = p.hist + row * B;
@@ -363,8 +363,11 @@ __global__ __launch_bounds__(64 * OUT_WAVES, 2) void k_refine_out(FwdParams p) {
   const float nv = p.causal ? (float)(qrow + 1) : (float)n;
   // (alpha = 2: several evaluation points per pass, see MultiState)
   using State = std::conditional_t<MODE == 1, MultiState<ALPHA2_POINTS>, RowState>;
-  State st = p.tau_init == 0 ? State::from_hist(p.tauh_ws[bh * n + qrow], B)
-                             : State::from_max(p.tauh_ws[bh * n + qrow], nv, p.alpha);
+  const float2 hm = p.tauh_ws[bh * n + qrow];   // (tau_h, x_max)
+  State st;
+  if (p.tau_init != 0) st = State::from_max(hm.y, nv, p.alpha);
+  else if constexpr (MODE == 0) st = State::from_hist_bounded(hm.x, B, hm.y, nv, p.alpha);
+  else st = State::from_hist(hm.x, B);
   float& tau = st.tau;
 
   // Walk over the sub-blocks a pass needs: candidate bits of the histogram pass, kept

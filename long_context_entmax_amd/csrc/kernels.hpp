@@ -55,7 +55,7 @@ struct FwdParams {
   unsigned long long* stats;  // optional [32]
   float* dmax;           // workspace: per (32-row chunk, 32-key sub-block) max of x*B
   uint32_t* cand;        // workspace: candidate sub-block bits per 32-row chunk [b*hq][n/32][NW32]
-  float* tauh_ws;        // workspace: tau_h per row [b*hq*n]
+  float2* tauh_ws;       // workspace: (tau_h, x_max) per row [b*hq*n]
   int b, hq, hkv, n, G;
   int causal, Br, Bc, B, max_iters;
   float cx;              // (alpha - 1) * scale

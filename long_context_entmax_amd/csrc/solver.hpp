@@ -120,6 +120,11 @@ struct PassSums {
   }
 };
 
+// General alpha has no exact-support test: a row stops once |sum p - 1| <= FTOL0 at the
+// evaluated tau. Where f is steep (alpha > 2 with a wide support of small weights, such as
+// all scores equal), a step that is small in tau can still leave sum p well away from 1.
+constexpr float FTOL0 = 1e-4f;
+
 // Solver state of one row: bracket [lo, hi] holding tau*, the evaluation point tau, the
 // previous secant iterate, and whether (after how many passes) the row has converged.
 struct RowState {
@@ -140,7 +145,22 @@ struct RowState {
     s.tau = tau_h + 0.25f * hB;
     return s;
   }
+  // General alpha: the histogram bracket narrowed by the plain bounds below (which hold
+  // for any row), started a quarter of the way into it. With many nearly equal scores at
+  // alpha > 2 the root lies within a tiny fraction of 1/B below x_max and f is steep
+  // there; the upper bound then sits at (all scores equal: exactly on) the root, while
+  // tau_h + 1/B would leave the first evaluations above every score, where f = -1 carries
+  // no slope for the secant.
+  __device__ __forceinline__ static RowState from_hist_bounded(float tau_h, int B, float xmax, float nvalid,
+                                                               float alpha) {
+    RowState s = from_hist(tau_h, B);
+    s.hi = fminf(s.hi, xmax - exp2f((1.0f - alpha) * log2f(nvalid)));
+    s.lo = fminf(fmaxf(s.lo, xmax - 1.0f), s.hi);
+    s.tau = fminf(fmaxf(tau_h + 0.25f * (s.hi - tau_h), s.lo), s.hi);
+    return s;
+  }
   // the plain bracket [x_max - 1, x_max - n_valid^(1-alpha)], started at its lower end
+  // (upper end: at that tau each of the n_valid weights is at most 1/n_valid)
   __device__ __forceinline__ static RowState from_max(float xmax, float nvalid, float alpha) {
     RowState s;
     s.lo = xmax - 1.0f;
@@ -158,6 +178,13 @@ struct RowState {
     const float f = tot[0] - 1.0f;
     const float t0 = tau;
     if (f >= 0.f) lo = t0; else hi = t0;
+    if constexpr (MODE == 0) {
+      if (fabsf(f) <= FTOL0) {        // tau stays at the evaluated point
+        done = true;
+        rowpass = npass;
+        return;
+      }
+    }
     // alpha in {1.5, 2}: the root of the equation restricted to the support {x > t0}
     // is exact when it keeps that support (it lies at or above t0 and no further than
     // the support's smallest gap): then stop without a confirming pass
@@ -198,6 +225,12 @@ struct RowState {
         if (first) {
           const float th = t0 + thi;   // the bracket's upper end at the start of the pass
           const float fh = tot[3] - 1.0f;
+          if (fabsf(fh) <= FTOL0) {    // the upper end already meets the test
+            tau = th;
+            done = true;
+            rowpass = npass;
+            return;
+          }
           if (fh >= 0.f) lo = fmaxf(lo, th); else hi = fminf(hi, th);
           tn = t0 - f * (th - t0) / (fh - f);
         } else {
@@ -206,6 +239,17 @@ struct RowState {
         tprev = t0;
         fprev = f;
       }
+    }
+    if constexpr (MODE == 0) {
+      // no exact test at general alpha: besides |f| <= FTOL0 above, a row ends only when
+      // fp32 can no longer move tau (a stalled step, or a bracket one ulp wide)
+      if (!(tn > lo && tn < hi)) tn = 0.5f * (lo + hi);
+      if (tn == t0 || tn <= lo || tn >= hi) {
+        done = true;
+        rowpass = npass;
+      }
+      tau = tn;
+      return;
     }
     // converged when the solver's own step is below tolerance (tested before the
     // bracket check: a vanishing step lands on a bracket end and must not be

@@ -126,3 +126,13 @@ def test_decode_fullsize_sampled_heads():
     ref = oracle.attn_decode(to64(q), to64(inp["k"]), to64(inp["v"]), None, w.alpha, w.n_bins)
     g = _run(q, inp["k"], inp["v"], [n], w.alpha, w.n_bins)
     _check(g, ref, w.n_bins)
+
+
+def test_decode_max_cache():
+    """A cache of the largest supported length, 2^19 keys, and a ragged shorter one."""
+    b, hq, hkv, n, d = 2, 2, 1, 1 << 19, 64
+    print("[case] decode max cache", flush=True)
+    q, k, v, lens = _inputs(b, hq, hkv, n, d, "bf16", "normal", [n, 300001], 31)
+    ref = oracle.attn_decode(to64(q), to64(k), to64(v), lens, 1.5, 16)
+    g = _run(q, k, v, lens, 1.5, 16)
+    _check(g, ref, 16)

@@ -14,6 +14,7 @@ import torch
 
 import oracle
 import synth
+import long_context_entmax_amd as lce
 from tests.gpu_helpers import (mask_bits, mask_mismatch_is_ambiguous, rel_fro, run_gpu, scores_x,
                                to64)
 
@@ -210,3 +211,50 @@ def test_determinism():
     b = run_gpu(inp, w)
     for kk in ("o", "tau", "mask", "aux", "hist", "tau_h", "dq", "dk", "dv"):
         assert torch.equal(a[kk], b[kk]), kk
+
+
+@pytest.mark.parametrize("alpha", [1.5, 2.0, 3.0])
+@pytest.mark.parametrize("causal", [True, False])
+def test_all_equal_scores(alpha, causal):
+    """q = 0 makes every score equal (every key in one histogram bin, every key in the
+    support): p_ij = 1/n_i, so tau_i = -n_i^(1-alpha) and o_i is the mean of the valid v_j,
+    with n_i = i + 1 under the causal mask and n otherwise."""
+    w = synth.Workload("t", 1, 2, 1, 256, 64, "bf16", alpha, causal, 64, 64, 16, "normal", seed=13)
+    print(f"[case] all-equal scores alpha {alpha} causal {causal}", flush=True)
+    inp = synth.make_inputs(w)
+    inp["q"] = torch.zeros_like(inp["q"])
+    g = run_gpu(inp, w)
+    n = w.seqlen
+    ni = np.arange(1, n + 1, dtype=np.float64) if causal else np.full(n, float(n))
+    tau_want = -ni ** (1.0 - alpha)
+    v = to64(inp["v"])[0, 0]
+    o_want = np.cumsum(v, axis=0) / ni[:, None] if causal else np.broadcast_to(v.mean(0), v.shape)
+    for h in range(2):
+        assert np.abs(g["tau"][0, h].numpy() - tau_want).max() < 1e-5
+        assert np.abs(g["o"][0, h].numpy() - o_want).max() < 1e-2
+    ref = _oracle(inp, w)
+    for name in ("dq", "dk", "dv"):
+        err = rel_fro(g[name].float().numpy().astype(np.float64), ref[name])
+        assert err < 2e-2, (name, err)
+
+
+def test_max_seqlen():
+    """The longest supported sequence, 2^19 tokens (one head): the first and last query tiles
+    against the oracle, and Proposition 1 on them."""
+    n = 1 << 19
+    w = synth.Workload("t", 1, 1, 1, n, 64, "bf16", 1.5, True, 64, 64, 16, "normal",
+                       extra={"qk_scale": 1.0}, seed=19)
+    print(f"[case] max seqlen {n}", flush=True)
+    inp = synth.make_inputs(w, need_grad_inputs=False)
+    d = torch.device("cuda:0")
+    r = lce.fwd(inp["q"].to(d), inp["k"].to(d), inp["v"].to(d), w.alpha, True, (64, 64), 16,
+                return_hist=True)
+    torch.cuda.synchronize()
+    q64, k64, v64 = to64(inp["q"][0, 0]), to64(inp["k"][0, 0]), to64(inp["v"][0, 0])
+    rows = np.concatenate([np.arange(0, 64), np.arange(n - 64, n)])
+    ref = oracle.attn_fwd_head(q64, k64, v64, w.alpha, True, 16, 64, 1.0 / math.sqrt(64), rows=rows)
+    tau = to64(r.tau[0, 0])[rows]
+    assert np.abs(tau - ref["tau"]).max() < 1e-3
+    assert np.abs(to64(r.o[0, 0])[rows] - ref["o"]).max() < 1e-2
+    th = to64(r.tau_h[0, 0])[rows]
+    assert np.all(th <= ref["tau"] + 1e-4) and np.all(th > ref["tau"] - 1.0 / 16 - 1e-4)

@@ -18,6 +18,7 @@ from scipy.optimize import brentq
 from scipy.special import softmax
 
 import oracle
+import oracle.dash
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -554,3 +555,113 @@ def test_decode_single_key_and_hand_derived_row():
     for t in range(6):
         want[19 - t] = 1.75 / 6 - 0.05 * t
     np.testing.assert_allclose(r["o"][0, 0], want, atol=1e-12)
+
+
+# ------------------------------------------------------------------------------------------------
+# DashAttention stages 1-2 (page 4, stages 1 and 2)
+# ------------------------------------------------------------------------------------------------
+
+def _dash_inputs(b, hq, hkv, n, d, nc, seed, ks_zero):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((b, hq, n, d))
+    k = rng.standard_normal((b, hkv, n, d))
+    v = rng.standard_normal((b, hkv, n, d))
+    ks = np.zeros((b, hkv, nc, d)) if ks_zero else rng.standard_normal((b, hkv, nc, d))
+    return q, k, v, ks
+
+
+@pytest.mark.parametrize("sigma", [0.0, 1.0, 2.5])
+def test_dash_uniform_routing_is_biased_causal_softmax(sigma):
+    """All summaries equal (zero): every routing row is uniform over its m_i earlier chunks
+    (wbar = 1/m_i, so every earlier chunk is routed) and stage 2 is causal softmax attention
+    with -sigma ln m_i added on the earlier chunks -- checked against torch's
+    scaled_dot_product_attention in fp64 with that additive mask."""
+    import torch
+    b, hq, hkv, n, d, C = 1, 4, 2, 96, 16, 8
+    q, k, v, ks = _dash_inputs(b, hq, hkv, n, d, n // C, 3, True)
+    r = oracle.dash.dash_fwd(q, k, v, ks, 1.5, 1.0, sigma, C)
+    i = np.arange(n)
+    m = i // C
+    for row in range(n):
+        want = np.zeros(n // C)
+        want[:m[row]] = 1.0 / max(m[row], 1) if m[row] else 0.0
+        np.testing.assert_allclose(r["wbar"][0, :, row], np.broadcast_to(want, (hkv, n // C)), atol=1e-12)
+    bias = np.full((n, n), -np.inf)
+    for row in range(n):
+        bias[row, :m[row] * C] = -sigma * np.log(max(m[row], 1))
+        bias[row, m[row] * C:row + 1] = 0.0
+    G = hq // hkv
+    kk = torch.from_numpy(np.repeat(k, G, axis=1))
+    vv = torch.from_numpy(np.repeat(v, G, axis=1))
+    o = torch.nn.functional.scaled_dot_product_attention(torch.from_numpy(q), kk, vv,
+                                                         attn_mask=torch.from_numpy(bias))
+    np.testing.assert_allclose(r["o"], o.numpy(), atol=1e-12)
+    # lse: the log of the softmax denominator, from the same additive mask
+    s = np.einsum("bhid,bhjd->bhij", q, np.repeat(k, G, axis=1)) / math.sqrt(d) + bias
+    np.testing.assert_allclose(r["lse"], np.log(np.exp(s).sum(-1)), atol=1e-12)
+
+
+def test_dash_sigma0_all_routed_is_causal_softmax():
+    """sigma = 0 with every earlier chunk routed: plain causal softmax attention."""
+    import torch
+    b, hq, hkv, n, d, C = 2, 2, 1, 64, 8, 16
+    q, k, v, ks = _dash_inputs(b, hq, hkv, n, d, n // C, 4, True)
+    r = oracle.dash.dash_fwd(q, k, v, ks, 2.0, 1.0, 0.0, C)
+    o = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(np.repeat(k, 2, axis=1)),
+        torch.from_numpy(np.repeat(v, 2, axis=1)), is_causal=True)
+    np.testing.assert_allclose(r["o"], o.numpy(), atol=1e-12)
+
+
+def test_dash_hand_derived_sparsemax_routing():
+    """alpha = 2 routing of row 3 with C = 1 against summaries whose logits are (1.5, 1, -5)
+    for head 0 and (-5, 1, 1.5) for head 1: by hand, sparsemax gives (0.75, 0.25, 0) and
+    (0, 0.25, 0.75) with tau 0.75; the group average is (0.375, 0.25, 0.375), its support
+    the union of the two."""
+    d = 2
+    q = np.zeros((2, 4, d))
+    q[0, 3] = [1.0, 0.0]
+    q[1, 3] = [0.0, 1.0]
+    ks = np.array([[1.5, -5.0], [1.0, 1.0], [-5.0, 1.5], [0.0, 0.0]])
+    r = oracle.dash.route_group(q, ks, 2.0, 1.0, 1.0, 1, [3])
+    np.testing.assert_allclose(r["what"][0, 0, :3], [0.75, 0.25, 0.0], atol=1e-12)
+    np.testing.assert_allclose(r["what"][1, 0, :3], [0.0, 0.25, 0.75], atol=1e-12)
+    np.testing.assert_allclose(r["tau"][:, 0], [0.75, 0.75], atol=1e-12)
+    np.testing.assert_allclose(r["wbar"][0, :3], [0.375, 0.25, 0.375], atol=1e-12)
+    # gamma scales the logits: gamma = 2 doubles them, sparsemax of (3, 2, -10) is (1, 0, 0)
+    r2 = oracle.dash.route_group(q, ks, 2.0, 2.0, 1.0, 1, [3])
+    np.testing.assert_allclose(r2["what"][0, 0, :3], [1.0, 0.0, 0.0], atol=1e-12)
+
+
+def test_dash_routing_invariants_and_mask_brute_force():
+    """Random summaries at alpha 1.5: each head's routing row sums to 1 over its m_i chunks,
+    wbar is their mean (support = union), the first chunk's rows route nothing; the chunk
+    mask equals a brute-force OR over each 64-row tile; stage 2 attends the diagonal keys
+    plus C keys per routed chunk, and its weights sum to 1 (o of v = 1 is 1)."""
+    b, hq, hkv, n, d, C = 1, 4, 2, 256, 16, 16
+    q, k, v, ks = _dash_inputs(b, hq, hkv, n, d, n // C, 5, False)
+    q *= 3.0
+    r = oracle.dash.dash_fwd(q, k, v, ks, 1.5, 1.0, 1.0, C)
+    G = hq // hkv
+    for g in range(hkv):
+        rt = oracle.dash.route_group(q[0, g * G:(g + 1) * G], ks[0, g], 1.5, 1.0, 1.0 / math.sqrt(d), C,
+                                     np.arange(n))
+        m = np.arange(n) // C
+        sums = rt["what"].sum(-1)
+        np.testing.assert_allclose(sums[:, m > 0], 1.0, atol=1e-12)
+        assert np.all(sums[:, m == 0] == 0.0)
+        np.testing.assert_array_equal(rt["wbar"] > 0, (rt["what"] > 0).any(0))
+        assert np.all(rt["wbar"][np.arange(n)[:, None] // C <= np.arange(n // C)[None, :]] == 0.0)
+        assert (rt["wbar"][m > 2] == 0).any(), "test construction: routing should be sparse"
+        # brute-force tile mask
+        want = np.zeros_like(r["mask"][0, g])
+        for i in range(n):
+            for c in range(n // C):
+                if rt["wbar"][i, c] > 0:
+                    want[i // 64, c // 32] |= 1 << (c % 32)
+        np.testing.assert_array_equal(r["mask"][0, g], want)
+        nk = (np.arange(n) % C + 1) + C * (rt["wbar"] > 0).sum(-1)
+        np.testing.assert_array_equal(r["nkeys"][0, g], nk)
+    ones = np.ones_like(v)
+    r1 = oracle.dash.dash_fwd(q, k, ones, ks, 1.5, 1.0, 1.0, C)
+    np.testing.assert_allclose(r1["o"], 1.0, atol=1e-12)

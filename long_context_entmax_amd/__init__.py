@@ -45,6 +45,16 @@ class Desc(ctypes.Structure):
     ]
 
 
+class DashDesc(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("heads_q", ctypes.c_int32), ("heads_kv", ctypes.c_int32),
+        ("seqlen", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32),
+        ("chunk", ctypes.c_int32), ("route_alpha", ctypes.c_float), ("gamma", ctypes.c_float),
+        ("sigma", ctypes.c_float), ("scale", ctypes.c_float), ("max_iters", ctypes.c_int32),
+        ("tol", ctypes.c_float),
+    ]
+
+
 class KernelTime(ctypes.Structure):
     _fields_ = [("name", ctypes.c_char * 32), ("total_ms", ctypes.c_double), ("launches", ctypes.c_int64)]
 
@@ -53,11 +63,13 @@ _lib = None
 _vp = ctypes.c_void_p
 _sz = ctypes.c_size_t
 _DP = ctypes.POINTER(Desc)
+_DDP = ctypes.POINTER(DashDesc)
 
 EXPORTS = [
     "entmax_attn_fwd_workspace_bytes", "entmax_attn_bwd_workspace_bytes", "entmax_attn_aux_bytes",
     "entmax_attn_mask_words", "entmax_attn_fwd", "entmax_attn_bwd", "entmax_attn_decode_workspace_bytes",
-    "entmax_attn_decode", "entmax_status_string",
+    "entmax_attn_decode", "entmax_dash_fwd_workspace_bytes", "entmax_dash_mask_words", "entmax_dash_fwd",
+    "entmax_status_string",
     "entmax_last_error", "entmax_attn_profile", "entmax_attn_profile_read",
 ]
 
@@ -82,6 +94,11 @@ def lib() -> ctypes.CDLL:
         L.entmax_attn_decode_workspace_bytes.argtypes = [_DP]
         L.entmax_attn_decode.restype = ctypes.c_int
         L.entmax_attn_decode.argtypes = [_DP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+        for f in ("entmax_dash_fwd_workspace_bytes", "entmax_dash_mask_words"):
+            getattr(L, f).restype = _sz
+            getattr(L, f).argtypes = [_DDP]
+        L.entmax_dash_fwd.restype = ctypes.c_int
+        L.entmax_dash_fwd.argtypes = [_DDP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
         L.entmax_status_string.restype = ctypes.c_char_p
         L.entmax_status_string.argtypes = [ctypes.c_int]
         L.entmax_last_error.restype = ctypes.c_char_p
@@ -273,6 +290,53 @@ def decode(q, k_cache, v_cache, alpha: float = 1.5, bins: int = 16, scale: Optio
                                 _ptr(slopes), _ptr(o), _ptr(tau), _ptr(hist), _ptr(tau_h), _ptr(workspace),
                                 workspace.numel(), _stream(dev)))
     return DecodeOut(o, tau, hist, tau_h)
+
+
+DashOut = namedtuple("DashOut", "o lse route_tau route_w chunk_mask")
+
+
+def make_dash_desc(batch: int, heads_q: int, heads_kv: int, seqlen: int, head_dim: int, dtype: int,
+                   chunk: int, route_alpha: float, gamma: float = 1.0, sigma: float = 1.0,
+                   scale: Optional[float] = None, max_iters: int = 0, tol: float = 0.0) -> DashDesc:
+    return DashDesc(batch, heads_q, heads_kv, seqlen, head_dim, dtype, int(chunk), float(route_alpha),
+                    float(gamma), float(sigma), float(scale or 0.0), int(max_iters), float(tol))
+
+
+def dash_fwd(q, k, v, k_summary, chunk: int = 64, route_alpha: float = 1.5, gamma: float = 1.0,
+             sigma: float = 1.0, scale: Optional[float] = None, max_iters: int = 0, tol: float = 0.0,
+             workspace=None) -> DashOut:
+    """DashAttention forward, stages 1-2 (include/dash_attn.h): alpha-entmax routing of each
+    query over the chunk summaries k_summary [b, hkv, n / chunk, d] (averaged over the query
+    heads of a KV group), then softmax over the routed chunks plus the query's own chunk with
+    sigma * ln(routing weight) added to the scores. Returns o [b, hq, n, d] (float32), lse and
+    route_tau [b, hq, n], route_w [b, hkv, n / chunk, n] (chunk-major group weights) and
+    chunk_mask [b, hkv, n / 64, ceil(n_chunks / 32)] (int32 view of the uint32 words)."""
+    torch = _torch()
+    _require_gpu(q, k, v, k_summary)
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape or k_summary.dim() != 4:
+        raise ValueError("q [b, hq, n, d], k and v [b, hkv, n, d], k_summary [b, hkv, n_chunks, d]")
+    b, hq, n, d = q.shape
+    if (k.shape[0] != b or k.shape[2] != n or k.shape[3] != d or k_summary.shape[:2] != k.shape[:2]
+            or k_summary.shape[3] != d or len({q.dtype, k.dtype, v.dtype, k_summary.dtype}) != 1):
+        raise ValueError("q, k, v and k_summary disagree in batch, heads, length, head_dim or dtype")
+    if chunk <= 0 or n % chunk or k_summary.shape[2] != n // chunk:
+        raise ValueError(f"k_summary needs seqlen / chunk = {n // max(chunk, 1)} rows")
+    dt = ENTMAX_BF16 if q.dtype == torch.bfloat16 else ENTMAX_F32
+    desc = make_dash_desc(b, hq, k.shape[1], n, d, dt, chunk, route_alpha, gamma, sigma, scale, max_iters, tol)
+    L = lib()
+    dev = q.device
+    nc = n // chunk
+    o = torch.empty((b, hq, n, d), dtype=torch.float32, device=dev)
+    lse = torch.empty((b, hq, n), dtype=torch.float32, device=dev)
+    rtau = torch.empty((b, hq, n), dtype=torch.float32, device=dev)
+    rw = torch.empty((b, k.shape[1], nc, n), dtype=torch.float32, device=dev)
+    cmask = torch.empty((b, k.shape[1], max(n // 64, 0), (nc + 31) // 32), dtype=torch.int32, device=dev)
+    nbytes = L.entmax_dash_fwd_workspace_bytes(ctypes.byref(desc))
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+    _check(L.entmax_dash_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(k_summary), _ptr(o), _ptr(lse),
+                             _ptr(rtau), _ptr(rw), _ptr(cmask), _ptr(workspace), workspace.numel(), _stream(dev)))
+    return DashOut(o, lse, rtau, rw, cmask)
 
 
 def workspace_bytes(desc: Desc) -> Tuple[int, int]:

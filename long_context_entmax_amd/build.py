@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libentmax_attn.so")
-SOURCES = ["api.hip", "fwd.hip", "bwd.hip", "prep.hip", "decode.hip"]
+SOURCES = ["api.hip", "fwd.hip", "bwd.hip", "prep.hip", "decode.hip", "dash.hip"]
 ARCH = os.environ.get("ENTMAX_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

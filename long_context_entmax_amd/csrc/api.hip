@@ -10,6 +10,7 @@
 #include <string>
 #include <vector>
 
+#include "../../include/dash_attn.h"
 #include "../../include/entmax_attn.h"
 #include "common.hpp"
 #include "kernels.hpp"
@@ -209,6 +210,57 @@ static WgMap make_map(int U, int R, int fold = 0) {
   m.xcd = (U > 0 && U % 8 == 0) ? 1 : 0;
   return m;
 }
+
+// DashAttention forward (stages 1-2): checks and derived sizes
+struct DashDerived {
+  int b, hq, hkv, n, D, G, dtype, C, nc, Tr, Wc, max_iters, mode;
+  float alpha, kappa, gamma, sigma, scale, tol;
+  size_t es;
+};
+
+static entmax_status derive_dash(const entmax_dash_desc* d, DashDerived& o) {
+  if (!d) return fail(ENTMAX_ERR_NULL, "desc is NULL");
+  o.b = d->batch; o.hq = d->heads_q; o.hkv = d->heads_kv; o.n = d->seqlen; o.D = d->head_dim;
+  if (o.b < 0 || o.hq < 0 || o.hkv < 0 || o.n < 0 || o.D <= 0)
+    return fail(ENTMAX_ERR_SHAPE, "negative size (batch %d, heads %d/%d, seqlen %d, head_dim %d)",
+                o.b, o.hq, o.hkv, o.n, o.D);
+  if (o.hkv == 0 && o.hq != 0) return fail(ENTMAX_ERR_SHAPE, "heads_kv is 0 but heads_q is %d", o.hq);
+  if (o.hkv > 0 && o.hq % o.hkv != 0)
+    return fail(ENTMAX_ERR_SHAPE, "heads_q (%d) is not a multiple of heads_kv (%d)", o.hq, o.hkv);
+  if (!(d->route_alpha > 1.0f && d->route_alpha <= 16.0f) || !isfinite(d->route_alpha))
+    return fail(ENTMAX_ERR_ALPHA, "route_alpha must be finite and in (1, 16], got %g", (double)d->route_alpha);
+  if (d->dtype != ENTMAX_F32 && d->dtype != ENTMAX_BF16)
+    return fail(ENTMAX_ERR_UNSUPPORTED, "dtype %d is not F32 (0) or BF16 (1)", d->dtype);
+  if (o.D != 64 && o.D != 128) return fail(ENTMAX_ERR_UNSUPPORTED, "head_dim %d: only 64 and 128", o.D);
+  o.C = d->chunk;
+  if (o.C != 64 && o.C != 128 && o.C != 256)
+    return fail(ENTMAX_ERR_UNSUPPORTED, "chunk %d: must be 64, 128 or 256", o.C);
+  if (o.n % o.C != 0) return fail(ENTMAX_ERR_SHAPE, "seqlen %d is not a multiple of the chunk %d", o.n, o.C);
+  o.nc = o.n / o.C;
+  if (o.nc > 256) return fail(ENTMAX_ERR_UNSUPPORTED, "%d chunks: at most 256", o.nc);
+  if (!(d->gamma >= 0.0f) || !isfinite(d->gamma)) return fail(ENTMAX_ERR_SHAPE, "gamma must be >= 0 and finite");
+  if (!(d->sigma >= 0.0f) || !isfinite(d->sigma)) return fail(ENTMAX_ERR_SHAPE, "sigma must be >= 0 and finite");
+  if (!(d->scale >= 0.0f) || !isfinite(d->scale)) return fail(ENTMAX_ERR_SHAPE, "scale must be >= 0 and finite");
+  if (!(d->tol >= 0.0f) || !isfinite(d->tol)) return fail(ENTMAX_ERR_SHAPE, "tol must be >= 0 and finite");
+  o.max_iters = d->max_iters != 0 ? d->max_iters : 15;
+  if (o.max_iters < 1 || o.max_iters > 15)
+    return fail(ENTMAX_ERR_SHAPE, "max_iters %d: must be 0 (default) or 1..15", d->max_iters);
+  o.dtype = d->dtype;
+  o.alpha = d->route_alpha;
+  o.kappa = (float)(1.0 / ((double)o.alpha - 1.0));
+  o.mode = (o.alpha == 2.0f) ? 1 : (o.alpha == 1.5f ? 2 : 0);
+  o.gamma = d->gamma == 0.0f ? 1.0f : d->gamma;
+  o.sigma = d->sigma;
+  o.scale = d->scale == 0.0f ? (float)(1.0 / sqrt((double)o.D)) : d->scale;
+  o.tol = d->tol == 0.0f ? ldexpf(1.0f, -20) : d->tol;
+  o.G = o.hkv > 0 ? o.hq / o.hkv : 1;
+  o.Tr = o.n / 64;
+  o.Wc = (o.nc + 31) / 32;
+  o.es = o.dtype == ENTMAX_BF16 ? 2 : 4;
+  return ENTMAX_OK;
+}
+
+static size_t dash_kv_bytes(const DashDerived& o) { return align256((size_t)o.b * o.hkv * o.n * o.D * o.es); }
 
 }  // namespace entmax
 
@@ -434,6 +486,58 @@ entmax_status entmax_attn_decode(const entmax_attn_desc* desc, const void* q, co
   p.am1 = o.alpha - 1.0f; p.alpha = o.alpha; p.kappa = o.kappa; p.tol = o.tol;
   const hipError_t e = launch_decode(p, o.dtype, o.D, o.mode, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "decode kernels");
+  return ENTMAX_OK;
+}
+
+size_t entmax_dash_fwd_workspace_bytes(const entmax_dash_desc* desc) {
+  DashDerived o;
+  if (derive_dash(desc, o) != ENTMAX_OK) return 0;
+  return 2 * dash_kv_bytes(o);
+}
+
+size_t entmax_dash_mask_words(const entmax_dash_desc* desc) {
+  DashDerived o;
+  if (derive_dash(desc, o) != ENTMAX_OK) return 0;
+  return (size_t)o.b * o.hkv * o.Tr * o.Wc;
+}
+
+entmax_status entmax_dash_fwd(const entmax_dash_desc* desc, const void* q, const void* k, const void* v,
+                              const void* k_summary, float* o_, float* lse, float* route_tau, float* route_w,
+                              uint32_t* chunk_mask, void* workspace, size_t workspace_bytes, void* stream) {
+  DashDerived o;
+  entmax_status st = derive_dash(desc, o);
+  if (st != ENTMAX_OK) return st;
+  if ((size_t)o.b * o.hq * o.n == 0) return ENTMAX_OK;
+  if (!q || !k || !v || !k_summary || !o_ || !route_w || !chunk_mask)
+    return fail(ENTMAX_ERR_NULL, "q, k, v, k_summary, o, route_w and chunk_mask are required");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(k_summary, 16) || !aligned(o_, 16) ||
+      !aligned(route_w, 4) || !aligned(chunk_mask, 4) || (lse && !aligned(lse, 4)) ||
+      (route_tau && !aligned(route_tau, 4)))
+    return fail(ENTMAX_ERR_ALIGN, "q, k, v, k_summary, o need 16-byte alignment; the others 4-byte");
+  const size_t need = 2 * dash_kv_bytes(o);
+  if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
+    return fail(ENTMAX_ERR_WORKSPACE, "DashAttention workspace: need %zu bytes, 256-byte aligned (got %zu)", need,
+                workspace_bytes);
+  hipStream_t s = (hipStream_t)stream;
+  char* wsb = (char*)workspace;
+  PrepBatch pb{};
+  pb.job[0] = Relayout{k, wsb, nullptr, nullptr, nullptr, o.b * o.hkv, "k"};
+  pb.job[1] = Relayout{v, nullptr, wsb + dash_kv_bytes(o), nullptr, nullptr, o.b * o.hkv, "v"};
+  pb.njobs = 2;
+  pb.n = o.n;
+  hipError_t e = launch_prep(pb, o.dtype, o.D, "dash_prep", s);
+  if (e != hipSuccess) return hip_fail(e, "fragment-major copies of K and V");
+  DashParams p{};
+  p.q = q; p.ks = k_summary; p.kf = wsb; p.vf = wsb + dash_kv_bytes(o);
+  p.o = o_; p.lse = lse; p.rtau = route_tau; p.rw = route_w; p.cmask = chunk_mask;
+  p.b = o.b; p.hq = o.hq; p.hkv = o.hkv; p.n = o.n; p.G = o.G; p.C = o.C; p.nc = o.nc; p.Tr = o.Tr; p.Wc = o.Wc;
+  p.max_iters = o.max_iters;
+  p.cx = (float)(((double)o.alpha - 1.0) * (double)o.gamma * (double)o.scale);
+  p.alpha = o.alpha; p.kappa = o.kappa; p.tol = o.tol;
+  p.c2 = (float)((double)o.scale * 1.4426950408889634);
+  p.sigma = o.sigma;
+  e = launch_dash(p, o.dtype, o.D, o.mode, s);
+  if (e != hipSuccess) return hip_fail(e, "DashAttention kernels");
   return ENTMAX_OK;
 }
 

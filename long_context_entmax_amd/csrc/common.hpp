@@ -257,6 +257,36 @@ struct Weight {
   }
 };
 
+// K operand loads and transposed score tiles of the attention kernels: fragment-major K
+// (the row layout of prep.hip), tile = keys x queries, lane c of the B operand = query.
+template <typename T, int D>
+struct KvOps {
+  static constexpr int DS = D / 16;
+  static constexpr int DC = D / 32;
+  // K fragments of sub-block kb (A operand: lane c is key 32 kb + c): one contiguous
+  // 1 KB run per fragment at a wave-uniform base plus lane * 8 elements
+  __device__ __forceinline__ static void load_k(Frag<T> (&f)[DS], const T* Kf, int kb, int c, int h) {
+    const T* kp = Kf + (size_t)kb * (DS * 512);
+    const int lo = (h * 32 + c) * 8;
+#pragma unroll
+    for (int s = 0; s < DS; ++s) load_frag(f[s], kp + s * 512 + lo);
+  }
+  // S^T tile (keys x queries) added to acc0; keys after the query (causal) become -inf
+  __device__ __forceinline__ static f32x16 scores(const Frag<T> (&kc)[DS], const Frag<T> (&qf)[DS], int kb,
+                                                  int row0, int qrow, int h, bool causal,
+                                                  const f32x16& acc0 = f32x16{}) {
+    f32x16 acc = acc0;
+#pragma unroll
+    for (int s = 0; s < DS; ++s) mma16(acc, kc[s], qf[s]);
+    if (causal && kb * 32 + 31 > row0) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (kb * 32 + acc_row(r, h) > qrow) acc[r] = -INFINITY;
+    }
+    return acc;
+  }
+};
+
 struct ProfileHook;  // host side
 
 }  // namespace entmax

@@ -141,7 +141,26 @@ struct DecParams {
   float cx, am1, alpha, kappa, tol;
 };
 
+// DashAttention stages 1-2 (dash.hip)
+struct DashParams {
+  const void* q;         // [b, hq, n, D]
+  const void* ks;        // chunk summaries [b, hkv, nc, D]
+  const void* kf;        // K, fragment-major rows
+  const void* vf;        // V, fragment-major columns
+  float* o;              // [b, hq, n, D] fp32
+  float* lse;            // optional [b, hq, n]
+  float* rtau;           // optional [b, hq, n]
+  float* rw;             // [b, hkv, nc, n] group-averaged routing weights
+  uint32_t* cmask;       // [b, hkv, Tr, Wc]
+  int b, hq, hkv, n, G, C, nc, Tr, Wc, max_iters;
+  float cx;              // (alpha - 1) * gamma * scale: routing logits on the x-scale
+  float alpha, kappa, tol;
+  float c2;              // scale * log2(e): token scores in base-2 units
+  float sigma;
+};
+
 hipError_t launch_fwd(const FwdParams& p, int dtype, int D, int mode, hipStream_t s);
+hipError_t launch_dash(const DashParams& p, int dtype, int D, int mode, hipStream_t s);
 hipError_t launch_decode(const DecParams& p, int dtype, int D, int mode, hipStream_t s);
 hipError_t launch_relayout(const Relayout& r, int dtype, int n, int D, hipStream_t s);
 hipError_t launch_prep(const PrepBatch& b, int dtype, int D, const char* name, hipStream_t s);

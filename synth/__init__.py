@@ -31,7 +31,7 @@ from typing import Optional, Sequence
 import torch
 
 # tensor ids of the counter-based streams
-TID_Q, TID_K, TID_V, TID_DO, TID_CENTROID, TID_PICKS, TID_QNOISE = 1, 2, 3, 4, 5, 6, 7
+TID_Q, TID_K, TID_V, TID_DO, TID_CENTROID, TID_PICKS, TID_QNOISE, TID_KSUM = 1, 2, 3, 4, 5, 6, 7, 8
 
 _GAMMA = 0x9E3779B97F4A7C15
 _M1 = 0xBF58476D1CE4E5B9
@@ -270,3 +270,22 @@ def make_inputs(w: Workload, device="cpu", heads: Optional[Sequence[int]] = None
     if need_grad_inputs:
         out["do"] = normal_tensor(w.seed, TID_DO, (b, hq, n, d), device, qh).to(dt).contiguous()
     return out
+
+
+def chunk_summaries(w: Workload, chunk: int, device="cpu") -> torch.Tensor:
+    """Chunk-summary keys [b, hkv, n / chunk, d] for DashAttention inputs (page 4, stage 0
+    gives one vector per chunk of keys), drawn with the spread a mean of ``chunk`` keys of
+    the recipe would have: N(0, qk_scale^2 / chunk) per element for ``normal`` and ``tiny``;
+    for ``centroid`` (chunk 64, one centroid per chunk) the chunk's centroid plus
+    0.3 N(0, 1/64). In the workload's dtype."""
+    b, hkv, n, d = w.batch, w.heads_kv, w.seqlen, w.head_dim
+    nc = n // chunk
+    noise = normal_tensor(w.seed, TID_KSUM, (b, hkv, nc, d), device)
+    if w.recipe == "centroid":
+        if chunk != 64:
+            raise ValueError("centroid summaries follow the 64-key centroid blocks")
+        cen = 3.0 * normal_tensor(w.seed, TID_CENTROID, (b, hkv, n // 64, d), device, None)
+        ks = cen + 0.3 * noise / 8.0
+    else:
+        ks = noise * (float(w.extra.get("qk_scale", 1.0)) / math.sqrt(chunk))
+    return ks.to(w.torch_dtype).contiguous()

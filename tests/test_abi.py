@@ -11,12 +11,17 @@ import long_context_entmax_amd as lce
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "entmax_attn.h")
+DASH_HEADER = os.path.join(ROOT, "include", "dash_attn.h")
 
 
 def _declared():
-    src = open(HEADER).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(entmax_[a-z_]+)\s*\(", src)))
+    names = set()
+    for h in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        if h.endswith(".h"):
+            src = open(os.path.join(ROOT, "include", h)).read()
+            src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+            names |= set(re.findall(r"\b(entmax_[a-z_]+)\s*\(", src))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
@@ -26,10 +31,12 @@ def L():
     return lce.lib()
 
 
-def test_desc_fields_match_header():
-    """The binding's Desc has the header struct's fields, in order and with 4-byte types."""
-    src = open(HEADER).read()
-    body = re.search(r"typedef struct \{(.*?)\} entmax_attn_desc;", src, flags=re.S).group(1)
+@pytest.mark.parametrize("header,struct,cls", [(HEADER, "entmax_attn_desc", lce.Desc),
+                                               (DASH_HEADER, "entmax_dash_desc", lce.DashDesc)])
+def test_desc_fields_match_header(header, struct, cls):
+    """The binding's descriptors have the header structs' fields, in order, 4-byte types."""
+    src = open(header).read()
+    body = re.search(r"typedef struct \{(.*?)\} " + struct + ";", src, flags=re.S).group(1)
     body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
     names = []
     for decl in body.split(";"):
@@ -39,8 +46,8 @@ def test_desc_fields_match_header():
         typ, _, rest = decl.partition(" ")
         assert typ in ("int32_t", "float"), decl
         names += [x.strip() for x in rest.split(",")]
-    assert names == [f[0] for f in lce.Desc._fields_]
-    assert ctypes.sizeof(lce.Desc) == 4 * len(names)
+    assert names == [f[0] for f in cls._fields_]
+    assert ctypes.sizeof(cls) == 4 * len(names)
 
 
 def test_exports_every_declared_symbol(L):
@@ -157,3 +164,50 @@ def test_decode_arguments(L):
     assert dec(ctypes.byref(empty), f, f, f, None, None, f, f, None, None, f, 1 << 30, None) == 2
     assert dec(ctypes.byref(_desc(batch=0)), None, None, None, None, None, None, None, None, None,
                None, 0, None) == 0
+
+
+def _dash_desc(**kw):
+    base = dict(batch=1, heads_q=4, heads_kv=2, seqlen=1024, head_dim=64, dtype=lce.ENTMAX_BF16,
+                chunk=64, route_alpha=1.5, gamma=1.0, sigma=1.0)
+    base.update(kw)
+    return lce.make_dash_desc(base["batch"], base["heads_q"], base["heads_kv"], base["seqlen"], base["head_dim"],
+                              base["dtype"], base["chunk"], base["route_alpha"], base["gamma"], base["sigma"],
+                              base.get("scale"), base.get("max_iters", 0), base.get("tol", 0.0))
+
+
+DASH_BAD = [
+    (dict(route_alpha=1.0), 3), (dict(route_alpha=float("inf")), 3), (dict(heads_q=3), 2),
+    (dict(chunk=32), 4), (dict(chunk=96), 4), (dict(seqlen=1000), 2), (dict(seqlen=64 * 257), 4),
+    (dict(head_dim=80), 4), (dict(dtype=3), 4), (dict(sigma=-1.0), 2), (dict(gamma=float("nan")), 2),
+    (dict(max_iters=16), 2), (dict(seqlen=-64), 2),
+]
+
+
+@pytest.mark.parametrize("kw,status", DASH_BAD, ids=[str(b[0]) for b in DASH_BAD])
+def test_dash_argument_errors(L, kw, status):
+    d = _dash_desc(**kw)
+    assert L.entmax_dash_fwd_workspace_bytes(ctypes.byref(d)) == 0
+    assert L.entmax_dash_mask_words(ctypes.byref(d)) == 0
+    f = ctypes.c_void_p(256)
+    st = L.entmax_dash_fwd(ctypes.byref(d), f, f, f, f, f, None, None, f, f, f, 1 << 30, None)
+    assert st == status, L.entmax_last_error()
+
+
+def test_dash_pointers_workspace_and_sizes(L):
+    d = _dash_desc()
+    f = ctypes.c_void_p(4096)
+    mis = ctypes.c_void_p(4098)
+    need = L.entmax_dash_fwd_workspace_bytes(ctypes.byref(d))
+    assert need == 2 * 1 * 2 * 1024 * 64 * 2           # K and V fragment-major copies
+    assert L.entmax_dash_mask_words(ctypes.byref(d)) == 1 * 2 * (1024 // 64) * 1
+    assert L.entmax_dash_fwd(None, f, f, f, f, f, None, None, f, f, f, need, None) == 1
+    assert L.entmax_dash_fwd(ctypes.byref(d), f, f, f, None, f, None, None, f, f, f, need, None) == 1
+    assert L.entmax_dash_fwd(ctypes.byref(d), f, f, f, f, f, None, None, None, f, f, need, None) == 1
+    assert L.entmax_dash_fwd(ctypes.byref(d), f, f, f, mis, f, None, None, f, f, f, need, None) == 5
+    assert L.entmax_dash_fwd(ctypes.byref(d), f, f, f, f, f, mis, None, f, f, f, need, None) == 5
+    assert L.entmax_dash_fwd(ctypes.byref(d), f, f, f, f, f, None, None, f, f, f, need - 1, None) == 6
+    assert L.entmax_dash_fwd(ctypes.byref(d), f, f, f, f, f, None, None, f, f, None, need, None) == 6
+    for kw in (dict(batch=0), dict(seqlen=0)):
+        e = _dash_desc(**kw)
+        assert L.entmax_dash_fwd(ctypes.byref(e), None, None, None, None, None, None, None, None, None, None, 0,
+                                 None) == 0

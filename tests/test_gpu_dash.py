@@ -1,0 +1,115 @@
+"""GPU parity of the DashAttention forward (stages 1-2, include/dash_attn.h) with the fp64
+oracle ``oracle.dash`` on the same seeded inputs (page 4, DashAttention, stages 1 and 2).
+
+Bars: bf16 -- max |d route_tau| <= 1e-3, max |d wbar| <= 1e-3, max |do| <= 1e-2,
+max |d lse| <= 1e-3. For routing alpha > 2 the weight d^kappa (kappa < 1) is only Hoelder in
+tau near the support boundary, |d(a)^kappa - d(b)^kappa| <= |a - b|^kappa, so there the
+weight bar is 1e-3 + (max |d route_tau| + 1e-6)^kappa, with the tau bar unchanged; chunk-mask bits equal to the OR of the kernel's own wbar > 0, and
+equal to the oracle's except on (tile, chunk) pairs whose largest weight on either side is
+below 1e-3 (a routing score within rounding of tau). fp32 -- the same at 1e-5 / 1e-5 /
+1e-4 / 1e-5.
+"""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.dash as odash
+import synth
+import long_context_entmax_amd as lce
+from tests.gpu_helpers import dev, to64
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(b, hq, hkv, n, d, dtype, C, seed, qk_scale=1.0):
+    w = synth.Workload("dash", b, hq, hkv, n, d, dtype, 1.5, True, 64, 64, 16, "normal",
+                       extra={"qk_scale": qk_scale}, seed=seed)
+    inp = synth.make_inputs(w, need_grad_inputs=False)
+    return inp["q"], inp["k"], inp["v"], synth.chunk_summaries(w, C)
+
+
+def _run(q, k, v, ks, C, alpha, gamma, sigma):
+    d0 = dev()
+    r = lce.dash_fwd(q.to(d0), k.to(d0), v.to(d0), ks.to(d0), C, alpha, gamma, sigma)
+    torch.cuda.synchronize()
+    return {kk: getattr(r, kk).cpu() for kk in ("o", "lse", "route_tau", "route_w", "chunk_mask")}
+
+
+def _mask_from_w(wbar_cm: np.ndarray, n: int) -> np.ndarray:
+    """Tile words from chunk-major weights [b, hkv, nc, n]."""
+    b, hkv, nc, _ = wbar_cm.shape
+    act = (wbar_cm > 0).transpose(0, 1, 3, 2).reshape(b, hkv, n // 64, 64, nc).any(3)   # [b,hkv,Tr,nc]
+    words = np.zeros((b, hkv, n // 64, (nc + 31) // 32), dtype=np.int64)
+    for c in range(nc):
+        words[..., c // 32] |= act[..., c].astype(np.int64) << (c % 32)
+    return words
+
+
+def _check(g, ref, n, tol, alpha):
+    t_tau, t_w, t_o, t_lse = tol
+    dtau = np.abs(g["route_tau"].numpy() - ref["tau"]).max()
+    assert dtau < t_tau
+    if alpha > 2.0:
+        t_w += (dtau + 1e-6) ** (1.0 / (alpha - 1.0))
+    w_gpu = g["route_w"].numpy().astype(np.float64)                    # [b, hkv, nc, n]
+    w_ref = ref["wbar"].transpose(0, 1, 3, 2)                            # [b, hkv, r, nc] -> chunk-major
+    assert np.abs(w_gpu - w_ref).max() < t_w
+    assert np.abs(g["o"].numpy() - ref["o"]).max() < t_o
+    assert np.abs(g["lse"].numpy() - ref["lse"]).max() < t_lse
+    gm = g["chunk_mask"].numpy().astype(np.int64) & 0xFFFFFFFF
+    np.testing.assert_array_equal(gm, _mask_from_w(w_gpu, n))
+    if not np.array_equal(gm, ref["mask"]):
+        # every differing bit: both sides' largest weight in that (tile, chunk) is tiny
+        b, hkv, nc, _ = w_gpu.shape
+        big = np.maximum(np.abs(w_gpu), np.abs(w_ref)).transpose(0, 1, 3, 2).reshape(b, hkv, n // 64, 64, nc).max(3)
+        diff = gm ^ ref["mask"]
+        for idx in zip(*np.nonzero(diff)):
+            bits = int(diff[idx])
+            for bit in range(32):
+                if bits >> bit & 1:
+                    c = idx[3] * 32 + bit
+                    assert big[idx[0], idx[1], idx[2], c] < 1e-3, (idx, c)
+
+
+DASH_CASES = [
+    # (b, hq, hkv, n, d, dtype, C, alpha, gamma, sigma, qk_scale)
+    (1, 4, 2, 1024, 64, "bf16", 64, 1.5, 8.0, 1.0, 1.0),
+    (2, 2, 1, 2048, 128, "bf16", 128, 2.0, 16.0, 1.0, 1.0),
+    (1, 8, 1, 1024, 64, "bf16", 64, 1.25, 4.0, 0.5, 1.0),
+    (1, 2, 2, 1536, 128, "bf16", 256, 3.0, 8.0, 2.0, 1.0),
+    (1, 4, 4, 2048, 64, "bf16", 64, 1.5, 1.0, 0.0, 1.0),        # nearly uniform routing, sigma 0
+    (1, 16, 2, 4096, 128, "bf16", 64, 1.5, 24.0, 1.0, 1.0),     # GQA 8, 64 chunks
+]
+
+
+@pytest.mark.parametrize("case", DASH_CASES, ids=[str(c) for c in DASH_CASES])
+def test_dash_bf16(case):
+    b, hq, hkv, n, d, dt, C, alpha, gamma, sigma, qs = case
+    print(f"[case] dash {case}", flush=True)
+    q, k, v, ks = _inputs(b, hq, hkv, n, d, dt, C, zlib.crc32(str(case).encode()) & 0xFFFF, qs)
+    ref = odash.dash_fwd(to64(q), to64(k), to64(v), to64(ks), alpha, gamma, sigma, C)
+    g = _run(q, k, v, ks, C, alpha, gamma, sigma)
+    _check(g, ref, n, (1e-3, 1e-3, 1e-2, 1e-3), alpha)
+
+
+def test_dash_fp32():
+    b, hq, hkv, n, d, C = 1, 4, 2, 1024, 64, 64
+    print("[case] dash fp32", flush=True)
+    q, k, v, ks = _inputs(b, hq, hkv, n, d, "f32", C, 77)
+    ref = odash.dash_fwd(to64(q), to64(k), to64(v), to64(ks), 1.5, 8.0, 1.0, C)
+    g = _run(q, k, v, ks, C, 1.5, 8.0, 1.0)
+    _check(g, ref, n, (1e-5, 1e-5, 1e-4, 1e-5), 1.5)
+
+
+def test_dash_uniform_summaries_route_every_chunk():
+    """Zero summaries: every earlier chunk is routed with weight 1/m_i exactly (the oracle
+    pins this case to torch's SDPA)."""
+    b, hq, hkv, n, d, C = 1, 2, 1, 512, 64, 64
+    print("[case] dash uniform summaries", flush=True)
+    q, k, v, ks = _inputs(b, hq, hkv, n, d, "bf16", C, 5)
+    ks = torch.zeros_like(ks)
+    ref = odash.dash_fwd(to64(q), to64(k), to64(v), to64(ks), 1.5, 1.0, 1.0, C)
+    g = _run(q, k, v, ks, C, 1.5, 1.0, 1.0)
+    _check(g, ref, n, (1e-5, 1e-6, 1e-2, 1e-3), 1.5)

@@ -50,6 +50,9 @@ def parse():
     ap.add_argument("--decode", action="store_true",
                     help="time one decode step (a new query row per head against the workload's "
                          "K/V as a cache) instead of the training step")
+    ap.add_argument("--dash", action="store_true",
+                    help="DashAttention forward (routing + prior-induced sparse softmax) at 16K tokens "
+                         "instead of the entmax attention step")
     ap.add_argument("--tau-error", action="store_true",
                     help="instead of timing, print the mean |tau_p - tau*| after p = 1..15 "
                          "refinement passes for both starts (tau* = the converged tau)")
@@ -218,6 +221,101 @@ def decode_bench(args, lce, w, inp, dev):
     print(json.dumps(line), flush=True)
 
 
+DASH_CHUNK, DASH_GAMMA, DASH_SIGMA = 64, 36.0, 1.0
+
+
+def dash_workload():
+    """16K-token DashAttention forward: b1, 32 query / 2 KV heads, d 128, bf16, chunks of 64
+    (256 chunks), routing alpha 1.5 with gamma 36 (about 75% of the causal keys skipped on
+    these inputs), sigma 1."""
+    import synth
+    return synth.Workload("D16K", 1, 32, 2, 16384, 128, "bf16", 1.5, True, 64, 64, 16, "normal", seed=0)
+
+
+def dash_cpu_baseline(w, q, k, v, ks, target_s: float):
+    """The fp64 DashAttention oracle on evenly spaced query rows until ~target_s; the time
+    per row is extrapolated to all rows (its cost grows with the keys a row attends, which
+    the even spacing samples)."""
+    import numpy as np
+    import oracle.dash as odash
+    n = w.seqlen
+    q64, k64, v64, s64 = (t.double().numpy() for t in (q, k, v, ks))
+    done, t0, step = 0, time.time(), 1024
+    while time.time() - t0 < target_s and step >= 1:
+        rows = np.arange(step // 2, n, step)
+        odash.dash_fwd(q64, k64, v64, s64, w.alpha, DASH_GAMMA, DASH_SIGMA, DASH_CHUNK, rows=rows)
+        done += rows.size
+        step //= 2
+    el = time.time() - t0
+    s_per_step = el / done * n * w.batch
+    return {"value": w.batch * n / s_per_step, "unit": "tokens/s", "ms_per_step": s_per_step * 1e3,
+            "cores": 1, "kind": "oracle",
+            "sample": f"{done} of {n} query rows (all heads), evenly spaced, {el:.1f} s, extrapolated to all rows"}
+
+
+def dash_bench(args, lce, dev):
+    """One DashAttention forward (stages 1-2) per step. Roofline of the stage-2 kernel: MFMA
+    FLOPs = 4 d per (query head, row, attended key) -- the score and the P.V products."""
+    import torch
+    import synth
+    w = dash_workload()
+    inp = synth.make_inputs(w, device=dev, need_grad_inputs=False)
+    q, k, v = inp["q"], inp["k"], inp["v"]
+    ks = synth.chunk_summaries(w, DASH_CHUNK, device=dev)
+    desc = lce.make_dash_desc(w.batch, w.heads_q, w.heads_kv, w.seqlen, w.head_dim, lce.ENTMAX_BF16, DASH_CHUNK,
+                              w.alpha, DASH_GAMMA, DASH_SIGMA)
+    ws = torch.empty(lce.lib().entmax_dash_fwd_workspace_bytes(ctypes.byref(desc)), dtype=torch.uint8, device=dev)
+    step = lambda: lce.dash_fwd(q, k, v, ks, DASH_CHUNK, w.alpha, DASH_GAMMA, DASH_SIGMA, workspace=ws)
+    for _ in range(args.warmup):
+        r = step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.time()
+    e0.record()
+    for _ in range(args.steps):
+        r = step()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.time() - t0
+    ms = e0.elapsed_time(e1) / args.steps
+    lce.profile(True)
+    lce.profile_read()
+    for _ in range(args.steps):
+        r = step()
+    torch.cuda.synchronize()
+    kt = lce.profile_read()
+    lce.profile(False)
+    kern = {name: t / max(c, 1) for name, (t, c) in kt.items()}
+    n, d, C, G = w.seqlen, w.head_dim, DASH_CHUNK, w.heads_q // w.heads_kv
+    routed = (r.route_w > 0).sum(dim=2).to(torch.float64)                 # [b, hkv, n]
+    rows = torch.arange(n, device=dev, dtype=torch.float64)
+    keys = (routed * C + (rows % C + 1)).sum().item() * G                 # over query heads
+    causal_keys = w.batch * w.heads_q * n * (n + 1) / 2.0
+    alg_attn = 4.0 * d * keys
+    alg_route = 2.0 * d * w.batch * w.heads_q * float((torch.div(rows, C, rounding_mode="floor")).sum().item())
+    achieved = alg_attn / (kern["dash_attn"] * 1e-3) / 1e12
+    line = {
+        "metric": "dash_fwd_tokens_per_s", "value": round(w.batch * n / (ms * 1e-3), 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (normal recipe; chunk summaries drawn with the spread of a 64-key mean)",
+        "config": {"workload": f"DashAttention forward {w.name}: b{w.batch} hq{w.heads_q}/hkv{w.heads_kv} "
+                               f"n{n} d{d} bf16, chunk {C}, routing alpha {w.alpha}, gamma {DASH_GAMMA}, "
+                               f"sigma {DASH_SIGMA}",
+                   "key_sparsity": round(1.0 - keys / causal_keys, 4)},
+        "roofline": {"kernel": "dash_attn", "bound": "mfma", "achieved": round(achieved, 3),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "algorithmic_flops_per_launch": alg_attn},
+        "kernels_ms": {kk: round(vv, 4) for kk, vv in kern.items()},
+        "kernel_tflops": {"dash_route": round(alg_route / (kern["dash_route"] * 1e-3) / 1e12, 2),
+                          "dash_attn": round(achieved, 2)},
+        "wall_s": round(wall, 3),
+    }
+    if not args.no_cpu_baseline and not args.profile_only:
+        line["cpu_baseline"] = dash_cpu_baseline(w, q.cpu(), k.cpu(), v.cpu(), ks.cpu(), args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -228,9 +326,12 @@ def main():
     import synth
     import long_context_entmax_amd as lce
 
-    w = synth.workload(args.config, alpha=args.alpha, sparsity=args.sparsity)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.dash:
+        dash_bench(args, lce, dev)
+        return
+    w = synth.workload(args.config, alpha=args.alpha, sparsity=args.sparsity)
     inp = synth.make_inputs(w, device=dev, need_grad_inputs=not args.decode)
     if args.decode:
         decode_bench(args, lce, w, inp, dev)

@@ -147,8 +147,13 @@ __global__ __launch_bounds__(64 * DASH_WAVES) void k_dash_route(DashParams p) {
 }
 
 // ================================================================================ stage 2
+// waves per SIMD the stage-2 register budget is held to (bf16: two, so one wave's exponentials
+// overlap the other's matrix products; fp32 operands would spill at two)
+template <typename T>
+constexpr int dash_attn_occ() { return sizeof(T) == 2 ? 2 : 1; }
+
 template <typename T, int D>
-__global__ __launch_bounds__(64 * DASH_WAVES) void k_dash_attn(DashParams p) {
+__global__ __launch_bounds__((64 * DASH_WAVES), (dash_attn_occ<T>())) void k_dash_attn(DashParams p) {
   using Ops = KvOps<T, D>;
   constexpr int DS = D / 16, DC = D / 32;
   const int U = p.b * p.hkv;
@@ -177,27 +182,41 @@ __global__ __launch_bounds__(64 * DASH_WAVES) void k_dash_attn(DashParams p) {
 #pragma unroll
   for (int s = 0; s < DS; ++s) load_frag(qf[s], Q + (size_t)qrow * D + 16 * s + 8 * h);
 
-  // the walk: the diagonal run of sub-blocks, then one run per routed chunk
+  // the walk: the diagonal run of sub-blocks, then one run per routed chunk. The weights of
+  // the next chunk in the mask are read one chunk ahead, so their latency hides under the
+  // current chunk's products.
   int kb = md * spc, kb_end = row0 / 32 + 1;
   float bias = 0.f;                              // base-2 prior of the current run
   int wi = 0;
   uint32_t word = uniform_u32(mw[0]);
-  auto next_run = [&]() -> bool {
-    for (;;) {
-      while (word == 0) {
-        if (++wi >= p.Wc) return false;
-        word = uniform_u32(mw[wi]);
+  int ch_next = -1;
+  float wv_next = 0.f;
+  auto fetch_next = [&]() {
+    while (word == 0) {
+      if (++wi >= p.Wc) {
+        ch_next = -1;
+        return;
       }
-      const int ch = wi * 32 + __builtin_ctz(word);
-      word &= word - 1;
-      const float wv = wcol[(size_t)ch * n];
+      word = uniform_u32(mw[wi]);
+    }
+    ch_next = wi * 32 + __builtin_ctz(word);
+    word &= word - 1;
+    wv_next = wcol[(size_t)ch_next * n];
+  };
+  auto next_run = [&]() -> bool {
+    while (ch_next >= 0) {
+      const int ch = ch_next;
+      const float wv = wv_next;
+      fetch_next();
       if (ballot(wv > 0.f) == 0) continue;       // no row of this wave routes it
       bias = wv > 0.f ? p.sigma * log2f(wv) : -INFINITY;
       kb = ch * spc;
       kb_end = kb + spc;
       return true;
     }
+    return false;
   };
+  fetch_next();
 
   f32x16 oacc[DC];
 #pragma unroll

@@ -113,3 +113,29 @@ def test_dash_uniform_summaries_route_every_chunk():
     ref = odash.dash_fwd(to64(q), to64(k), to64(v), to64(ks), 1.5, 1.0, 1.0, C)
     g = _run(q, k, v, ks, C, 1.5, 1.0, 1.0)
     _check(g, ref, n, (1e-5, 1e-6, 1e-2, 1e-3), 1.5)
+
+
+def test_dash_fullsize_sampled_rows():
+    """The 16K benchmark shape (b1, 32 query / 2 KV heads, d 128, 256 chunks of 64, routing
+    alpha 1.5, gamma 36, sigma 1), run whole in the benchmark's launch configuration; 64 rows
+    (the first and last tiles' edges and evenly spaced ones) against the oracle, and the chunk
+    mask against the kernel's own weights everywhere."""
+    import bench
+    w = bench.dash_workload()
+    C, gamma, sigma = bench.DASH_CHUNK, bench.DASH_GAMMA, bench.DASH_SIGMA
+    print(f"[case] dash full size {w.name}", flush=True)
+    inp = synth.make_inputs(w, need_grad_inputs=False)
+    ks = synth.chunk_summaries(w, C)
+    g = _run(inp["q"], inp["k"], inp["v"], ks, C, w.alpha, gamma, sigma)
+    n = w.seqlen
+    rows = np.unique(np.concatenate([np.arange(0, 4), np.arange(60, 68), np.arange(n - 8, n),
+                                     np.linspace(100, n - 100, 44).astype(np.int64)]))
+    ref = odash.dash_fwd(to64(inp["q"]), to64(inp["k"]), to64(inp["v"]), to64(ks), w.alpha, gamma, sigma, C,
+                         rows=rows)
+    assert np.abs(g["route_tau"].numpy()[:, :, rows] - ref["tau"]).max() < 1e-3
+    w_gpu = g["route_w"].numpy()[:, :, :, rows].astype(np.float64)
+    assert np.abs(w_gpu - ref["wbar"].transpose(0, 1, 3, 2)).max() < 1e-3
+    assert np.abs(g["o"].numpy()[:, :, rows] - ref["o"]).max() < 1e-2
+    assert np.abs(g["lse"].numpy()[:, :, rows] - ref["lse"]).max() < 1e-3
+    gm = g["chunk_mask"].numpy().astype(np.int64) & 0xFFFFFFFF
+    np.testing.assert_array_equal(gm, _mask_from_w(g["route_w"].numpy().astype(np.float64), n))

@@ -255,7 +255,10 @@ def dash_cpu_baseline(w, q, k, v, ks, target_s: float):
 
 def dash_bench(args, lce, dev):
     """One DashAttention forward (stages 1-2) per step. Roofline of the stage-2 kernel: MFMA
-    FLOPs = 4 d per (query head, row, attended key) -- the score and the P.V products."""
+    FLOPs of the tiles it must multiply -- 4 d x 32 x 32 (score and P.V products) per query
+    head and (32-row block, 32-key sub-block) pair where the sub-block lies in a chunk that
+    some row of the block routes, or in the block's diagonal chunk. The FLOPs per attended
+    (row, key) pair, 4 d each, are reported beside it."""
     import torch
     import synth
     w = dash_workload()
@@ -292,8 +295,15 @@ def dash_bench(args, lce, dev):
     keys = (routed * C + (rows % C + 1)).sum().item() * G                 # over query heads
     causal_keys = w.batch * w.heads_q * n * (n + 1) / 2.0
     alg_attn = 4.0 * d * keys
+    # work the kernel does: every 32-key sub-block of a chunk that some row of a 32-row block
+    # routes (plus the diagonal run), for each query head
+    nb32 = n // 32
+    blk_routed = (r.route_w > 0).view(w.batch, w.heads_kv, n // C, nb32, 32).any(dim=4)   # [b,hkv,nc,nb32]
+    diag_sub = ((torch.arange(nb32, device=dev) * 32) % C) // 32 + 1                        # diagonal sub-blocks
+    visited = (blk_routed.sum(dim=2).to(torch.float64) * (C // 32) + diag_sub).sum().item() * G
+    visited_flops = 4.0 * d * 32 * 32 * visited
     alg_route = 2.0 * d * w.batch * w.heads_q * float((torch.div(rows, C, rounding_mode="floor")).sum().item())
-    achieved = alg_attn / (kern["dash_attn"] * 1e-3) / 1e12
+    achieved = visited_flops / (kern["dash_attn"] * 1e-3) / 1e12
     line = {
         "metric": "dash_fwd_tokens_per_s", "value": round(w.batch * n / (ms * 1e-3), 1), "unit": "tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
@@ -305,10 +315,12 @@ def dash_bench(args, lce, dev):
                    "key_sparsity": round(1.0 - keys / causal_keys, 4)},
         "roofline": {"kernel": "dash_attn", "bound": "mfma", "achieved": round(achieved, 3),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None, "algorithmic_flops_per_launch": alg_attn},
+                     "traffic": None, "algorithmic_flops_per_launch": visited_flops},
         "kernels_ms": {kk: round(vv, 4) for kk, vv in kern.items()},
         "kernel_tflops": {"dash_route": round(alg_route / (kern["dash_route"] * 1e-3) / 1e12, 2),
-                          "dash_attn": round(achieved, 2)},
+                          "dash_attn": round(achieved, 2),
+                          "dash_attn_per_attended_key": round(alg_attn / (kern["dash_attn"] * 1e-3) / 1e12, 2)},
+        "dash_attn_tiles_over_attended_keys": round(visited_flops / alg_attn, 3),
         "wall_s": round(wall, 3),
     }
     if not args.no_cpu_baseline and not args.profile_only:

@@ -81,6 +81,8 @@ DASH_CASES = [
     (1, 2, 2, 1536, 128, "bf16", 256, 3.0, 8.0, 2.0, 1.0),
     (1, 4, 4, 2048, 64, "bf16", 64, 1.5, 1.0, 0.0, 1.0),        # nearly uniform routing, sigma 0
     (1, 16, 2, 4096, 128, "bf16", 64, 1.5, 24.0, 1.0, 1.0),     # GQA 8, 64 chunks
+    (2, 6, 2, 768, 64, "bf16", 64, 1.5, 12.0, 1.0, 1.0),        # GQA 3 (not a power of two), batch 2
+    (1, 2, 1, 64, 64, "bf16", 64, 1.5, 8.0, 1.0, 1.0),          # one chunk: no row routes anything
 ]
 
 

@@ -71,101 +71,128 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void k_bwd_dkv(BwdParams p)
     dv[dc] = f32x16{};
   }
 
-  int t = 0;
-  for (int g = 0; g < p.G; ++g) {
-    const int head = kvh * p.G + g;
-    const size_t qrow0 = (size_t)(bi * p.hq + head) * n;
-    const T* Qr = reinterpret_cast<const T*>(p.qr) + qrow0 * D;
+  // This wave's items in list order: for each query head g of the group, each query tile I
+  // with bit J in the head's column mask, each 32-row chunk qc of I -- every NS-th, none
+  // above the diagonal. The next item's Q rows (the first operand needed) are loaded while
+  // the current item is multiplied.
+  int t = 0, g = 0, wi = 0, I = 0, qc = QCB;
+  const uint32_t* colw = p.maskT + ((size_t)(bi * p.hq + kvh * p.G) * p.Tc + J) * p.WT;
+  uint32_t word = uniform_u32(colw[0]);
+  auto next_item = [&](int& gi, int& q0i) -> bool {
+    for (;;) {
+      if (qc >= QCB) {
+        while (word == 0) {
+          if (++wi >= p.WT) {
+            if (++g >= p.G) return false;
+            wi = 0;
+            colw = p.maskT + ((size_t)(bi * p.hq + kvh * p.G + g) * p.Tc + J) * p.WT;
+          }
+          word = uniform_u32(colw[wi]);
+        }
+        I = wi * 32 + __builtin_ctz(word);
+        word &= word - 1;
+        qc = 0;
+      }
+      const int q0c = I * p.Br + 32 * qc;
+      ++qc;
+      const bool mine = (t++ % NS) == slot;
+      if (!mine || (p.causal && key0 > q0c + 31)) continue;   // sub-tile above the diagonal
+      gi = g;
+      q0i = q0c;
+      return true;
+    }
+  };
+  auto row_base = [&](int gi) -> size_t { return (size_t)(bi * p.hq + kvh * p.G + gi) * n; };
+  int g_next = 0, q0_next = 0;
+  bool have = next_item(g_next, q0_next);
+  Frag<T> qn[DS];
+  auto load_rows = [&](int gi, int q0i) {
+    const T* Qr = reinterpret_cast<const T*>(p.qr) + row_base(gi) * D;
+#pragma unroll
+    for (int s = 0; s < DS; ++s) load_frag(qn[s], Qr + rows_off(q0i >> 5, s, DS, lane));
+  };
+  if (have) load_rows(g_next, q0_next);
+  while (have) {
+    const int gc = g_next, q0 = q0_next;
+    const int head = kvh * p.G + gc;
+    const size_t qrow0 = row_base(gc);
     const T* DOr = reinterpret_cast<const T*>(p.dor) + qrow0 * D;
     const T* Qc = reinterpret_cast<const T*>(p.qc) + qrow0 * D;
     const T* DOc = reinterpret_cast<const T*>(p.doc) + qrow0 * D;
-    const float* tau = p.tau + qrow0;
-    const float* delta = p.delta + qrow0;
     const float cm = BIAS ? p.slopes[head] * p.am1 : 0.0f;   // position bias on the x-scale
-    const uint32_t* colw = p.maskT + ((size_t)(bi * p.hq + head) * p.Tc + J) * p.WT;
-    for (int wi = 0; wi < p.WT; ++wi) {
-      uint32_t word = uniform_u32(colw[wi]);
-      while (word) {
-        const int I = wi * 32 + __builtin_ctz(word);
-        word &= word - 1;
-        for (int qc = 0; qc < QCB; ++qc) {
-          const bool mine = (t++ % NS) == slot;
-          const int q0 = I * p.Br + 32 * qc;
-          if (!mine || (p.causal && key0 > q0 + 31)) continue;   // sub-tile above the diagonal
-          const int qb = q0 >> 5;
-          Frag<T> qa[DS], da[DS], qt[2][DC], dt[2][DC];
+    const int qb = q0 >> 5;
+    Frag<T> qa[DS], da[DS], qt[2][DC], dt[2][DC];
+    f32x4 tv[4], dl[4];
 #pragma unroll
-          for (int s = 0; s < DS; ++s) {
-            load_frag(qa[s], Qr + rows_off(qb, s, DS, lane));
-            load_frag(da[s], DOr + rows_off(qb, s, DS, lane));
-          }
-          f32x4 tv[4], dl[4];
+    for (int s = 0; s < DS; ++s) {
+      qa[s] = qn[s];
+      load_frag(da[s], DOr + rows_off(qb, s, DS, lane));
+    }
 #pragma unroll
-          for (int g4 = 0; g4 < 4; ++g4) {
-            tv[g4] = *reinterpret_cast<const f32x4*>(tau + q0 + 8 * g4 + 4 * h);
-            dl[g4] = *reinterpret_cast<const f32x4*>(delta + q0 + 8 * g4 + 4 * h);
-          }
+    for (int g4 = 0; g4 < 4; ++g4) {
+      tv[g4] = *reinterpret_cast<const f32x4*>(p.tau + qrow0 + q0 + 8 * g4 + 4 * h);
+      dl[g4] = *reinterpret_cast<const f32x4*>(p.delta + qrow0 + q0 + 8 * g4 + 4 * h);
+    }
 #pragma unroll
-          for (int m = 0; m < 2; ++m)
+    for (int m = 0; m < 2; ++m)
 #pragma unroll
-            for (int dc = 0; dc < DC; ++dc) {
-              load_frag(qt[m][dc], Qc + cols_off(qb, dc, m, DC, lane));
-              load_frag(dt[m][dc], DOc + cols_off(qb, dc, m, DC, lane));
-            }
-          f32x16 S = f32x16{};
+      for (int dc = 0; dc < DC; ++dc) {
+        load_frag(qt[m][dc], Qc + cols_off(qb, dc, m, DC, lane));
+        load_frag(dt[m][dc], DOc + cols_off(qb, dc, m, DC, lane));
+      }
+    have = next_item(g_next, q0_next);
+    if (have) load_rows(g_next, q0_next);
+    f32x16 S = f32x16{};
 #pragma unroll
-          for (int s = 0; s < DS; ++s) mma16(S, qa[s], kb[s]);   // S[q][key]
-          // -tau of each entry's row (and the position bias): x - tau = cx S + off
-          f32x16 off;
+    for (int s = 0; s < DS; ++s) mma16(S, qa[s], kb[s]);   // S[q][key]
+    // -tau of each entry's row (and the position bias): x - tau = cx S + off
+    f32x16 off;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) off[r] = -tv[r >> 2][r & 3];
-          if (BIAS && cm != 0.0f) {
-            const f32x16 bb = bias16<1>(0.0f, cm, (float)(q0 + 4 * h - key0 - c), p.causal);
+    for (int r = 0; r < 16; ++r) off[r] = -tv[r >> 2][r & 3];
+    if (BIAS && cm != 0.0f) {
+      const f32x16 bb = bias16<1>(0.0f, cm, (float)(q0 + 4 * h - key0 - c), p.causal);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) off[r] += bb[r];
-          }
-          // P and G; rows 8(r/4) + 4h + r%4 of the chunk, key c of the sub-block
-          const bool diag = p.causal && key0 + 31 > q0;
-          f32x16 P, G;
-          float mx = 0.f;
-          if (diag) {
+      for (int r = 0; r < 16; ++r) off[r] += bb[r];
+    }
+    // P and G; rows 8(r/4) + 4h + r%4 of the chunk, key c of the sub-block
+    const bool diag = p.causal && key0 + 31 > q0;
+    f32x16 P, G;
+    float mx = 0.f;
+    if (diag) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              float tt = fmaf(cx, S[r], off[r]);
-              tt = (key0 + c <= q0 + acc_row(r, h)) ? tt : -1.0f;
-              const float dm = fmaxf(tt, 0.f);
-              P[r] = Weight<MODE>::p(dm, kappa);
-              G[r] = Weight<MODE>::g(dm, kappa);
-              mx = fmaxf(mx, dm);
-            }
-          } else {
+      for (int r = 0; r < 16; ++r) {
+        float tt = fmaf(cx, S[r], off[r]);
+        tt = (key0 + c <= q0 + acc_row(r, h)) ? tt : -1.0f;
+        const float dm = fmaxf(tt, 0.f);
+        P[r] = Weight<MODE>::p(dm, kappa);
+        G[r] = Weight<MODE>::g(dm, kappa);
+        mx = fmaxf(mx, dm);
+      }
+    } else {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const float dm = fmaxf(fmaf(cx, S[r], off[r]), 0.f);
-              P[r] = Weight<MODE>::p(dm, kappa);
-              G[r] = Weight<MODE>::g(dm, kappa);
-              mx = fmaxf(mx, dm);
-            }
-          }
-          if (ballot(mx > 0.f) == 0) continue;
-          f32x16 dP = f32x16{};
+      for (int r = 0; r < 16; ++r) {
+        const float dm = fmaxf(fmaf(cx, S[r], off[r]), 0.f);
+        P[r] = Weight<MODE>::p(dm, kappa);
+        G[r] = Weight<MODE>::g(dm, kappa);
+        mx = fmaxf(mx, dm);
+      }
+    }
+    if (ballot(mx > 0.f) == 0) continue;
+    f32x16 dP = f32x16{};
 #pragma unroll
-          for (int s = 0; s < DS; ++s) mma16(dP, da[s], vb[s]);  // dP[q][key]
-          f32x16 dS;
+    for (int s = 0; s < DS; ++s) mma16(dP, da[s], vb[s]);  // dP[q][key]
+    f32x16 dS;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) dS[r] = G[r] * (dP[r] - dl[r >> 2][r & 3]);
+    for (int r = 0; r < 16; ++r) dS[r] = G[r] * (dP[r] - dl[r >> 2][r & 3]);
 #pragma unroll
-          for (int m = 0; m < 2; ++m) {
-            Frag<T> pf, sf;
-            acc_frag(pf, P, m);
-            acc_frag(sf, dS, m);
+    for (int m = 0; m < 2; ++m) {
+      Frag<T> pf, sf;
+      acc_frag(pf, P, m);
+      acc_frag(sf, dS, m);
 #pragma unroll
-            for (int dc = 0; dc < DC; ++dc) {
-              mma16(dv[dc], dt[m][dc], pf);   // dV^T[d][key] += dO^T P
-              mma16(dk[dc], qt[m][dc], sf);   // dK^T[d][key] += Q^T dS
-            }
-          }
-        }
+      for (int dc = 0; dc < DC; ++dc) {
+        mma16(dv[dc], dt[m][dc], pf);   // dV^T[d][key] += dO^T P
+        mma16(dk[dc], qt[m][dc], sf);   // dK^T[d][key] += Q^T dS
       }
     }
   }
@@ -248,73 +275,99 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void k_bwd_dq(BwdParams p) 
   for (int dc = 0; dc < DC; ++dc) dq[dc] = f32x16{};
 
   const uint32_t* roww = p.mask + ((size_t)(bi * p.hq + head) * p.Tr + I) * p.W;
-  int t = 0;
-  for (int wi = 0; wi < p.W; ++wi) {
-    uint32_t word = uniform_u32(roww[wi]);
-    while (word) {
-      const int J = wi * 32 + __builtin_ctz(word);
-      word &= word - 1;
-      for (int ks = 0; ks < KC; ++ks) {
-        const bool mine = (t++ % NS) == slot;
-        const int key0 = J * p.Bc + 32 * ks;
-        if (!mine || (p.causal && key0 > q0 + 31)) continue;
-        const int kbk = key0 >> 5;
-        Frag<T> ka[DS], va[DS], kt[2][DC];
-#pragma unroll
-        for (int s = 0; s < DS; ++s) {
-          load_frag(ka[s], Kr + rows_off(kbk, s, DS, lane));
-          load_frag(va[s], Vr + rows_off(kbk, s, DS, lane));
+  // This wave's items in list order: the 32-key sub-blocks ks of each set key block J of the
+  // row's mask, every NS-th, none above the diagonal. The next item's K fragments (the first
+  // operand needed) are loaded while the current item is multiplied.
+  int wi = 0, t = 0, ks = KC, J = 0;
+  uint32_t word = uniform_u32(roww[0]);
+  auto next_item = [&](int& kbk) -> bool {
+    for (;;) {
+      if (ks >= KC) {
+        while (word == 0) {
+          if (++wi >= p.W) return false;
+          word = uniform_u32(roww[wi]);
         }
-#pragma unroll
-        for (int m = 0; m < 2; ++m)
-#pragma unroll
-          for (int dc = 0; dc < DC; ++dc) load_frag(kt[m][dc], Kc + cols_off(kbk, dc, m, DC, lane));
-        f32x16 S = f32x16{};
-#pragma unroll
-        for (int s = 0; s < DS; ++s) mma16(S, ka[s], qb[s]);   // S^T[key][q]
-        // x - tau = cx S + off (the row's -tau and the position bias)
-        f32x16 off;
-        if (BIAS && cm != 0.0f) {
-          off = bias16<-1>(-tq, cm, (float)(q0 + c - key0 - 4 * h), p.causal);
-        } else {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) off[r] = -tq;
-        }
-        const bool diag = p.causal && key0 + 31 > q0;
-        f32x16 G;
-        float mx = 0.f;
-        if (diag) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            float tt = fmaf(cx, S[r], off[r]);
-            tt = (key0 + acc_row(r, h) <= q0 + c) ? tt : -1.0f;
-            const float dm = fmaxf(tt, 0.f);
-            G[r] = Weight<MODE>::g(dm, kappa);
-            mx = fmaxf(mx, dm);
-          }
-        } else {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float dm = fmaxf(fmaf(cx, S[r], off[r]), 0.f);
-            G[r] = Weight<MODE>::g(dm, kappa);
-            mx = fmaxf(mx, dm);
-          }
-        }
-        if (ballot(mx > 0.f) == 0) continue;
-        f32x16 dP = f32x16{};
-#pragma unroll
-        for (int s = 0; s < DS; ++s) mma16(dP, va[s], db[s]);   // dP^T[key][q]
-        f32x16 dS;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) dS[r] = G[r] * (dP[r] - dq_delta);
-#pragma unroll
-        for (int m = 0; m < 2; ++m) {
-          Frag<T> sf;
-          acc_frag(sf, dS, m);
-#pragma unroll
-          for (int dc = 0; dc < DC; ++dc) mma16(dq[dc], kt[m][dc], sf);   // dQ^T[d][q] += K^T dS^T
-        }
+        J = wi * 32 + __builtin_ctz(word);
+        word &= word - 1;
+        ks = 0;
       }
+      const int k0 = J * p.Bc + 32 * ks;
+      ++ks;
+      const bool mine = (t++ % NS) == slot;
+      if (!mine || (p.causal && k0 > q0 + 31)) continue;   // sub-tile above the diagonal
+      kbk = k0 >> 5;
+      return true;
+    }
+  };
+  int kb_next = 0;
+  bool have = next_item(kb_next);
+  Frag<T> kn[DS];
+  if (have) {
+#pragma unroll
+    for (int s = 0; s < DS; ++s) load_frag(kn[s], Kr + rows_off(kb_next, s, DS, lane));
+  }
+  while (have) {
+    const int kbk = kb_next;
+    const int key0 = kbk * 32;
+    Frag<T> ka[DS], va[DS], kt[2][DC];
+#pragma unroll
+    for (int s = 0; s < DS; ++s) {
+      ka[s] = kn[s];
+      load_frag(va[s], Vr + rows_off(kbk, s, DS, lane));
+    }
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int dc = 0; dc < DC; ++dc) load_frag(kt[m][dc], Kc + cols_off(kbk, dc, m, DC, lane));
+    have = next_item(kb_next);
+    if (have) {
+#pragma unroll
+      for (int s = 0; s < DS; ++s) load_frag(kn[s], Kr + rows_off(kb_next, s, DS, lane));
+    }
+    f32x16 S = f32x16{};
+#pragma unroll
+    for (int s = 0; s < DS; ++s) mma16(S, ka[s], qb[s]);   // S^T[key][q]
+    // x - tau = cx S + off (the row's -tau and the position bias)
+    f32x16 off;
+    if (BIAS && cm != 0.0f) {
+      off = bias16<-1>(-tq, cm, (float)(q0 + c - key0 - 4 * h), p.causal);
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) off[r] = -tq;
+    }
+    const bool diag = p.causal && key0 + 31 > q0;
+    f32x16 G;
+    float mx = 0.f;
+    if (diag) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float tt = fmaf(cx, S[r], off[r]);
+        tt = (key0 + acc_row(r, h) <= q0 + c) ? tt : -1.0f;
+        const float dm = fmaxf(tt, 0.f);
+        G[r] = Weight<MODE>::g(dm, kappa);
+        mx = fmaxf(mx, dm);
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float dm = fmaxf(fmaf(cx, S[r], off[r]), 0.f);
+        G[r] = Weight<MODE>::g(dm, kappa);
+        mx = fmaxf(mx, dm);
+      }
+    }
+    if (ballot(mx > 0.f) == 0) continue;
+    f32x16 dP = f32x16{};
+#pragma unroll
+    for (int s = 0; s < DS; ++s) mma16(dP, va[s], db[s]);   // dP^T[key][q]
+    f32x16 dS;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dS[r] = G[r] * (dP[r] - dq_delta);
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      Frag<T> sf;
+      acc_frag(sf, dS, m);
+#pragma unroll
+      for (int dc = 0; dc < DC; ++dc) mma16(dq[dc], kt[m][dc], sf);   // dQ^T[d][q] += K^T dS^T
     }
   }
 

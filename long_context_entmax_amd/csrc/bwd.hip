@@ -105,11 +105,18 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void k_bwd_dkv(BwdParams p)
   auto row_base = [&](int gi) -> size_t { return (size_t)(bi * p.hq + kvh * p.G + gi) * n; };
   int g_next = 0, q0_next = 0;
   bool have = next_item(g_next, q0_next);
-  Frag<T> qn[DS];
+  // (head_dim 128, one wave per SIMD: the dO rows too)
+  constexpr bool DEEP = D == 128;
+  Frag<T> qn[DS], dn[DEEP ? DS : 1];
   auto load_rows = [&](int gi, int q0i) {
     const T* Qr = reinterpret_cast<const T*>(p.qr) + row_base(gi) * D;
 #pragma unroll
     for (int s = 0; s < DS; ++s) load_frag(qn[s], Qr + rows_off(q0i >> 5, s, DS, lane));
+    if constexpr (DEEP) {
+      const T* DOn = reinterpret_cast<const T*>(p.dor) + row_base(gi) * D;
+#pragma unroll
+      for (int s = 0; s < DS; ++s) load_frag(dn[s], DOn + rows_off(q0i >> 5, s, DS, lane));
+    }
   };
   if (have) load_rows(g_next, q0_next);
   while (have) {
@@ -126,7 +133,8 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void k_bwd_dkv(BwdParams p)
 #pragma unroll
     for (int s = 0; s < DS; ++s) {
       qa[s] = qn[s];
-      load_frag(da[s], DOr + rows_off(qb, s, DS, lane));
+      if constexpr (DEEP) da[s] = dn[s];
+      else load_frag(da[s], DOr + rows_off(qb, s, DS, lane));
     }
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {

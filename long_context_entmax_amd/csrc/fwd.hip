@@ -468,15 +468,39 @@ __global__ __launch_bounds__(64 * OUT_WAVES, 2) void k_refine_out(FwdParams p) {
   int mw = -1;
   uint32_t mbits = 0;
   {
+    // head_dim 64: the next sub-block's V is loaded with its K (most visited sub-blocks hold
+    // a weight), so the P.V product does not wait for it
+    constexpr bool VPRE = D == 64;
+    Frag<T> vn[VPRE ? DC : 1][2];
+    auto load_v = [&](Frag<T> (&dst)[VPRE ? DC : 1][2], int kbv) {
+      const T* vp = Vf + (size_t)kbv * (DC * 1024);
+#pragma unroll
+      for (int dc = 0; dc < (VPRE ? DC : 1); ++dc)
+#pragma unroll
+        for (int m = 0; m < 2; ++m) load_frag(dst[dc][m], vp + (dc * 2 + m) * 512 + lane * 8);
+    };
     Walk wk{-1, 0u};
     int kb = walk_next(wk, othr);
-    if (kb >= 0) Ops::load_k(kf, Kf, kb, c, h);
+    if (kb >= 0) {
+      Ops::load_k(kf, Kf, kb, c, h);
+      if constexpr (VPRE) load_v(vn, kb);
+    }
     while (kb >= 0) {
       Frag<T> kc[DS];
 #pragma unroll
       for (int s = 0; s < DS; ++s) kc[s] = kf[s];
+      Frag<T> vc[VPRE ? DC : 1][2];
+      if constexpr (VPRE) {
+#pragma unroll
+        for (int dc = 0; dc < DC; ++dc)
+#pragma unroll
+          for (int m = 0; m < 2; ++m) vc[dc][m] = vn[dc][m];
+      }
       const int kn = walk_next(wk, othr);
-      if (kn >= 0) Ops::load_k(kf, Kf, kn, c, h);
+      if (kn >= 0) {
+        Ops::load_k(kf, Kf, kn, c, h);
+        if constexpr (VPRE) load_v(vn, kn);
+      }
       const f32x16 t = tile(kc, kb);
       f32x16 pw, gw;
       float mx = 0.f;
@@ -498,11 +522,18 @@ __global__ __launch_bounds__(64 * OUT_WAVES, 2) void k_refine_out(FwdParams p) {
         }
         mbits |= 1u << (J & 31);
         Frag<T> vf[DC][2];
-        const T* vp = Vf + (size_t)kb * (DC * 1024);
+        if constexpr (VPRE) {
 #pragma unroll
-        for (int dc = 0; dc < DC; ++dc)
+          for (int dc = 0; dc < DC; ++dc)
 #pragma unroll
-          for (int m = 0; m < 2; ++m) load_frag(vf[dc][m], vp + (dc * 2 + m) * 512 + lane * 8);
+            for (int m = 0; m < 2; ++m) vf[dc][m] = vc[dc][m];
+        } else {
+          const T* vp = Vf + (size_t)kb * (DC * 1024);
+#pragma unroll
+          for (int dc = 0; dc < DC; ++dc)
+#pragma unroll
+            for (int m = 0; m < 2; ++m) load_frag(vf[dc][m], vp + (dc * 2 + m) * 512 + lane * 8);
+        }
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
           Frag<T> pf, gf;

@@ -95,7 +95,7 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void k_bwd_dkv(BwdParams p)
       }
       const int q0c = I * p.Br + 32 * qc;
       ++qc;
-      const bool mine = (t++ % NS) == slot;
+      const bool mine = (t++ & (NS - 1)) == slot;   // NS is 1, 2 or 4
       if (!mine || (p.causal && key0 > q0c + 31)) continue;   // sub-tile above the diagonal
       gi = g;
       q0i = q0c;
@@ -301,7 +301,7 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void k_bwd_dq(BwdParams p) 
       }
       const int k0 = J * p.Bc + 32 * ks;
       ++ks;
-      const bool mine = (t++ % NS) == slot;
+      const bool mine = (t++ & (NS - 1)) == slot;   // NS is 1, 2 or 4
       if (!mine || (p.causal && k0 > q0 + 31)) continue;   // sub-tile above the diagonal
       kbk = k0 >> 5;
       return true;

@@ -465,6 +465,7 @@ __global__ __launch_bounds__(64 * OUT_WAVES, 2) void k_refine_out(FwdParams p) {
   unsigned long long n_out = 0;
   // exact mask bits of this wave, OR-ed into the tile's words one word at a time
   uint32_t* mrow = p.mask + (bh * p.Tr + row0 / p.Br) * p.W;
+  const int bc_shift = p.Bc == 32 ? 0 : (p.Bc == 64 ? 1 : 2);   // sub-blocks per key block: 1, 2, 4
   int mw = -1;
   uint32_t mbits = 0;
   {
@@ -514,7 +515,7 @@ __global__ __launch_bounds__(64 * OUT_WAVES, 2) void k_refine_out(FwdParams p) {
       }
       if (ballot(mx > 0.f) != 0) {
         ++n_out;
-        const int J = (kb * 32) / p.Bc;          // key block of this sub-block
+        const int J = kb >> bc_shift;            // key block of this sub-block
         if ((J >> 5) != mw) {
           if (mw >= 0 && lane == 0) atomicOr(mrow + mw, mbits);
           mw = J >> 5;

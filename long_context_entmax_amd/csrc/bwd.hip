@@ -171,7 +171,7 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void k_bwd_dkv(BwdParams p)
       for (int r = 0; r < 16; ++r) {
         float tt = fmaf(cx, S[r], off[r]);
         tt = (key0 + c <= q0 + acc_row(r, h)) ? tt : -1.0f;
-        const float dm = fmaxf(tt, 0.f);
+        const float dm = relu_raw(tt);
         P[r] = Weight<MODE>::p(dm, kappa);
         G[r] = Weight<MODE>::g(dm, kappa);
         mx = fmaxf(mx, dm);
@@ -179,7 +179,7 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void k_bwd_dkv(BwdParams p)
     } else {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float dm = fmaxf(fmaf(cx, S[r], off[r]), 0.f);
+        const float dm = relu_raw(fmaf(cx, S[r], off[r]));
         P[r] = Weight<MODE>::p(dm, kappa);
         G[r] = Weight<MODE>::g(dm, kappa);
         mx = fmaxf(mx, dm);
@@ -351,14 +351,14 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void k_bwd_dq(BwdParams p) 
       for (int r = 0; r < 16; ++r) {
         float tt = fmaf(cx, S[r], off[r]);
         tt = (key0 + acc_row(r, h) <= q0 + c) ? tt : -1.0f;
-        const float dm = fmaxf(tt, 0.f);
+        const float dm = relu_raw(tt);
         G[r] = Weight<MODE>::g(dm, kappa);
         mx = fmaxf(mx, dm);
       }
     } else {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float dm = fmaxf(fmaf(cx, S[r], off[r]), 0.f);
+        const float dm = relu_raw(fmaf(cx, S[r], off[r]));
         G[r] = Weight<MODE>::g(dm, kappa);
         mx = fmaxf(mx, dm);
       }

@@ -210,6 +210,14 @@ __device__ __forceinline__ uint32_t cvt_u32_sat(float x) {
   return r;
 }
 
+// max(x, 0) in one instruction: without the canonicalisation (signalling-NaN quieting) that
+// fmaxf adds in IEEE mode; matrix-core results and their sums are never signalling NaNs
+__device__ __forceinline__ float relu_raw(float x) {
+  float r;
+  asm("v_max_f32 %0, 0, %1" : "=v"(r) : "v"(x));
+  return r;
+}
+
 // max of three without canonicalising the inputs (no IEEE-mode NaN quieting)
 __device__ __forceinline__ float max3_raw(float a, float b, float c) {
   float r;

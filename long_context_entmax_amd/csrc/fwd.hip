@@ -507,7 +507,7 @@ __global__ __launch_bounds__(64 * OUT_WAVES, 2) void k_refine_out(FwdParams p) {
       float mx = 0.f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float dm = fmaxf(t[r], 0.f);
+        const float dm = relu_raw(t[r]);
         pw[r] = Weight<MODE>::p(dm, kappa);
         gw[r] = Weight<MODE>::g(dm, kappa);
         sg += gw[r];

@@ -9,6 +9,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "common.hpp"
+
 namespace entmax {
 
 // tau_h from merged counts c[0..B-1] (bin k has lower edge l_k = (T - B + 1 + k)/B).
@@ -97,13 +99,13 @@ struct PassSums {
   template <int MODE>
   __device__ __forceinline__ void add(float tt, float thi, bool sec_first, float kappa) {
     if constexpr (MODE == 2) {
-      const float dm = fmaxf(tt, 0.f);
+      const float dm = relu_raw(tt);
       F0 = fmaf(dm, dm, F0);
       F1 += dm;
       cnt += (tt > 0.f) ? 1 : 0;
       mrelb = min(mrelb, __float_as_uint(tt));
     } else if constexpr (MODE == 1) {
-      F0 += fmaxf(tt, 0.f);
+      F0 += relu_raw(tt);
       cnt += (tt > 0.f) ? 1 : 0;
       mrelb = min(mrelb, __float_as_uint(tt));
     } else {
@@ -387,7 +389,7 @@ struct MultiSums {
 #pragma unroll
     for (int k = 0; k < NP; ++k) {
       const float d = k == 0 ? tt : tt - off[k];
-      F[k] += fmaxf(d, 0.f);
+      F[k] += relu_raw(d);
       N[k] += d > 0.f ? 1 : 0;
     }
   }

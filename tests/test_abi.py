@@ -211,3 +211,20 @@ def test_dash_pointers_workspace_and_sizes(L):
         e = _dash_desc(**kw)
         assert L.entmax_dash_fwd(ctypes.byref(e), None, None, None, None, None, None, None, None, None, None, 0,
                                  None) == 0
+
+
+def test_plain_c_program_uses_the_abi(L, tmp_path):
+    """tests/c_abi/abi_check.c, compiled with gcc against include/ and linked to the library,
+    exercises the size queries and argument checks from plain C (no Python, no GPU)."""
+    import shutil
+    import subprocess
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc is not available")
+    exe = tmp_path / "abi_check"
+    libdir = os.path.dirname(lce.LIB_PATH)
+    subprocess.check_call(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"),
+                           os.path.join(ROOT, "tests", "c_abi", "abi_check.c"), "-o", str(exe),
+                           "-L", libdir, "-lentmax_attn", "-Wl,-rpath," + libdir])
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "abi_check: ok" in r.stdout

@@ -69,6 +69,10 @@ CASES = [
     (1, 2, 2, 384, 128, 2.0, True, 128, 64, 16, 1.2),
     (1, 1, 1, 256, 128, 1.5, False, 128, 128, 16, 0.7),
     (1, 8, 2, 128, 64, 1.5, True, 64, 64, 16, 2.0),
+    # GQA 16 at both head dims, and blocks 32 x 128 (one query tile row per 32-row chunk)
+    (1, 16, 1, 192, 64, 1.5, True, 64, 64, 16, 1.0),
+    (2, 16, 1, 128, 128, 2.0, True, 32, 128, 8, 1.0),
+    (1, 3, 1, 160, 64, 1.5, True, 32, 32, 16, 1.0),    # GQA 3: no power of two
 ]
 
 

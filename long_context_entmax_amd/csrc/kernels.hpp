@@ -162,10 +162,7 @@ struct DashParams {
 hipError_t launch_fwd(const FwdParams& p, int dtype, int D, int mode, hipStream_t s);
 hipError_t launch_dash(const DashParams& p, int dtype, int D, int mode, hipStream_t s);
 hipError_t launch_decode(const DecParams& p, int dtype, int D, int mode, hipStream_t s);
-hipError_t launch_relayout(const Relayout& r, int dtype, int n, int D, hipStream_t s);
 hipError_t launch_prep(const PrepBatch& b, int dtype, int D, const char* name, hipStream_t s);
-hipError_t launch_mask_transpose(const uint32_t* mask, uint32_t* maskT, int planes, int Tr, int Tc, int W,
-                                 int WT, hipStream_t s);
 hipError_t launch_bwd_dkv(const BwdParams& p, int dtype, int D, int mode, hipStream_t s);
 hipError_t launch_bwd_dq(const BwdParams& p, int dtype, int D, int mode, hipStream_t s);
 

@@ -1,6 +1,6 @@
-// Data-movement kernels around the attention kernels (HBM-bound, O(n d)).
+// Data movement around the attention kernels (HBM-bound, O(n d)), all in k_prep.
 //
-// k_relayout stages one 32-row tile of X [H, n, D] in LDS and writes any of:
+// A re-layout job stages one 32-row tile of X [H, n, D] in LDS and writes any of:
 //   rows  fragment-major copy for MFMA operands whose 32 lanes walk rows and whose
 //         contraction runs over the head dimension: 32-row block b, 16-wide chunk s,
 //         half h, lane c hold X[32b + c][16s + 8h .. +7] at unit ((b*DS + s)*2 + h)*32 + c
@@ -13,10 +13,10 @@
 //         accumulator holds the rows of a 16-row chunk);
 //   delta delta_i = X_i . aux_i (fp32), the row term of the entmax backward when X = dO
 //         and aux = o~ from the forward.
-// k_mask_transpose: block mask [P, Tr, W] -> column-major copy [P, Tc, WT] (bit I of the
+// The mask transpose: block mask [P, Tr, W] -> column-major copy [P, Tc, WT] (bit I of the
 //   words of key block J), one 32x32 bit block per wave through 32 ballots.
-// k_prep runs several of these jobs in one launch (one range of work groups per job), so
-// the small copies before the backward do not each pay a launch and a drain.
+// k_prep runs several re-layout jobs and the transpose in one launch (one range of work
+// groups per job), so the small copies do not each pay a launch and a drain.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -79,14 +79,6 @@ __device__ __forceinline__ void relayout_tile(const T* __restrict__ src, T* __re
   }
 }
 
-template <typename T, int D>
-__global__ __launch_bounds__(256) void k_relayout(const T* __restrict__ src, T* __restrict__ rows,
-                                                  T* __restrict__ cols, const float* __restrict__ aux,
-                                                  float* __restrict__ delta, int n) {
-  __shared__ __align__(16) T tile[RelayoutTile<T, D>::LDS_ELEMS];
-  relayout_tile<T, D>(src, rows, cols, aux, delta, n, blockIdx.x, blockIdx.y, tile);
-}
-
 // One wave per (plane, 32 query tiles, 32 key blocks): lane l < 32 holds the mask word of
 // tile I0 + l; ballot over bit b gives the column word of key block J0 + b.
 __device__ __forceinline__ void mask_transpose_wave(const uint32_t* __restrict__ mask,
@@ -110,12 +102,6 @@ __device__ __forceinline__ void mask_transpose_wave(const uint32_t* __restrict__
   if (lane < 32 && J < Tc) maskT[((size_t)pl * Tc + J) * WT + wt] = mine;
 }
 
-__global__ __launch_bounds__(256) void k_mask_transpose(const uint32_t* __restrict__ mask,
-                                                        uint32_t* __restrict__ maskT, int planes,
-                                                        int Tr, int Tc, int W, int WT) {
-  mask_transpose_wave(mask, maskT, planes, Tr, Tc, W, WT, (long long)blockIdx.x * 4 + (threadIdx.x >> 6));
-}
-
 // Several re-layout jobs and an optional mask transpose in one launch: work groups
 // [start[j], start[j + 1]) run job j (one 32-row tile each), the rest the transpose (four
 // waves each).
@@ -137,25 +123,6 @@ __global__ __launch_bounds__(256) void k_prep(PrepBatch b) {
 }
 
 template <typename T>
-static hipError_t relayout_t(const Relayout& r, int n, int D, hipStream_t s) {
-  if (r.heads == 0 || n == 0) return hipSuccess;
-  dim3 grid(n / 32, r.heads);
-  prof_begin(r.name, s);
-  if (D == 64)
-    hipLaunchKernelGGL((k_relayout<T, 64>), grid, dim3(256), 0, s, (const T*)r.src, (T*)r.rows, (T*)r.cols,
-                       r.aux, r.delta, n);
-  else
-    hipLaunchKernelGGL((k_relayout<T, 128>), grid, dim3(256), 0, s, (const T*)r.src, (T*)r.rows, (T*)r.cols,
-                       r.aux, r.delta, n);
-  prof_end(s);
-  return hipGetLastError();
-}
-
-hipError_t launch_relayout(const Relayout& r, int dtype, int n, int D, hipStream_t s) {
-  return dtype == 1 ? relayout_t<__bf16>(r, n, D, s) : relayout_t<float>(r, n, D, s);
-}
-
-template <typename T>
 static hipError_t prep_t(PrepBatch b, int D, const char* name, hipStream_t s) {
   int grid = 0;
   for (int j = 0; j < b.njobs; ++j) {
@@ -174,17 +141,6 @@ static hipError_t prep_t(PrepBatch b, int D, const char* name, hipStream_t s) {
 
 hipError_t launch_prep(const PrepBatch& b, int dtype, int D, const char* name, hipStream_t s) {
   return dtype == 1 ? prep_t<__bf16>(b, D, name, s) : prep_t<float>(b, D, name, s);
-}
-
-hipError_t launch_mask_transpose(const uint32_t* mask, uint32_t* maskT, int planes, int Tr, int Tc, int W,
-                                 int WT, hipStream_t s) {
-  const long long waves = (long long)planes * W * WT;
-  if (waves == 0) return hipSuccess;
-  prof_begin("mask_transpose", s);
-  hipLaunchKernelGGL(k_mask_transpose, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, mask, maskT, planes,
-                     Tr, Tc, W, WT);
-  prof_end(s);
-  return hipGetLastError();
 }
 
 }  // namespace entmax

@@ -175,18 +175,9 @@ __device__ __forceinline__ int xor32i(int v) {
   return (int)((threadIdx.x & 32) ? r[0] : r[1]);
 }
 
-// Wave-wide max / min with DPP row operations (no LDS traffic); the result is uniform.
+// Wave-wide min with DPP row operations (no LDS traffic); the result is uniform.
 #define ENTMAX_DPP(v, ctrl, rmask) \
   __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), ctrl, rmask, 0xF, false))
-__device__ __forceinline__ float wave_max(float v) {
-  v = fmaxf(v, ENTMAX_DPP(v, 0xB1, 0xF));    // quad_perm 1,0,3,2
-  v = fmaxf(v, ENTMAX_DPP(v, 0x4E, 0xF));    // quad_perm 2,3,0,1
-  v = fmaxf(v, ENTMAX_DPP(v, 0x141, 0xF));   // row_half_mirror
-  v = fmaxf(v, ENTMAX_DPP(v, 0x140, 0xF));   // row_mirror
-  v = fmaxf(v, ENTMAX_DPP(v, 0x142, 0xA));   // row_bcast15 into rows 1, 3
-  v = fmaxf(v, ENTMAX_DPP(v, 0x143, 0xC));   // row_bcast31 into rows 2, 3
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
-}
 __device__ __forceinline__ float wave_min(float v) {
   v = fminf(v, ENTMAX_DPP(v, 0xB1, 0xF));
   v = fminf(v, ENTMAX_DPP(v, 0x4E, 0xF));
@@ -294,7 +285,5 @@ struct KvOps {
     return acc;
   }
 };
-
-struct ProfileHook;  // host side
 
 }  // namespace entmax

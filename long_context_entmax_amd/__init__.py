@@ -1,6 +1,7 @@
 """alpha-entmax attention (AdaSplash-2 method) on AMD MI355X -- Python binding.
 
-Thin ctypes layer over ``libentmax_attn.so`` (C ABI in ``include/entmax_attn.h``):
+Thin ctypes layer over ``libentmax_attn.so`` (C ABI in ``include/entmax_attn.h`` and
+``include/dash_attn.h``):
 it checks tensor placement, allocates outputs and workspace with PyTorch and passes
 raw device pointers and the current HIP stream. Every step of the computation runs
 in the library's HIP kernels; there is no fallback path -- if the library is not
@@ -9,6 +10,8 @@ built, every call raises.
     o, tau, mask, aux = fwd(q, k, v, alpha=1.5, causal=True, block=(64, 64), bins=16)
     dq, dk, dv = bwd(q, k, v, do, tau, mask, aux, alpha=1.5, causal=True, block=(64, 64), bins=16)
     o = entmax_attention(q, k, v, alpha=1.5)          # autograd-aware
+    o, tau, hist, tau_h = decode(q_new, k_cache, v_cache, alpha=1.5, lengths=lens)
+    o, lse, route_tau, route_w, chunk_mask = dash_fwd(q, k, v, k_summary, chunk=64)
 
 Shapes: q, do [b, hq, n, d]; k, v [b, hkv, n, d]; dtype float32 or bfloat16.
 ``slopes`` (optional, float32 [hq] on the device): per-head position-bias slopes; head h

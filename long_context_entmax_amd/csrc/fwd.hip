@@ -52,7 +52,7 @@ template <typename T, int D>
 constexpr int hist_waves() { return (D == 128 && sizeof(T) == 2) ? 4 : 8; }
 template <typename T, int D>
 constexpr int hist_occ() { return (D == 64 && sizeof(T) == 2) ? HIST_OCC64 : (D == 128 && sizeof(T) == 2) ? 3 : 2; }
-constexpr int ALPHA2_POINTS = 4;   // evaluation points per refinement pass at alpha = 2
+constexpr int ALPHA2_POINTS = 2;   // evaluation points per refinement pass at alpha = 2 (2 beat 3 and 4)
 constexpr int OUT_WAVES = 4;
 
 // ================================================================================ k_hist

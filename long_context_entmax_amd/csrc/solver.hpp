@@ -307,9 +307,11 @@ struct MultiState {
     s.lo = tau_h - 0.0625f * hB;
     s.hi = tau_h + hB;
     s.tau = tau_h + 0.02f * hB;
+    // first-pass points above the start, in units of 1/B (set on the workloads' rows)
     const float first[4] = {0.0f, 0.03f, 0.08f, 0.23f};
+    const float first2[2] = {0.0f, 0.02f};
 #pragma unroll
-    for (int k = 0; k < NP; ++k) s.off[k] = first[k < 4 ? k : 3] * hB;
+    for (int k = 0; k < NP; ++k) s.off[k] = (NP == 2 ? first2[k] : first[k < 4 ? k : 3]) * hB;
     return s;
   }
   __device__ __forceinline__ static MultiState from_max(float xmax, float nvalid, float alpha) {

@@ -223,19 +223,30 @@ __device__ __forceinline__ float max16(const f32x16& a) {
   const float m4 = max3_raw(a[12], a[13], a[14]);
   return max3_raw(max3_raw(m0, m1, m2), max3_raw(m3, m4, a[15]), m0);
 }
-// Wave-wide max with DPP-fused v_max (one instruction per step; s_nop 1 covers the
-// VALU-write -> DPP-read hazard); the result is uniform.
-__device__ __forceinline__ float wave_max_dpp(float v) {
+// Wave-wide maxima of two values at once: v_permlane32_swap folds the upper half-wave of
+// `a` onto the lower and the lower half of `b` onto the upper, so lanes 0-31 then reduce a
+// and lanes 32-63 reduce b; DPP-fused v_max steps (s_nop 1 covers the VALU-write -> DPP-read
+// hazard) finish each 32-lane half, whose result ends in lane 31 (a) and lane 63 (b).
+__device__ __forceinline__ void pair_max_dpp(float a, float b, float& ma, float& mb) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  float v;
   asm volatile(
+      "s_nop 1\n v_max_f32 %0, %1, %2\n"
       "s_nop 1\n v_max_f32_dpp %0, %0, %0 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n"
       "s_nop 1\n v_max_f32_dpp %0, %0, %0 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n"
       "s_nop 1\n v_max_f32_dpp %0, %0, %0 row_half_mirror row_mask:0xf bank_mask:0xf\n"
       "s_nop 1\n v_max_f32_dpp %0, %0, %0 row_mirror row_mask:0xf bank_mask:0xf\n"
       "s_nop 1\n v_max_f32_dpp %0, %0, %0 row_bcast:15 row_mask:0xa bank_mask:0xf\n"
-      "s_nop 1\n v_max_f32_dpp %0, %0, %0 row_bcast:31 row_mask:0xc bank_mask:0xf\n"
       "s_nop 4"
-      : "+v"(v));
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+      : "=&v"(v)
+      : "v"(__uint_as_float(sw[0])), "v"(__uint_as_float(sw[1])));
+  ma = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 31));
+  mb = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+// v[lane] = x for a wave-uniform x and lane (lane select through M0: one SGPR operand per
+// VOP3 instruction)
+__device__ __forceinline__ void write_lane(float& v, float x, int lane) {
+  asm volatile("s_mov_b32 m0, %2\n s_nop 1\n v_writelane_b32 %0, %1, m0" : "+v"(v) : "s"(x), "s"(lane) : "m0");
 }
 
 // ------------------------------------------------------------------------------------------

@@ -192,15 +192,16 @@ __global__ __launch_bounds__((64 * hist_waves<T, D>()), (hist_occ<T, D>())) void
     const bool act1 = fin && t1 >= thrB;
     const uint64_t b0 = ballot(act0), b1 = ballot(act1);
     if ((b0 | b1) != 0) {
+      // largest x*B of the 32 rows in each sub-block, kept by lane (sub-block mod 32)
+      float cm0, cm1;
+      pair_max_dpp(t0, t1, cm0, cm1);
       if (b0) {
-        const float cm = wave_max_dpp(t0);     // largest x*B of the 32 rows in this sub-block
-        if (lane == (kb & 31)) dreg = cm;
+        write_lane(dreg, cm0, kb & 31);
         cword |= 1u << (kb & 31);
         ++n_cand;
       }
       if (b1) {
-        const float cm = wave_max_dpp(t1);
-        if (lane == ((kb + 1) & 31)) dreg = cm;
+        write_lane(dreg, cm1, (kb + 1) & 31);
         cword |= 1u << ((kb + 1) & 31);
         ++n_cand;
       }

@@ -172,9 +172,9 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // forward workspace: K and V fragment-major copies, then per (chunk, sub-block) maxima
 static size_t fwd_kv_bytes(const Derived& o) { return align256((size_t)o.b * o.hkv * o.D * o.n * o.es); }
 static size_t fwd_dmax_bytes(const Derived& o) { return align256((size_t)o.b * o.hq * (size_t)o.nkb * o.nkb * 4); }
-static size_t fwd_cand_bytes(const Derived& o) { return align256((size_t)o.b * o.hq * (size_t)o.nkb * o.NW32 * 4); }
+static size_t fwd_wmax_bytes(const Derived& o) { return align256((size_t)o.b * o.hq * (size_t)o.nkb * o.NW32 * 4); }
 static size_t fwd_ws(const Derived& o) {
-  return 2 * fwd_kv_bytes(o) + fwd_dmax_bytes(o) + fwd_cand_bytes(o) + align256((size_t)o.b * o.hq * o.n * 8);
+  return 2 * fwd_kv_bytes(o) + fwd_dmax_bytes(o) + fwd_wmax_bytes(o) + align256((size_t)o.b * o.hq * o.n * 8);
 }
 
 // backward workspace: delta, transposed mask, then fragment-major copies of Q and dO
@@ -328,8 +328,8 @@ entmax_status entmax_attn_fwd(const entmax_attn_desc* desc, const void* q, const
   p.q = q; p.kf = wsb; p.vf = wsb + fwd_kv_bytes(o); p.o = (float*)o_; p.tau = tau; p.mask = block_mask; p.aux = (float*)aux;
   p.hist = hist_counts; p.tau_h = tau_h; p.stats = (unsigned long long*)stats;
   p.dmax = (float*)(wsb + 2 * fwd_kv_bytes(o));
-  p.cand = (uint32_t*)(wsb + 2 * fwd_kv_bytes(o) + fwd_dmax_bytes(o));
-  p.tauh_ws = (float2*)(wsb + 2 * fwd_kv_bytes(o) + fwd_dmax_bytes(o) + fwd_cand_bytes(o));
+  p.wmax = (float*)(wsb + 2 * fwd_kv_bytes(o) + fwd_dmax_bytes(o));
+  p.tauh_ws = (float2*)(wsb + 2 * fwd_kv_bytes(o) + fwd_dmax_bytes(o) + fwd_wmax_bytes(o));
   p.b = o.b; p.hq = o.hq; p.hkv = o.hkv; p.n = o.n; p.G = o.G;
   p.causal = o.causal; p.Br = o.Br; p.Bc = o.Bc; p.B = o.B; p.max_iters = o.max_iters;
   p.tau_init = o.tau_init;

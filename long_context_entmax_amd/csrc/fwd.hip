@@ -86,7 +86,7 @@ __global__ __launch_bounds__((64 * hist_waves<T, D>()), (hist_occ<T, D>())) void
   uint32_t* hist = lds + (w * (B + 2)) * 64;   // [B + 2][64] of this wave
   for (int i = lane; i < (B + 2) * 64; i += 64) hist[i] = 0;
   float* dmx = p.dmax + (bh * p.nkb + (row0 >> 5)) * p.nkb;
-  uint32_t* cw_out = p.cand + (bh * p.nkb + (row0 >> 5)) * p.NW32;
+  float* wx_out = p.wmax + (bh * p.nkb + (row0 >> 5)) * p.NW32;
 
   // clear the block-mask words of this work group's tiles (k_refine_out ORs bits in)
   {
@@ -135,7 +135,6 @@ __global__ __launch_bounds__((64 * hist_waves<T, D>()), (hist_occ<T, D>())) void
 #pragma unroll
   for (int r = 0; r < 16; ++r) negb[r] = (float)B;
   uint32_t* const hl = hist + lane;          // this lane's column: cell j at hl[64 j]
-  uint32_t cword = 0;
   float dreg = -INFINITY; // lane j < 32 keeps the chunk max of sub-block 32*word + j
   unsigned long long n_cand = 0;
 
@@ -197,12 +196,10 @@ __global__ __launch_bounds__((64 * hist_waves<T, D>()), (hist_occ<T, D>())) void
       pair_max_dpp(t0, t1, cm0, cm1);
       if (b0) {
         write_lane(dreg, cm0, kb & 31);
-        cword |= 1u << (kb & 31);
         ++n_cand;
       }
       if (b1) {
         write_lane(dreg, cm1, (kb + 1) & 31);
-        cword |= 1u << ((kb + 1) & 31);
         ++n_cand;
       }
       const bool act = act0 || act1;
@@ -247,12 +244,14 @@ __global__ __launch_bounds__((64 * hist_waves<T, D>()), (hist_occ<T, D>())) void
         }
       }
     }
-    // flush a finished word of sub-block bits and chunk maxima (pairs never straddle a
-    // word; the word is complete once its lowest sub-block, kb == 0 mod 32, is done)
+    // flush a finished word of chunk maxima and its own maximum (-inf: no candidate in the
+    // word; pairs never straddle a word, which is complete once its lowest sub-block,
+    // kb == 0 mod 32, is done)
     if ((kb & 31) == 0) {
-      if (lane == 0) cw_out[kb >> 5] = cword;
+      float wm, wm_hi;
+      pair_max_dpp(dreg, dreg, wm, wm_hi);   // lanes 32..63 of dreg stay -inf
+      if (lane == 0) wx_out[kb >> 5] = wm;
       if (lane < 32 && kb + lane < kb_end) dmx[kb + lane] = dreg;
-      cword = 0;
       dreg = -INFINITY;
     }
   }
@@ -320,7 +319,7 @@ __global__ __launch_bounds__(64 * OUT_WAVES, 2) void k_refine_out(FwdParams p) {
   const T* Kf = reinterpret_cast<const T*>(p.kf) + ((size_t)(bi * p.hkv + kvh) * n) * D;
   const T* Vf = reinterpret_cast<const T*>(p.vf) + ((size_t)(bi * p.hkv + kvh) * n) * D;
   const float* dmx = p.dmax + (bh * p.nkb + chunk) * p.nkb;
-  const uint32_t* cwords = p.cand + (bh * p.nkb + chunk) * p.NW32;
+  const float* wmx = p.wmax + (bh * p.nkb + chunk) * p.NW32;
 
   Frag<T> qf[DS];
 #pragma unroll
@@ -343,23 +342,29 @@ __global__ __launch_bounds__(64 * OUT_WAVES, 2) void k_refine_out(FwdParams p) {
   else st = State::from_hist(hm.x, B);
   float& tau = st.tau;
 
-  // Walk over the sub-blocks a pass needs: candidate bits of the histogram pass, kept
-  // where the recorded chunk max exceeds the threshold (read 32 at a time).
+  // Walk over the sub-blocks a pass needs: those whose recorded chunk maximum exceeds the
+  // threshold (non-candidates hold -inf). Words of 32 sub-blocks are screened 64 at a time
+  // through their maxima (one load per lane), so a pass loads the chunk maxima of the words
+  // it needs only.
   struct Walk {
-    int wi;
-    uint32_t word;
-  };
-  auto needed_word = [&](int wi, float thr) -> uint32_t {
-    const uint32_t cw = uniform_u32(cwords[wi]);
-    if (cw == 0) return 0u;
-    const int kbl = wi * 32 + (lane & 31);
-    const float dv = (kbl < kb_end) ? dmx[kbl] : -INFINITY;
-    return cw & (uint32_t)ballot(dv > thr);
+    int g;          // group of 64 words being walked
+    uint64_t nm;    // its needed words not yet started
+    int wi;         // current word
+    uint32_t word;  // its needed sub-blocks not yet taken
   };
   auto walk_next = [&](Walk& wk, float thr) -> int {
     while (wk.word == 0) {
-      if (++wk.wi >= nwords) return -1;
-      wk.word = needed_word(wk.wi, thr);
+      while (wk.nm == 0) {
+        if (64 * (++wk.g) >= nwords) return -1;
+        const int wl = 64 * wk.g + lane;
+        const float wm = wl < nwords ? wmx[wl] : -INFINITY;
+        wk.nm = ballot(wm > thr);
+      }
+      wk.wi = 64 * wk.g + __builtin_ctzll(wk.nm);
+      wk.nm &= wk.nm - 1;
+      const int kbl = wk.wi * 32 + (lane & 31);
+      const float dv = kbl < kb_end ? dmx[kbl] : -INFINITY;
+      wk.word = (uint32_t)ballot(dv > thr);
     }
     const int kb = wk.wi * 32 + __builtin_ctz(wk.word);
     wk.word &= wk.word - 1;
@@ -404,7 +409,7 @@ __global__ __launch_bounds__(64 * OUT_WAVES, 2) void k_refine_out(FwdParams p) {
     PassSums sums;
     MultiSums<ALPHA2_POINTS> msums;
     const float thi = st.hi - st.tau;    // secant start: f at the bracket's upper end
-    Walk wk{-1, 0u};
+    Walk wk{-1, 0ull, -1, 0u};
     int kb = walk_next(wk, thr);
     if (kb >= 0) Ops::load_k(kf, Kf, kb, c, h);
     while (kb >= 0) {
@@ -481,7 +486,7 @@ __global__ __launch_bounds__(64 * OUT_WAVES, 2) void k_refine_out(FwdParams p) {
 #pragma unroll
         for (int m = 0; m < 2; ++m) load_frag(dst[dc][m], vp + (dc * 2 + m) * 512 + lane * 8);
     };
-    Walk wk{-1, 0u};
+    Walk wk{-1, 0ull, -1, 0u};
     int kb = walk_next(wk, othr);
     if (kb >= 0) {
       Ops::load_k(kf, Kf, kb, c, h);

@@ -54,7 +54,7 @@ struct FwdParams {
   float* tau_h;          // optional [b, hq, n]
   unsigned long long* stats;  // optional [32]
   float* dmax;           // workspace: per (32-row chunk, 32-key sub-block) max of x*B
-  uint32_t* cand;        // workspace: candidate sub-block bits per 32-row chunk [b*hq][n/32][NW32]
+  float* wmax;           // workspace: per (32-row chunk, word of 32 sub-blocks) max of dmax [b*hq][n/32][NW32]
   float2* tauh_ws;       // workspace: (tau_h, x_max) per row [b*hq*n]
   int b, hq, hkv, n, G;
   int causal, Br, Bc, B, max_iters;

@@ -75,19 +75,33 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void k_bwd_dkv(BwdParams p)
   // with bit J in the head's column mask, each 32-row chunk qc of I -- every NS-th, none
   // above the diagonal. The next item's Q rows (the first operand needed) are loaded while
   // the current item is multiplied.
-  int t = 0, g = 0, wi = 0, I = 0, qc = QCB;
-  const uint32_t* colw = p.maskT + ((size_t)(bi * p.hq + kvh * p.G) * p.Tc + J) * p.WT;
-  uint32_t word = uniform_u32(colw[0]);
+  // Under the causal mask the query tiles before the one holding key J*Bc have no bit: the
+  // walk starts at that tile's word. The mask word after the current one is loaded ahead.
+  const int ws = p.causal ? ((J * p.Bc / p.Br) >> 5) : 0;
+  auto word_at = [&](int gg, int ww) -> uint32_t {
+    return uniform_u32(p.maskT[((size_t)(bi * p.hq + kvh * p.G + gg) * p.Tc + J) * p.WT + ww]);
+  };
+  auto advance = [&](int& gg, int& ww) {
+    if (++ww >= p.WT) {
+      ww = ws;
+      ++gg;
+    }
+  };
+  int t = 0, g = 0, wi = ws, I = 0, qc = QCB;
+  uint32_t word = word_at(0, ws);
+  int gn = 0, wn = ws;                  // position of the word loaded ahead
+  advance(gn, wn);
+  uint32_t wnx = gn < p.G ? word_at(gn, wn) : 0u;
   auto next_item = [&](int& gi, int& q0i) -> bool {
     for (;;) {
       if (qc >= QCB) {
         while (word == 0) {
-          if (++wi >= p.WT) {
-            if (++g >= p.G) return false;
-            wi = 0;
-            colw = p.maskT + ((size_t)(bi * p.hq + kvh * p.G + g) * p.Tc + J) * p.WT;
-          }
-          word = uniform_u32(colw[wi]);
+          if (gn >= p.G) return false;
+          g = gn;
+          wi = wn;
+          word = wnx;
+          advance(gn, wn);
+          wnx = gn < p.G ? word_at(gn, wn) : 0u;
         }
         I = wi * 32 + __builtin_ctz(word);
         word &= word - 1;
@@ -286,14 +300,19 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void k_bwd_dq(BwdParams p) 
   // This wave's items in list order: the 32-key sub-blocks ks of each set key block J of the
   // row's mask, every NS-th, none above the diagonal. The next item's K fragments (the first
   // operand needed) are loaded while the current item is multiplied.
+  // Under the causal mask no key block after the one holding the tile's last row has a bit:
+  // the walk ends at that block's word. The mask word after the current one is loaded ahead.
+  const int wend = p.causal ? min(p.W, (((I * p.Br + p.Br - 1) / p.Bc) >> 5) + 1) : p.W;
   int wi = 0, t = 0, ks = KC, J = 0;
   uint32_t word = uniform_u32(roww[0]);
+  uint32_t wnx = wend > 1 ? uniform_u32(roww[1]) : 0u;
   auto next_item = [&](int& kbk) -> bool {
     for (;;) {
       if (ks >= KC) {
         while (word == 0) {
-          if (++wi >= p.W) return false;
-          word = uniform_u32(roww[wi]);
+          if (++wi >= wend) return false;
+          word = wnx;
+          wnx = wi + 1 < wend ? uniform_u32(roww[wi + 1]) : 0u;
         }
         J = wi * 32 + __builtin_ctz(word);
         word &= word - 1;

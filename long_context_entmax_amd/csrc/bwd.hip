@@ -76,32 +76,21 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void k_bwd_dkv(BwdParams p)
   // above the diagonal. The next item's Q rows (the first operand needed) are loaded while
   // the current item is multiplied.
   // Under the causal mask the query tiles before the one holding key J*Bc have no bit: the
-  // walk starts at that tile's word. The mask word after the current one is loaded ahead.
+  // walk over each head's words starts at that tile's word.
   const int ws = p.causal ? ((J * p.Bc / p.Br) >> 5) : 0;
-  auto word_at = [&](int gg, int ww) -> uint32_t {
-    return uniform_u32(p.maskT[((size_t)(bi * p.hq + kvh * p.G + gg) * p.Tc + J) * p.WT + ww]);
-  };
-  auto advance = [&](int& gg, int& ww) {
-    if (++ww >= p.WT) {
-      ww = ws;
-      ++gg;
-    }
-  };
   int t = 0, g = 0, wi = ws, I = 0, qc = QCB;
-  uint32_t word = word_at(0, ws);
-  int gn = 0, wn = ws;                  // position of the word loaded ahead
-  advance(gn, wn);
-  uint32_t wnx = gn < p.G ? word_at(gn, wn) : 0u;
+  const uint32_t* colw = p.maskT + ((size_t)(bi * p.hq + kvh * p.G) * p.Tc + J) * p.WT;
+  uint32_t word = uniform_u32(colw[ws]);
   auto next_item = [&](int& gi, int& q0i) -> bool {
     for (;;) {
       if (qc >= QCB) {
         while (word == 0) {
-          if (gn >= p.G) return false;
-          g = gn;
-          wi = wn;
-          word = wnx;
-          advance(gn, wn);
-          wnx = gn < p.G ? word_at(gn, wn) : 0u;
+          if (++wi >= p.WT) {
+            if (++g >= p.G) return false;
+            wi = ws;
+            colw = p.maskT + ((size_t)(bi * p.hq + kvh * p.G + g) * p.Tc + J) * p.WT;
+          }
+          word = uniform_u32(colw[wi]);
         }
         I = wi * 32 + __builtin_ctz(word);
         word &= word - 1;

@@ -262,3 +262,40 @@ def test_max_seqlen():
     assert np.abs(to64(r.o[0, 0])[rows] - ref["o"]).max() < 1e-2
     th = to64(r.tau_h[0, 0])[rows]
     assert np.all(th <= ref["tau"] + 1e-4) and np.all(th > ref["tau"] - 1.0 / 16 - 1e-4)
+
+
+def test_long_noncausal():
+    """2^17 keys without the causal mask (one head): every 32-row chunk walks 128 words of 32
+    sub-blocks, two screening groups, in each refinement pass, and the backward walks whole
+    mask rows and columns. Sampled query tiles against the oracle (tau, O, dQ, the histogram
+    bound), and the gradient sums that hold at any size: the dK rows cancel and the dV rows add
+    up to the sum of dO (each row of P sums to one)."""
+    n = 1 << 17
+    w = synth.Workload("t", 1, 1, 1, n, 64, "bf16", 1.5, False, 64, 64, 16, "normal",
+                       extra={"qk_scale": 2.0}, seed=23)
+    print(f"[case] long non-causal {n}", flush=True)
+    inp = synth.make_inputs(w)
+    d = torch.device("cuda:0")
+    q, k, v, do = (inp[x].to(d) for x in ("q", "k", "v", "do"))
+    r = lce.fwd(q, k, v, w.alpha, False, (64, 64), 16, return_hist=True)
+    dq, dk, dv = lce.bwd(q, k, v, do, r.tau, r.mask, r.aux, w.alpha, False, (64, 64), 16)
+    torch.cuda.synchronize()
+    q64, k64, v64, do64 = (to64(inp[x][0, 0]) for x in ("q", "k", "v", "do"))
+    rows = np.concatenate([np.arange(0, 64), np.arange(n // 2, n // 2 + 64), np.arange(n - 64, n)])
+    scale = 1.0 / math.sqrt(64)
+    ref = oracle.attn_fwd_head(q64, k64, v64, w.alpha, False, 16, 64, scale, rows=rows)
+    rb = oracle.attn_bwd_rows_head(q64, k64, v64, do64, ref["tau"], w.alpha, False, scale,
+                                   rows=ref["rows"])
+    rows = ref["rows"]
+    assert np.abs(to64(r.tau[0, 0])[rows] - ref["tau"]).max() < 1e-3
+    assert np.abs(to64(r.o[0, 0])[rows] - ref["o"]).max() < 1e-2
+    assert rel_fro(to64(dq[0, 0])[rows], rb["dq"]) < 2e-2
+    th = to64(r.tau_h[0, 0])[rows]
+    assert np.all(th <= ref["tau"] + 1e-4) and np.all(th > ref["tau"] - 1.0 / 16 - 1e-4)
+    dk_all, dv_all = to64(dk[0, 0]), to64(dv[0, 0])
+    err_k = float((np.abs(dk_all.sum(axis=0)) / np.abs(dk_all).sum(axis=0)).max())
+    sum_do = do64.sum(axis=0)
+    err_v = float(np.abs(dv_all.sum(axis=0) - sum_do).max() / np.abs(sum_do).max())
+    print(f"[case] long non-causal: sum dK {err_k:.2e}, sum dV vs sum dO {err_v:.2e}", flush=True)
+    assert err_k <= 2.0 ** -6
+    assert err_v <= 1e-2

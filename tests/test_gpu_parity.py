@@ -264,13 +264,14 @@ def test_max_seqlen():
     assert np.all(th <= ref["tau"] + 1e-4) and np.all(th > ref["tau"] - 1.0 / 16 - 1e-4)
 
 
-def test_long_noncausal():
-    """2^17 keys without the causal mask (one head): every 32-row chunk walks 128 words of 32
-    sub-blocks, two screening groups, in each refinement pass, and the backward walks whole
-    mask rows and columns. Sampled query tiles against the oracle (tau, O, dQ, the histogram
-    bound), and the gradient sums that hold at any size: the dK rows cancel and the dV rows add
-    up to the sum of dO (each row of P sums to one)."""
-    n = 1 << 17
+@pytest.mark.parametrize("n", [1 << 17, 65 * 1024])
+def test_long_noncausal(n):
+    """Long sequences without the causal mask (one head): every 32-row chunk walks all n/1024
+    words of 32 sub-blocks in each refinement pass, screened 64 words at a time (2^17 keys:
+    two whole groups; 65 * 1024: a whole group and a one-word group), and the backward walks
+    whole mask rows and columns. Sampled query tiles against the oracle (tau, O, dQ, the
+    histogram bound), and the gradient sums that hold at any size: the dK rows cancel and the
+    dV rows add up to the sum of dO (each row of P sums to one)."""
     w = synth.Workload("t", 1, 1, 1, n, 64, "bf16", 1.5, False, 64, 64, 16, "normal",
                        extra={"qk_scale": 2.0}, seed=23)
     print(f"[case] long non-causal {n}", flush=True)

@@ -2,16 +2,23 @@
 
 A step is one forward and one backward of the whole hot path (histogram pass,
 refinement, output pass, backward preparation, dK/dV and dQ kernels) over one
-batch of synthetic inputs resident in HBM. The default workload is the 4K-token
-configuration (batch 4, 8 heads, n 4096, d 64, bf16, causal, alpha 1.5, 64x64
-blocks, B 16) with the centroid-cluster generator calibrated to ~90% block
-sparsity; ``--config C3|C4|C5`` and ``--alpha``/``--sparsity`` select the others.
+batch of synthetic inputs resident in HBM. The default workload is the largest
+single-GPU configuration of the 4K-128K study: the LLaMA-3-1B-shaped layer at 128K
+tokens (batch 1, 32 query / 8 KV heads, d 64, bf16, causal, alpha 1.5, 64x64 blocks,
+B 16) with the centroid-cluster generator calibrated to ~97% block sparsity;
+``--config C2|C3|C4`` and ``--alpha``/``--sparsity`` select the others.
 
 Prints one JSON line: value = effective TFLOP/s (dense-equivalent FLOPs of a causal
 attention fwd+bwd, 3.5 x 4 b h n^2 d / 2, divided by the measured step time),
 plus a roofline object for the dominant kernel (algorithmic MFMA FLOPs per launch
-over its HIP-event-timed average duration) and the CPU oracle timed on a bounded
-sample of the same workload.
+over its HIP-event-timed average duration), the MFMA utilisation on the non-zero
+blocks, and the CPU oracle timed on a bounded sample of the same workload.
+
+``--dense`` runs the ablation without block skipping (every causally valid block is
+multiplied; outputs are unchanged). ``--sweep`` times every configured point of the
+block-sparsity study (and the extra sweep points), each with and without skipping,
+fits step time against the non-zero block count per sweep, and prints one JSON line
+per point plus a summary line (not the default line; ``--sweep-md`` writes a table).
 """
 from __future__ import annotations
 
@@ -38,7 +45,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", default="C2")
+    ap.add_argument("--config", default="C5")
     ap.add_argument("--alpha", type=float, default=None)
     ap.add_argument("--sparsity", type=float, default=None)
     ap.add_argument("--tau-init", choices=("hist", "bracket"), default="hist",
@@ -47,6 +54,12 @@ def parse():
     ap.add_argument("--nape", action="store_true",
                     help="NAPE heads: the first half of the query heads without position "
                          "encoding, the second half ALiBi (per-head slopes of the scores)")
+    ap.add_argument("--dense", action="store_true",
+                    help="ablation: no block skipping (every causally valid block multiplied)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="time every point of the block-sparsity study, with and without skipping, "
+                         "and fit step time against the non-zero block count")
+    ap.add_argument("--sweep-md", default=None, help="with --sweep: write a markdown table here")
     ap.add_argument("--decode", action="store_true",
                     help="time one decode step (a new query row per head against the workload's "
                          "K/V as a cache) instead of the training step")
@@ -97,48 +110,127 @@ def popcount_mask(mask) -> int:
     return int(cnt.sum().item())
 
 
+def cpu_threads():
+    """Threads the oracle may use: the cores this process may run on, at most 16 (the CPU
+    share of one GPU on a shared host), and the host's total core count."""
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count() or 1
+    return max(1, min(16, avail)), os.cpu_count() or avail
+
+
+def valid_pairs(w) -> float:
+    """Causally valid (query, key) pairs over all query heads."""
+    n = float(w.seqlen)
+    per = n * (n + 1) / 2.0 if w.causal else n * n
+    return per * w.batch * w.heads_q
+
+
 def cpu_baseline(w, inp_cpu, target_s: float):
-    """Time the fp64 oracle (fwd + bwd) on whole query heads until ~target_s, extrapolate."""
+    """The fp64 oracle's fwd+bwd on a bounded sample of the workload, extrapolated.
+
+    Row side (forward: scores, tau by bisection, o, histogram; backward per row: dq and
+    delta): 64-row query tiles evenly spaced over all (batch, head, tile) indices, the
+    spacing halved until about 2/3 of the time budget is spent; the time per row is
+    extrapolated to all rows (even spacing samples the causal row lengths). Key side (dk, dv per key, summed
+    over the GQA group): the last m keys of KV head 0 of batch 0 -- under the causal mask
+    they need tau and delta only of the last m rows, which the oracle computes first
+    (untimed) -- with m doubled until about 1/3 of the budget is spent; the time per
+    valid (row, key) pair is extrapolated to all valid pairs."""
+    import numpy as np
     import oracle
-    threads = oracle.default_threads()
+    threads, host_cores = cpu_threads()
     G = w.heads_q // w.heads_kv
     scale = 1.0 / math.sqrt(w.head_dim)
-    heads_done = 0
-    t0 = time.time()
-    for bi in range(w.batch):
-        for h in range(w.heads_q):
-            if heads_done > 0 and time.time() - t0 > target_s:
-                break
-            kh = h // G
-            qh = inp_cpu["q"][bi, h].double().numpy()
-            kk = inp_cpu["k"][bi, kh].double().numpy()
-            vv = inp_cpu["v"][bi, kh].double().numpy()
-            do = inp_cpu["do"][bi, h].double().numpy()
-            f = oracle.attn_fwd_head(qh, kk, vv, w.alpha, w.causal, w.n_bins, w.block_k, scale,
+    n, b, hq = w.seqlen, w.batch, w.heads_q
+    q64 = {}
+
+    def qh(bi, h):
+        if (bi, h) not in q64:
+            q64[(bi, h)] = (inp_cpu["q"][bi, h].double().numpy(), inp_cpu["do"][bi, h].double().numpy())
+        return q64[(bi, h)]
+
+    kv64 = {}
+
+    def kvh(bi, kh):
+        if (bi, kh) not in kv64:
+            kv64[(bi, kh)] = (inp_cpu["k"][bi, kh].double().numpy(), inp_cpu["v"][bi, kh].double().numpy())
+        return kv64[(bi, kh)]
+
+    total_rows = b * hq * n
+    tile = min(64, n)
+    ntiles = total_rows // tile
+    rows_done, t_rows, step = 0, 0.0, 1
+    while step * 2 <= ntiles // 16:
+        step *= 2
+    while t_rows < target_s * 2.0 / 3.0 and step >= 1:
+        flat = np.arange(step // 2, ntiles, step, dtype=np.int64) if step > 1 else np.arange(ntiles)
+        by_head = {}
+        for u in flat.tolist():
+            r0 = u * tile
+            by_head.setdefault((r0 // (hq * n), (r0 // n) % hq), []).extend(range(r0 % n, r0 % n + tile))
+        for (bi, h), rows in by_head.items():
+            qq, do = qh(bi, h)
+            kk, vv = kvh(bi, h // G)
+            t0 = time.time()
+            f = oracle.attn_fwd_head(qq, kk, vv, w.alpha, w.causal, w.n_bins, w.block_k, scale, rows=rows,
                                      threads=threads)
-            r = oracle.attn_bwd_rows_head(qh, kk, vv, do, f["tau"], w.alpha, w.causal, scale,
-                                          threads=threads)
-            # the key-side backward of this query head's share of its KV head
-            oracle.attn_bwd_keys_group(qh[None], kk, vv, do[None], f["tau"][None], r["delta"][None],
-                                       w.alpha, w.causal, scale, threads=threads)
-            heads_done += 1
-    el = time.time() - t0
-    total_heads = w.batch * w.heads_q
-    s_per_step = el * total_heads / heads_done
+            oracle.attn_bwd_rows_head(qq, kk, vv, do, f["tau"], w.alpha, w.causal, scale, rows=f["rows"],
+                                      threads=threads)
+            t_rows += time.time() - t0
+        rows_done += flat.size * tile
+        if step == 1:
+            break
+        step //= 2
+    s_rows = t_rows / rows_done * total_rows
+
+    # key side
+    kk, vv = kvh(0, 0)
+    qg = np.stack([qh(0, g)[0] for g in range(G)])
+    dog = np.stack([qh(0, g)[1] for g in range(G)])
+    m, t_keys, pairs_done = 16, 0.0, 0.0
+    while True:
+        m = min(m, n)
+        rows = np.arange(n - m, n) if w.causal else np.arange(n)
+        taug = np.full((G, n), np.inf)
+        deltag = np.zeros((G, n))
+        for g in range(G):
+            f = oracle.attn_fwd_head(qg[g], kk, vv, w.alpha, w.causal, w.n_bins, w.block_k, scale, rows=rows,
+                                     threads=threads)
+            rb = oracle.attn_bwd_rows_head(qg[g], kk, vv, dog[g], f["tau"], w.alpha, w.causal, scale,
+                                           rows=f["rows"], threads=threads)
+            taug[g, f["rows"]] = f["tau"]
+            deltag[g, f["rows"]] = rb["delta"]
+        keys = np.arange(n - m, n)
+        t0 = time.time()
+        oracle.attn_bwd_keys_group(qg, kk, vv, dog, taug, deltag, w.alpha, w.causal, scale, keys=keys,
+                                   threads=threads)
+        t_keys = time.time() - t0
+        pairs_done = G * (m * (m + 1) / 2.0 if w.causal else float(m) * n)
+        if t_keys >= target_s / 3.0 or m >= n or not w.causal:
+            break
+        m *= 2
+    s_keys = t_keys / pairs_done * valid_pairs(w)
+    s_per_step = s_rows + s_keys
     return {
         "value": dense_eq_flops(w) / s_per_step / 1e12,
         "unit": "TFLOP/s (effective)",
         "ms_per_step": s_per_step * 1e3,
         "cores": threads,
+        "host_cores": host_cores,
         "kind": "oracle",
-        "sample": f"{heads_done} of {total_heads} query heads, full length, fwd+bwd, {el:.1f} s, "
-                  f"extrapolated linearly to all heads",
+        "extrapolated": True,
+        "sample": (f"fp64 oracle on {threads} threads ({host_cores} host cores): fwd + per-row bwd of "
+                   f"{rows_done} of {total_rows} query rows (64-row tiles evenly spaced over all heads), {t_rows:.1f} s, "
+                   f"per row x all rows = {s_rows:.0f} s); dK/dV of the last {m} keys of one KV group "
+                   f"({t_keys:.1f} s, per valid (row, key) pair x all pairs = {s_keys:.0f} s)"),
     }
 
 
 def tau_error_study(lce, w, q, k, v, blk, wsf):
     """Mean absolute error of tau per refinement pass, histogram start vs plain bracket
-    (the study of the pages' Fig. 3, page 5 section 4). tau* is the histogram-started solve
+    (the study of the pages' Fig. 3, AdaSplash-2 (es) §4). tau* is the histogram-started solve
     with the largest pass cap; the bracket-started solve at that cap is reported beside it."""
     import torch
     b, hq, n, d = q.shape
@@ -328,6 +420,209 @@ def dash_bench(args, lce, dev):
     print(json.dumps(line), flush=True)
 
 
+
+
+def make_problem(lce, w, dev, tau_init: int = 0, nape: bool = False):
+    """Inputs, outputs and workspaces of one workload, resident on the device."""
+    import torch
+    import synth
+    inp = synth.make_inputs(w, device=dev)
+    q = inp["q"]
+    b, hq, n, d = q.shape
+    blk = (w.block_q, w.block_k)
+    Tr, W = lce.mask_shape(n, blk)
+    outs = lce.FwdOut(torch.empty(q.shape, dtype=torch.float32, device=dev),
+                      torch.empty((b, hq, n), dtype=torch.float32, device=dev),
+                      torch.empty((b, hq, Tr, W), dtype=torch.int32, device=dev),
+                      torch.empty((b, hq, n, d), dtype=torch.float32, device=dev), None, None)
+    grads = (torch.empty_like(q), torch.empty_like(inp["k"]), torch.empty_like(inp["v"]))
+    slopes = (torch.tensor(lce.nape_slopes(hq), dtype=torch.float32, device=dev) if nape else None)
+    desc = lce._desc_for(q, inp["k"], w.alpha, w.causal, blk, w.n_bins, None, 0, 0.0, tau_init)
+    fws, bws = lce.workspace_bytes(desc)
+    return {"inp": inp, "outs": outs, "grads": grads, "slopes": slopes, "tau_init": tau_init, "blk": blk,
+            "wsf": torch.empty(max(fws, 256), dtype=torch.uint8, device=dev),
+            "wsb": torch.empty(max(bws, 256), dtype=torch.uint8, device=dev)}
+
+
+def time_point(lce, w, prob, steps: int, warmup: int, dense: bool = False, copy_probe_mib: int = 0):
+    """Warm up, time `steps` fwd+bwd steps between synchronisations, then the same steps with
+    HIP events around every kernel, then one untimed step for the method's statistics."""
+    import torch
+    inp, outs, grads, blk = prob["inp"], prob["outs"], prob["grads"], prob["blk"]
+    q, k, v, do = inp["q"], inp["k"], inp["v"], inp["do"]
+    dev = q.device
+
+    def step(stats=None):
+        r = lce.fwd(q, k, v, w.alpha, w.causal, blk, w.n_bins, workspace=prob["wsf"], out=outs, stats=stats,
+                    tau_init=prob["tau_init"], slopes=prob["slopes"], dense=dense)
+        lce.bwd(q, k, v, do, r.tau, r.mask, r.aux, w.alpha, w.causal, blk, w.n_bins, workspace=prob["wsb"],
+                out=grads, slopes=prob["slopes"], dense=dense)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.time()
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.time() - t0
+    ms = e0.elapsed_time(e1) / steps
+    if copy_probe_mib > 0:
+        nel = copy_probe_mib * (1 << 20) // 4
+        src = torch.ones(nel, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+    # per-kernel HIP-event timing (same steps, separate loop, events recorded on the stream
+    # each kernel is launched on)
+    lce.profile(True)
+    lce.profile_read()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ktimes = lce.profile_read()
+    lce.profile(False)
+    stats = torch.zeros(32, dtype=torch.int64, device=dev)
+    step(stats)
+    torch.cuda.synchronize()
+    st = stats.cpu().tolist()
+    b, hq, n, d = q.shape
+    nnzb = popcount_mask(outs.mask)
+    nvb = valid_blocks(w) * b * hq
+    blockflop = 2.0 * w.block_q * w.block_k * d
+    subflop = 2.0 * 32 * 32 * d
+    # algorithmic MFMA FLOPs per launch: one 32x32xd score product per sub-block the
+    # histogram pass scores and per refinement visit, a score and a P.V product per
+    # output visit, and per non-zero Br x Bc block 4 products in dK/dV and 3 in dQ
+    alg = {
+        "entmax_fwd_hist": subflop * st[20],
+        "entmax_fwd_refine_out": subflop * (st[21] + 2 * st[22]),
+        "entmax_bwd_dkv": 4 * blockflop * nnzb,
+        "entmax_bwd_dq": 3 * blockflop * nnzb,
+    }
+    kern = {name: tt / max(c, 1) for name, (tt, c) in ktimes.items()}
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
+    # MFMA utilisation on the non-zero blocks: the 10 products of a non-zero block (3
+    # forward, 7 backward) over the time of the kernels that multiply blocks (refinement
+    # and output, dK/dV, dQ), against the dtype's dense peak
+    t_blk = sum(kern.get(nm, 0.0) for nm in ("entmax_fwd_refine_out", "entmax_bwd_dkv", "entmax_bwd_dq"))
+    sbu = 10.0 * blockflop * nnzb / (t_blk * 1e-3) / 1e12 / peak if t_blk > 0 else None
+    return {"ms": ms, "wall": wall, "kern": kern, "alg": alg, "stats": st, "nnzb": nnzb, "nvb": nvb,
+            "sparsity": 1.0 - nnzb / nvb, "peak": peak, "sparse_block_mfma_util": sbu}
+
+
+def workload_label(w):
+    return (f"{w.name}: b{w.batch} hq{w.heads_q}/hkv{w.heads_kv} n{w.seqlen} d{w.head_dim} "
+            f"{w.dtype} {'causal' if w.causal else 'full'} alpha {w.alpha:g} blocks "
+            f"{w.block_q}x{w.block_k} B {w.n_bins}")
+
+
+SWEEP_POINTS = [
+    # (workload, alpha, target block sparsity, configured point of the study?)
+    ("C1", None, None, True),
+    ("C2", 1.5, 0.0, True), ("C2", 1.5, 0.3, False), ("C2", 1.5, 0.6, True), ("C2", 1.5, 0.8, False),
+    ("C2", 1.5, 0.9, True), ("C2", 1.5, 0.95, False),
+    ("C2", 2.0, 0.0, True), ("C2", 2.0, 0.3, False), ("C2", 2.0, 0.6, True), ("C2", 2.0, 0.8, False),
+    ("C2", 2.0, 0.9, True), ("C2", 2.0, 0.95, False),
+    ("C3", 1.5, 0.6, True), ("C3", 1.5, 0.7, False), ("C3", 1.5, 0.8, True), ("C3", 1.5, 0.9, False),
+    ("C3", 1.5, 0.95, True),
+    ("C4", 2.0, 0.95, True),
+    ("C5", 1.5, 0.97, True),
+]
+
+
+def fit_line(xs, ys):
+    """Least-squares t = a + b x and its R^2."""
+    nn = len(xs)
+    mx, my = sum(xs) / nn, sum(ys) / nn
+    sxx = sum((x - mx) ** 2 for x in xs)
+    sxy = sum((x - mx) * (y - my) for x, y in zip(xs, ys))
+    bb = sxy / sxx if sxx > 0 else 0.0
+    aa = my - bb * mx
+    ss_tot = sum((y - my) ** 2 for y in ys)
+    ss_res = sum((y - aa - bb * x) ** 2 for x, y in zip(xs, ys))
+    return aa, bb, (1.0 - ss_res / ss_tot) if ss_tot > 0 else 1.0
+
+
+def sweep(args, lce, dev):
+    import torch
+    import synth
+    from synth.betas import key, load_table
+    table = load_table()
+    rows = []
+    for name, alpha, target, configured in SWEEP_POINTS:
+        if name != "C1" and key(name, alpha, target) not in table:
+            print(json.dumps({"sweep_point": f"{name} alpha {alpha} sparsity {target}",
+                              "skipped": "no calibrated beta"}), flush=True)
+            continue
+        w = synth.workload(name, alpha=alpha, sparsity=target)
+        print(f"[sweep] {workload_label(w)} target sparsity {target}", file=sys.stderr, flush=True)
+        prob = make_problem(lce, w, dev)
+        big = w.seqlen >= 65536
+        steps = 5 if big else args.steps
+        r = time_point(lce, w, prob, steps, 2 if big else args.warmup)
+        # the skipping run's results, to check that the ablation does not change them
+        ref = prob["outs"]
+        o_skip, tau_skip = ref.o.clone(), ref.tau.clone()
+        g_skip = [g.clone() for g in prob["grads"]]
+        rd = time_point(lce, w, prob, 3 if big else max(3, args.steps // 4), 1, dense=True)
+        eff = dense_eq_flops(w) / (r["ms"] * 1e-3) / 1e12
+        alg_total = sum(r["alg"].values())
+        passes = {str(p): r["stats"][p] for p in range(1, 17) if r["stats"][p]}
+        row = {
+            "sweep_point": workload_label(w), "configured_point": configured,
+            "target_block_sparsity": target, "beta": w.beta,
+            "achieved_block_sparsity": round(r["sparsity"], 4), "nonzero_blocks": r["nnzb"],
+            "valid_blocks": r["nvb"], "ms_per_step": round(r["ms"], 4),
+            "effective_tflops": round(eff, 2),
+            "algorithmic_tflops": round(alg_total / (r["ms"] * 1e-3) / 1e12, 2),
+            "algorithmic_frac_of_peak": round(alg_total / (r["ms"] * 1e-3) / 1e12 / r["peak"], 4),
+            "sparse_block_mfma_util": None if r["sparse_block_mfma_util"] is None
+            else round(r["sparse_block_mfma_util"], 4),
+            "kernels_ms": {kk: round(vv, 4) for kk, vv in r["kern"].items()},
+            "refine_passes_rows": passes,
+            "dense_ablation_ms": round(rd["ms"], 4),
+            "dense_ablation_kernels_ms": {kk: round(vv, 4) for kk, vv in rd["kern"].items()},
+            "skip_speedup": round(rd["ms"] / r["ms"], 3),
+        }
+        row["dense_vs_skip_max_abs"] = {
+            "o": float((ref.o - o_skip).abs().max()), "tau": float((ref.tau - tau_skip).abs().max()),
+            "dq": float((prob["grads"][0].float() - g_skip[0].float()).abs().max()),
+            "dk": float((prob["grads"][1].float() - g_skip[1].float()).abs().max()),
+            "dv": float((prob["grads"][2].float() - g_skip[2].float()).abs().max())}
+        print(json.dumps(row), flush=True)
+        rows.append((name, alpha, row))
+        del prob
+        torch.cuda.empty_cache()
+    fits = {}
+    for name, alpha in (("C2", 1.5), ("C2", 2.0), ("C3", 1.5)):
+        pts = [(rw["nonzero_blocks"], rw["ms_per_step"]) for nm, al, rw in rows if nm == name and al == alpha]
+        if len(pts) >= 3:
+            aa, bb, r2 = fit_line([p[0] for p in pts], [p[1] for p in pts])
+            fits[f"{name} alpha {alpha:g}"] = {"points": len(pts), "a_ms": round(aa, 5),
+                                               "b_us_per_kblock": round(bb * 1e6, 4), "r2": round(r2, 5)}
+    print(json.dumps({"sweep_fits": fits}), flush=True)
+    if args.sweep_md:
+        with open(args.sweep_md, "w") as fh:
+            fh.write("| point | configured | sparsity | nnzb | ms/step | eff. TFLOP/s | alg. TFLOP/s | "
+                     "sparse-block MFMA util | dense ablation ms | skip speed-up | passes |\n")
+            fh.write("|---|---|---|---|---|---|---|---|---|---|---|\n")
+            for nm, al, rw in rows:
+                fh.write(f"| {rw['sweep_point']} | {'yes' if rw['configured_point'] else 'extra'} | "
+                         f"{rw['achieved_block_sparsity']} | {rw['nonzero_blocks']} | {rw['ms_per_step']} | "
+                         f"{rw['effective_tflops']} | {rw['algorithmic_tflops']} | "
+                         f"{rw['sparse_block_mfma_util']} | {rw['dense_ablation_ms']} | {rw['skip_speedup']} | "
+                         f"{rw['refine_passes_rows']} |\n")
+            fh.write("\n| sweep | points | a (ms) | b (us per 1000 non-zero blocks) | R^2 |\n|---|---|---|---|---|\n")
+            for kk, vv in fits.items():
+                fh.write(f"| {kk} | {vv['points']} | {vv['a_ms']} | {vv['b_us_per_kblock']} | {vv['r2']} |\n")
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -343,99 +638,34 @@ def main():
     if args.dash:
         dash_bench(args, lce, dev)
         return
+    if args.sweep:
+        sweep(args, lce, dev)
+        return
     w = synth.workload(args.config, alpha=args.alpha, sparsity=args.sparsity)
-    inp = synth.make_inputs(w, device=dev, need_grad_inputs=not args.decode)
     if args.decode:
+        inp = synth.make_inputs(w, device=dev, need_grad_inputs=False)
         decode_bench(args, lce, w, inp, dev)
         return
-    q, k, v, do = inp["q"], inp["k"], inp["v"], inp["do"]
-    blk = (w.block_q, w.block_k)
-    b, hq, n, d = q.shape
-    Tr, W = lce.mask_shape(n, blk)
-    outs = lce.FwdOut(torch.empty(q.shape, dtype=torch.float32, device=dev),
-                      torch.empty((b, hq, n), dtype=torch.float32, device=dev),
-                      torch.empty((b, hq, Tr, W), dtype=torch.int32, device=dev),
-                      torch.empty((b, hq, n, d), dtype=torch.float32, device=dev), None, None)
-    grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
     tau_init = 0 if args.tau_init == "hist" else 1
-    slopes = (torch.tensor(lce.nape_slopes(hq), dtype=torch.float32, device=dev) if args.nape else None)
-    desc = lce._desc_for(q, k, w.alpha, w.causal, blk, w.n_bins, None, 0, 0.0, tau_init)
-    fws, bws = lce.workspace_bytes(desc)
-    wsf = torch.empty(max(fws, 256), dtype=torch.uint8, device=dev)
-    wsb = torch.empty(max(bws, 256), dtype=torch.uint8, device=dev)
-
+    print(f"[bench] {workload_label(w)}", file=sys.stderr, flush=True)
+    prob = make_problem(lce, w, dev, tau_init, args.nape)
     if args.tau_error:
-        print(json.dumps(tau_error_study(lce, w, q, k, v, blk, wsf)), flush=True)
+        inp = prob["inp"]
+        print(json.dumps(tau_error_study(lce, w, inp["q"], inp["k"], inp["v"], prob["blk"], prob["wsf"])),
+              flush=True)
         return
-
-    def step(stats=None):
-        r = lce.fwd(q, k, v, w.alpha, w.causal, blk, w.n_bins, workspace=wsf, out=outs, stats=stats,
-                    tau_init=tau_init, slopes=slopes)
-        lce.bwd(q, k, v, do, r.tau, r.mask, r.aux, w.alpha, w.causal, blk, w.n_bins, workspace=wsb,
-                out=grads, slopes=slopes)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.time()
-    e0.record()
-    for _ in range(args.steps):
-        step()
-    e1.record()
-    torch.cuda.synchronize()
-    wall = time.time() - t0
-    ms = e0.elapsed_time(e1) / args.steps
-
-    if args.copy_probe_mib > 0:
-        nel = args.copy_probe_mib * (1 << 20) // 4
-        src = torch.ones(nel, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            torch.mul(src, 1.0, out=dst)
-        torch.cuda.synchronize()
-        del src, dst
-
-    # per-kernel HIP-event timing (same steps, separate loop, events recorded on the
-    # stream each kernel is launched on)
-    lce.profile(True)
-    lce.profile_read()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    ktimes = lce.profile_read()
-    lce.profile(False)
-    # method statistics from one extra, untimed step
-    stats = torch.zeros(32, dtype=torch.int64, device=dev)
-    step(stats)
-    torch.cuda.synchronize()
-    st = stats.cpu().tolist()
-    nnzb = popcount_mask(outs.mask)
-    nvb = valid_blocks(w) * b * hq
-    sparsity = 1.0 - nnzb / nvb
-    blockflop = 2.0 * w.block_q * w.block_k * d
-    subflop = 2.0 * 32 * 32 * d
-    # algorithmic MFMA FLOPs per launch: one 32x32xd score product per sub-block the
-    # histogram pass scores and per refinement visit, a score and a P.V product per
-    # output visit, and per non-zero 64x64 block 4 products in dK/dV and 3 in dQ
-    alg = {
-        "entmax_fwd_hist": subflop * st[20],
-        "entmax_fwd_refine_out": subflop * (st[21] + 2 * st[22]),
-        "entmax_bwd_dkv": 4 * blockflop * nnzb,
-        "entmax_bwd_dq": 3 * blockflop * nnzb,
-    }
-    kern = {name: {"avg_ms": t / max(c, 1), "launches_per_step": c / args.steps}
-            for name, (t, c) in ktimes.items()}
-    dom = max(alg, key=lambda nm: kern.get(nm, {"avg_ms": 0})["avg_ms"])
-    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
-    achieved = alg[dom] / (kern[dom]["avg_ms"] * 1e-3) / 1e12
+    r = time_point(lce, w, prob, args.steps, args.warmup, dense=args.dense, copy_probe_mib=args.copy_probe_mib)
+    kern, alg, st = r["kern"], r["alg"], r["stats"]
+    ms = r["ms"]
+    dom = max(alg, key=lambda nm: kern.get(nm, 0.0))
+    peak = r["peak"]
+    achieved = alg[dom] / (kern[dom] * 1e-3) / 1e12
     # HBM bytes per launch of the dominant kernel from the committed rocprofv3 counter
     # summary of this workload (FETCH_SIZE + WRITE_SIZE scaled by a copy of known size);
     # null when the kernel sources changed since the counters were taken
     traffic = None
     tfile = os.path.join(ROOT, "profiles", f"entmax_attn_{w.name}_traffic.json")
-    if os.path.exists(tfile):
+    if os.path.exists(tfile) and not args.dense and not args.nape and tau_init == 0:
         with open(tfile) as f:
             tj = json.load(f)
         if tj.get("src_digest") == src_digest() and tj.get("workload") == w.name:
@@ -454,28 +684,29 @@ def main():
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": "synthetic (seeded centroid-cluster generator, beta calibrated to the target block sparsity)",
         "config": {
-            "workload": f"{w.name}: b{w.batch} hq{w.heads_q}/hkv{w.heads_kv} n{w.seqlen} d{w.head_dim} "
-                        f"{w.dtype} {'causal' if w.causal else 'full'} alpha {w.alpha} blocks "
-                        f"{w.block_q}x{w.block_k} B {w.n_bins}",
+            "workload": workload_label(w),
             "tau_start": "histogram" if tau_init == 0 else "plain bracket (ablation)",
             "position_bias": "NAPE (half the heads ALiBi)" if args.nape else "none",
+            "block_skipping": "off (dense ablation)" if args.dense else "on",
             "target_block_sparsity": w.target_sparsity, "beta": w.beta,
-            "achieved_block_sparsity": round(sparsity, 4), "nonzero_blocks": nnzb, "valid_blocks": nvb,
+            "achieved_block_sparsity": round(r["sparsity"], 4), "nonzero_blocks": r["nnzb"],
+            "valid_blocks": r["nvb"],
         },
         "roofline": {
             "kernel": dom, "bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
             "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,
             "algorithmic_flops_per_launch": alg[dom],
         },
-        "kernels_ms": {kk: round(vv["avg_ms"], 4) for kk, vv in kern.items()},
-        "kernel_tflops": {kk: round(alg[kk] / (kern[kk]["avg_ms"] * 1e-3) / 1e12, 2)
-                          for kk in alg if kk in kern},
+        "sparse_block_mfma_util": None if r["sparse_block_mfma_util"] is None
+        else round(r["sparse_block_mfma_util"], 4),
+        "kernels_ms": {kk: round(vv, 4) for kk, vv in kern.items()},
+        "kernel_tflops": {kk: round(alg[kk] / (kern[kk] * 1e-3) / 1e12, 2) for kk in alg if kk in kern},
         "refine_passes_rows": passes,
         "subblock_stats": sub_stats,
-        "wall_s": round(wall, 3),
+        "wall_s": round(r["wall"], 3),
     }
     if not args.no_cpu_baseline and not args.profile_only:
-        inp_cpu = {kk: vv.cpu() for kk, vv in inp.items() if hasattr(vv, "cpu")}
+        inp_cpu = {kk: vv.cpu() for kk, vv in prob["inp"].items() if hasattr(vv, "cpu")}
         line["cpu_baseline"] = cpu_baseline(w, inp_cpu, args.cpu_seconds)
     print(json.dumps(line), flush=True)
 

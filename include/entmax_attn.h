@@ -4,19 +4,19 @@
  * The operation (AdaSplash-2, "Faster Differentiable Sparse Attention", gist.science
  * summaries): alpha-entmax attention, a sparse and differentiable replacement of
  * softmax attention whose normaliser tau is found per query row by root finding
- * (pages 1/3/5, section 1). For row i with scores s_ij = scale * q_i . k_j:
+ * (AdaSplash-2 (zh, ja, es) §1). For row i with scores s_ij = scale * q_i . k_j:
  *
  *     x_ij = (alpha - 1) s_ij,   p_ij = [x_ij - tau_i]_+^(1/(alpha-1)),   sum_j p_ij = 1,
  *     o_i  = sum_j p_ij v_j.
  *
  * tau_i is initialised from a B-bin histogram of the row's scores built while keys
- * stream through on-chip memory (page 1 section 2.1; page 3 section 2.1,
+ * stream through on-chip memory (AdaSplash-2 (zh) §2.1; AdaSplash-2 (ja) §2.1,
  * Proposition 1: tau* - 1/B < tau_h <= tau*), refined by a safeguarded hybrid
  * solver -- Halley for alpha <= 1.5, Newton for 1.5 < alpha <= 2, secant above,
- * bisection whenever a step leaves the bracket (page 1 section 2.2; page 3
- * section 2.2) -- and a bit-packed block mask, 32 key blocks per 32-bit word,
- * lets the forward and backward skip all-zero key blocks (page 1 section 2.3;
- * page 3 section 2.3). Threshold, bins and bracket live on the x-scale above.
+ * bisection whenever a step leaves the bracket (AdaSplash-2 (zh) §2.2; AdaSplash-2 (ja)
+ * §2.2) -- and a bit-packed block mask, 32 key blocks per 32-bit word,
+ * lets the forward and backward skip all-zero key blocks (AdaSplash-2 (zh) §2.3;
+ * AdaSplash-2 (ja) §2.3). Threshold, bins and bracket live on the x-scale above.
  *
  * Layout (all tensors contiguous, row-major):
  *   q, dout, dq            [batch, heads_q,  seqlen, head_dim]   dtype
@@ -35,8 +35,8 @@
  *   slopes                 [heads_q] float32, optional (NULL = no position bias):
  *                          query head h adds -slopes[h] * |i - j| to s_ij before the
  *                          transform (ALiBi; slope 0 = a head without position encoding,
- *                          so NAPE -- half the heads without encoding, half ALiBi, pages 2
- *                          section 4 and 1 section 4.2 -- is one slopes array). Under the
+ *                          so NAPE -- half the heads without encoding, half ALiBi, AdaSplash-2
+ *                          (it) §4 and (zh) §4.2 -- is one slopes array). Under the
  *                          causal mask |i - j| = i - j. Forward and backward must get the
  *                          same slopes.
  *
@@ -90,11 +90,18 @@ typedef struct {
                              2^-20. Other alpha stop when |sum p - 1| <= 1e-4 at the
                              evaluated tau (tol unused there) */
     int32_t tau_init;     /* start of the refinement: 0 = the histogram bound tau_h and the
-                             bracket [tau_h, tau_h + 1/B] (page 1 section 2.1-2.2, page 3
-                             section 2.1-2.2); 1 = no histogram, the plain bracket
+                             bracket [tau_h, tau_h + 1/B] (AdaSplash-2 (zh) §2.1-2.2, AdaSplash-2 (ja)
+                             §2.1-2.2); 1 = no histogram, the plain bracket
                              [x_max - 1, x_max - n_valid^(1-alpha)] from its lower end (the
-                             start the pages measure the histogram against, page 5 section 4),
+                             start the pages measure the histogram against, AdaSplash-2 (es) §4),
                              for ablation; max_iters 0 then means 15 */
+    int32_t dense;        /* 0 = skip all-zero key blocks (the method, AdaSplash-2 (zh) §2.3:
+                             work O(|M|) instead of O(Tr x Tc)); 1 = ablation without
+                             skipping: refinement, output and both backward kernels visit
+                             every causally valid block and multiply it in full, and the
+                             forward returns a block_mask with every valid bit set. tau, o,
+                             aux and the gradients equal those of dense = 0 (the skipped
+                             blocks hold only zero weights); only the time differs */
 } entmax_attn_desc;
 
 /* Supported: head_dim 64 or 128 (bf16 and fp32); seqlen <= 2^19 (and a multiple of both blocks). */
@@ -110,7 +117,7 @@ size_t entmax_attn_aux_bytes(const entmax_attn_desc *desc);
 size_t entmax_attn_mask_words(const entmax_attn_desc *desc);
 
 /*
- * Forward (pages 1/3/5 section 2): per query row, one streaming pass over every
+ * Forward (AdaSplash-2 (zh, ja, es) §2): per query row, one streaming pass over every
  * valid key block builds the B-bin histogram and tau_h; refinement passes over
  * the candidate key blocks find tau; a last pass over the blocks that hold a
  * non-zero weight forms o, aux and the exact block mask.
@@ -133,7 +140,7 @@ entmax_status entmax_attn_fwd(const entmax_attn_desc *desc,
 
 /*
  * Backward: the exact gradient of alpha-entmax attention (the pages state only
- * that the backward also skips zero blocks, page 1 section 2.3). With
+ * that the backward also skips zero blocks, AdaSplash-2 (zh) §2.3). With
  * g_ij = [x_ij - tau_i]_+^(1/(alpha-1) - 1), dP_ij = dO_i . v_j, delta_i = dO_i . o~_i:
  *   dS_ij = g_ij (dP_ij - delta_i),  dq_i = scale sum_j dS_ij k_j,
  *   dk_j = scale sum_i dS_ij q_i,    dv_j = sum_i p_ij dO_i  (summed over the GQA group).
@@ -152,8 +159,8 @@ entmax_status entmax_attn_bwd(const entmax_attn_desc *desc,
 
 /*
  * Decode: one new query row per (sequence, query head) against a KV cache, forward only
- * (the pages leave inference to future work, page 3 section 5; DashAttention decodes
- * incrementally on the same primitives, page 4). The query follows the cached keys, so
+ * (the pages leave inference to future work, AdaSplash-2 (ja) §5; DashAttention decodes
+ * incrementally on the same primitives, DashAttention (it)). The query follows the cached keys, so
  * keys 0..len_b-1 of sequence b are all valid and, with a position bias, key j sits at
  * distance len_b - 1 - j. The threshold is found as in the forward: the B-bin histogram
  * of the row's scores gives tau_h (Proposition 1), the same hybrid solver refines it, and

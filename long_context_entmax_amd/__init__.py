@@ -45,6 +45,7 @@ class Desc(ctypes.Structure):
         ("alpha", ctypes.c_float), ("causal", ctypes.c_int32), ("block_q", ctypes.c_int32),
         ("block_k", ctypes.c_int32), ("n_bins", ctypes.c_int32), ("scale", ctypes.c_float),
         ("max_iters", ctypes.c_int32), ("tol", ctypes.c_float), ("tau_init", ctypes.c_int32),
+        ("dense", ctypes.c_int32),
     ]
 
 
@@ -123,10 +124,10 @@ def _check(status: int) -> None:
 def make_desc(batch: int, heads_q: int, heads_kv: int, seqlen: int, head_dim: int, dtype: int,
               alpha: float, causal: bool, block: Tuple[int, int], bins: int,
               scale: Optional[float] = None, max_iters: int = 0, tol: float = 0.0,
-              tau_init: int = 0) -> Desc:
+              tau_init: int = 0, dense: bool = False) -> Desc:
     return Desc(batch, heads_q, heads_kv, seqlen, head_dim, dtype, float(alpha), int(bool(causal)),
                 int(block[0]), int(block[1]), int(bins), float(scale or 0.0), int(max_iters), float(tol),
-                int(tau_init))
+                int(tau_init), int(bool(dense)))
 
 
 def _torch():
@@ -134,7 +135,8 @@ def _torch():
     return torch
 
 
-def _desc_for(q, k, alpha, causal, block, bins, scale, max_iters, tol, tau_init: int = 0) -> Desc:
+def _desc_for(q, k, alpha, causal, block, bins, scale, max_iters, tol, tau_init: int = 0,
+              dense: bool = False) -> Desc:
     torch = _torch()
     if q.dim() != 4 or k.dim() != 4:
         raise ValueError("q and k must be [batch, heads, seqlen, head_dim]")
@@ -146,7 +148,7 @@ def _desc_for(q, k, alpha, causal, block, bins, scale, max_iters, tol, tau_init:
         raise ValueError(f"unsupported dtype {q.dtype}")
     b, hq, n, d = q.shape
     return make_desc(b, hq, k.shape[1], n, d, dt, alpha, causal, block, bins, scale, max_iters, tol,
-                     tau_init)
+                     tau_init, dense)
 
 
 def _ptr(t) -> Optional[int]:
@@ -176,6 +178,47 @@ def _require_gpu(*ts) -> None:
             raise ValueError("tensors must be contiguous")
 
 
+def _expect(name: str, t, shape, dtype, device) -> None:
+    """Raise ValueError unless tensor ``t`` has exactly ``shape``, ``dtype`` and ``device``
+    (the C ABI takes raw pointers, so a wrong size here would be read or written out of
+    bounds on the device)."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device} (the device of q)")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _check_qkv(q, k, v) -> None:
+    """q [b, hq, n, d]; k and v [b, hkv, n, d] with hq % hkv == 0, one dtype and device."""
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k and v must be [batch, heads, seqlen, head_dim]")
+    b, hq, n, d = q.shape
+    hkv = k.shape[1]
+    if hkv == 0 or hq % hkv != 0:
+        raise ValueError(f"heads of q ({hq}) must be a multiple of the heads of k ({hkv})")
+    _expect("k", k, (b, hkv, n, d), q.dtype, q.device)
+    _expect("v", v, (b, hkv, n, d), q.dtype, q.device)
+
+
+def _check_workspace(ws, device) -> None:
+    torch = _torch()
+    if ws is not None and (ws.dtype != torch.uint8 or ws.dim() != 1 or ws.device != device):
+        raise ValueError("workspace must be a 1-D uint8 tensor on the device of q")
+
+
+def _check_stats(stats, device) -> None:
+    torch = _torch()
+    if stats is not None and (stats.dtype != torch.int64 or stats.dim() != 1 or stats.numel() < 32
+                              or stats.device != device):
+        raise ValueError("stats must be a 1-D int64 tensor of at least 32 entries on the device of q")
+
+
 def mask_shape(n: int, block: Tuple[int, int]) -> Tuple[int, int]:
     Tr, Tc = n // block[0], n // block[1]
     return Tr, (Tc + 31) // 32
@@ -187,7 +230,7 @@ FwdOut = namedtuple("FwdOut", "o tau mask aux hist tau_h")
 def nape_slopes(heads: int):
     """Slopes of NAPE heads as a list: the first half of the heads without position encoding
     (slope 0), the second half ALiBi with the geometric slopes 2^(-8 k / H') of H' = heads/2
-    ALiBi heads, k = 1..H'. The pages name the split (half and half, page 2 section 4) but not
+    ALiBi heads, k = 1..H'. The pages name the split (half and half, AdaSplash-2 (it) §4) but not
     which half or the slopes; this is the reading taken."""
     if heads < 2 or heads % 2:
         raise ValueError("NAPE needs an even number of heads")
@@ -198,31 +241,46 @@ def nape_slopes(heads: int):
 def fwd(q, k, v, alpha: float = 1.5, causal: bool = True, block=(64, 64), bins: int = 16,
         scale: Optional[float] = None, max_iters: int = 0, tol: float = 0.0,
         return_hist: bool = False, stats=None, workspace=None, out=None, tau_init: int = 0,
-        slopes=None) -> FwdOut:
+        slopes=None, dense: bool = False) -> FwdOut:
     """alpha-entmax attention forward. Returns (o, tau, mask, aux, hist, tau_h); o is float32.
 
     hist/tau_h are the histogram stage's counts [b,hq,n,B] and lower bound [b,hq,n]
     (None unless return_hist). ``stats``: optional int64 CUDA tensor [32] (accumulated).
     ``out``: optional FwdOut of preallocated tensors to write into. ``tau_init``: 0 starts
     the refinement from the histogram bound, 1 from the plain bracket below the row max.
+    ``dense``: visit every causally valid key block (no block skipping; the mask comes back
+    with every valid bit set) -- the ablation that times the method without sparsity.
+    Every tensor is checked for shape, dtype and device before a pointer is taken.
     """
     torch = _torch()
-    _require_gpu(q, k, v, slopes)
+    _check_qkv(q, k, v)
     _check_slopes(slopes, q.shape[1])
-    desc = _desc_for(q, k, alpha, causal, block, bins, scale, max_iters, tol, tau_init)
-    L = lib()
+    desc = _desc_for(q, k, alpha, causal, block, bins, scale, max_iters, tol, tau_init, dense)
     b, hq, n, d = q.shape
     dev = q.device
     Tr, W = mask_shape(n, block)
-    if out is None:
-        o = torch.empty(q.shape, dtype=torch.float32, device=dev)
-        tau = torch.empty((b, hq, n), dtype=torch.float32, device=dev)
-        mask = torch.empty((b, hq, Tr, W), dtype=torch.int32, device=dev)
-        aux = torch.empty((b, hq, n, d), dtype=torch.float32, device=dev)
-        hist = torch.empty((b, hq, n, bins), dtype=torch.int32, device=dev) if return_hist else None
-        tau_h = torch.empty((b, hq, n), dtype=torch.float32, device=dev) if return_hist else None
-    else:
+    f32, i32 = torch.float32, torch.int32
+    if out is not None:
         o, tau, mask, aux, hist, tau_h = out
+        _expect("out.o", o, (b, hq, n, d), f32, dev)
+        _expect("out.tau", tau, (b, hq, n), f32, dev)
+        _expect("out.mask", mask, (b, hq, Tr, W), i32, dev)
+        _expect("out.aux", aux, (b, hq, n, d), f32, dev)
+        _expect("out.hist", hist, (b, hq, n, bins), i32, dev)
+        _expect("out.tau_h", tau_h, (b, hq, n), f32, dev)
+        if any(x is None for x in (o, tau, mask, aux)):
+            raise ValueError("out needs o, tau, mask and aux")
+    _check_stats(stats, dev)
+    _check_workspace(workspace, dev)
+    _require_gpu(q, k, v, slopes)
+    L = lib()
+    if out is None:
+        o = torch.empty(q.shape, dtype=f32, device=dev)
+        tau = torch.empty((b, hq, n), dtype=f32, device=dev)
+        mask = torch.empty((b, hq, Tr, W), dtype=i32, device=dev)
+        aux = torch.empty((b, hq, n, d), dtype=f32, device=dev)
+        hist = torch.empty((b, hq, n, bins), dtype=i32, device=dev) if return_hist else None
+        tau_h = torch.empty((b, hq, n), dtype=f32, device=dev) if return_hist else None
     nbytes = L.entmax_attn_fwd_workspace_bytes(ctypes.byref(desc))
     if workspace is None or workspace.numel() < nbytes:
         workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
@@ -233,19 +291,35 @@ def fwd(q, k, v, alpha: float = 1.5, causal: bool = True, block=(64, 64), bins: 
 
 
 def bwd(q, k, v, do, tau, mask, aux, alpha: float = 1.5, causal: bool = True, block=(64, 64),
-        bins: int = 16, scale: Optional[float] = None, workspace=None, out=None, slopes=None):
+        bins: int = 16, scale: Optional[float] = None, workspace=None, out=None, slopes=None,
+        dense: bool = False):
     """alpha-entmax attention backward: (dq, dk, dv) given the forward's tau, mask, aux
-    (and the forward's slopes)."""
+    (and the forward's slopes). ``dense``: no block skipping (pass the mask of a dense
+    forward). Every tensor is checked for shape, dtype and device before a pointer is taken."""
     torch = _torch()
-    _require_gpu(q, k, v, do, tau, mask, aux, slopes)
+    _check_qkv(q, k, v)
     _check_slopes(slopes, q.shape[1])
-    desc = _desc_for(q, k, alpha, causal, block, bins, scale, 0, 0.0)
-    L = lib()
+    desc = _desc_for(q, k, alpha, causal, block, bins, scale, 0, 0.0, 0, dense)
+    b, hq, n, d = q.shape
     dev = q.device
+    Tr, W = mask_shape(n, block)
+    f32 = torch.float32
+    _expect("do", do, q.shape, q.dtype, dev)
+    _expect("tau", tau, (b, hq, n), f32, dev)
+    _expect("mask", mask, (b, hq, Tr, W), torch.int32, dev)
+    _expect("aux", aux, (b, hq, n, d), f32, dev)
+    if out is not None:
+        dq, dk, dv = out
+        _expect("out.dq", dq, q.shape, q.dtype, dev)
+        _expect("out.dk", dk, k.shape, k.dtype, dev)
+        _expect("out.dv", dv, v.shape, v.dtype, dev)
+        if any(x is None for x in (dq, dk, dv)):
+            raise ValueError("out needs dq, dk and dv")
+    _check_workspace(workspace, dev)
+    _require_gpu(q, k, v, do, tau, mask, aux, slopes)
+    L = lib()
     if out is None:
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    else:
-        dq, dk, dv = out
     nbytes = L.entmax_attn_bwd_workspace_bytes(ctypes.byref(desc))
     if workspace is None or workspace.numel() < nbytes:
         workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)

@@ -83,7 +83,7 @@ void prof_end(hipStream_t s) {
 // argument checks and derived sizes
 // ------------------------------------------------------------------------------------------
 struct Derived {
-  int b, hq, hkv, n, D, G, dtype, causal, Br, Bc, B, max_iters, tau_init;
+  int b, hq, hkv, n, D, G, dtype, causal, Br, Bc, B, max_iters, tau_init, dense;
   float alpha, scale, tol, kappa;
   int mode;               // 1: alpha = 2, 2: alpha = 1.5, 0: other
   int Tr, Tc, W, WT, nkb, NW32;
@@ -128,6 +128,8 @@ static entmax_status derive(const entmax_attn_desc* d, Derived& o, bool decode =
   if (d->tau_init != 0 && d->tau_init != 1)
     return fail(ENTMAX_ERR_UNSUPPORTED, "tau_init %d: must be 0 (histogram) or 1 (plain bracket)", d->tau_init);
   o.tau_init = d->tau_init;
+  if (d->dense != 0 && d->dense != 1) return fail(ENTMAX_ERR_SHAPE, "dense must be 0 or 1");
+  o.dense = decode ? 0 : d->dense;
   o.max_iters = d->max_iters != 0       ? d->max_iters
                 : (o.tau_init == 1)    ? 15
                 : d->alpha > 2.0f      ? 15
@@ -333,6 +335,7 @@ entmax_status entmax_attn_fwd(const entmax_attn_desc* desc, const void* q, const
   p.b = o.b; p.hq = o.hq; p.hkv = o.hkv; p.n = o.n; p.G = o.G;
   p.causal = o.causal; p.Br = o.Br; p.Bc = o.Bc; p.B = o.B; p.max_iters = o.max_iters;
   p.tau_init = o.tau_init;
+  p.dense = o.dense;
   p.slopes = slopes;
   p.cx = (float)(((double)o.alpha - 1.0) * (double)o.scale);
   p.alpha = o.alpha; p.kappa = o.kappa; p.tol = o.tol;
@@ -404,6 +407,7 @@ entmax_status entmax_attn_bwd(const entmax_attn_desc* desc, const void* q, const
   p.scale = o.scale; p.kappa = o.kappa;
   p.am1 = o.alpha - 1.0f; p.slopes = slopes;
   p.Tr = o.Tr; p.Tc = o.Tc; p.W = o.W; p.WT = o.WT;
+  p.dense = o.dense;
 
   p.map = make_map(o.b * o.hkv, o.Tc);
   prof_begin("entmax_bwd_dkv", s);

@@ -1,6 +1,6 @@
 // Backward of alpha-entmax attention: dK/dV per key block and dQ per query tile, each
-// walking only the set bits of the block mask (AdaSplash-2 pages, page 1 section 2.3 and
-// page 3 section 2.3: the mask lets the backward skip all-zero blocks; local accumulators
+// walking only the set bits of the block mask (AdaSplash-2 pages, AdaSplash-2 (zh) §2.3 and
+// AdaSplash-2 (ja) §2.3: the mask lets the backward skip all-zero blocks; local accumulators
 // instead of atomics).
 //
 // Gradient (the exact alpha-entmax Jacobian; the pages do not spell it out): with
@@ -188,7 +188,7 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void k_bwd_dkv(BwdParams p)
         mx = fmaxf(mx, dm);
       }
     }
-    if (ballot(mx > 0.f) == 0) continue;
+    if (!p.dense && ballot(mx > 0.f) == 0) continue;   // an all-zero sub-tile
     f32x16 dP = f32x16{};
 #pragma unroll
     for (int s = 0; s < DS; ++s) mma16(dP, da[s], vb[s]);  // dP[q][key]
@@ -371,7 +371,7 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void k_bwd_dq(BwdParams p) 
         mx = fmaxf(mx, dm);
       }
     }
-    if (ballot(mx > 0.f) == 0) continue;
+    if (!p.dense && ballot(mx > 0.f) == 0) continue;   // an all-zero sub-tile
     f32x16 dP = f32x16{};
 #pragma unroll
     for (int s = 0; s < DS; ++s) mma16(dP, va[s], db[s]);   // dP^T[key][q]

@@ -1,7 +1,7 @@
 // Decode forward of alpha-entmax attention: one new query row per (sequence, query head)
-// against a KV cache. The pages leave inference to future work (page 3 section 5) and
-// DashAttention decodes incrementally on the same primitives (page 4); the threshold is
-// found exactly as in the forward (page 1 sections 2.1-2.2, page 3 sections 2.1-2.2): a
+// against a KV cache. The pages leave inference to future work (AdaSplash-2 (ja) §5) and
+// DashAttention decodes incrementally on the same primitives (DashAttention (it)); the threshold is
+// found exactly as in the forward (AdaSplash-2 (zh) §2.1-2.2, AdaSplash-2 (ja) §2.1-2.2): a
 // B-bin histogram of the row's scores gives tau_h (Proposition 1), the safeguarded hybrid
 // solver refines it, and o = sum_j p_j v_j with p = [x - tau]_+^(1/(alpha-1)).
 //

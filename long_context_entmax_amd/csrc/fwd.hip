@@ -1,6 +1,6 @@
 // Forward of alpha-entmax attention: a histogram kernel and a refinement/output kernel.
 //
-// Stages (AdaSplash-2 pages, page 1 section 2, page 3 section 2, page 5 section 2):
+// Stages (AdaSplash-2 pages, AdaSplash-2 (zh) §2, AdaSplash-2 (ja) §2, AdaSplash-2 (es) §2):
 //   1. k_hist -- histogram pass: every valid key block streams through once; each lane
 //      keeps an online max and a B-bin histogram of its scores on the anchored grid
 //      (bins [m/B, (m+1)/B), window = the B cells ending with the max's cell); a window
@@ -14,10 +14,10 @@
 //      f(tau) = sum_j [x_j - tau]_+^kappa - 1 in the bracket [tau_h, tau_h + 1/B]:
 //      Halley (alpha <= 1.5), Newton (1.5 < alpha <= 2), secant (alpha > 2, started by
 //      false position on the bracket ends), bisection whenever a step leaves the bracket
-//      (page 1 section 2.2, page 3 section 2.2). Each pass visits only the marked
+//      (AdaSplash-2 (zh) §2.2, AdaSplash-2 (ja) §2.2). Each pass visits only the marked
 //      sub-blocks whose recorded maximum exceeds the evaluation point. Then the output
 //      pass: p = [x - tau]_+^kappa, o = P V, o~ = G V / sum G with g = [x - tau]_+^(kappa-1),
-//      and the exact block mask (bit-packed, 32 blocks per word; page 1 section 2.3).
+//      and the exact block mask (bit-packed, 32 blocks per word; AdaSplash-2 (zh) §2.3).
 //
 // MI355X decomposition. Scores are computed transposed (keys x queries) on 32x32 MFMA
 // tiles so that a lane owns one query (two lanes per query, 16 keys each per tile): the
@@ -353,6 +353,7 @@ __global__ __launch_bounds__(64 * OUT_WAVES, 2) void k_refine_out(FwdParams p) {
     uint32_t word;  // its needed sub-blocks not yet taken
   };
   auto walk_next = [&](Walk& wk, float thr) -> int {
+    if (p.dense) return ++wk.wi < kb_end ? wk.wi : -1;   // ablation: every valid sub-block
     while (wk.word == 0) {
       while (wk.nm == 0) {
         if (64 * (++wk.g) >= nwords) return -1;
@@ -519,7 +520,7 @@ __global__ __launch_bounds__(64 * OUT_WAVES, 2) void k_refine_out(FwdParams p) {
         sg += gw[r];
         mx = fmaxf(mx, dm);
       }
-      if (ballot(mx > 0.f) != 0) {
+      if (p.dense || ballot(mx > 0.f) != 0) {
         ++n_out;
         const int J = kb >> bc_shift;            // key block of this sub-block
         if ((J >> 5) != mw) {

@@ -68,6 +68,7 @@ struct FwdParams {
   WgMap map;             // histogram kernel
   WgMap map2;            // refinement/output kernel
   int tau_init;          // 0: histogram bound; 1: plain bracket from the row max (no histogram)
+  int dense;             // 1: no block skipping (every valid sub-block visited, every valid mask bit set)
   const float* slopes;   // optional [hq]: position-bias slope m of each query head (scores - m |i - j|)
 };
 
@@ -115,6 +116,7 @@ struct BwdParams {
   float am1;             // alpha - 1 (scales the position bias onto the x-scale)
   const float* slopes;   // optional [hq] position-bias slopes
   int Tr, Tc, W, WT;
+  int dense;             // 1: every item of the mask multiplied in full (no zero-block skip)
   WgMap map;
 };
 

@@ -1,5 +1,5 @@
 // The per-row threshold solver shared by the prefill and decode forwards (AdaSplash-2
-// pages, page 1 sections 2.1-2.2, page 3 sections 2.1-2.2): tau_h from the B-bin histogram
+// pages, AdaSplash-2 (zh) §2.1-2.2, AdaSplash-2 (ja) §2.1-2.2): tau_h from the B-bin histogram
 // (Proposition 1: tau* - 1/B < tau_h <= tau*), then a safeguarded hybrid root solver on
 // f(tau) = sum_j [x_j - tau]_+^kappa - 1 -- Halley (alpha <= 1.5), Newton (1.5 < alpha <= 2),
 // secant started by false position (alpha > 2), bisection whenever a step leaves the

@@ -9,6 +9,7 @@ It is test infrastructure: it calls only the oracle and the generator and writes
 
     python -m oracle.calibrate_beta            # all workloads (minutes on 8 cores)
     python -m oracle.calibrate_beta C2         # one workload
+    python -m oracle.calibrate_beta --extra    # the extra sweep points not yet in the table
 """
 from __future__ import annotations
 
@@ -30,6 +31,12 @@ TARGETS = {
     "C3": [(1.5, 0.6), (1.5, 0.8), (1.5, 0.95)],
     "C4": [(2.0, 0.95)],
     "C5": [(1.5, 0.97)],
+}
+# extra points of the block-sparsity sweeps (between and beyond the configured ones), so that
+# the fit of step time against non-zero blocks rests on more than three points per sweep
+SWEEP_EXTRA = {
+    "C2": [(1.5, 0.3), (1.5, 0.8), (1.5, 0.95), (2.0, 0.3), (2.0, 0.8), (2.0, 0.95)],
+    "C3": [(1.5, 0.7), (1.5, 0.9)],
 }
 NOMINAL_C2 = [0.5, 2.0, 6.0]
 
@@ -114,10 +121,15 @@ def calibrate(name: str, alpha: float, target: float, tiles: int = 32, iters: in
 
 
 def main(argv):
-    names = argv[1:] or list(TARGETS)
+    extra = "--extra" in argv
+    args = [a for a in argv[1:] if not a.startswith("--")]
+    src = SWEEP_EXTRA if extra else TARGETS
+    names = args or list(src)
     table = load_table()
     for name in names:
-        for alpha, target in TARGETS[name]:
+        for alpha, target in src.get(name, []):
+            if extra and key(name, alpha, target) in table:
+                continue
             t0 = time.time()
             beta, s, nz, va = calibrate(name, alpha, target)
             table[key(name, alpha, target)] = {
@@ -128,7 +140,7 @@ def main(argv):
                   f"({nz}/{va}) [{time.time() - t0:.0f}s]", flush=True)
             with open(_TABLE, "w") as f:
                 json.dump(table, f, indent=1, sort_keys=True)
-        if name == "C2":
+        if name == "C2" and not extra:
             for beta in NOMINAL_C2:
                 w = base_workload("C2", 1.5, 0.0)
                 s, nz, va = block_sparsity(w, beta)

@@ -1,21 +1,21 @@
 """fp64 CPU oracle of DashAttention stages 1-2 -- TEST INFRASTRUCTURE ONLY.
 
 Only ``tests/``, the smoke check and the benchmark's CPU-baseline leg may use it.
-It follows the DashAttention page (page 4, Italian summary, "Metodologia",
+It follows the DashAttention page (DashAttention (it), "Metodologia",
 stages 1 and 2) and takes, where the page leaves a step open, the readings below.
 
 Inputs: q [b, hq, n, d]; k, v [b, hkv, n, d]; ks [b, hkv, nc, d], the chunk summaries
 of stage 0 (one vector per complete chunk of C keys, nc = n / C). Query head h belongs
 to KV group g = h // G, G = hq / hkv.
 
-Stage 1, routing (page 4, "Stadio 1"): query row i has m_i = floor(i / C) complete
+Stage 1, routing (DashAttention (it), "Stadio 1"): query row i has m_i = floor(i / C) complete
 chunks before its own. Its routing logits are zbar[h, i, c] = gamma * scale * q[h, i] .
 ks[g, c] for c < m_i, and what[h, i, :] = alpha-entmax(zbar[h, i, :]) (tau on the x-scale
 x = (alpha - 1) zbar). The query heads of a KV group average their routing weights:
 wbar[g, i, c] = mean over h in g of what[h, i, c]; the shared support is {c : wbar > 0}.
 A row with m_i = 0 routes nothing (tau reported as 0, wbar = 0).
 
-Stage 2, prior-induced sparse softmax (page 4, "Stadio 2"): the softmax whose KL
+Stage 2, prior-induced sparse softmax (DashAttention (it), "Stadio 2"): the softmax whose KL
 reference is the prior g instead of the uniform distribution is softmax(s + log g). The
 prior on key j of a routed chunk c is wbar[g, i, c] raised to sigma (sigma = 0: uniform
 over the active keys; sigma = 1: the routing weights themselves); the query's own chunk

@@ -11,13 +11,13 @@
  * Proposition 1):
  *   - alpha-entmax gives a sparse, differentiable distribution with exact zeros;
  *     its normaliser tau plays the role of log-sum-exp and is a root of a
- *     monotone equation (pages 1/3/5, section 1 "problem").
+ *     monotone equation (AdaSplash-2 (zh, ja, es) §1 "problem").
  *   - histogram initialisation: scores mapped into a unit window, B bins,
  *     tau_h solves the B-bin problem, tau* - h < tau_h <= tau* with h the bin
- *     width (page 1 section 2.1, page 3 section 2.1 "Proposition 1",
- *     page 5 section 2A).
+ *     width (AdaSplash-2 (zh) §2.1, AdaSplash-2 (ja) §2.1 "Proposition 1",
+ *     AdaSplash-2 (es) §2A).
  *   - block mask: a key block is marked when it holds a non-zero weight,
- *     32 blocks per 32-bit word (page 1 section 2.3, page 3 section 2.3).
+ *     32 blocks per 32-bit word (AdaSplash-2 (zh) §2.3, AdaSplash-2 (ja) §2.3).
  * Readings where the pages are silent (formula, scale of tau, bin grid, bin
  * representative, backward) are listed at the top of each function.
  *
@@ -29,7 +29,7 @@
  * [x_max - 1, x_max - n^(1-alpha)], a window of width at most 1.
  *
  * Position bias (NAPE heads: half of the heads without position encoding, half
- * with ALiBi; page 2 section 4, page 1 section 4.2): a head with slope m adds
+ * with ALiBi; AdaSplash-2 (it) §4, AdaSplash-2 (zh) §4.2): a head with slope m adds
  * -m |i - j| to every score s_ij before the transform, so
  *   x_ij = (alpha - 1) (scale q_i . k_j - m |i - j|),
  * and m = 0 is a head without position encoding. Under the causal mask
@@ -55,8 +55,8 @@ static double entmax_mass(const double *x, long n, double tau, double kappa)
 }
 
 /*
- * tau* by bisection on f(tau) = sum_j [x_j - tau]_+^kappa - 1 (pages 1/3/5,
- * section 1: tau is found by root-finding; bisection is the plain method).
+ * tau* by bisection on f(tau) = sum_j [x_j - tau]_+^kappa - 1 (AdaSplash-2 (zh, ja, es),
+ * §1: tau is found by root-finding; bisection is the plain method).
  * Bracket: f(x_max - 1) >= 0 because the largest term alone is 1;
  * f(x_max - n^(1-alpha)) <= 0 because each term is at most 1/n.
  * Stops at width 1e-12 (or when the midpoint no longer moves) and returns the
@@ -84,8 +84,8 @@ double oracle_entmax_tau(const double *x, long n, double alpha)
 }
 
 /*
- * Histogram of one row on the anchored grid (page 1 section 2.1, page 2
- * section 2A, page 3 section 2.1, page 5 section 2A: scores mapped to a unit
+ * Histogram of one row on the anchored grid (AdaSplash-2 (zh) §2.1, AdaSplash-2 (it)
+ * §2A, AdaSplash-2 (ja) §2.1, AdaSplash-2 (es) §2A: scores mapped to a unit
  * window and counted in B bins).
  * Reading: bins are the cells [m/B, (m+1)/B) of the absolute grid of step
  * h = 1/B; the window is the B cells ending with the cell of x_max, i.e.
@@ -114,7 +114,7 @@ void oracle_histogram(const double *x, long n, int B, int32_t *counts, int64_t *
 /*
  * tau_h: root of the B-bin problem sum_k c_k [l_k - tau]_+^kappa = 1, where
  * each count sits at the lower edge l_k = (T - B + 1 + k)/B of its bin (reading
- * of "the n-root problem becomes a sum over B bins", page 1 section 2.1; lower
+ * of "the n-root problem becomes a sum over B bins", AdaSplash-2 (zh) §2.1; lower
  * edges make tau_h a lower bound, Proposition 1). Bisection on
  * [l_top - 1, l_top]: at l_top - 1 the top bin alone (count >= 1) gives >= 1.
  * Returns the lower end of the final bracket, so the B-bin mass there is >= 1.
@@ -168,7 +168,7 @@ static void row_x(long d, long i, const double *qi, const double *k, long nv, do
  *   p_j = [x_j - tau_i]_+^kappa (no renormalisation) ; o_i = sum_j p_j v_j;
  *   histogram counts and T of the row, tau_h from the B-bin problem;
  *   rowbits: bit J of the row's W = ceil(n/Bc) words (LSB first, 32 per word)
- *   is set when key block J holds a j with p_j > 0 (page 1 section 2.3);
+ *   is set when key block J holds a j with p_j > 0 (AdaSplash-2 (zh) §2.3);
  *   xgap_i = min_j |x_j - tau_i| (distance of the nearest score to the threshold);
  *   psum_i = sum_j p_j (equals 1 up to rounding).
  * Any output pointer may be NULL except o and tau.

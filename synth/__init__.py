@@ -273,7 +273,7 @@ def make_inputs(w: Workload, device="cpu", heads: Optional[Sequence[int]] = None
 
 
 def chunk_summaries(w: Workload, chunk: int, device="cpu") -> torch.Tensor:
-    """Chunk-summary keys [b, hkv, n / chunk, d] for DashAttention inputs (page 4, stage 0
+    """Chunk-summary keys [b, hkv, n / chunk, d] for DashAttention inputs (DashAttention (it), stage 0
     gives one vector per chunk of keys), drawn with the spread a mean of ``chunk`` keys of
     the recipe would have: N(0, qk_scale^2 / chunk) per element for ``normal`` and ``tiny``;
     for ``centroid`` (chunk 64, one centroid per chunk) the chunk's centroid plus

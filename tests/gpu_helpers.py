@@ -21,18 +21,18 @@ def to64(t: torch.Tensor) -> np.ndarray:
 
 
 def run_gpu(inp: dict, w: synth.Workload, with_bwd: bool = True, stats=None, tau_init: int = 0,
-            slopes=None):
+            slopes=None, dense: bool = False):
     d = dev()
     q, k, v = inp["q"].to(d), inp["k"].to(d), inp["v"].to(d)
     blk = (w.block_q, w.block_k)
     sl = None if slopes is None else torch.tensor(list(slopes), dtype=torch.float32, device=d)
     r = lce.fwd(q, k, v, w.alpha, w.causal, blk, w.n_bins, return_hist=True, stats=stats,
-                tau_init=tau_init, slopes=sl)
+                tau_init=tau_init, slopes=sl, dense=dense)
     out = {"o": r.o, "tau": r.tau, "mask": r.mask, "aux": r.aux, "hist": r.hist, "tau_h": r.tau_h}
     if with_bwd:
         do = inp["do"].to(d)
         dq, dk, dv = lce.bwd(q, k, v, do, r.tau, r.mask, r.aux, w.alpha, w.causal, blk, w.n_bins,
-                             slopes=sl)
+                             slopes=sl, dense=dense)
         out.update(dq=dq, dk=dk, dv=dv)
     torch.cuda.synchronize()
     return {kk: (vv.cpu() if isinstance(vv, torch.Tensor) else vv) for kk, vv in out.items()}
@@ -79,3 +79,15 @@ def mask_mismatch_is_ambiguous(gpu_mask, ref_mask, x, tau_ref, w, band):
             if gap.size == 0 or gap.min() > band:
                 return False
     return True
+
+
+def valid_block_mask(b: int, hq: int, n: int, Br: int, Bc: int, causal: bool) -> np.ndarray:
+    """Mask words [b, hq, Tr, W] with every causally valid (query tile, key block) bit set."""
+    Tr, Tc = n // Br, n // Bc
+    W = (Tc + 31) // 32
+    m = np.zeros((Tr, W), dtype=np.int64)
+    for I in range(Tr):
+        last = min(Tc - 1, (I * Br + Br - 1) // Bc) if causal else Tc - 1
+        for J in range(last + 1):
+            m[I, J // 32] |= 1 << (J % 32)
+    return np.broadcast_to(m, (b, hq, Tr, W)).copy()

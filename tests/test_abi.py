@@ -228,3 +228,113 @@ def test_plain_c_program_uses_the_abi(L, tmp_path):
     r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0, r.stdout + r.stderr
     assert "abi_check: ok" in r.stdout
+
+
+def _cpu_problem(b=1, hq=4, hkv=2, n=128, d=64):
+    import torch
+    q = torch.zeros(b, hq, n, d, dtype=torch.bfloat16)
+    k = torch.zeros(b, hkv, n, d, dtype=torch.bfloat16)
+    return q, k, k.clone()
+
+
+def _fwd_out(b=1, hq=4, n=128, d=64, Tr=2, W=1, bins=16):
+    import torch
+    return lce.FwdOut(torch.zeros(b, hq, n, d), torch.zeros(b, hq, n), torch.zeros(b, hq, Tr, W, dtype=torch.int32),
+                      torch.zeros(b, hq, n, d), torch.zeros(b, hq, n, bins, dtype=torch.int32), torch.zeros(b, hq, n))
+
+
+@pytest.mark.parametrize("case,match", [
+    ("k_batch", "k must have shape"), ("k_seqlen", "k must have shape"), ("k_dim", "k must have shape"),
+    ("k_dtype", "k must be"), ("v_shape", "v must have shape"), ("heads", "multiple of the heads"),
+    ("o_dtype", "out.o must be"), ("tau_shape", "out.tau must have shape"),
+    ("mask_block", "out.mask must have shape"), ("aux_shape", "out.aux must have shape"),
+    ("hist_bins", "out.hist must have shape"), ("stats_short", "stats must be"),
+    ("stats_dtype", "stats must be"), ("ws_dtype", "workspace must be"),
+])
+def test_binding_checks_forward_tensors(case, match):
+    """Every tensor of the forward binding is checked (shape, dtype, device) before any
+    pointer is taken: a mismatch raises ValueError naming the tensor, not a device fault."""
+    import torch
+    q, k, v = _cpu_problem()
+    kw = {}
+    if case == "k_batch":
+        k = torch.zeros(2, 2, 128, 64, dtype=torch.bfloat16)
+    elif case == "k_seqlen":
+        k = torch.zeros(1, 2, 64, 64, dtype=torch.bfloat16)
+    elif case == "k_dim":
+        k = torch.zeros(1, 2, 128, 128, dtype=torch.bfloat16)
+    elif case == "k_dtype":
+        k = k.float()
+    elif case == "v_shape":
+        v = torch.zeros(1, 2, 64, 64, dtype=torch.bfloat16)
+    elif case == "heads":
+        k = torch.zeros(1, 3, 128, 64, dtype=torch.bfloat16)
+        v = k.clone()
+    else:
+        out = _fwd_out()
+        if case == "o_dtype":
+            out = out._replace(o=out.o.bfloat16())
+        elif case == "tau_shape":
+            out = out._replace(tau=torch.zeros(1, 4, 64))
+        elif case == "mask_block":   # the mask of a 32x32-block run is 4 x 1 words per head
+            out = out._replace(mask=torch.zeros(1, 4, 4, 1, dtype=torch.int32))
+        elif case == "aux_shape":
+            out = out._replace(aux=torch.zeros(1, 4, 128, 32))
+        elif case == "hist_bins":
+            out = out._replace(hist=torch.zeros(1, 4, 128, 8, dtype=torch.int32))
+        elif case == "stats_short":
+            kw["stats"] = torch.zeros(16, dtype=torch.int64)
+        elif case == "stats_dtype":
+            kw["stats"] = torch.zeros(32, dtype=torch.float32)
+        elif case == "ws_dtype":
+            kw["workspace"] = torch.zeros(1024, dtype=torch.float32)
+        kw["out"] = out
+    with pytest.raises(ValueError, match=match):
+        lce.fwd(q, k, v, 1.5, True, (64, 64), 16, **kw)
+
+
+@pytest.mark.parametrize("case,match", [
+    ("do_shape", "do must have shape"), ("tau_dtype", "tau must be"), ("tau_shape", "tau must have shape"),
+    ("mask_block", "mask must have shape"), ("mask_dtype", "mask must be"), ("aux_shape", "aux must have shape"),
+    ("dq_shape", "out.dq must have shape"), ("dk_dtype", "out.dk must be"), ("dv_shape", "out.dv must have shape"),
+])
+def test_binding_checks_backward_tensors(case, match):
+    import torch
+    q, k, v = _cpu_problem()
+    do = torch.zeros_like(q)
+    tau = torch.zeros(1, 4, 128)
+    mask = torch.zeros(1, 4, 2, 1, dtype=torch.int32)
+    aux = torch.zeros(1, 4, 128, 64)
+    kw = {}
+    if case == "do_shape":
+        do = torch.zeros(1, 4, 64, 64, dtype=torch.bfloat16)
+    elif case == "tau_dtype":
+        tau = tau.bfloat16()
+    elif case == "tau_shape":
+        tau = torch.zeros(1, 2, 128)
+    elif case == "mask_block":
+        mask = torch.zeros(1, 4, 4, 1, dtype=torch.int32)
+    elif case == "mask_dtype":
+        mask = mask.long()
+    elif case == "aux_shape":
+        aux = torch.zeros(1, 4, 128, 32)
+    elif case == "dq_shape":
+        kw["out"] = (torch.zeros(1, 4, 64, 64, dtype=torch.bfloat16), torch.zeros_like(k), torch.zeros_like(v))
+    elif case == "dk_dtype":
+        kw["out"] = (torch.zeros_like(q), torch.zeros(k.shape), torch.zeros_like(v))
+    elif case == "dv_shape":
+        kw["out"] = (torch.zeros_like(q), torch.zeros_like(k), torch.zeros(1, 2, 64, 64, dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match=match):
+        lce.bwd(q, k, v, do, tau, mask, aux, 1.5, True, (64, 64), 16, **kw)
+
+
+def test_binding_accepts_consistent_cpu_tensors_up_to_the_device_check():
+    """A consistent set of tensors passes every shape check and stops only at the device
+    check (the library runs on the GPU only)."""
+    import torch
+    q, k, v = _cpu_problem()
+    with pytest.raises(ValueError, match="GPU only"):
+        lce.fwd(q, k, v, 1.5, True, (64, 64), 16, out=_fwd_out(), stats=torch.zeros(32, dtype=torch.int64))
+    with pytest.raises(ValueError, match="GPU only"):
+        lce.bwd(q, k, v, torch.zeros_like(q), torch.zeros(1, 4, 128), torch.zeros(1, 4, 2, 1, dtype=torch.int32),
+                torch.zeros(1, 4, 128, 64), 1.5, True, (64, 64), 16)

@@ -1,5 +1,5 @@
 """GPU parity of the DashAttention forward (stages 1-2, include/dash_attn.h) with the fp64
-oracle ``oracle.dash`` on the same seeded inputs (page 4, DashAttention, stages 1 and 2).
+oracle ``oracle.dash`` on the same seeded inputs (DashAttention (it), stages 1 and 2).
 
 Bars: bf16 -- max |d route_tau| <= 1e-3, max |d wbar| <= 1e-3, max |do| <= 1e-2,
 max |d lse| <= 1e-3. For routing alpha > 2 the weight d^kappa (kappa < 1) is only Hoelder in

@@ -3,7 +3,7 @@ cache) with the fp64 oracle: the oracle's decode row is row L-1 of a causal forw
 the first L cached keys with the query placed there.
 
 Bars as for the forward: bf16 max |dtau| <= 1e-3, max |do| <= 1e-2; tau_h satisfies
-Proposition 1 against the oracle's tau* (page 3 section 2.1); the fp32 grid case compares
+Proposition 1 against the oracle's tau* (AdaSplash-2 (ja) §2.1); the fp32 grid case compares
 histogram counts bit for bit.
 """
 import zlib

@@ -30,8 +30,16 @@ from tests.gpu_helpers import dev, rel_fro, to64
 
 pytestmark = pytest.mark.gpu
 
-CONFIGS = ["C2", "C3", "C4", "C5"]
+# every configured point of the 4K-128K study: (workload, alpha, target block sparsity)
+POINTS = [("C2", 1.5, 0.0), ("C2", 1.5, 0.6), ("C2", 1.5, 0.9),
+          ("C2", 2.0, 0.0), ("C2", 2.0, 0.6), ("C2", 2.0, 0.9),
+          ("C3", 1.5, 0.6), ("C3", 1.5, 0.8), ("C3", 1.5, 0.95),
+          ("C4", 2.0, 0.95), ("C5", 1.5, 0.97)]
 TAU_TOL, O_TOL, G_TOL = 1e-3, 1e-2, 2e-2
+
+
+def _pid(pt):
+    return f"{pt[0]}-a{pt[1]:g}-s{pt[2]:g}"
 
 
 def _sample_tiles(w, rng):
@@ -46,14 +54,15 @@ def _bits_of_tile(row_bits: np.ndarray) -> np.ndarray:
     return np.bitwise_or.reduce(row_bits, axis=0)
 
 
-def _run(cfg, slopes=None):
-    w = synth.workload(cfg)
+def _run(cfg, slopes=None, alpha=None, sparsity=None):
+    w = synth.workload(cfg, alpha=alpha, sparsity=sparsity)
     d = dev()
     inp = synth.make_inputs(w, device=d)
     q, k, v, do = inp["q"], inp["k"], inp["v"], inp["do"]
     blk = (w.block_q, w.block_k)
     print(f"[fullsize] {cfg}: b{w.batch} hq{w.heads_q} hkv{w.heads_kv} n{w.seqlen} d{w.head_dim} "
-          f"alpha {w.alpha} blocks {blk} B {w.n_bins}", flush=True)
+          f"alpha {w.alpha} blocks {blk} B {w.n_bins} target sparsity {w.target_sparsity} beta {w.beta:.4g}",
+          flush=True)
     desc = lce._desc_for(q, k, w.alpha, w.causal, blk, w.n_bins, None, 0, 0.0)
     fws, bws = lce.workspace_bytes(desc)
     wsf = torch.empty(max(fws, 256), dtype=torch.uint8, device=d)
@@ -66,9 +75,19 @@ def _run(cfg, slopes=None):
     return w, inp, r, (dq, dk, dv)
 
 
-@pytest.mark.parametrize("cfg", CONFIGS)
-def test_fullsize_sampled_tiles(cfg):
-    w, inp, r, (dq, dk, dv) = _run(cfg)
+@pytest.fixture(scope="module", params=POINTS, ids=_pid)
+def point(request):
+    """One full-size run per configured point, shared by that point's tests (pytest groups
+    the tests of a module-scoped parameter, so one run is held at a time)."""
+    cfg, alpha, sparsity = request.param
+    res = _run(cfg, alpha=alpha, sparsity=sparsity)
+    yield request.param, res
+    del res
+    torch.cuda.empty_cache()
+
+
+def test_fullsize_sampled_tiles(point):
+    (cfg, _, _), (w, inp, r, (dq, dk, dv)) = point
     rng = np.random.default_rng(20260)
     G = w.heads_q // w.heads_kv
     scale = 1.0 / math.sqrt(w.head_dim)
@@ -128,13 +147,12 @@ def test_fullsize_sampled_tiles(cfg):
     print(f"[fullsize] {cfg} worst: {worst}", flush=True)
 
 
-@pytest.mark.parametrize("cfg", CONFIGS)
-def test_fullsize_keys_from_sampled_rows(cfg):
+def test_fullsize_keys_from_sampled_rows(point):
     """dK and dV at full size with dO kept on a sampled row set R and zeroed elsewhere: a row
     with dO = 0 has dP = 0 and delta = 0, so it adds nothing to dK or dV, and the oracle
     needs tau and delta of the rows in R only. Keys are sampled from the key blocks the rows
     of R attend to (non-zero gradients), plus random keys (zero or small gradients)."""
-    w, inp, r, _ = _run(cfg)
+    (cfg, _, _), (w, inp, r, _) = point
     G = w.heads_q // w.heads_kv
     scale = 1.0 / math.sqrt(w.head_dim)
     n, Br, Bc, B = w.seqlen, w.block_q, w.block_k, w.n_bins
@@ -196,10 +214,9 @@ def test_fullsize_keys_from_sampled_rows(cfg):
     assert rdk <= G_TOL and rdv <= G_TOL
 
 
-@pytest.mark.parametrize("cfg", CONFIGS)
-def test_fullsize_gradient_sums(cfg):
+def test_fullsize_gradient_sums(point):
     """Per KV head the dK rows sum to zero and the dV rows sum to the group's sum of dO."""
-    w, inp, r, (dq, dk, dv) = _run(cfg)
+    (cfg, _, _), (w, inp, r, (dq, dk, dv)) = point
     G = w.heads_q // w.heads_kv
     bi = 0
     for kh in sorted({0, w.heads_kv - 1}):

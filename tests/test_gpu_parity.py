@@ -4,7 +4,7 @@ Bars: fp32 tiny configuration -- histogram counts, support and block mask bit-ex
 |dtau| <= 1e-5, |dO| <= 1e-4, gradients within 1e-4 relative Frobenius error; bf16 --
 max |dO| <= 1e-2, max |dtau| <= 1e-3, gradients within 2e-2 relative Frobenius error,
 block mask equal except in blocks whose nearest score lies within 1e-3 of tau*.
-tau_h always satisfies Proposition 1 against the oracle's tau* (page 3 section 2.1).
+tau_h always satisfies Proposition 1 against the oracle's tau* (AdaSplash-2 (ja) §2.1).
 """
 import math
 
@@ -16,7 +16,7 @@ import oracle
 import synth
 import long_context_entmax_amd as lce
 from tests.gpu_helpers import (mask_bits, mask_mismatch_is_ambiguous, rel_fro, run_gpu, scores_x,
-                               to64)
+                               to64, valid_block_mask)
 
 pytestmark = pytest.mark.gpu
 
@@ -93,6 +93,35 @@ def test_bf16_random_shapes(case):
     for name in ("dq", "dk", "dv"):
         err = rel_fro(g[name].float().numpy().astype(np.float64), ref[name])
         assert err < 2e-2, (name, err)
+
+
+DENSE_CASES = [CASES[0], CASES[1], CASES[2], CASES[3], CASES[4], CASES[6], CASES[8], CASES[11]]
+
+
+@pytest.mark.parametrize("case", DENSE_CASES, ids=[str(c) for c in DENSE_CASES])
+def test_dense_ablation_matches_skipping(case):
+    """The ablation without block skipping (every causally valid block multiplied in the
+    refinement, output and backward kernels) returns every valid mask bit and the same
+    results: tau, o and aux bit for bit (the skipped blocks add exact zeros to every sum),
+    the gradients up to the fp32 order of the backward's partial sums, and both within the
+    oracle's bars."""
+    b, hq, hkv, n, d, alpha, causal, Br, Bc, B, qs = case
+    print(f"[case] dense ablation {case}", flush=True)
+    w = synth.Workload("t", b, hq, hkv, n, d, "bf16", alpha, causal, Br, Bc, B, "normal",
+                       extra={"qk_scale": qs}, seed=hash(case) & 0xFFFF)
+    inp = synth.make_inputs(w)
+    g = run_gpu(inp, w)
+    gd = run_gpu(inp, w, dense=True)
+    np.testing.assert_array_equal(mask_bits(gd["mask"].numpy()), valid_block_mask(b, hq, n, Br, Bc, causal))
+    for name in ("tau", "o", "aux", "tau_h", "hist"):
+        assert torch.equal(g[name], gd[name]), name
+    for name in ("dq", "dk", "dv"):
+        err = rel_fro(gd[name].float().numpy().astype(np.float64), g[name].float().numpy().astype(np.float64))
+        assert err < 1e-3, (name, err)
+    ref = _oracle(inp, w)
+    assert np.abs(gd["o"].float().numpy() - ref["o"]).max() < 1e-2
+    for name in ("dq", "dk", "dv"):
+        assert rel_fro(gd[name].float().numpy().astype(np.float64), ref[name]) < 2e-2, name
 
 
 BRACKET_CASES = [CASES[0], CASES[1], CASES[3], CASES[4], CASES[6]]

@@ -3,8 +3,8 @@
 None of these checks re-runs the oracle's own formula: each compares it with
 an independent result -- a closed form from the literature (sorted sparsemax,
 exact sort-based 1.5-entmax), brute-force support enumeration with a library
-root finder, the strict bound of Proposition 1 (AdaSplash-2 pages, page 3
-section 2.1), hand-derived fixtures under tests/golden/, the softmax limit,
+root finder, the strict bound of Proposition 1 (AdaSplash-2 pages, AdaSplash-2 (ja)
+§2.1), hand-derived fixtures under tests/golden/, the softmax limit,
 central finite differences and exact invariants of the gradient.
 """
 import itertools
@@ -246,7 +246,7 @@ def test_histogram_shift_by_grid_steps():
 
 
 def test_support_within_histogram_window():
-    """The support at tau_h contains the true support (page 5 section 2A)."""
+    """The support at tau_h contains the true support (AdaSplash-2 (es) §2A)."""
     rng = np.random.default_rng(5)
     for alpha in (1.5, 2.0):
         for _ in range(20):
@@ -407,7 +407,7 @@ def test_backward_softmax_limit():
 
 
 # ------------------------------------------------------------------------------------------------
-# position bias (NAPE heads: half without position encoding, half ALiBi; page 2 section 4)
+# position bias (NAPE heads: half without position encoding, half ALiBi; AdaSplash-2 (it) §4)
 # ------------------------------------------------------------------------------------------------
 
 @pytest.mark.parametrize("causal", [False, True])
@@ -558,7 +558,7 @@ def test_decode_single_key_and_hand_derived_row():
 
 
 # ------------------------------------------------------------------------------------------------
-# DashAttention stages 1-2 (page 4, stages 1 and 2)
+# DashAttention stages 1-2 (DashAttention (it), stages 1 and 2)
 # ------------------------------------------------------------------------------------------------
 
 def _dash_inputs(b, hq, hkv, n, d, nc, seed, ks_zero):

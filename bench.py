@@ -127,91 +127,106 @@ def valid_pairs(w) -> float:
     return per * w.batch * w.heads_q
 
 
+def progressive_order(count: int):
+    """0..count-1 in rounds of evenly spaced indices, each round halving the spacing (so any
+    prefix of the sequence is spread over the whole range)."""
+    step = 1
+    while step * 2 <= count:
+        step *= 2
+    seen = set()
+    while step >= 1:
+        for u in range(step // 2 if step > 1 else 0, count, step):
+            if u not in seen:
+                seen.add(u)
+                yield u
+        step //= 2
+
+
 def cpu_baseline(w, inp_cpu, target_s: float):
     """The fp64 oracle's fwd+bwd on a bounded sample of the workload, extrapolated.
 
     Row side (forward: scores, tau by bisection, o, histogram; backward per row: dq and
-    delta): 64-row query tiles evenly spaced over all (batch, head, tile) indices, the
-    spacing halved until about 2/3 of the time budget is spent; the time per row is
-    extrapolated to all rows (even spacing samples the causal row lengths). Key side (dk, dv per key, summed
-    over the GQA group): the last m keys of KV head 0 of batch 0 -- under the causal mask
-    they need tau and delta only of the last m rows, which the oracle computes first
-    (untimed) -- with m doubled until about 1/3 of the budget is spent; the time per
-    valid (row, key) pair is extrapolated to all valid pairs."""
+    delta): 64-row query tiles taken in an evenly spaced, progressively refined order over
+    all (batch, head, tile) indices, one tile per host thread, until about 2/3 of the time
+    budget is spent; the time per row is extrapolated to all rows (even spacing samples the
+    causal row lengths). Key side (dk, dv per key, summed over the GQA group): keys of KV
+    head 0 of batch 0 in the same kind of order, 32 keys per thread task, for the remaining
+    third; each key scores every valid row of the group, and the rows whose tau the row side
+    computed also take the support work (the others count as outside the support, about 1%
+    of the key-side work at the study's sparsities); the time per key is extrapolated to
+    all keys of all KV heads. Progress goes to stderr."""
     import numpy as np
+    from concurrent.futures import FIRST_COMPLETED, ThreadPoolExecutor, wait
     import oracle
     threads, host_cores = cpu_threads()
     G = w.heads_q // w.heads_kv
     scale = 1.0 / math.sqrt(w.head_dim)
     n, b, hq = w.seqlen, w.batch, w.heads_q
-    q64 = {}
-
-    def qh(bi, h):
-        if (bi, h) not in q64:
-            q64[(bi, h)] = (inp_cpu["q"][bi, h].double().numpy(), inp_cpu["do"][bi, h].double().numpy())
-        return q64[(bi, h)]
-
-    kv64 = {}
-
-    def kvh(bi, kh):
-        if (bi, kh) not in kv64:
-            kv64[(bi, kh)] = (inp_cpu["k"][bi, kh].double().numpy(), inp_cpu["v"][bi, kh].double().numpy())
-        return kv64[(bi, kh)]
-
-    total_rows = b * hq * n
+    q64 = {(bi, h): (inp_cpu["q"][bi, h].double().numpy(), inp_cpu["do"][bi, h].double().numpy())
+           for bi in range(b) for h in range(hq)}
+    kv64 = {(bi, kh): (inp_cpu["k"][bi, kh].double().numpy(), inp_cpu["v"][bi, kh].double().numpy())
+            for bi in range(b) for kh in range(w.heads_kv)}
     tile = min(64, n)
-    ntiles = total_rows // tile
-    rows_done, t_rows, step = 0, 0.0, 1
-    while step * 2 <= ntiles // 16:
-        step *= 2
-    while t_rows < target_s * 2.0 / 3.0 and step >= 1:
-        flat = np.arange(step // 2, ntiles, step, dtype=np.int64) if step > 1 else np.arange(ntiles)
-        by_head = {}
-        for u in flat.tolist():
-            r0 = u * tile
-            by_head.setdefault((r0 // (hq * n), (r0 // n) % hq), []).extend(range(r0 % n, r0 % n + tile))
-        for (bi, h), rows in by_head.items():
-            qq, do = qh(bi, h)
-            kk, vv = kvh(bi, h // G)
-            t0 = time.time()
-            f = oracle.attn_fwd_head(qq, kk, vv, w.alpha, w.causal, w.n_bins, w.block_k, scale, rows=rows,
-                                     threads=threads)
-            oracle.attn_bwd_rows_head(qq, kk, vv, do, f["tau"], w.alpha, w.causal, scale, rows=f["rows"],
-                                      threads=threads)
-            t_rows += time.time() - t0
-        rows_done += flat.size * tile
-        if step == 1:
-            break
-        step //= 2
-    s_rows = t_rows / rows_done * total_rows
+    ntiles = b * hq * n // tile
+    tau_of = {}     # (bi, h) -> {row: (tau, delta)}
 
-    # key side
-    kk, vv = kvh(0, 0)
-    qg = np.stack([qh(0, g)[0] for g in range(G)])
-    dog = np.stack([qh(0, g)[1] for g in range(G)])
-    m, t_keys, pairs_done = 16, 0.0, 0.0
-    while True:
-        m = min(m, n)
-        rows = np.arange(n - m, n) if w.causal else np.arange(n)
-        taug = np.full((G, n), np.inf)
-        deltag = np.zeros((G, n))
-        for g in range(G):
-            f = oracle.attn_fwd_head(qg[g], kk, vv, w.alpha, w.causal, w.n_bins, w.block_k, scale, rows=rows,
-                                     threads=threads)
-            rb = oracle.attn_bwd_rows_head(qg[g], kk, vv, dog[g], f["tau"], w.alpha, w.causal, scale,
-                                           rows=f["rows"], threads=threads)
-            taug[g, f["rows"]] = f["tau"]
-            deltag[g, f["rows"]] = rb["delta"]
-        keys = np.arange(n - m, n)
-        t0 = time.time()
-        oracle.attn_bwd_keys_group(qg, kk, vv, dog, taug, deltag, w.alpha, w.causal, scale, keys=keys,
-                                   threads=threads)
-        t_keys = time.time() - t0
-        pairs_done = G * (m * (m + 1) / 2.0 if w.causal else float(m) * n)
-        if t_keys >= target_s / 3.0 or m >= n or not w.causal:
-            break
-        m *= 2
-    s_keys = t_keys / pairs_done * valid_pairs(w)
+    def run_tile(u):
+        r0 = u * tile
+        bi, h, i0 = r0 // (hq * n), (r0 // n) % hq, r0 % n
+        qq, do = q64[(bi, h)]
+        kk, vv = kv64[(bi, h // G)]
+        rows = list(range(i0, i0 + tile))
+        f = oracle.attn_fwd_head(qq, kk, vv, w.alpha, w.causal, w.n_bins, w.block_k, scale, rows=rows, threads=1)
+        rb = oracle.attn_bwd_rows_head(qq, kk, vv, do, f["tau"], w.alpha, w.causal, scale, rows=f["rows"],
+                                       threads=1)
+        return bi, h, f["rows"], f["tau"], rb["delta"]
+
+    def run_pool(fn, order, budget):
+        done, t0, tlast = [], time.time(), time.time()
+        with ThreadPoolExecutor(max_workers=threads) as ex:
+            it, inflight = iter(order), set()
+            while True:
+                while len(inflight) < threads and time.time() - t0 < budget:
+                    u = next(it, None)
+                    if u is None:
+                        break
+                    inflight.add(ex.submit(fn, u))
+                if not inflight:
+                    break
+                fin, inflight = wait(inflight, return_when=FIRST_COMPLETED)
+                done.extend(x.result() for x in fin)
+                if time.time() - tlast > 5.0:
+                    tlast = time.time()
+                    print(f"[cpu_baseline] {fn.__name__}: {len(done)} done, {tlast - t0:.0f} s", file=sys.stderr,
+                          flush=True)
+        return done, time.time() - t0
+
+    res, t_rows = run_pool(run_tile, progressive_order(ntiles), target_s * 2.0 / 3.0)
+    rows_done = len(res) * tile
+    for bi, h, rows, tau, delta in res:
+        d = tau_of.setdefault((bi, h), {})
+        for r, t_, dl in zip(rows.tolist(), tau.tolist(), delta.tolist()):
+            d[r] = (t_, dl)
+    s_rows = t_rows / rows_done * (b * hq * n)
+
+    kk, vv = kv64[(0, 0)]
+    qg = np.stack([q64[(0, g)][0] for g in range(G)])
+    dog = np.stack([q64[(0, g)][1] for g in range(G)])
+    taug = np.full((G, n), np.inf)
+    deltag = np.zeros((G, n))
+    for g in range(G):
+        for r, (t_, dl) in tau_of.get((0, g), {}).items():
+            taug[g, r], deltag[g, r] = t_, dl
+
+    def run_keys(js):
+        oracle.attn_bwd_keys_group(qg, kk, vv, dog, taug, deltag, w.alpha, w.causal, scale, keys=js, threads=1)
+        return len(js)
+
+    korder = list(progressive_order(n))
+    groups = [korder[i:i + 32] for i in range(0, n, 32)]   # 32 keys per task
+    done_keys, t_keys = run_pool(run_keys, groups, target_s / 3.0)
+    nkeys = sum(done_keys)
+    s_keys = t_keys / nkeys * n * b * w.heads_kv
     s_per_step = s_rows + s_keys
     return {
         "value": dense_eq_flops(w) / s_per_step / 1e12,
@@ -222,9 +237,9 @@ def cpu_baseline(w, inp_cpu, target_s: float):
         "kind": "oracle",
         "extrapolated": True,
         "sample": (f"fp64 oracle on {threads} threads ({host_cores} host cores): fwd + per-row bwd of "
-                   f"{rows_done} of {total_rows} query rows (64-row tiles evenly spaced over all heads), {t_rows:.1f} s, "
-                   f"per row x all rows = {s_rows:.0f} s); dK/dV of the last {m} keys of one KV group "
-                   f"({t_keys:.1f} s, per valid (row, key) pair x all pairs = {s_keys:.0f} s)"),
+                   f"{rows_done} of {b * hq * n} query rows (64-row tiles evenly spread over all heads, "
+                   f"{t_rows:.1f} s; per row x all rows = {s_rows:.0f} s) and dK/dV of {nkeys} of {n} keys "
+                   f"of one KV group ({t_keys:.1f} s; per key x all keys of all KV heads = {s_keys:.0f} s)"),
     }
 
 
@@ -570,7 +585,9 @@ def sweep(args, lce, dev):
         ref = prob["outs"]
         o_skip, tau_skip = ref.o.clone(), ref.tau.clone()
         g_skip = [g.clone() for g in prob["grads"]]
+        print(f"[sweep] skipping: {r['ms']:.4f} ms/step", file=sys.stderr, flush=True)
         rd = time_point(lce, w, prob, 3 if big else max(3, args.steps // 4), 1, dense=True)
+        print(f"[sweep] dense ablation: {rd['ms']:.4f} ms/step", file=sys.stderr, flush=True)
         eff = dense_eq_flops(w) / (r["ms"] * 1e-3) / 1e12
         alg_total = sum(r["alg"].values())
         passes = {str(p): r["stats"][p] for p in range(1, 17) if r["stats"][p]}
@@ -655,6 +672,7 @@ def main():
               flush=True)
         return
     r = time_point(lce, w, prob, args.steps, args.warmup, dense=args.dense, copy_probe_mib=args.copy_probe_mib)
+    print(f"[bench] timed: {r['ms']:.4f} ms/step", file=sys.stderr, flush=True)
     kern, alg, st = r["kern"], r["alg"], r["stats"]
     ms = r["ms"]
     dom = max(alg, key=lambda nm: kern.get(nm, 0.0))

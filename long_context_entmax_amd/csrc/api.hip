@@ -173,16 +173,21 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // forward workspace: K and V fragment-major copies, then per (chunk, sub-block) maxima
 static size_t fwd_kv_bytes(const Derived& o) { return align256((size_t)o.b * o.hkv * o.D * o.n * o.es); }
-static size_t fwd_dmax_bytes(const Derived& o) { return align256((size_t)o.b * o.hq * (size_t)o.nkb * o.nkb * 4); }
+// per (query head, 32-row chunk) the maxima of the 32-key sub-blocks the chunk can see: a packed
+// lower triangle under the causal mask
+static size_t fwd_dmax_bytes(const Derived& o) {
+  const size_t per_head = o.causal ? (size_t)o.nkb * (o.nkb + 1) / 2 : (size_t)o.nkb * o.nkb;
+  return align256((size_t)o.b * o.hq * per_head * 4);
+}
 static size_t fwd_wmax_bytes(const Derived& o) { return align256((size_t)o.b * o.hq * (size_t)o.nkb * o.NW32 * 4); }
 static size_t fwd_ws(const Derived& o) {
-  return 2 * fwd_kv_bytes(o) + fwd_dmax_bytes(o) + fwd_wmax_bytes(o) + align256((size_t)o.b * o.hq * o.n * 8);
+  return 2 * fwd_kv_bytes(o) + fwd_dmax_bytes(o) + fwd_wmax_bytes(o) + align256((size_t)o.b * o.hq * o.n * 16);
 }
 
-// backward workspace: delta, transposed mask, then fragment-major copies of Q and dO
-// (rows and cols layouts), K (rows and cols) and V (rows)
+// backward workspace: delta, transposed mask, then fragment-major rows copies of Q, dO, K
+// and V (the kernels form the transposed operands on the matrix core)
 struct BwdLayout {
-  size_t delta, maskT, qr, qc, dor, doc, kr, kc, vr, total;
+  size_t delta, maskT, qr, dor, kr, vr, total;
 };
 static BwdLayout bwd_ws(const Derived& o) {
   BwdLayout L;
@@ -192,11 +197,8 @@ static BwdLayout bwd_ws(const Derived& o) {
   L.delta = off; off += align256((size_t)o.b * o.hq * o.n * 4);
   L.maskT = off; off += align256((size_t)o.b * o.hq * o.Tc * o.WT * 4);
   L.qr = off; off += qbytes;
-  L.qc = off; off += qbytes;
   L.dor = off; off += qbytes;
-  L.doc = off; off += qbytes;
   L.kr = off; off += kbytes;
-  L.kc = off; off += kbytes;
   L.vr = off; off += kbytes;
   L.total = off;
   return L;
@@ -331,7 +333,7 @@ entmax_status entmax_attn_fwd(const entmax_attn_desc* desc, const void* q, const
   p.hist = hist_counts; p.tau_h = tau_h; p.stats = (unsigned long long*)stats;
   p.dmax = (float*)(wsb + 2 * fwd_kv_bytes(o));
   p.wmax = (float*)(wsb + 2 * fwd_kv_bytes(o) + fwd_dmax_bytes(o));
-  p.tauh_ws = (float2*)(wsb + 2 * fwd_kv_bytes(o) + fwd_dmax_bytes(o) + fwd_wmax_bytes(o));
+  p.tauh_ws = (float4*)(wsb + 2 * fwd_kv_bytes(o) + fwd_dmax_bytes(o) + fwd_wmax_bytes(o));
   p.b = o.b; p.hq = o.hq; p.hkv = o.hkv; p.n = o.n; p.G = o.G;
   p.causal = o.causal; p.Br = o.Br; p.Bc = o.Bc; p.B = o.B; p.max_iters = o.max_iters;
   p.tau_init = o.tau_init;
@@ -380,12 +382,12 @@ entmax_status entmax_attn_bwd(const entmax_attn_desc* desc, const void* q, const
   char* ws = (char*)workspace;
 
   const int hq_all = o.b * o.hq, hkv_all = o.b * o.hkv;
-  // one launch: fragment-major copies of Q and dO (both layouts, with delta = dO . o~),
-  // K (both layouts) and V (row layout), and the transposed block mask
+  // one launch: fragment-major rows copies of dO (with delta = dO . o~), Q, K and V, and the
+  // transposed block mask
   PrepBatch pb{};
-  pb.job[0] = Relayout{dout, ws + L.dor, ws + L.doc, (const float*)aux, (float*)(ws + L.delta), hq_all, "do"};
-  pb.job[1] = Relayout{q, ws + L.qr, ws + L.qc, nullptr, nullptr, hq_all, "q"};
-  pb.job[2] = Relayout{k, ws + L.kr, ws + L.kc, nullptr, nullptr, hkv_all, "k"};
+  pb.job[0] = Relayout{dout, ws + L.dor, nullptr, (const float*)aux, (float*)(ws + L.delta), hq_all, "do"};
+  pb.job[1] = Relayout{q, ws + L.qr, nullptr, nullptr, nullptr, hq_all, "q"};
+  pb.job[2] = Relayout{k, ws + L.kr, nullptr, nullptr, nullptr, hkv_all, "k"};
   pb.job[3] = Relayout{v, ws + L.vr, nullptr, nullptr, nullptr, hkv_all, "v"};
   pb.njobs = 4;
   pb.n = o.n;
@@ -396,8 +398,8 @@ entmax_status entmax_attn_bwd(const entmax_attn_desc* desc, const void* q, const
   if (e != hipSuccess) return hip_fail(e, "backward preparation");
 
   BwdParams p{};
-  p.qr = ws + L.qr; p.qc = ws + L.qc; p.dor = ws + L.dor; p.doc = ws + L.doc;
-  p.kr = ws + L.kr; p.kc = ws + L.kc; p.vr = ws + L.vr;
+  p.qr = ws + L.qr; p.dor = ws + L.dor;
+  p.kr = ws + L.kr; p.vr = ws + L.vr;
   p.tau = tau; p.delta = (const float*)(ws + L.delta);
   p.mask = block_mask; p.maskT = (const uint32_t*)(ws + L.maskT);
   p.dq = dq; p.dk = dk; p.dv = dv;

@@ -9,10 +9,12 @@
 //   dS_ij = g_ij (dP_ij - delta_i),  dq_i = scale sum_j dS_ij k_j,
 //   dk_j  = scale sum_i dS_ij q_i,   dv_j = sum_i p_ij dO_i.
 //
-// Every MFMA operand is read from a fragment-major copy (rows: lanes walk rows, 8
-// consecutive head-dimension elements per lane; cols: lanes walk the head dimension, 8
-// rows per lane in accumulator order), so a wave's operand load is one contiguous 1 KB
-// run at a wave-uniform base plus lane * 16 bytes.
+// Every operand is read from a fragment-major rows copy (lanes walk rows, 8 consecutive
+// head-dimension elements per lane), so a wave's operand load is one contiguous 1 KB run at
+// a wave-uniform base plus lane * 16 bytes. The operands of the products contracted over
+// rows (Q^T and dO^T in dK/dV, K^T in dQ: lanes walk the head dimension, 8 rows per lane in
+// accumulator order) are formed from those same fragments on the matrix core
+// (rows_to_cols, an exact copy), so each item's Q, dO or K rows come from memory once.
 //
 // k_bwd_dkv: one work group per (batch, KV head, key block J). Wave w owns the 32-key
 // sub-block w % KC of J and every NS-th item of the list (query head of the GQA group,
@@ -31,9 +33,6 @@ namespace {
 // offset (in elements) of a wave's operand fragment in a fragment-major copy
 __device__ __forceinline__ size_t rows_off(int blk32, int s, int DS, int lane) {
   return ((size_t)(blk32 * DS + s) * 64 + lane) * 8;
-}
-__device__ __forceinline__ size_t cols_off(int blk32, int dc, int m, int DC, int lane) {
-  return ((size_t)((blk32 * DC + dc) * 2 + m) * 64 + lane) * 8;
 }
 
 }  // namespace
@@ -70,6 +69,8 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void k_bwd_dkv(BwdParams p)
     dk[dc] = f32x16{};
     dv[dc] = f32x16{};
   }
+  Frag<T> eye[2];
+  eye_frags(eye, c, h);
 
   // This wave's items in list order: for each query head g of the group, each query tile I
   // with bit J in the head's column mask, each 32-row chunk qc of I -- every NS-th, none
@@ -127,11 +128,9 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void k_bwd_dkv(BwdParams p)
     const int head = kvh * p.G + gc;
     const size_t qrow0 = row_base(gc);
     const T* DOr = reinterpret_cast<const T*>(p.dor) + qrow0 * D;
-    const T* Qc = reinterpret_cast<const T*>(p.qc) + qrow0 * D;
-    const T* DOc = reinterpret_cast<const T*>(p.doc) + qrow0 * D;
     const float cm = BIAS ? p.slopes[head] * p.am1 : 0.0f;   // position bias on the x-scale
     const int qb = q0 >> 5;
-    Frag<T> qa[DS], da[DS], qt[2][DC], dt[2][DC];
+    Frag<T> qa[DS], da[DS];
     f32x4 tv[4], dl[4];
 #pragma unroll
     for (int s = 0; s < DS; ++s) {
@@ -144,13 +143,6 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void k_bwd_dkv(BwdParams p)
       tv[g4] = *reinterpret_cast<const f32x4*>(p.tau + qrow0 + q0 + 8 * g4 + 4 * h);
       dl[g4] = *reinterpret_cast<const f32x4*>(p.delta + qrow0 + q0 + 8 * g4 + 4 * h);
     }
-#pragma unroll
-    for (int m = 0; m < 2; ++m)
-#pragma unroll
-      for (int dc = 0; dc < DC; ++dc) {
-        load_frag(qt[m][dc], Qc + cols_off(qb, dc, m, DC, lane));
-        load_frag(dt[m][dc], DOc + cols_off(qb, dc, m, DC, lane));
-      }
     have = next_item(g_next, q0_next);
     if (have) load_rows(g_next, q0_next);
     f32x16 S = f32x16{};
@@ -195,6 +187,9 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void k_bwd_dkv(BwdParams p)
     f32x16 dS;
 #pragma unroll
     for (int r = 0; r < 16; ++r) dS[r] = G[r] * (dP[r] - dl[r >> 2][r & 3]);
+    Frag<T> qt[2][DC], dt[2][DC];        // Q^T and dO^T of the chunk (cols layout)
+    rows_to_cols<T, DS>(qt, qa, eye);
+    rows_to_cols<T, DS>(dt, da, eye);
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
       Frag<T> pf, sf;
@@ -271,7 +266,6 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void k_bwd_dq(BwdParams p) 
   const size_t kvoff = (size_t)(bi * p.hkv + kvh) * n * D;
   const T* Kr = reinterpret_cast<const T*>(p.kr) + kvoff;
   const T* Vr = reinterpret_cast<const T*>(p.vr) + kvoff;
-  const T* Kc = reinterpret_cast<const T*>(p.kc) + kvoff;
   Frag<T> qb[DS], db[DS];
 #pragma unroll
   for (int s = 0; s < DS; ++s) {
@@ -284,6 +278,8 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void k_bwd_dq(BwdParams p) 
   f32x16 dq[DC];
 #pragma unroll
   for (int dc = 0; dc < DC; ++dc) dq[dc] = f32x16{};
+  Frag<T> eye[2];
+  eye_frags(eye, c, h);
 
   const uint32_t* roww = p.mask + ((size_t)(bi * p.hq + head) * p.Tr + I) * p.W;
   // This wave's items in list order: the 32-key sub-blocks ks of each set key block J of the
@@ -325,16 +321,12 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void k_bwd_dq(BwdParams p) 
   while (have) {
     const int kbk = kb_next;
     const int key0 = kbk * 32;
-    Frag<T> ka[DS], va[DS], kt[2][DC];
+    Frag<T> ka[DS], va[DS];
 #pragma unroll
     for (int s = 0; s < DS; ++s) {
       ka[s] = kn[s];
       load_frag(va[s], Vr + rows_off(kbk, s, DS, lane));
     }
-#pragma unroll
-    for (int m = 0; m < 2; ++m)
-#pragma unroll
-      for (int dc = 0; dc < DC; ++dc) load_frag(kt[m][dc], Kc + cols_off(kbk, dc, m, DC, lane));
     have = next_item(kb_next);
     if (have) {
 #pragma unroll
@@ -378,6 +370,8 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void k_bwd_dq(BwdParams p) 
     f32x16 dS;
 #pragma unroll
     for (int r = 0; r < 16; ++r) dS[r] = G[r] * (dP[r] - dq_delta);
+    Frag<T> kt[2][DC];                   // K^T of the sub-block (cols layout)
+    rows_to_cols<T, DS>(kt, ka, eye);
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
       Frag<T> sf;

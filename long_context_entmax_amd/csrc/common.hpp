@@ -144,6 +144,38 @@ __device__ __forceinline__ void mma16(f32x16& acc, const Frag<float>& a, const F
   acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.b[3], b.b[3], acc, 0, 0, 0);
 }
 
+// Exact transposition of 32-column blocks through the matrix core. For a rows-layout A
+// operand X (lane c = row; contraction chunk s = columns 16 s .. 16 s + 15, half h holding
+// 8 h .. 8 h + 7 of them), the product X_{2 dc} E_0 + X_{2 dc + 1} E_1 with the constant B
+// operands below (lane (c, h), element jj: 1 iff c == 16 sh + 8 h + jj) is the block
+// X[:, 32 dc .. 32 dc + 31] in accumulator layout: lane c = column 32 dc + c, register r =
+// row acc_row(r, h). Its registers 8m .. 8m + 7 are therefore the cols-layout fragment m of
+// the block (rows 16 m + sigma(8 h + j)), ready as the A operand of a product contracted
+// over rows. Products with 1 and sums with 0 are exact, so the copy is bit for bit.
+template <typename T>
+__device__ __forceinline__ void eye_frags(Frag<T> (&e)[2], int c, int h) {
+#pragma unroll
+  for (int sh = 0; sh < 2; ++sh) {
+    const int j0 = c - 16 * sh - 8 * h;   // the element that is 1, if 0 <= j0 < 8
+    set_frag(e[sh], j0 == 0 ? 1.f : 0.f, j0 == 1 ? 1.f : 0.f, j0 == 2 ? 1.f : 0.f, j0 == 3 ? 1.f : 0.f,
+             j0 == 4 ? 1.f : 0.f, j0 == 5 ? 1.f : 0.f, j0 == 6 ? 1.f : 0.f, j0 == 7 ? 1.f : 0.f);
+  }
+}
+
+// cols-layout fragments t[m][dc] of a 32-row block held as rows-layout fragments x[s]
+template <typename T, int DS>
+__device__ __forceinline__ void rows_to_cols(Frag<T> (&t)[2][DS / 2], const Frag<T> (&x)[DS],
+                                             const Frag<T> (&e)[2]) {
+#pragma unroll
+  for (int dc = 0; dc < DS / 2; ++dc) {
+    f32x16 acc = f32x16{};
+    mma16(acc, x[2 * dc], e[0]);
+    mma16(acc, x[2 * dc + 1], e[1]);
+    acc_frag(t[0][dc], acc, 0);
+    acc_frag(t[1][dc], acc, 1);
+  }
+}
+
 // ------------------------------------------------------------------------------------------
 // element stores
 // ------------------------------------------------------------------------------------------

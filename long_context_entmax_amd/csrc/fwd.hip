@@ -85,7 +85,7 @@ __global__ __launch_bounds__((64 * hist_waves<T, D>()), (hist_occ<T, D>())) void
   const float cmB = BIAS ? p.slopes[head] * (p.alpha - 1.0f) * (float)B : 0.0f;
   uint32_t* hist = lds + (w * (B + 2)) * 64;   // [B + 2][64] of this wave
   for (int i = lane; i < (B + 2) * 64; i += 64) hist[i] = 0;
-  float* dmx = p.dmax + (bh * p.nkb + (row0 >> 5)) * p.nkb;
+  float* dmx = p.dmax + dmax_row(p, bh, row0 >> 5);
   float* wx_out = p.wmax + (bh * p.nkb + (row0 >> 5)) * p.NW32;
 
   // clear the block-mask words of this work group's tiles (k_refine_out ORs bits in)
@@ -276,7 +276,10 @@ __global__ __launch_bounds__((64 * hist_waves<T, D>()), (hist_occ<T, D>())) void
   const float tau_h = p.tau_init == 0 ? tau_from_counts<MODE>(cnt, Tf, B, p.kappa) : xmax - 1.0f;
   if (h == 0) {
     const size_t row = bh * n + qrow;
-    p.tauh_ws[row] = make_float2(tau_h, xmax);
+    float start = tau_h;   // alpha = 1.5: the spread-count root (other alpha start from tau_h itself)
+    if constexpr (MODE == 2)
+      if (p.tau_init == 0) start = tau_spread_start(cnt, Tf, B, tau_h);
+    p.tauh_ws[row] = make_float4(tau_h, xmax, start, 0.0f);
     if (p.tau_h) p.tau_h[row] = tau_h;
     if (p.hist) {
       int32_t* dst = p.hist + row * B;
@@ -318,7 +321,7 @@ __global__ __launch_bounds__(64 * OUT_WAVES, 2) void k_refine_out(FwdParams p) {
   const T* Q = reinterpret_cast<const T*>(p.q) + bh * n * D;
   const T* Kf = reinterpret_cast<const T*>(p.kf) + ((size_t)(bi * p.hkv + kvh) * n) * D;
   const T* Vf = reinterpret_cast<const T*>(p.vf) + ((size_t)(bi * p.hkv + kvh) * n) * D;
-  const float* dmx = p.dmax + (bh * p.nkb + chunk) * p.nkb;
+  const float* dmx = p.dmax + dmax_row(p, bh, chunk);
   const float* wmx = p.wmax + (bh * p.nkb + chunk) * p.NW32;
 
   Frag<T> qf[DS];
@@ -335,10 +338,11 @@ __global__ __launch_bounds__(64 * OUT_WAVES, 2) void k_refine_out(FwdParams p) {
   const float nv = p.causal ? (float)(qrow + 1) : (float)n;
   // (alpha = 2: several evaluation points per pass, see MultiState)
   using State = std::conditional_t<MODE == 1, MultiState<ALPHA2_POINTS>, RowState>;
-  const float2 hm = p.tauh_ws[bh * n + qrow];   // (tau_h, x_max)
+  const float4 hm = p.tauh_ws[bh * n + qrow];   // (tau_h, x_max, start)
   State st;
   if (p.tau_init != 0) st = State::from_max(hm.y, nv, p.alpha);
   else if constexpr (MODE == 0) st = State::from_hist_bounded(hm.x, B, hm.y, nv, p.alpha);
+  else if constexpr (MODE == 2) st = State::from_hist_at(hm.x, B, hm.z);
   else st = State::from_hist(hm.x, B);
   float& tau = st.tau;
 
@@ -400,7 +404,7 @@ __global__ __launch_bounds__(64 * OUT_WAVES, 2) void k_refine_out(FwdParams p) {
   const bool secant = alpha > 2.0f;
   int npass = 0;
   unsigned long long n_ref = 0;
-  Frag<T> kf[DS];
+  Frag<T> kf[DS], kf1[DS], kf2[DS];
   while (npass < p.max_iters) {
     if (ballot(!st.done) == 0) break;
     const bool first = (npass == 0);
@@ -411,16 +415,10 @@ __global__ __launch_bounds__(64 * OUT_WAVES, 2) void k_refine_out(FwdParams p) {
     MultiSums<ALPHA2_POINTS> msums;
     const float thi = st.hi - st.tau;    // secant start: f at the bracket's upper end
     Walk wk{-1, 0ull, -1, 0u};
-    int kb = walk_next(wk, thr);
-    if (kb >= 0) Ops::load_k(kf, Kf, kb, c, h);
-    while (kb >= 0) {
-      Frag<T> kc[DS];
-#pragma unroll
-      for (int s = 0; s < DS; ++s) kc[s] = kf[s];
-      const int kn = walk_next(wk, thr);
-      if (kn >= 0) Ops::load_k(kf, Kf, kn, c, h);
+    // a visit: the scores of sub-block kbv against this pass's evaluation points
+    auto visit = [&](const Frag<T> (&kc)[DS], int kbv) {
       ++n_ref;
-      const f32x16 t = tile(kc, kb);
+      const f32x16 t = tile(kc, kbv);
       if constexpr (MODE == 1) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) msums.add(t[r], st.off);
@@ -428,7 +426,26 @@ __global__ __launch_bounds__(64 * OUT_WAVES, 2) void k_refine_out(FwdParams p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) sums.add<MODE>(t[r], thi, secant && first, kappa);
       }
-      kb = kn;
+    };
+    // The K fragments of the next KPF sub-blocks are in flight while one is scored (a visit
+    // is short next to the latency of a load from beyond the L2). Three register slots used
+    // in turn, the loop unrolled by three so that no fragment is moved between slots.
+    int kb0 = walk_next(wk, thr);
+    int kb1 = kb0 >= 0 ? walk_next(wk, thr) : -1;
+    if (kb0 >= 0) Ops::load_k(kf, Kf, kb0, c, h);
+    if (kb1 >= 0) Ops::load_k(kf1, Kf, kb1, c, h);
+    while (kb0 >= 0) {
+      int kb2 = kb1 >= 0 ? walk_next(wk, thr) : -1;
+      if (kb2 >= 0) Ops::load_k(kf2, Kf, kb2, c, h);
+      visit(kf, kb0);
+      if (kb1 < 0) break;
+      kb0 = kb2 >= 0 ? walk_next(wk, thr) : -1;
+      if (kb0 >= 0) Ops::load_k(kf, Kf, kb0, c, h);
+      visit(kf1, kb1);
+      if (kb2 < 0) break;
+      kb1 = kb0 >= 0 ? walk_next(wk, thr) : -1;
+      if (kb1 >= 0) Ops::load_k(kf1, Kf, kb1, c, h);
+      visit(kf2, kb2);
     }
     ++npass;
     if constexpr (MODE == 1) {

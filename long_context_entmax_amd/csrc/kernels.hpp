@@ -53,9 +53,9 @@ struct FwdParams {
   int32_t* hist;         // optional [b, hq, n, B]
   float* tau_h;          // optional [b, hq, n]
   unsigned long long* stats;  // optional [32]
-  float* dmax;           // workspace: per (32-row chunk, 32-key sub-block) max of x*B
+  float* dmax;           // workspace: per (32-row chunk, 32-key sub-block) max of x*B (rows: dmax_row)
   float* wmax;           // workspace: per (32-row chunk, word of 32 sub-blocks) max of dmax [b*hq][n/32][NW32]
-  float2* tauh_ws;       // workspace: (tau_h, x_max) per row [b*hq*n]
+  float4* tauh_ws;       // workspace: (tau_h, x_max, refinement start, 0) per row [b*hq*n]
   int b, hq, hkv, n, G;
   int causal, Br, Bc, B, max_iters;
   float cx;              // (alpha - 1) * scale
@@ -71,6 +71,14 @@ struct FwdParams {
   int dense;             // 1: no block skipping (every valid sub-block visited, every valid mask bit set)
   const float* slopes;   // optional [hq]: position-bias slope m of each query head (scores - m |i - j|)
 };
+
+// Offset of the sub-block maxima of (query head bh, 32-row chunk) in FwdParams::dmax: one fp32
+// per 32-key sub-block the chunk can see -- under the causal mask chunk c sees sub-blocks
+// 0..c, so the table is a packed lower triangle of nkb (nkb + 1) / 2 entries per head.
+__host__ __device__ __forceinline__ size_t dmax_row(const FwdParams& p, size_t bh, int chunk) {
+  if (p.causal) return bh * ((size_t)p.nkb * (p.nkb + 1) / 2) + (size_t)chunk * (chunk + 1) / 2;
+  return (bh * p.nkb + chunk) * (size_t)p.nkb;
+}
 
 // one re-layout of X [heads, n, D] (prep.hip): any of the fragment-major row copy,
 // the fragment-major column copy and delta = X . aux per row (X = dO, aux = o~)
@@ -96,12 +104,9 @@ struct PrepBatch {
 };
 
 struct BwdParams {
-  const void* qr;        // fragment-major copies (rows / cols layouts of prep.hip)
-  const void* qc;
+  const void* qr;        // fragment-major rows copies (prep.hip)
   const void* dor;
-  const void* doc;
   const void* kr;
-  const void* kc;
   const void* vr;
   const float* tau;
   const float* delta;

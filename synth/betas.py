@@ -29,5 +29,5 @@ def beta_for(w) -> float:
     t = load_table()
     k = key(w.name, w.alpha, w.target_sparsity)
     if k not in t:
-        raise KeyError(f"no calibrated beta for {k}; run synth/calibrate_beta.py")
+        raise KeyError(f"no calibrated beta for {k}; run python -m oracle.calibrate_beta")
     return float(t[k]["beta"])

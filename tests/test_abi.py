@@ -338,3 +338,4 @@ def test_binding_accepts_consistent_cpu_tensors_up_to_the_device_check():
     with pytest.raises(ValueError, match="GPU only"):
         lce.bwd(q, k, v, torch.zeros_like(q), torch.zeros(1, 4, 128), torch.zeros(1, 4, 2, 1, dtype=torch.int32),
                 torch.zeros(1, 4, 128, 64), 1.5, True, (64, 64), 16)
+

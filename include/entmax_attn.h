@@ -186,6 +186,30 @@ entmax_status entmax_attn_decode(const entmax_attn_desc *desc,
                                  float *o, float *tau, int32_t *hist_counts, float *tau_h,
                                  void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * Decode without allocation, for callers that cannot allocate device memory or pass a
+ * workspace: code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc. Same arguments, results and checks as entmax_attn_decode, minus the
+ * workspace: the library uses a static scratch of ENTMAX_DECODE_SCRATCH_BYTES bytes per
+ * device instead (allocated when the library's code is loaded on a device, held until the
+ * process ends; its address is looked up on the first call on each device). This call
+ * makes no hipMalloc, hipFree or allocating library call.
+ * Limit: problems whose entmax_attn_decode_workspace_bytes() exceeds the scratch size
+ * (about 16 MB of fp32 scores for 32 query heads x 128K cached keys, plus partial sums)
+ * return ENTMAX_ERR_WORKSPACE before anything is enqueued.
+ * Sharing: every call on a device uses that device's one scratch, and its contents are
+ * left from the last call (nothing in it is read before it is written within a call).
+ * Calls that overlap on one device -- on different streams or host threads without
+ * ordering between them -- race on the scratch; serialise them (one stream, or events).
+ * The stream must belong to the current device.
+ */
+#define ENTMAX_DECODE_SCRATCH_BYTES ((size_t)32 << 20)
+entmax_status entmax_attn_decode_noalloc(const entmax_attn_desc *desc,
+                                         const void *q, const void *k_cache, const void *v_cache,
+                                         const int32_t *lengths, const float *slopes,
+                                         float *o, float *tau, int32_t *hist_counts, float *tau_h,
+                                         void *stream);
+
 const char *entmax_status_string(entmax_status s);
 const char *entmax_last_error(void);
 

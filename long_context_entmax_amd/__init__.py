@@ -72,7 +72,7 @@ _DDP = ctypes.POINTER(DashDesc)
 EXPORTS = [
     "entmax_attn_fwd_workspace_bytes", "entmax_attn_bwd_workspace_bytes", "entmax_attn_aux_bytes",
     "entmax_attn_mask_words", "entmax_attn_fwd", "entmax_attn_bwd", "entmax_attn_decode_workspace_bytes",
-    "entmax_attn_decode", "entmax_dash_fwd_workspace_bytes", "entmax_dash_mask_words", "entmax_dash_fwd",
+    "entmax_attn_decode", "entmax_attn_decode_noalloc", "entmax_dash_fwd_workspace_bytes", "entmax_dash_mask_words", "entmax_dash_fwd",
     "entmax_status_string",
     "entmax_last_error", "entmax_attn_profile", "entmax_attn_profile_read",
 ]
@@ -98,6 +98,8 @@ def lib() -> ctypes.CDLL:
         L.entmax_attn_decode_workspace_bytes.argtypes = [_DP]
         L.entmax_attn_decode.restype = ctypes.c_int
         L.entmax_attn_decode.argtypes = [_DP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+        L.entmax_attn_decode_noalloc.restype = ctypes.c_int
+        L.entmax_attn_decode_noalloc.argtypes = [_DP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
         for f in ("entmax_dash_fwd_workspace_bytes", "entmax_dash_mask_words"):
             getattr(L, f).restype = _sz
             getattr(L, f).argtypes = [_DDP]
@@ -366,6 +368,50 @@ def decode(q, k_cache, v_cache, alpha: float = 1.5, bins: int = 16, scale: Optio
     _check(L.entmax_attn_decode(ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(lengths),
                                 _ptr(slopes), _ptr(o), _ptr(tau), _ptr(hist), _ptr(tau_h), _ptr(workspace),
                                 workspace.numel(), _stream(dev)))
+    return DecodeOut(o, tau, hist, tau_h)
+
+
+# bytes of the static scratch behind decode_noalloc (ENTMAX_DECODE_SCRATCH_BYTES)
+DECODE_SCRATCH_BYTES = 32 << 20
+
+
+def decode_noalloc(q, k_cache, v_cache, alpha: float = 1.5, bins: int = 16, scale: Optional[float] = None,
+                   lengths=None, slopes=None, max_iters: int = 0, tol: float = 0.0, tau_init: int = 0,
+                   out=None) -> DecodeOut:
+    """``decode`` through the library's allocation-free entry point (entmax_attn_decode_noalloc):
+    the library takes its scratch from a static per-device buffer of DECODE_SCRATCH_BYTES
+    instead of a workspace. ``out``: optional DecodeOut of preallocated o [b, hq, d] float32,
+    tau [b, hq] float32 and (both or neither) hist [b, hq, bins] int32 and tau_h [b, hq]; with
+    it this call allocates nothing. Calls that overlap on one device share the scratch."""
+    torch = _torch()
+    if q.dim() != 3 or k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("q must be [b, hq, d] and the caches [b, hkv, n_ctx, d]")
+    b, hq, d = q.shape
+    if k_cache.shape[0] != b or k_cache.shape[3] != d or q.dtype != k_cache.dtype:
+        raise ValueError("q and the caches disagree in batch, head_dim or dtype")
+    if lengths is not None and (lengths.dtype != torch.int32 or lengths.numel() != b):
+        raise ValueError("lengths must be int32 with one value per sequence")
+    _check_slopes(slopes, hq)
+    dev = q.device
+    if out is not None:
+        o, tau, hist, tau_h = out
+        _expect("out.o", o, (b, hq, d), torch.float32, dev)
+        _expect("out.tau", tau, (b, hq), torch.float32, dev)
+        _expect("out.hist", hist, (b, hq, bins), torch.int32, dev)
+        _expect("out.tau_h", tau_h, (b, hq), torch.float32, dev)
+        if o is None or tau is None:
+            raise ValueError("out needs o and tau")
+    _require_gpu(q, k_cache, v_cache, lengths, slopes)
+    dt = ENTMAX_BF16 if q.dtype == torch.bfloat16 else ENTMAX_F32
+    desc = make_desc(b, hq, k_cache.shape[1], k_cache.shape[2], d, dt, alpha, True, (32, 32), bins,
+                     scale, max_iters, tol, tau_init)
+    if out is None:
+        o = torch.empty((b, hq, d), dtype=torch.float32, device=dev)
+        tau = torch.empty((b, hq), dtype=torch.float32, device=dev)
+        hist, tau_h = None, None
+    _check(lib().entmax_attn_decode_noalloc(ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                            _ptr(lengths), _ptr(slopes), _ptr(o), _ptr(tau), _ptr(hist),
+                                            _ptr(tau_h), _stream(dev)))
     return DecodeOut(o, tau, hist, tau_h)
 
 

@@ -266,6 +266,39 @@ static entmax_status derive_dash(const entmax_dash_desc* d, DashDerived& o) {
 
 static size_t dash_kv_bytes(const DashDerived& o) { return align256((size_t)o.b * o.hkv * o.n * o.D * o.es); }
 
+// Scratch of the allocation-free decode entry point. Every device that loads this library
+// holds its own instance until the process ends. In host code `scratch` only names the
+// symbol: its device address (per device) comes from hipGetSymbolAddress, and only that
+// address is handed to kernels.
+static __device__ __align__(256) unsigned char scratch[ENTMAX_DECODE_SCRATCH_BYTES];
+
+namespace {
+constexpr int SCRATCH_MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+char* g_scratch_ptr[SCRATCH_MAX_DEVICES] = {};
+}  // namespace
+
+// Device address of the current device's scratch, looked up once per device (with that
+// device current) and kept.
+static entmax_status decode_scratch(char** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= SCRATCH_MAX_DEVICES)
+    return fail(ENTMAX_ERR_UNSUPPORTED, "device %d: the static scratch serves devices 0..%d", dev,
+                SCRATCH_MAX_DEVICES - 1);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!ptr) return fail(ENTMAX_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = (char*)ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return ENTMAX_OK;
+}
+
 }  // namespace entmax
 
 using namespace entmax;
@@ -493,6 +526,27 @@ entmax_status entmax_attn_decode(const entmax_attn_desc* desc, const void* q, co
   const hipError_t e = launch_decode(p, o.dtype, o.D, o.mode, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "decode kernels");
   return ENTMAX_OK;
+}
+
+entmax_status entmax_attn_decode_noalloc(const entmax_attn_desc* desc, const void* q, const void* k_cache,
+                                         const void* v_cache, const int32_t* lengths, const float* slopes,
+                                         float* o_, float* tau, int32_t* hist_counts, float* tau_h,
+                                         void* stream) {
+  Derived o;
+  entmax_status st = derive(desc, o, true);
+  if (st != ENTMAX_OK) return st;
+  const size_t need = dec_ws(o).total;
+  if (need > (size_t)ENTMAX_DECODE_SCRATCH_BYTES)
+    return fail(ENTMAX_ERR_WORKSPACE,
+                "decode without allocation: this problem needs %zu bytes of scratch, the static scratch "
+                "holds %zu; call entmax_attn_decode with a workspace instead",
+                need, (size_t)ENTMAX_DECODE_SCRATCH_BYTES);
+  if ((size_t)o.b * o.hq == 0) return ENTMAX_OK;
+  char* ws = nullptr;
+  st = decode_scratch(&ws);
+  if (st != ENTMAX_OK) return st;
+  return entmax_attn_decode(desc, q, k_cache, v_cache, lengths, slopes, o_, tau, hist_counts, tau_h, ws, need,
+                            stream);
 }
 
 size_t entmax_dash_fwd_workspace_bytes(const entmax_dash_desc* desc) {

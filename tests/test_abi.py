@@ -339,3 +339,15 @@ def test_binding_accepts_consistent_cpu_tensors_up_to_the_device_check():
         lce.bwd(q, k, v, torch.zeros_like(q), torch.zeros(1, 4, 128), torch.zeros(1, 4, 2, 1, dtype=torch.int32),
                 torch.zeros(1, 4, 128, 64), 1.5, True, (64, 64), 16)
 
+
+def test_noalloc_decode_rejects_problems_beyond_the_scratch(L):
+    """The allocation-free decode refuses, before any HIP call, a problem whose workspace
+    exceeds the static scratch, and accepts the 128K-key, 32-query-head cache."""
+    big = lce.make_desc(4, 32, 8, 131072, 64, lce.ENTMAX_BF16, 1.5, True, (32, 32), 16)
+    assert L.entmax_attn_decode_workspace_bytes(ctypes.byref(big)) > lce.DECODE_SCRATCH_BYTES
+    st = L.entmax_attn_decode_noalloc(ctypes.byref(big), 16, 16, 16, None, None, 16, 16, None, None, None)
+    assert st == 6 and b"static scratch" in L.entmax_last_error()
+    c5 = lce.make_desc(1, 32, 8, 131072, 64, lce.ENTMAX_BF16, 1.5, True, (32, 32), 16)
+    assert L.entmax_attn_decode_workspace_bytes(ctypes.byref(c5)) <= lce.DECODE_SCRATCH_BYTES
+    bad = lce.make_desc(1, 32, 8, 131072, 64, lce.ENTMAX_BF16, 0.5, True, (32, 32), 16)
+    assert L.entmax_attn_decode_noalloc(ctypes.byref(bad), 16, 16, 16, None, None, 16, 16, None, None, None) == 3

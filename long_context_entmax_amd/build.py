@@ -24,6 +24,8 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"),
     "-Wno-unused-command-line-argument",
+    # extra hipcc flags for tuning builds (e.g. -DENTMAX_HIST_WAVES64=4)
+    *os.environ.get("ENTMAX_HIPCC_FLAGS", "").split(),
 ]
 
 

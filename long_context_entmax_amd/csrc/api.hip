@@ -156,7 +156,7 @@ static entmax_status derive(const entmax_attn_desc* d, Derived& o, bool decode =
   // histogram work group: HW waves x 32 rows over GP query heads of one KV head (HW = 4 at
   // head_dim 128 in bf16, else 8; the kernels check that they were built for the same shape)
   o.QW = 32;
-  const int HW = (o.D == 128 && d->dtype == ENTMAX_BF16) ? 4 : 8;
+  const int HW = (o.D == 128 && d->dtype == ENTMAX_BF16) ? 4 : (o.D == 64 && d->dtype == ENTMAX_BF16) ? ENTMAX_HIST_WAVES64 : 8;
   o.GP = 1;
   for (int gp : {8, 4, 2}) {
     if (gp <= HW && o.G % gp == 0 && ((HW / gp) * o.QW) % o.Br == 0) {
@@ -376,6 +376,8 @@ entmax_status entmax_attn_fwd(const entmax_attn_desc* desc, const void* q, const
   p.alpha = o.alpha; p.kappa = o.kappa; p.tol = o.tol;
   p.GP = o.GP; p.RH = o.RH; p.RG = o.RG;
   p.nkb = o.nkb; p.NW32 = o.NW32; p.Tr = o.Tr; p.Tc = o.Tc; p.W = o.W;
+  p.out_lds_wmax = (int)(((size_t)o.nkb * 2 + 15) & ~(size_t)15);
+  p.out_lds_wave = p.out_lds_wmax + (int)(((size_t)o.NW32 * 4 + 15) & ~(size_t)15);
   // Causal rows differ in length. When the whole histogram grid is resident at once (two
   // 8-wave groups per CU at head_dim 64 in bf16), pair long and short groups on a CU;
   // otherwise longest first is the better order.

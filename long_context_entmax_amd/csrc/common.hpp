@@ -299,12 +299,40 @@ struct Weight {
   }
 };
 
+// Buffer resource over `bytes` bytes at p (raw buffer: loads past the end return 0).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+// One 16-byte buffer load at byte offset voff (per lane) + soff (wave-uniform).
+__device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+}
+
 // K operand loads and transposed score tiles of the attention kernels: fragment-major K
 // (the row layout of prep.hip), tile = keys x queries, lane c of the B operand = query.
 template <typename T, int D>
 struct KvOps {
   static constexpr int DS = D / 16;
   static constexpr int DC = D / 32;
+  // The same fragments of sub-block kb through a buffer resource over one head's K copy:
+  // the per-lane offset is fixed and the sub-block offset is a scalar, so a load needs no
+  // vector address arithmetic (and no address register that a wait would have to guard).
+  __device__ __forceinline__ static void load_k_buf(Frag<T> (&f)[DS], __amdgpu_buffer_rsrc_t r, int kb, int lane) {
+    const uint32_t soff = (uint32_t)kb * (uint32_t)(DS * 512 * sizeof(T));
+#pragma unroll
+    for (int s = 0; s < DS; ++s) {
+      const uint32_t voff = (uint32_t)(s * 512 + lane * 8) * (uint32_t)sizeof(T);
+      if constexpr (sizeof(T) == 2) {
+        const u32x4 v = buffer_load16(r, voff, soff);
+        f[s].v = __builtin_bit_cast(bf16x8, v);
+      } else {
+        const u32x4 a = buffer_load16(r, voff, soff);
+        const u32x4 b = buffer_load16(r, voff + 16, soff);
+        f[s].a = __builtin_bit_cast(f32x4, a);
+        f[s].b = __builtin_bit_cast(f32x4, b);
+      }
+    }
+  }
   // K fragments of sub-block kb (A operand: lane c is key 32 kb + c): one contiguous
   // 1 KB run per fragment at a wave-uniform base plus lane * 8 elements
   __device__ __forceinline__ static void load_k(Frag<T> (&f)[DS], const T* Kf, int kb, int c, int h) {

@@ -41,17 +41,14 @@
 namespace entmax {
 
 
-#ifndef HIST_OCC64
-#define HIST_OCC64 4
-#endif
 // Waves per histogram work group and the waves per SIMD the register budget allows: eight
 // 32-row waves at head_dim 64 (four per SIMD in bf16, 128 registers); four at head_dim 128
 // in bf16, where a wave needs more than 128 registers, so that three groups (three waves per
 // SIMD) share a CU instead of one eight-wave group.
 template <typename T, int D>
-constexpr int hist_waves() { return (D == 128 && sizeof(T) == 2) ? 4 : 8; }
+constexpr int hist_waves() { return (D == 128 && sizeof(T) == 2) ? 4 : (D == 64 && sizeof(T) == 2) ? ENTMAX_HIST_WAVES64 : 8; }
 template <typename T, int D>
-constexpr int hist_occ() { return (D == 64 && sizeof(T) == 2) ? HIST_OCC64 : (D == 128 && sizeof(T) == 2) ? 3 : 2; }
+constexpr int hist_occ() { return (D == 64 && sizeof(T) == 2) ? ENTMAX_HIST_OCC64 : (D == 128 && sizeof(T) == 2) ? 3 : 2; }
 constexpr int ALPHA2_POINTS = 2;   // evaluation points per refinement pass at alpha = 2 (2 beat 3 and 4)
 constexpr int OUT_WAVES = 4;
 
@@ -321,6 +318,7 @@ __global__ __launch_bounds__(64 * OUT_WAVES, 2) void k_refine_out(FwdParams p) {
   const T* Q = reinterpret_cast<const T*>(p.q) + bh * n * D;
   const T* Kf = reinterpret_cast<const T*>(p.kf) + ((size_t)(bi * p.hkv + kvh) * n) * D;
   const T* Vf = reinterpret_cast<const T*>(p.vf) + ((size_t)(bi * p.hkv + kvh) * n) * D;
+  const __amdgpu_buffer_rsrc_t krs = buffer_rsrc(Kf, (uint32_t)((size_t)n * D * sizeof(T)));
   const float* dmx = p.dmax + dmax_row(p, bh, chunk);
   const float* wmx = p.wmax + (bh * p.nkb + chunk) * p.NW32;
 
@@ -346,10 +344,30 @@ __global__ __launch_bounds__(64 * OUT_WAVES, 2) void k_refine_out(FwdParams p) {
   else st = State::from_hist(hm.x, B);
   float& tau = st.tau;
 
+  // The chunk's sub-block maxima and word maxima are staged once in this wave's part of LDS
+  // (sub-block maxima as bf16 rounded up, so a walk never skips a sub-block it needs), so the
+  // walks below read them from LDS: reads of the maxima from global memory would share the
+  // vector-memory wait counter with the K fragments in flight, and every wait for a maximum
+  // would also wait for the prefetched K.
+  extern __shared__ __align__(16) uint8_t out_lds[];
+  uint16_t* const ldmax = reinterpret_cast<uint16_t*>(out_lds + (size_t)w * p.out_lds_wave);
+  float* const lwmax = reinterpret_cast<float*>(out_lds + (size_t)w * p.out_lds_wave + p.out_lds_wmax);
+  if (!p.dense) {
+    for (int i = lane; i < kb_end; i += 64) {
+      const uint32_t bits = __float_as_uint(dmx[i]);
+      // bf16 rounded towards +inf: truncation raises a negative value; a positive value with
+      // dropped bits goes one step up (-inf and +inf stay)
+      const uint32_t up = ((bits >> 31) == 0 && (bits & 0xFFFFu) != 0) ? 1u : 0u;
+      ldmax[i] = (uint16_t)((bits >> 16) + up);
+    }
+    for (int i = lane; i < nwords; i += 64) lwmax[i] = wmx[i];
+    // (only this wave reads its part, and a wave's LDS accesses complete in order)
+    __builtin_amdgcn_wave_barrier();
+  }
   // Walk over the sub-blocks a pass needs: those whose recorded chunk maximum exceeds the
   // threshold (non-candidates hold -inf). Words of 32 sub-blocks are screened 64 at a time
-  // through their maxima (one load per lane), so a pass loads the chunk maxima of the words
-  // it needs only.
+  // through their maxima (one LDS read per lane), so a pass reads the chunk maxima of the
+  // words it needs only.
   struct Walk {
     int g;          // group of 64 words being walked
     uint64_t nm;    // its needed words not yet started
@@ -362,13 +380,13 @@ __global__ __launch_bounds__(64 * OUT_WAVES, 2) void k_refine_out(FwdParams p) {
       while (wk.nm == 0) {
         if (64 * (++wk.g) >= nwords) return -1;
         const int wl = 64 * wk.g + lane;
-        const float wm = wl < nwords ? wmx[wl] : -INFINITY;
+        const float wm = wl < nwords ? lwmax[wl] : -INFINITY;
         wk.nm = ballot(wm > thr);
       }
       wk.wi = 64 * wk.g + __builtin_ctzll(wk.nm);
       wk.nm &= wk.nm - 1;
       const int kbl = wk.wi * 32 + (lane & 31);
-      const float dv = kbl < kb_end ? dmx[kbl] : -INFINITY;
+      const float dv = kbl < kb_end ? __uint_as_float((uint32_t)ldmax[kbl] << 16) : -INFINITY;
       wk.word = (uint32_t)ballot(dv > thr);
     }
     const int kb = wk.wi * 32 + __builtin_ctz(wk.word);
@@ -430,21 +448,24 @@ __global__ __launch_bounds__(64 * OUT_WAVES, 2) void k_refine_out(FwdParams p) {
     // The K fragments of the next KPF sub-blocks are in flight while one is scored (a visit
     // is short next to the latency of a load from beyond the L2). Three register slots used
     // in turn, the loop unrolled by three so that no fragment is moved between slots.
+    // Every stage issues its load (sub-block 0 stands in once the walk has ended), so each
+    // slot's fragments are a fixed number of loads behind the newest and the compiler's wait
+    // before a visit covers that slot only.
     int kb0 = walk_next(wk, thr);
     int kb1 = kb0 >= 0 ? walk_next(wk, thr) : -1;
-    if (kb0 >= 0) Ops::load_k(kf, Kf, kb0, c, h);
-    if (kb1 >= 0) Ops::load_k(kf1, Kf, kb1, c, h);
+    Ops::load_k_buf(kf, krs, max(kb0, 0), lane);
+    Ops::load_k_buf(kf1, krs, max(kb1, 0), lane);
     while (kb0 >= 0) {
       int kb2 = kb1 >= 0 ? walk_next(wk, thr) : -1;
-      if (kb2 >= 0) Ops::load_k(kf2, Kf, kb2, c, h);
+      Ops::load_k_buf(kf2, krs, max(kb2, 0), lane);
       visit(kf, kb0);
       if (kb1 < 0) break;
       kb0 = kb2 >= 0 ? walk_next(wk, thr) : -1;
-      if (kb0 >= 0) Ops::load_k(kf, Kf, kb0, c, h);
+      Ops::load_k_buf(kf, krs, max(kb0, 0), lane);
       visit(kf1, kb1);
       if (kb2 < 0) break;
       kb1 = kb0 >= 0 ? walk_next(wk, thr) : -1;
-      if (kb1 >= 0) Ops::load_k(kf1, Kf, kb1, c, h);
+      Ops::load_k_buf(kf1, krs, max(kb1, 0), lane);
       visit(kf2, kb2);
     }
     ++npass;
@@ -665,8 +686,12 @@ static hipError_t launch_fwd_t(const FwdParams& p, int mode, hipStream_t s) {
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // (at head_dim 128 the extra accumulator block of the folded form would spill)
   void (*out_fn)(FwdParams) = out_kernel<T, D>(qs && D == 64, bias, mode);
+  const size_t out_lds = (size_t)OUT_WAVES * p.out_lds_wave;
+  if (out_lds > 160 * 1024) return hipErrorInvalidConfiguration;
+  e = hipFuncSetAttribute((const void*)out_fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)out_lds);
+  if (e != hipSuccess) return e;
   prof_begin("entmax_fwd_refine_out", s);
-  hipLaunchKernelGGL(out_fn, dim3(grid2), dim3(64 * OUT_WAVES), 0, s, p);
+  hipLaunchKernelGGL(out_fn, dim3(grid2), dim3(64 * OUT_WAVES), out_lds, s, p);
   prof_end(s);
   return hipGetLastError();
 }

@@ -5,6 +5,15 @@
 
 namespace entmax {
 
+// Waves (32 query rows each) of a histogram work group at head_dim 64 in bf16, and the waves
+// per SIMD its register budget is built for (both tunable at build time).
+#ifndef ENTMAX_HIST_WAVES64
+#define ENTMAX_HIST_WAVES64 8
+#endif
+#ifndef ENTMAX_HIST_OCC64
+#define ENTMAX_HIST_OCC64 4
+#endif
+
 // Work-group to (unit, rank) map. A unit is one (batch, KV head); all of its work
 // groups land on the same XCD (work group i runs on XCD i % 8) so K/V blocks are
 // reused from that XCD's L2. rank 0 is the longest work item of the unit.
@@ -64,6 +73,8 @@ struct FwdParams {
   int RH;                // rows per head per work group
   int RG;                // row groups per head = ceil(n / RH)
   int nkb, NW32;         // 32-key sub-blocks, words of sub-block bits
+  int out_lds_wave;      // refinement kernel: LDS bytes per wave (sub-block maxima as bf16, then word maxima)
+  int out_lds_wmax;      // offset of the word maxima in a wave's LDS part
   int Tr, Tc, W;
   WgMap map;             // histogram kernel
   WgMap map2;            // refinement/output kernel

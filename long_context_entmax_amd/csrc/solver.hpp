@@ -369,19 +369,28 @@ struct MultiState {
 #pragma unroll
     for (int k = 0; k < NP; ++k)
       if (F[k] - 1.0f >= 0.0f) klo = k;          // f decreases: a prefix of the points
+    // the values at points klo and klo + 1, picked with constant indices (selects, so the
+    // arrays stay in registers)
+    float off_lo = 0.f, f_lo = 0.f, off_nx = 0.f, f_nx = 0.f;
+    int n_lo = 0, n_nx = -1;
+#pragma unroll
+    for (int k = 0; k < NP; ++k) {
+      if (k == klo) { off_lo = off[k]; f_lo = F[k] - 1.0f; n_lo = N[k]; }
+      if (k == klo + 1) { off_nx = off[k]; f_nx = F[k] - 1.0f; n_nx = N[k]; }
+    }
     if (klo >= 0) {
-      lo = tau + off[klo];
-      flo = F[klo] - 1.0f;
-      nlo = N[klo];
+      lo = tau + off_lo;
+      flo = f_lo;
+      nlo = n_lo;
     }
     int nnext = -1;
     float tnext = hi;
     if (klo + 1 < NP) {
-      tnext = tau + off[klo + 1];
+      tnext = tau + off_nx;
       hi = tnext;
-      fhi = F[klo + 1] - 1.0f;
+      fhi = f_nx;
       fhi_known = true;
-      nnext = N[klo + 1];
+      nnext = n_nx;
     }
     const float tabs = tol * fmaxf(1.0f, fabsf(lo));
     if (nlo > 0) {

@@ -143,8 +143,11 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void k_bwd_dkv(BwdParams p)
       tv[g4] = *reinterpret_cast<const f32x4*>(p.tau + qrow0 + q0 + 8 * g4 + 4 * h);
       dl[g4] = *reinterpret_cast<const f32x4*>(p.delta + qrow0 + q0 + 8 * g4 + 4 * h);
     }
+    // the next item's rows are loaded on every item (the current item's again after the
+    // last), so the wait before an operand counts a fixed number of newer loads and does
+    // not drain the prefetch
     have = next_item(g_next, q0_next);
-    if (have) load_rows(g_next, q0_next);
+    load_rows(have ? g_next : gc, have ? q0_next : q0);
     f32x16 S = f32x16{};
 #pragma unroll
     for (int s = 0; s < DS; ++s) mma16(S, qa[s], kb[s]);   // S[q][key]
@@ -327,10 +330,13 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void k_bwd_dq(BwdParams p) 
       ka[s] = kn[s];
       load_frag(va[s], Vr + rows_off(kbk, s, DS, lane));
     }
+    // loaded on every item (the current sub-block again after the last), so the waits
+    // before the current item's operands do not drain the prefetch
     have = next_item(kb_next);
-    if (have) {
+    {
+      const int kbl = have ? kb_next : kbk;
 #pragma unroll
-      for (int s = 0; s < DS; ++s) load_frag(kn[s], Kr + rows_off(kb_next, s, DS, lane));
+      for (int s = 0; s < DS; ++s) load_frag(kn[s], Kr + rows_off(kbl, s, DS, lane));
     }
     f32x16 S = f32x16{};
 #pragma unroll

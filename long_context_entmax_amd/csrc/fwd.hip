@@ -141,8 +141,10 @@ __global__ __launch_bounds__((64 * hist_waves<T, D>()), (hist_occ<T, D>())) void
   // in any recency-weighted data) the running max settles early and the far, lower tiles
   // find the window already in place (fewer slides, fewer active tiles).
   const int last_pair = (kb_end - 1) >> 1;
-  Ops::load_k(kf, Kf, 2 * last_pair, c, h);
-  if (2 * last_pair + 1 < kb_end) Ops::load_k(kf2, Kf, 2 * last_pair + 1, c, h);
+  // K fragments through a buffer resource: a fixed lane offset and a scalar sub-block offset
+  const __amdgpu_buffer_rsrc_t krs = buffer_rsrc(Kf, (uint32_t)((size_t)n * D * sizeof(T)));
+  Ops::load_k_buf(kf, krs, 2 * last_pair, lane);
+  Ops::load_k_buf(kf2, krs, min(2 * last_pair + 1, kb_end - 1), lane);
   // x * B - base of sub-block kbb (with the head's position bias)
   auto tile = [&](const Frag<T> (&kc)[DS], int kbb) -> f32x16 {
     if constexpr (BIAS) {
@@ -171,10 +173,10 @@ __global__ __launch_bounds__((64 * hist_waves<T, D>()), (hist_occ<T, D>())) void
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc1[r] = -INFINITY;
     }
-    if (kb >= 2) {                      // every pair below the last one is whole
-      Ops::load_k(kf, Kf, kb - 2, c, h);
-      Ops::load_k(kf2, Kf, kb - 1, c, h);
-    }
+    // the next pair (every pair below the last one is whole); loaded on every step, the
+    // first pair again at the end, so the waits at the next step count a fixed number of loads
+    Ops::load_k_buf(kf, krs, max(kb - 2, 0), lane);
+    Ops::load_k_buf(kf2, krs, max(kb - 1, 0), lane);
     const float bF = (float)base;
     const float t0 = max16(acc0) + bF;   // largest x*B of each tile
     const float t1 = max16(acc1) + bF;
@@ -518,18 +520,34 @@ __global__ __launch_bounds__(64 * OUT_WAVES, 2) void k_refine_out(FwdParams p) {
     // a weight), so the P.V product does not wait for it
     constexpr bool VPRE = D == 64;
     Frag<T> vn[VPRE ? DC : 1][2];
+    // V fragments of sub-block kbv through a buffer resource (fixed lane offset, scalar
+    // sub-block offset), like K
+    const __amdgpu_buffer_rsrc_t vrs = buffer_rsrc(Vf, (uint32_t)((size_t)n * D * sizeof(T)));
     auto load_v = [&](Frag<T> (&dst)[VPRE ? DC : 1][2], int kbv) {
-      const T* vp = Vf + (size_t)kbv * (DC * 1024);
+      const uint32_t soff = (uint32_t)kbv * (uint32_t)(DC * 1024 * sizeof(T));
 #pragma unroll
       for (int dc = 0; dc < (VPRE ? DC : 1); ++dc)
 #pragma unroll
-        for (int m = 0; m < 2; ++m) load_frag(dst[dc][m], vp + (dc * 2 + m) * 512 + lane * 8);
+        for (int m = 0; m < 2; ++m) {
+          const uint32_t voff = (uint32_t)((dc * 2 + m) * 512 + lane * 8) * (uint32_t)sizeof(T);
+          if constexpr (sizeof(T) == 2) {
+            dst[dc][m].v = __builtin_bit_cast(bf16x8, buffer_load16(vrs, voff, soff));
+          } else {
+            dst[dc][m].a = __builtin_bit_cast(f32x4, buffer_load16(vrs, voff, soff));
+            dst[dc][m].b = __builtin_bit_cast(f32x4, buffer_load16(vrs, voff + 16, soff));
+          }
+        }
     };
     Walk wk{-1, 0ull, -1, 0u};
     int kb = walk_next(wk, othr);
-    if (kb >= 0) {
+    // head_dim 64: the next sub-block's fragments are loaded on every visit (sub-block 0
+    // once the walk has ended), so a visit's waits do not drain them. (At head_dim 128 the
+    // same form measured slower: 16K output pass +17%.)
+    if constexpr (VPRE) {
+      Ops::load_k_buf(kf, krs, max(kb, 0), lane);
+      load_v(vn, max(kb, 0));
+    } else if (kb >= 0) {
       Ops::load_k(kf, Kf, kb, c, h);
-      if constexpr (VPRE) load_v(vn, kb);
     }
     while (kb >= 0) {
       Frag<T> kc[DS];
@@ -543,9 +561,11 @@ __global__ __launch_bounds__(64 * OUT_WAVES, 2) void k_refine_out(FwdParams p) {
           for (int m = 0; m < 2; ++m) vc[dc][m] = vn[dc][m];
       }
       const int kn = walk_next(wk, othr);
-      if (kn >= 0) {
+      if constexpr (VPRE) {
+        Ops::load_k_buf(kf, krs, max(kn, 0), lane);
+        load_v(vn, max(kn, 0));
+      } else if (kn >= 0) {
         Ops::load_k(kf, Kf, kn, c, h);
-        if constexpr (VPRE) load_v(vn, kn);
       }
       const f32x16 t = tile(kc, kb);
       f32x16 pw, gw;

@@ -49,6 +49,46 @@ template <typename T, int D>
 constexpr int hist_waves() { return (D == 128 && sizeof(T) == 2) ? 4 : (D == 64 && sizeof(T) == 2) ? ENTMAX_HIST_WAVES64 : 8; }
 template <typename T, int D>
 constexpr int hist_occ() { return (D == 64 && sizeof(T) == 2) ? ENTMAX_HIST_OCC64 : (D == 128 && sizeof(T) == 2) ? 3 : 2; }
+// Histogram cells per wave in LDS: 18 rows of 64 lane columns (4608 B), enough for the
+// B + 2 cells of every supported B (B <= 16); the row of a cell is the second byte of its
+// LDS address, so the wave's histogram lies at a fixed multiple of 4608 B.
+constexpr int HIST_ROWS = 18;
+constexpr uint32_t HIST_WAVE_BYTES = HIST_ROWS * 64 * 4;
+
+// Count 16 scores of a tile: cell = trunc(y) saturated at 0 goes straight into the second byte
+// of the lane's address register (an SDWA conversion that keeps the other bytes: lane * 4 in
+// the first byte, zero above), and the wave's histogram offset is the instruction's immediate.
+// One conversion and one LDS add per score; cells of any y in [0, 18) stay inside the wave's
+// rows, y < 1 (and NaN) lands in the discard cell 0.
+template <uint32_t OFF>
+__device__ __forceinline__ void count16(const f32x16& a, uint32_t& ad, uint32_t one) {
+#define ENTMAX_CNT(i) "v_cvt_u32_f32_sdwa %0, %" #i " dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:DWORD\n" \
+                      "ds_add_u32 %0, %1 offset:%18\n"
+  asm volatile(ENTMAX_CNT(2) ENTMAX_CNT(3) ENTMAX_CNT(4) ENTMAX_CNT(5) ENTMAX_CNT(6) ENTMAX_CNT(7)
+               ENTMAX_CNT(8) ENTMAX_CNT(9) ENTMAX_CNT(10) ENTMAX_CNT(11) ENTMAX_CNT(12) ENTMAX_CNT(13)
+               ENTMAX_CNT(14) ENTMAX_CNT(15) ENTMAX_CNT(16) ENTMAX_CNT(17)
+               : "+v"(ad)
+               : "v"(one), "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]),
+                 "v"(a[7]), "v"(a[8]), "v"(a[9]), "v"(a[10]), "v"(a[11]), "v"(a[12]), "v"(a[13]),
+                 "v"(a[14]), "v"(a[15]), "i"(OFF)
+               : "memory");
+#undef ENTMAX_CNT
+}
+// both tiles of a step into the histogram of wave w (w < HW)
+template <int HW>
+__device__ __forceinline__ void count_pair(int w, const f32x16& a0, const f32x16& a1, uint32_t& ad, uint32_t one) {
+#define ENTMAX_CASE(k)                                      \
+  case k:                                                   \
+    if constexpr (k < HW) {                                 \
+      count16<k * HIST_WAVE_BYTES>(a0, ad, one);            \
+      count16<k * HIST_WAVE_BYTES>(a1, ad, one);            \
+    }                                                       \
+    break;
+  switch (w) { ENTMAX_CASE(0) ENTMAX_CASE(1) ENTMAX_CASE(2) ENTMAX_CASE(3)
+               ENTMAX_CASE(4) ENTMAX_CASE(5) ENTMAX_CASE(6) ENTMAX_CASE(7) }
+#undef ENTMAX_CASE
+}
+
 constexpr int ALPHA2_POINTS = 2;   // evaluation points per refinement pass at alpha = 2 (2 beat 3 and 4)
 constexpr int OUT_WAVES = 4;
 
@@ -80,7 +120,8 @@ __global__ __launch_bounds__((64 * hist_waves<T, D>()), (hist_occ<T, D>())) void
   const T* Kf = reinterpret_cast<const T*>(p.kf) + ((size_t)(bi * p.hkv + kvh) * n) * D;
   // position bias of this head on the x*B scale: x*B gains -cmB |i - j|
   const float cmB = BIAS ? p.slopes[head] * (p.alpha - 1.0f) * (float)B : 0.0f;
-  uint32_t* hist = lds + (w * (B + 2)) * 64;   // [B + 2][64] of this wave
+  static_assert(HW <= 8, "histogram offsets are written for at most eight waves");
+  uint32_t* hist = lds + w * (HIST_ROWS * 64);  // [B + 2][64] of this wave (in an 18-row slot)
   for (int i = lane; i < (B + 2) * 64; i += 64) hist[i] = 0;
   float* dmx = p.dmax + dmax_row(p, bh, row0 >> 5);
   float* wx_out = p.wmax + (bh * p.nkb + (row0 >> 5)) * p.NW32;
@@ -131,7 +172,6 @@ __global__ __launch_bounds__((64 * hist_waves<T, D>()), (hist_occ<T, D>())) void
   f32x16 negb;            // -base in every register (initial accumulator)
 #pragma unroll
   for (int r = 0; r < 16; ++r) negb[r] = (float)B;
-  uint32_t* const hl = hist + lane;          // this lane's column: cell j at hl[64 j]
   float dreg = -INFINITY; // lane j < 32 keeps the chunk max of sub-block 32*word + j
   unsigned long long n_cand = 0;
 
@@ -163,13 +203,17 @@ __global__ __launch_bounds__((64 * hist_waves<T, D>()), (hist_occ<T, D>())) void
       return a;
     }
   };
+  uint32_t cad = 4u * (uint32_t)lane;        // LDS address of a count: cell in its second byte
+  const uint32_t one = 1u;
   for (int kb = 2 * last_pair; kb >= 0; kb -= 2) {
+    // The second tile of the last pair may lie past the last valid sub-block: under the causal
+    // mask every one of its keys comes after the wave's rows (so it is -inf already), and its
+    // loads past the end of K read zeros through the buffer bounds.
     const bool two = kb + 1 < kb_end;
     f32x16 acc0 = tile(kf, kb);
-    f32x16 acc1;
-    if (two) {
-      acc1 = tile(kf2, kb + 1);
-    } else {
+    f32x16 acc1 = tile(kf2, kb + 1);
+    if (!two) {
+      asm volatile("" ::: "memory");   // a branch taken once per wave at most: keep it one
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc1[r] = -INFINITY;
     }
@@ -228,20 +272,7 @@ __global__ __launch_bounds__((64 * hist_waves<T, D>()), (hist_occ<T, D>())) void
         have = true;
       }
       // count every score of both tiles (lanes with no active tile land in cell 0)
-      if (p.tau_init == 0) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const uint32_t cell = cvt_u32_sat(acc0[r]);
-          atomicAdd(hl + (cell << 6), 1u);
-        }
-        if (two) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const uint32_t cell = cvt_u32_sat(acc1[r]);
-            atomicAdd(hl + (cell << 6), 1u);
-          }
-        }
-      }
+      if (p.tau_init == 0) count_pair<HW>(w, acc0, acc1, cad, one);
     }
     // flush a finished word of chunk maxima and its own maximum (-inf: no candidate in the
     // word; pairs never straddle a word, which is complete once its lowest sub-block,
@@ -682,11 +713,11 @@ static void (*out_kernel(bool qs, bool bias, int mode))(FwdParams) {
                                                                      : k_refine_out<T, D, 0, false, false>;
 }
 
-static size_t fwd_lds_bytes(int B, int waves) { return (size_t)(waves * (B + 2) * 64) * sizeof(uint32_t); }
+static size_t fwd_lds_bytes(int waves) { return (size_t)waves * HIST_WAVE_BYTES; }
 
 template <typename T, int D>
 static hipError_t launch_fwd_t(const FwdParams& p, int mode, hipStream_t s) {
-  const size_t lds = fwd_lds_bytes(p.B, hist_waves<T, D>());
+  const size_t lds = fwd_lds_bytes(hist_waves<T, D>());
   // the work decomposition (rows per head and work group) is sized for this group shape
   if (p.RH != (hist_waves<T, D>() / p.GP) * 32) return hipErrorInvalidConfiguration;
   const int grid = wgmap_grid(p.map);

@@ -54,7 +54,7 @@ typedef struct {
     float gamma;          /* routing logit multiplier, > 0; 0 means 1 */
     float sigma;          /* prior strength, >= 0 (0: uniform over the active keys) */
     float scale;          /* score scale; 0 means 1/sqrt(head_dim) */
-    int32_t max_iters;    /* routing solver pass cap, 0 (= 15) or 1..15 */
+    int32_t max_iters;    /* routing solver pass cap, 0 (= 15, 30 for alpha > 2) or 1..30 */
     float tol;            /* routing solver tolerance as in entmax_attn_desc; 0 means 2^-20 */
 } entmax_dash_desc;
 

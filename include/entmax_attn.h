@@ -85,16 +85,19 @@ typedef struct {
     int32_t n_bins;       /* B, histogram bins: 2, 4, 8 or 16 (bin width 1/B on the x-scale) */
     float scale;          /* score scale; 0 means 1/sqrt(head_dim) */
     int32_t max_iters;    /* cap on refinement passes; 0 means 8 for alpha <= 1.5, 12 for
-                             1.5 < alpha <= 2, 15 for alpha > 2; at most 15 */
+                             1.5 < alpha <= 2, 30 for alpha > 2 (where a key sitting on the
+                             root can stall the secant; those rows end at the cap or when
+                             fp32 can no longer move tau); at most 30 */
     float tol;            /* alpha 1.5 and 2: stop when |step| <= tol * max(1, |tau|); 0 means
-                             2^-20. Other alpha stop when |sum p - 1| <= 1e-4 at the
-                             evaluated tau (tol unused there) */
+                             2^-20. Other alpha stop when |sum p - 1| <= 1e-4 min(1, |f'|)
+                             at the evaluated tau, f' = -sum_j p_ij^(2-alpha) / (alpha - 1)
+                             the slope of sum p in tau (tol unused there) */
     int32_t tau_init;     /* start of the refinement: 0 = the histogram bound tau_h and the
                              bracket [tau_h, tau_h + 1/B] (AdaSplash-2 (zh) §2.1-2.2, AdaSplash-2 (ja)
                              §2.1-2.2); 1 = no histogram, the plain bracket
                              [x_max - 1, x_max - n_valid^(1-alpha)] from its lower end (the
                              start the pages measure the histogram against, AdaSplash-2 (es) §4),
-                             for ablation; max_iters 0 then means 15 */
+                             for ablation; max_iters 0 then means 15 (30 for alpha > 2) */
     int32_t dense;        /* 0 = skip all-zero key blocks (the method, AdaSplash-2 (zh) §2.3:
                              work O(|M|) instead of O(Tr x Tc)); 1 = ablation without
                              skipping: refinement, output and both backward kernels visit
@@ -126,7 +129,8 @@ size_t entmax_attn_mask_words(const entmax_attn_desc *desc);
  * hist_counts and tau_h (the histogram stage's output,
  * a test hook), stats (device uint64[32], accumulated, never cleared by the library:
  * stats[p] for p = 1..max_iters counts query rows whose refinement stopped after p
- * passes, stats[max_iters + 1] rows that hit the cap; stats[20] key sub-blocks
+ * passes, stats[max_iters + 1] rows that hit the cap, except that rows with 16 or more
+ * passes (or capped at 16 or more) all count in stats[16]; stats[20] key sub-blocks
  * (32 keys x 32 rows) scored by the histogram pass, stats[21] by refinement passes,
  * stats[22] by the output pass with a non-zero weight, stats[23] sub-blocks that the
  * histogram pass marked as candidates).

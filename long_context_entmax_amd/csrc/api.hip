@@ -131,12 +131,12 @@ static entmax_status derive(const entmax_attn_desc* d, Derived& o, bool decode =
   if (d->dense != 0 && d->dense != 1) return fail(ENTMAX_ERR_SHAPE, "dense must be 0 or 1");
   o.dense = decode ? 0 : d->dense;
   o.max_iters = d->max_iters != 0       ? d->max_iters
+                : d->alpha > 2.0f      ? 30
                 : (o.tau_init == 1)    ? 15
-                : d->alpha > 2.0f      ? 15
                 : d->alpha > 1.5f      ? 12
                                        : 8;
-  if (o.max_iters < 1 || o.max_iters > 15)
-    return fail(ENTMAX_ERR_SHAPE, "max_iters %d: must be 0 (default) or 1..15", d->max_iters);
+  if (o.max_iters < 1 || o.max_iters > 30)
+    return fail(ENTMAX_ERR_SHAPE, "max_iters %d: must be 0 (default) or 1..30", d->max_iters);
   if (!(d->scale >= 0.0f) || !isfinite(d->scale)) return fail(ENTMAX_ERR_SHAPE, "scale must be >= 0 and finite");
   if (!(d->tol >= 0.0f) || !isfinite(d->tol)) return fail(ENTMAX_ERR_SHAPE, "tol must be >= 0 and finite");
   o.dtype = d->dtype;
@@ -246,9 +246,9 @@ static entmax_status derive_dash(const entmax_dash_desc* d, DashDerived& o) {
   if (!(d->sigma >= 0.0f) || !isfinite(d->sigma)) return fail(ENTMAX_ERR_SHAPE, "sigma must be >= 0 and finite");
   if (!(d->scale >= 0.0f) || !isfinite(d->scale)) return fail(ENTMAX_ERR_SHAPE, "scale must be >= 0 and finite");
   if (!(d->tol >= 0.0f) || !isfinite(d->tol)) return fail(ENTMAX_ERR_SHAPE, "tol must be >= 0 and finite");
-  o.max_iters = d->max_iters != 0 ? d->max_iters : 15;
-  if (o.max_iters < 1 || o.max_iters > 15)
-    return fail(ENTMAX_ERR_SHAPE, "max_iters %d: must be 0 (default) or 1..15", d->max_iters);
+  o.max_iters = d->max_iters != 0 ? d->max_iters : (d->route_alpha > 2.0f ? 30 : 15);
+  if (o.max_iters < 1 || o.max_iters > 30)
+    return fail(ENTMAX_ERR_SHAPE, "max_iters %d: must be 0 (default) or 1..30", d->max_iters);
   o.dtype = d->dtype;
   o.alpha = d->route_alpha;
   o.kappa = (float)(1.0 / ((double)o.alpha - 1.0));

@@ -669,9 +669,10 @@ __global__ __launch_bounds__(64 * OUT_WAVES, 2) void k_refine_out(FwdParams p) {
   }
   if (p.stats) {
     {
-      // rows by refinement passes (rows that hit the cap go to max_iters + 1)
-      for (int ps = 1; ps <= p.max_iters + 1; ++ps) {
-        const int rp = st.done ? st.rowpass : p.max_iters + 1;
+      // rows by refinement passes (rows that hit the cap go to max_iters + 1; 16 and more
+      // passes share the last bucket)
+      for (int ps = 1; ps <= min(p.max_iters + 1, 16); ++ps) {
+        const int rp = min(st.done ? st.rowpass : p.max_iters + 1, 16);
         const int cntp = __popcll(ballot(h == 0 && rp == ps));
         if (lane == 0 && cntp) atomicAdd(&p.stats[ps], (unsigned long long)cntp);
       }

@@ -160,6 +160,9 @@ struct PassSums {
 // General alpha has no exact-support test: a row stops once |sum p - 1| <= FTOL0 at the
 // evaluated tau. Where f is steep (alpha > 2 with a wide support of small weights, such as
 // all scores equal), a step that is small in tau can still leave sum p well away from 1.
+// Where f is flat the same mass error means a larger error in tau (about |f| / |f'| with
+// |f'| = kappa F1; a single-key support at alpha = 16 has |f'| = 1/15), so the test is
+// |f| <= FTOL0 min(1, kappa F1): both sum p and tau end within about FTOL0 of their targets.
 constexpr float FTOL0 = 1e-4f;
 
 // Solver state of one row: bracket [lo, hi] holding tau*, the evaluation point tau, the
@@ -222,7 +225,7 @@ struct RowState {
     const float t0 = tau;
     if (f >= 0.f) lo = t0; else hi = t0;
     if constexpr (MODE == 0) {
-      if (fabsf(f) <= FTOL0) {        // tau stays at the evaluated point
+      if (fabsf(f) <= FTOL0 * fminf(1.0f, kappa * tot[1])) {   // tau stays at the evaluated point
         done = true;
         rowpass = npass;
         return;
@@ -268,7 +271,9 @@ struct RowState {
         if (first) {
           const float th = t0 + thi;   // the bracket's upper end at the start of the pass
           const float fh = tot[3] - 1.0f;
-          if (fabsf(fh) <= FTOL0) {    // the upper end already meets the test
+          // the upper end already meets the test (its slope is not summed; with a support
+          // of weights at most 1, F1 >= 1 there when kappa < 1, so kappa bounds kappa F1)
+          if (fabsf(fh) <= FTOL0 * fminf(1.0f, kappa)) {
             tau = th;
             done = true;
             rowpass = npass;

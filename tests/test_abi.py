@@ -74,7 +74,7 @@ BAD = [
     (dict(heads_q=3, heads_kv=2), 2), (dict(seqlen=100), 2), (dict(seqlen=-64), 2),
     (dict(head_dim=96), 4), (dict(block=(48, 64)), 4), (dict(block=(64, 256)), 4),
     (dict(bins=12), 4), (dict(bins=32), 4), (dict(dtype=7), 4), (dict(seqlen=1 << 20), 4),
-    (dict(max_iters=16), 2), (dict(heads_kv=0), 2), (dict(tau_init=2), 4), (dict(tau_init=-1), 4),
+    (dict(max_iters=31), 2), (dict(heads_kv=0), 2), (dict(tau_init=2), 4), (dict(tau_init=-1), 4),
 ]
 
 
@@ -179,7 +179,7 @@ DASH_BAD = [
     (dict(route_alpha=1.0), 3), (dict(route_alpha=float("inf")), 3), (dict(heads_q=3), 2),
     (dict(chunk=32), 4), (dict(chunk=96), 4), (dict(seqlen=1000), 2), (dict(seqlen=64 * 257), 4),
     (dict(head_dim=80), 4), (dict(dtype=3), 4), (dict(sigma=-1.0), 2), (dict(gamma=float("nan")), 2),
-    (dict(max_iters=16), 2), (dict(seqlen=-64), 2),
+    (dict(max_iters=31), 2), (dict(seqlen=-64), 2),
 ]
 
 

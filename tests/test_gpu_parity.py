@@ -95,6 +95,52 @@ def test_bf16_random_shapes(case):
         assert err < 2e-2, (name, err)
 
 
+# Large alpha: x = (alpha - 1) s spreads the scores so far that most rows keep one key, where
+# f(tau) = sum p - 1 is flattest (slope 1/(alpha - 1) at a single key) and a test on the mass
+# alone would leave tau off by up to 1e-4 (alpha - 1). tau is compared on every row. p =
+# (x - tau)^(1/(alpha - 1)) and g = (x - tau)^(1/(alpha - 1) - 1) are not Lipschitz at x = tau
+# (a key 1e-6 above tau already has p = 0.14 at alpha = 8), so O and the gradients are
+# compared on the rows whose every valid score lies at least 1e-2 from the oracle's tau (the
+# other rows get dO = 0, so they add nothing to dK and dV on either side). On these inputs
+# such rows keep one key, whose weight is 1 and whose dQ and dK terms vanish: the gradient
+# error is taken relative to max(|reference|, 1).
+LARGE_ALPHA = [
+    (1, 2, 2, 128, 64, 8.0, True, 64, 64, 16, 1.0),
+    (1, 2, 1, 128, 64, 16.0, False, 64, 64, 16, 1.0),
+    (1, 1, 1, 192, 128, 16.0, True, 64, 64, 8, 1.0),
+]
+
+
+@pytest.mark.parametrize("case", LARGE_ALPHA, ids=[str(c) for c in LARGE_ALPHA])
+def test_large_alpha_single_key_rows(case):
+    b, hq, hkv, n, d, alpha, causal, Br, Bc, B, qs = case
+    print(f"[case] large alpha {case}", flush=True)
+    w = synth.Workload("t", b, hq, hkv, n, d, "bf16", alpha, causal, Br, Bc, B, "normal",
+                       extra={"qk_scale": qs}, seed=hash(case) & 0xFFFF)
+    inp = synth.make_inputs(w)
+    ref = _oracle(inp, w)
+    x = scores_x(to64(inp["q"]), to64(inp["k"]), alpha, 1.0 / math.sqrt(d), hq // hkv)
+    if causal:
+        x = np.where(np.tril(np.ones((n, n), dtype=bool))[None, None], x, np.nan)
+    gap = np.nanmin(np.abs(x - ref["tau"][..., None]), axis=-1)
+    support = np.nansum(x > ref["tau"][..., None], axis=-1)
+    assert (support == 1).mean() > 0.5, "test construction: most rows should keep one key"
+    good = gap >= 1e-2
+    assert good.mean() > 0.5, "test construction: most rows should be well separated"
+    inp["do"] = (inp["do"].float() * torch.from_numpy(good[..., None].astype(np.float32))).to(inp["do"].dtype)
+    ref = _oracle(inp, w)
+    g = run_gpu(inp, w)
+    assert np.abs(g["tau"].numpy() - ref["tau"]).max() < 1e-3
+    assert np.abs(g["o"].float().numpy() - ref["o"])[good].max() < 1e-2
+    _check_prop1(g, ref, B)
+    assert mask_mismatch_is_ambiguous(g["mask"].numpy(), ref["mask"], np.nan_to_num(x, nan=-np.inf),
+                                      ref["tau"], w, 1e-3)
+    for name in ("dq", "dk", "dv"):
+        gg = g[name].float().numpy().astype(np.float64)
+        err = float(np.linalg.norm(gg - ref[name]) / max(np.linalg.norm(ref[name]), 1.0))
+        assert err < 2e-2, (name, err)
+
+
 DENSE_CASES = [CASES[0], CASES[1], CASES[2], CASES[3], CASES[4], CASES[6], CASES[8], CASES[11]]
 
 

@@ -125,7 +125,7 @@ def test_entmax15_closed_form(n):
             np.testing.assert_allclose(p, p_ref, atol=1e-11)
 
 
-@pytest.mark.parametrize("alpha", [1.25, 1.5, 2.0, 3.0])
+@pytest.mark.parametrize("alpha", [1.25, 1.5, 2.0, 3.0, 8.0, 16.0])
 def test_brute_force_supports(alpha):
     rng = np.random.default_rng(int(alpha * 100))
     for n in range(1, 9):
@@ -136,7 +136,7 @@ def test_brute_force_supports(alpha):
             assert abs(t - t_ref) < 1e-10, (alpha, x)
 
 
-@pytest.mark.parametrize("alpha", [1.25, 1.5, 2.0, 3.0])
+@pytest.mark.parametrize("alpha", [1.25, 1.5, 2.0, 3.0, 8.0, 16.0])
 def test_distribution_properties(alpha):
     """Rows sum to one with exact zeros; shift and permutation behave as the definition says."""
     rng = np.random.default_rng(7)

@@ -60,23 +60,31 @@ constexpr uint32_t HIST_WAVE_BYTES = HIST_ROWS * 64 * 4;
 // the first byte, zero above), and the wave's histogram offset is the instruction's immediate.
 // One conversion and one LDS add per score; cells of any y in [0, 18) stay inside the wave's
 // rows, y < 1 (and NaN) lands in the discard cell 0.
+// Four address registers (all lane * 4 in the first byte) take the conversions in turn, so
+// four conversions go out back to back before their four adds instead of one conversion
+// waiting for the previous add's address.
+struct CountRegs {
+  uint32_t a0, a1, a2, a3;
+};
 template <uint32_t OFF>
-__device__ __forceinline__ void count16(const f32x16& a, uint32_t& ad, uint32_t one) {
-#define ENTMAX_CNT(i) "v_cvt_u32_f32_sdwa %0, %" #i " dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:DWORD\n" \
-                      "ds_add_u32 %0, %1 offset:%18\n"
-  asm volatile(ENTMAX_CNT(2) ENTMAX_CNT(3) ENTMAX_CNT(4) ENTMAX_CNT(5) ENTMAX_CNT(6) ENTMAX_CNT(7)
-               ENTMAX_CNT(8) ENTMAX_CNT(9) ENTMAX_CNT(10) ENTMAX_CNT(11) ENTMAX_CNT(12) ENTMAX_CNT(13)
-               ENTMAX_CNT(14) ENTMAX_CNT(15) ENTMAX_CNT(16) ENTMAX_CNT(17)
-               : "+v"(ad)
+__device__ __forceinline__ void count16(const f32x16& a, CountRegs& r, uint32_t one) {
+#define ENTMAX_CV(d, i) "v_cvt_u32_f32_sdwa %" #d ", %" #i " dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:DWORD\n"
+#define ENTMAX_AD(d) "ds_add_u32 %" #d ", %4 offset:%21\n"
+#define ENTMAX_Q(i0, i1, i2, i3) ENTMAX_CV(0, i0) ENTMAX_CV(1, i1) ENTMAX_CV(2, i2) ENTMAX_CV(3, i3) \
+                                 ENTMAX_AD(0) ENTMAX_AD(1) ENTMAX_AD(2) ENTMAX_AD(3)
+  asm volatile(ENTMAX_Q(5, 6, 7, 8) ENTMAX_Q(9, 10, 11, 12) ENTMAX_Q(13, 14, 15, 16) ENTMAX_Q(17, 18, 19, 20)
+               : "+v"(r.a0), "+v"(r.a1), "+v"(r.a2), "+v"(r.a3)
                : "v"(one), "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]),
                  "v"(a[7]), "v"(a[8]), "v"(a[9]), "v"(a[10]), "v"(a[11]), "v"(a[12]), "v"(a[13]),
                  "v"(a[14]), "v"(a[15]), "i"(OFF)
                : "memory");
-#undef ENTMAX_CNT
+#undef ENTMAX_Q
+#undef ENTMAX_AD
+#undef ENTMAX_CV
 }
 // both tiles of a step into the histogram of wave w (w < HW)
 template <int HW>
-__device__ __forceinline__ void count_pair(int w, const f32x16& a0, const f32x16& a1, uint32_t& ad, uint32_t one) {
+__device__ __forceinline__ void count_pair(int w, const f32x16& a0, const f32x16& a1, CountRegs& ad, uint32_t one) {
 #define ENTMAX_CASE(k)                                      \
   case k:                                                   \
     if constexpr (k < HW) {                                 \
@@ -203,7 +211,8 @@ __global__ __launch_bounds__((64 * hist_waves<T, D>()), (hist_occ<T, D>())) void
       return a;
     }
   };
-  uint32_t cad = 4u * (uint32_t)lane;        // LDS address of a count: cell in its second byte
+  const uint32_t l4 = 4u * (uint32_t)lane;
+  CountRegs cad{l4, l4, l4, l4};              // LDS addresses of counts: cell in the second byte
   const uint32_t one = 1u;
   for (int kb = 2 * last_pair; kb >= 0; kb -= 2) {
     // The second tile of the last pair may lie past the last valid sub-block: under the causal

@@ -28,11 +28,25 @@ Chunk mask: bit (g, query tile t of 64 rows, chunk c) is set iff some row of the
 has wbar[g, i, c] > 0; words [b, hkv, ceil(n / 64), ceil(nc / 32)], bit c % 32 of word
 c // 32.
 
+Backward (``dash_bwd``; DashAttention (it), stage 1 "Differenziabilità": gradients flow back
+through the routing to the chunk summaries). With L the loss and dO = dL/do:
+  stage 2, per row and head: P = softmax(s), dP_j = dO . v_j, delta = dO . o,
+    dS_j = P_j (dP_j - delta); dq += scale sum_j dS_j k_j, dk_j += scale dS_j q, dv_j += P_j dO;
+    the bias sigma ln wbar_c of a routed chunk gets sum_{j in c} dS_j;
+  group average: dwbar_c = sigma / wbar_c * sum over the group's heads of that chunk sum;
+    each head's routing weights get dwbar / G;
+  stage 1, per row and head (the alpha-entmax Jacobian diag(g) - g g^T / sum g with
+    g = [x - tau]_+^(1/(alpha-1) - 1), x = (alpha - 1) zbar): dz = g (dw - (g . dw) / sum g);
+    zbar = gamma scale q . ks, so dq += gamma scale sum_c dz_c ks_c, dks_c += gamma scale dz_c q.
+Chunks outside the support carry no gradient (g = 0 there, and their keys are masked).
+
 Pins (tests/test_oracle_pins.py): all-equal summaries make routing uniform, so sigma = 0
 is causal softmax attention and sigma = 1 is causal softmax attention with -ln m_i added
 on earlier chunks (both checked against torch's scaled_dot_product_attention in fp64); a
 hand-derived sparsemax routing row; the GQA average, its union support and the chunk mask
-by brute force. No function here is parity-unpinned.
+by brute force; the backward against central finite differences of sum(o * dO) in q, k, v
+and the summaries, and at sigma = 0 (no prior) a summary gradient of exactly 0 and a dq
+equal to that of masked softmax attention. No function here is parity-unpinned.
 """
 from __future__ import annotations
 
@@ -150,3 +164,62 @@ def dash_fwd(q, k, v, ks, alpha: float, gamma: float, sigma: float, C: int,
             if full:
                 out["mask"][bi, g] = chunk_mask(rt["wbar"], rows, n)
     return out
+
+
+def dash_bwd(q, k, v, ks, dout, alpha: float, gamma: float, sigma: float, C: int,
+             scale: float | None = None) -> dict:
+    """Gradients of stages 1-2 of a whole problem with respect to q, k, v and the summaries ks,
+    given dO (the backward written out in the module docstring). Returns dq [b, hq, n, d],
+    dk, dv [b, hkv, n, d] and dks [b, hkv, nc, d]."""
+    q, k, v, ks, dout = _f64(q), _f64(k), _f64(v), _f64(ks), _f64(dout)
+    b, hq, n, d = q.shape
+    hkv, nc = k.shape[1], ks.shape[2]
+    G = hq // hkv
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    kappa = 1.0 / (alpha - 1.0)
+    dq, dk, dv, dks = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v), np.zeros_like(ks)
+    for bi in range(b):
+        for g in range(hkv):
+            kk, vv, kg = k[bi, g], v[bi, g], ks[bi, g]
+            for i in range(n):
+                m = i // C
+                # stage 1 forward of the row
+                zs, ps, taus = [], [], []
+                for h in range(G):
+                    z = gamma * scale * (kg[:m] @ q[bi, g * G + h, i]) if m else np.zeros(0)
+                    p, t = _entmax(z, alpha) if m else (np.zeros(0), 0.0)
+                    zs.append(z); ps.append(p); taus.append(t)
+                wbar = np.mean(ps, axis=0) if m else np.zeros(0)
+                routed = [c for c in range(m) if wbar[c] > 0.0]
+                keys = [np.arange(c * C, (c + 1) * C) for c in routed] + [np.arange(m * C, i + 1)]
+                bias = [np.full(C, sigma * np.log(wbar[c])) for c in routed] + [np.zeros(i + 1 - m * C)]
+                keys, bias = np.concatenate(keys), np.concatenate(bias)
+                dwbar = np.zeros(m)
+                for h in range(G):
+                    hh = g * G + h
+                    # stage 2 forward and backward of the row
+                    s = scale * (kk[keys] @ q[bi, hh, i]) + bias
+                    e = np.exp(s - s.max())
+                    P = e / e.sum()
+                    o = P @ vv[keys]
+                    dP = vv[keys] @ dout[bi, hh, i]
+                    dS = P * (dP - dout[bi, hh, i] @ o)
+                    dq[bi, hh, i] += scale * (dS @ kk[keys])
+                    dk[bi, g, keys] += scale * np.outer(dS, q[bi, hh, i])
+                    dv[bi, g, keys] += np.outer(P, dout[bi, hh, i])
+                    for ci, c in enumerate(routed):
+                        dwbar[c] += sigma / wbar[c] * dS[ci * C:(ci + 1) * C].sum()
+                if not m:
+                    continue
+                # stage 1 backward of the row
+                for h in range(G):
+                    hh = g * G + h
+                    x = (alpha - 1.0) * zs[h]
+                    dlt = np.maximum(x - taus[h], 0.0)
+                    gg = np.where(dlt > 0.0, dlt ** (kappa - 1.0), 0.0)
+                    dw = dwbar / G
+                    dz = gg * (dw - (gg @ dw) / gg.sum())
+                    dq[bi, hh, i] += gamma * scale * (dz @ kg[:m])
+                    dks[bi, g, :m] += gamma * scale * np.outer(dz, q[bi, hh, i])
+    return {"dq": dq, "dk": dk, "dv": dv, "dks": dks}

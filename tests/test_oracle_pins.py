@@ -665,3 +665,75 @@ def test_dash_routing_invariants_and_mask_brute_force():
     ones = np.ones_like(v)
     r1 = oracle.dash.dash_fwd(q, k, ones, ks, 1.5, 1.0, 1.0, C)
     np.testing.assert_allclose(r1["o"], 1.0, atol=1e-12)
+
+
+def _dash_loss(q, k, v, ks, do, alpha, gamma, sigma, C):
+    return float((oracle.dash.dash_fwd(q, k, v, ks, alpha, gamma, sigma, C)["o"] * do).sum())
+
+
+@pytest.mark.parametrize("alpha,G", [(1.5, 2), (2.0, 1), (1.25, 3)])
+def test_dash_backward_finite_differences(alpha, G):
+    """dash_bwd against central differences of sum(o * dO) in sampled coordinates of q, k, v
+    and the chunk summaries (eps 1e-4 in fp64: the oracle's bisection leaves tau within
+    1e-12, so a smaller step would measure that noise; a coordinate whose perturbation moved
+    a routing support boundary would show as a kink, none does at these seeds)."""
+    b, hkv, n, d, C = 1, 1, 80, 8, 16
+    hq = G * hkv
+    q, k, v, ks = _dash_inputs(b, hq, hkv, n, d, n // C, 11 + G, False)
+    do = np.random.default_rng(5).standard_normal(q.shape)
+    gamma, sigma = 2.0, 1.5
+    gr = oracle.dash.dash_bwd(q, k, v, ks, do, alpha, gamma, sigma, C)
+    rng = np.random.default_rng(7)
+    eps = 1e-4
+    for name, arr in (("dq", q), ("dk", k), ("dv", v), ("dks", ks)):
+        for _ in range(6):
+            idx = tuple(int(rng.integers(0, s)) for s in arr.shape)
+            old = arr[idx]
+            arr[idx] = old + eps
+            lp = _dash_loss(q, k, v, ks, do, alpha, gamma, sigma, C)
+            arr[idx] = old - eps
+            lm = _dash_loss(q, k, v, ks, do, alpha, gamma, sigma, C)
+            arr[idx] = old
+            fd = (lp - lm) / (2 * eps)
+            assert abs(fd - gr[name][idx]) < 1e-6 * max(1.0, abs(fd)) + 2e-7, (name, idx, fd, gr[name][idx])
+    # the summaries get gradient through the routing alone: some must be non-zero here
+    assert np.abs(gr["dks"]).max() > 1e-3
+
+
+def test_dash_backward_sigma0_and_fixed_prior_against_autograd():
+    """With the prior treated as a fixed additive mask, stage 2 is masked softmax attention:
+    torch autograd in fp64 through scaled_dot_product_attention gives dk and dv exactly as
+    dash_bwd (the routing does not reach k and v), and at sigma = 0 (no prior: the routing
+    only selects chunks) also dq, with a summary gradient of exactly 0."""
+    import torch
+    b, hq, hkv, n, d, C = 1, 4, 2, 96, 8, 16
+    q, k, v, ks = _dash_inputs(b, hq, hkv, n, d, n // C, 21, False)
+    do = np.random.default_rng(9).standard_normal(q.shape)
+    G = hq // hkv
+    for sigma in (0.0, 1.0):
+        f = oracle.dash.dash_fwd(q, k, v, ks, 1.5, 3.0, sigma, C)
+        gr = oracle.dash.dash_bwd(q, k, v, ks, do, 1.5, 3.0, sigma, C)
+        bias = np.full((b, hq, n, n), -np.inf)
+        for g in range(hkv):
+            for i in range(n):
+                m = i // C
+                for c in range(m):
+                    w = f["wbar"][0, g, i, c]
+                    if w > 0:
+                        bias[0, g * G:(g + 1) * G, i, c * C:(c + 1) * C] = sigma * np.log(w)
+                bias[0, g * G:(g + 1) * G, i, m * C:i + 1] = 0.0
+        qt = torch.from_numpy(q).requires_grad_()
+        kt = torch.from_numpy(k).requires_grad_()
+        vt = torch.from_numpy(v).requires_grad_()
+        o = torch.nn.functional.scaled_dot_product_attention(
+            qt, kt.repeat_interleave(G, dim=1), vt.repeat_interleave(G, dim=1),
+            attn_mask=torch.from_numpy(bias))
+        (o * torch.from_numpy(do)).sum().backward()
+        np.testing.assert_allclose(o.detach().numpy(), f["o"], atol=1e-12)
+        np.testing.assert_allclose(gr["dk"], kt.grad.numpy(), atol=1e-10)
+        np.testing.assert_allclose(gr["dv"], vt.grad.numpy(), atol=1e-10)
+        if sigma == 0.0:
+            np.testing.assert_allclose(gr["dq"], qt.grad.numpy(), atol=1e-10)
+            assert np.abs(gr["dks"]).max() == 0.0
+        else:
+            assert np.abs(gr["dq"] - qt.grad.numpy()).max() > 1e-6   # the routing's share

@@ -64,8 +64,8 @@ def parse():
                     help="time one decode step (a new query row per head against the workload's "
                          "K/V as a cache) instead of the training step")
     ap.add_argument("--dash", action="store_true",
-                    help="DashAttention forward (routing + prior-induced sparse softmax) at 16K tokens "
-                         "instead of the entmax attention step")
+                    help="DashAttention training step (routing + prior-induced sparse softmax, forward and "
+                         "backward) at 16K tokens instead of the entmax attention step")
     ap.add_argument("--tau-error", action="store_true",
                     help="instead of timing, print the mean |tau_p - tau*| after p = 1..15 "
                          "refinement passes for both starts (tau* = the converged tau)")
@@ -339,59 +339,77 @@ def dash_workload():
     return synth.Workload("D16K", 1, 32, 2, 16384, 128, "bf16", 1.5, True, 64, 64, 16, "normal", seed=0)
 
 
-def dash_cpu_baseline(w, q, k, v, ks, target_s: float):
-    """The fp64 DashAttention oracle on evenly spaced query rows until ~target_s; the time
-    per row is extrapolated to all rows (its cost grows with the keys a row attends, which
-    the even spacing samples)."""
+def dash_cpu_baseline(w, q, k, v, ks, do, target_s: float):
+    """The fp64 DashAttention oracle, forward and backward, on evenly spaced query rows until
+    ~target_s; the time per row is extrapolated to all rows (a row's cost grows with the keys
+    it attends, which the even spacing samples; the backward of a row does all of that row's
+    work, also what it adds to dK, dV and the summaries' gradient)."""
     import numpy as np
     import oracle.dash as odash
     n = w.seqlen
-    q64, k64, v64, s64 = (t.double().numpy() for t in (q, k, v, ks))
+    q64, k64, v64, s64, d64 = (t.double().numpy() for t in (q, k, v, ks, do))
     done, t0, step = 0, time.time(), 1024
     while time.time() - t0 < target_s and step >= 1:
         rows = np.arange(step // 2, n, step)
         odash.dash_fwd(q64, k64, v64, s64, w.alpha, DASH_GAMMA, DASH_SIGMA, DASH_CHUNK, rows=rows)
+        odash.dash_bwd(q64, k64, v64, s64, d64, w.alpha, DASH_GAMMA, DASH_SIGMA, DASH_CHUNK, rows=rows)
         done += rows.size
         step //= 2
     el = time.time() - t0
     s_per_step = el / done * n * w.batch
     return {"value": w.batch * n / s_per_step, "unit": "tokens/s", "ms_per_step": s_per_step * 1e3,
             "cores": 1, "kind": "oracle",
-            "sample": f"{done} of {n} query rows (all heads), evenly spaced, {el:.1f} s, extrapolated to all rows"}
+            "sample": f"forward and backward of {done} of {n} query rows (all heads), evenly spaced, {el:.1f} s, "
+                      "extrapolated to all rows"}
 
 
 def dash_bench(args, lce, dev):
-    """One DashAttention forward (stages 1-2) per step. Roofline of the stage-2 kernel: MFMA
-    FLOPs of the tiles it must multiply -- 4 d x 32 x 32 (score and P.V products) per query
-    head and (32-row block, 32-key sub-block) pair where the sub-block lies in a chunk that
-    some row of the block routes, or in the block's diagonal chunk. The FLOPs per attended
-    (row, key) pair, 4 d each, are reported beside it."""
+    """One DashAttention training step (stages 1-2, forward then backward) per step; the
+    forward alone is timed beside it. Roofline of the slowest of the three stage-2 kernels,
+    on MFMA FLOPs of the tiles it must multiply: per query head and (32-row block, 32-key
+    sub-block) pair where the sub-block lies in a chunk that some row of the block routes, or
+    in the block's diagonal chunk, 2 d x 32 x 32 per product -- the forward's score and P.V
+    products (2), the dK/dV kernel's score, dP, dV and dK products (4), the dQ kernel's score,
+    dP and dQ products (3). The FLOPs per attended (row, key) pair are reported beside it."""
     import torch
     import synth
     w = dash_workload()
-    inp = synth.make_inputs(w, device=dev, need_grad_inputs=False)
-    q, k, v = inp["q"], inp["k"], inp["v"]
+    inp = synth.make_inputs(w, device=dev, need_grad_inputs=True)
+    q, k, v, do = inp["q"], inp["k"], inp["v"], inp["do"]
     ks = synth.chunk_summaries(w, DASH_CHUNK, device=dev)
     desc = lce.make_dash_desc(w.batch, w.heads_q, w.heads_kv, w.seqlen, w.head_dim, lce.ENTMAX_BF16, DASH_CHUNK,
                               w.alpha, DASH_GAMMA, DASH_SIGMA)
-    ws = torch.empty(lce.lib().entmax_dash_fwd_workspace_bytes(ctypes.byref(desc)), dtype=torch.uint8, device=dev)
-    step = lambda: lce.dash_fwd(q, k, v, ks, DASH_CHUNK, w.alpha, DASH_GAMMA, DASH_SIGMA, workspace=ws)
-    for _ in range(args.warmup):
-        r = step()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    L = lce.lib()
+    ws = torch.empty(L.entmax_dash_fwd_workspace_bytes(ctypes.byref(desc)), dtype=torch.uint8, device=dev)
+    wsb = torch.empty(L.entmax_dash_bwd_workspace_bytes(ctypes.byref(desc)), dtype=torch.uint8, device=dev)
+    fwd = lambda: lce.dash_fwd(q, k, v, ks, DASH_CHUNK, w.alpha, DASH_GAMMA, DASH_SIGMA, workspace=ws)
+
+    def train_step():
+        r = fwd()
+        g = lce.dash_bwd(q, k, v, ks, do, r.o, r.lse, r.route_tau, r.route_w, r.chunk_mask, DASH_CHUNK, w.alpha,
+                         DASH_GAMMA, DASH_SIGMA, workspace=wsb)
+        return r, g
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            out = fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps, out
+
     t0 = time.time()
-    e0.record()
-    for _ in range(args.steps):
-        r = step()
-    e1.record()
-    torch.cuda.synchronize()
+    ms_fwd, r = timed(fwd)
+    ms, _ = timed(train_step)
     wall = time.time() - t0
-    ms = e0.elapsed_time(e1) / args.steps
     lce.profile(True)
     lce.profile_read()
     for _ in range(args.steps):
-        r = step()
+        train_step()
     torch.cuda.synchronize()
     kt = lce.profile_read()
     lce.profile(False)
@@ -401,40 +419,42 @@ def dash_bench(args, lce, dev):
     rows = torch.arange(n, device=dev, dtype=torch.float64)
     keys = (routed * C + (rows % C + 1)).sum().item() * G                 # over query heads
     causal_keys = w.batch * w.heads_q * n * (n + 1) / 2.0
-    alg_attn = 4.0 * d * keys
-    # work the kernel does: every 32-key sub-block of a chunk that some row of a 32-row block
+    # work the kernels do: every 32-key sub-block of a chunk that some row of a 32-row block
     # routes (plus the diagonal run), for each query head
     nb32 = n // 32
     blk_routed = (r.route_w > 0).view(w.batch, w.heads_kv, n // C, nb32, 32).any(dim=4)   # [b,hkv,nc,nb32]
     diag_sub = ((torch.arange(nb32, device=dev) * 32) % C) // 32 + 1                        # diagonal sub-blocks
     visited = (blk_routed.sum(dim=2).to(torch.float64) * (C // 32) + diag_sub).sum().item() * G
-    visited_flops = 4.0 * d * 32 * 32 * visited
+    tile = 2.0 * d * 32 * 32 * visited                                     # one product over the tiles
+    flops = {"dash_attn": 2 * tile, "dash_bwd_dkv": 4 * tile, "dash_bwd_dq": 3 * tile}
     alg_route = 2.0 * d * w.batch * w.heads_q * float((torch.div(rows, C, rounding_mode="floor")).sum().item())
-    achieved = visited_flops / (kern["dash_attn"] * 1e-3) / 1e12
+    tflops = {kk: f / (kern[kk] * 1e-3) / 1e12 for kk, f in flops.items()}
+    dom = max(flops, key=lambda kk: kern[kk])
     line = {
-        "metric": "dash_fwd_tokens_per_s", "value": round(w.batch * n / (ms * 1e-3), 1), "unit": "tokens/s",
+        "metric": "dash_train_tokens_per_s", "value": round(w.batch * n / (ms * 1e-3), 1), "unit": "tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (normal recipe; chunk summaries drawn with the spread of a 64-key mean)",
-        "config": {"workload": f"DashAttention forward {w.name}: b{w.batch} hq{w.heads_q}/hkv{w.heads_kv} "
+        "config": {"workload": f"DashAttention forward + backward {w.name}: b{w.batch} hq{w.heads_q}/hkv{w.heads_kv} "
                                f"n{n} d{d} bf16, chunk {C}, routing alpha {w.alpha}, gamma {DASH_GAMMA}, "
                                f"sigma {DASH_SIGMA}",
                    "key_sparsity": round(1.0 - keys / causal_keys, 4)},
-        "roofline": {"kernel": "dash_attn", "bound": "mfma", "achieved": round(achieved, 3),
-                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None, "algorithmic_flops_per_launch": visited_flops},
+        "fwd_ms_per_step": round(ms_fwd, 4),
+        "fwd_tokens_per_s": round(w.batch * n / (ms_fwd * 1e-3), 1),
+        "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(tflops[dom], 3),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(tflops[dom] / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "algorithmic_flops_per_launch": flops[dom]},
         "kernels_ms": {kk: round(vv, 4) for kk, vv in kern.items()},
-        "kernel_tflops": {"dash_route": round(alg_route / (kern["dash_route"] * 1e-3) / 1e12, 2),
-                          "dash_attn": round(achieved, 2),
-                          "dash_attn_per_attended_key": round(alg_attn / (kern["dash_attn"] * 1e-3) / 1e12, 2)},
-        "dash_attn_tiles_over_attended_keys": round(visited_flops / alg_attn, 3),
+        "kernel_tflops": dict({kk: round(vv, 2) for kk, vv in tflops.items()},
+                              dash_route=round(alg_route / (kern["dash_route"] * 1e-3) / 1e12, 2),
+                              dash_attn_per_attended_key=round(2.0 * 2.0 * d * keys / (kern["dash_attn"] * 1e-3) / 1e12,
+                                                               2)),
+        "dash_attn_tiles_over_attended_keys": round(tile / (2.0 * d * keys), 3),
         "wall_s": round(wall, 3),
     }
     if not args.no_cpu_baseline and not args.profile_only:
-        line["cpu_baseline"] = dash_cpu_baseline(w, q.cpu(), k.cpu(), v.cpu(), ks.cpu(), args.cpu_seconds)
+        line["cpu_baseline"] = dash_cpu_baseline(w, q.cpu(), k.cpu(), v.cpu(), ks.cpu(), do.cpu(), args.cpu_seconds)
     print(json.dumps(line), flush=True)
-
-
 
 
 def make_problem(lce, w, dev, tau_init: int = 0, nape: bool = False):

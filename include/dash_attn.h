@@ -78,6 +78,35 @@ entmax_status entmax_dash_fwd(const entmax_dash_desc *desc,
                               uint32_t *chunk_mask,
                               void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * Backward of stages 1 and 2 (DashAttention page, Italian summary, stage 1: the routing is
+ * differentiable, so the gradients reach the chunk summaries). Given dO = dL/do, returns
+ *   dq, dk, dv   the gradients of q, k, v (stage 2 is softmax attention with the prior
+ *                sigma ln wbar as an additive term on routed chunks; dq also carries the
+ *                routing's share, below);
+ *   dk_summary   [batch, heads_kv, n_chunks, head_dim], the gradient of the summaries.
+ * The prior term of chunk c in row i gets s_ic = sum over the chunk's keys of
+ * dS_ij = p_ij (dO_i . v_j - dO_i . o_i); the group's routing weights get
+ * dwbar(c) = sigma / wbar(c) * sum over the group's heads of s_ic, each head's weights
+ * dwbar / G, and through the alpha-entmax Jacobian diag(g) - g g^T / sum g, with
+ * g = [x - tau]_+^(1/(alpha-1) - 1) at the forward's tau, the logits get
+ * du = g (dw - (g . dw) / sum g); then dq += gamma scale du . k_summary and
+ * dk_summary(c) = gamma scale sum over the group's heads and rows of du(c) q. Chunks outside
+ * a row's support carry no gradient.
+ * Inputs: q, k, v, k_summary and the forward's outputs o, lse, route_tau, route_w and
+ * chunk_mask (all required), dout [batch, heads_q, seqlen, head_dim] in dtype. Outputs
+ * dq, dk, dv, dk_summary in dtype. Alignment: 16 bytes (route_tau, chunk_mask 4 bytes).
+ * workspace: at least entmax_dash_bwd_workspace_bytes(desc) bytes, 256-byte aligned.
+ * Results are bitwise deterministic (fixed reduction orders, no atomics).
+ */
+size_t entmax_dash_bwd_workspace_bytes(const entmax_dash_desc *desc);
+entmax_status entmax_dash_bwd(const entmax_dash_desc *desc,
+                              const void *q, const void *k, const void *v, const void *k_summary,
+                              const float *o, const float *lse, const float *route_tau,
+                              const float *route_w, const uint32_t *chunk_mask, const void *dout,
+                              void *dq, void *dk, void *dv, void *dk_summary,
+                              void *workspace, size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

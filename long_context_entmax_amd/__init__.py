@@ -12,6 +12,7 @@ built, every call raises.
     o = entmax_attention(q, k, v, alpha=1.5)          # autograd-aware
     o, tau, hist, tau_h = decode(q_new, k_cache, v_cache, alpha=1.5, lengths=lens)
     o, lse, route_tau, route_w, chunk_mask = dash_fwd(q, k, v, k_summary, chunk=64)
+    dq, dk, dv, dk_summary = dash_bwd(q, k, v, k_summary, do, o, lse, route_tau, route_w, chunk_mask, chunk=64)
 
 Shapes: q, do [b, hq, n, d]; k, v [b, hkv, n, d]; dtype float32 or bfloat16.
 ``slopes`` (optional, float32 [hq] on the device): per-head position-bias slopes; head h
@@ -73,7 +74,7 @@ EXPORTS = [
     "entmax_attn_fwd_workspace_bytes", "entmax_attn_bwd_workspace_bytes", "entmax_attn_aux_bytes",
     "entmax_attn_mask_words", "entmax_attn_fwd", "entmax_attn_bwd", "entmax_attn_decode_workspace_bytes",
     "entmax_attn_decode", "entmax_attn_decode_noalloc", "entmax_dash_fwd_workspace_bytes", "entmax_dash_mask_words", "entmax_dash_fwd",
-    "entmax_status_string",
+    "entmax_dash_bwd_workspace_bytes", "entmax_dash_bwd", "entmax_status_string",
     "entmax_last_error", "entmax_attn_profile", "entmax_attn_profile_read",
 ]
 
@@ -100,11 +101,13 @@ def lib() -> ctypes.CDLL:
         L.entmax_attn_decode.argtypes = [_DP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
         L.entmax_attn_decode_noalloc.restype = ctypes.c_int
         L.entmax_attn_decode_noalloc.argtypes = [_DP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
-        for f in ("entmax_dash_fwd_workspace_bytes", "entmax_dash_mask_words"):
+        for f in ("entmax_dash_fwd_workspace_bytes", "entmax_dash_mask_words", "entmax_dash_bwd_workspace_bytes"):
             getattr(L, f).restype = _sz
             getattr(L, f).argtypes = [_DDP]
         L.entmax_dash_fwd.restype = ctypes.c_int
         L.entmax_dash_fwd.argtypes = [_DDP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+        L.entmax_dash_bwd.restype = ctypes.c_int
+        L.entmax_dash_bwd.argtypes = [_DDP] + [_vp] * 15 + [_sz, _vp]
         L.entmax_status_string.restype = ctypes.c_char_p
         L.entmax_status_string.argtypes = [ctypes.c_int]
         L.entmax_last_error.restype = ctypes.c_char_p
@@ -460,6 +463,49 @@ def dash_fwd(q, k, v, k_summary, chunk: int = 64, route_alpha: float = 1.5, gamm
     _check(L.entmax_dash_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(k_summary), _ptr(o), _ptr(lse),
                              _ptr(rtau), _ptr(rw), _ptr(cmask), _ptr(workspace), workspace.numel(), _stream(dev)))
     return DashOut(o, lse, rtau, rw, cmask)
+
+
+DashGrads = namedtuple("DashGrads", "dq dk dv dk_summary")
+
+
+def dash_bwd(q, k, v, k_summary, do, o, lse, route_tau, route_w, chunk_mask, chunk: int = 64,
+             route_alpha: float = 1.5, gamma: float = 1.0, sigma: float = 1.0, scale: Optional[float] = None,
+             max_iters: int = 0, tol: float = 0.0, workspace=None) -> DashGrads:
+    """DashAttention backward, stages 1-2 (include/dash_attn.h): given do = dL/do and the
+    forward's outputs (same settings), returns dq, dk, dv and dk_summary in the inputs' dtype.
+    The gradient reaches q and k_summary through the routing (the alpha-entmax Jacobian) as
+    well as through the prior term sigma * ln(routing weight) of stage 2."""
+    torch = _torch()
+    _require_gpu(q, k, v, k_summary, do, o, lse, route_tau, route_w, chunk_mask)
+    b, hq, n, d = q.shape
+    hkv = k.shape[1]
+    if chunk <= 0 or n % chunk:
+        raise ValueError("seqlen must be a multiple of chunk")
+    nc = n // chunk
+    _expect("k", k, (b, hkv, n, d), q.dtype, q.device)
+    _expect("v", v, (b, hkv, n, d), q.dtype, q.device)
+    _expect("k_summary", k_summary, (b, hkv, nc, d), q.dtype, q.device)
+    _expect("do", do, (b, hq, n, d), q.dtype, q.device)
+    _expect("o", o, (b, hq, n, d), torch.float32, q.device)
+    _expect("lse", lse, (b, hq, n), torch.float32, q.device)
+    _expect("route_tau", route_tau, (b, hq, n), torch.float32, q.device)
+    _expect("route_w", route_w, (b, hkv, nc, n), torch.float32, q.device)
+    _expect("chunk_mask", chunk_mask, (b, hkv, n // 64, (nc + 31) // 32), torch.int32, q.device)
+    dt = ENTMAX_BF16 if q.dtype == torch.bfloat16 else ENTMAX_F32
+    desc = make_dash_desc(b, hq, hkv, n, d, dt, chunk, route_alpha, gamma, sigma, scale, max_iters, tol)
+    L = lib()
+    dev = q.device
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    dks = torch.empty_like(k_summary)
+    nbytes = L.entmax_dash_bwd_workspace_bytes(ctypes.byref(desc))
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+    _check(L.entmax_dash_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(k_summary), _ptr(o), _ptr(lse),
+                             _ptr(route_tau), _ptr(route_w), _ptr(chunk_mask), _ptr(do), _ptr(dq), _ptr(dk),
+                             _ptr(dv), _ptr(dks), _ptr(workspace), workspace.numel(), _stream(dev)))
+    return DashGrads(dq, dk, dv, dks)
 
 
 def workspace_bytes(desc: Desc) -> Tuple[int, int]:

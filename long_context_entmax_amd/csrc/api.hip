@@ -603,6 +603,136 @@ entmax_status entmax_dash_fwd(const entmax_dash_desc* desc, const void* q, const
   return ENTMAX_OK;
 }
 
+// ------------------------------------------------------------------------ DashAttention backward
+// Stage 2 runs through the attention backward (mode 3) as softmax attention over 64 x 64
+// blocks; this is its descriptor, and the layout of the backward's workspace.
+static entmax_status dash_attn_view(const DashDerived& o, Derived& a) {
+  entmax_attn_desc ad{};
+  ad.batch = o.b; ad.heads_q = o.hq; ad.heads_kv = o.hkv; ad.seqlen = o.n; ad.head_dim = o.D;
+  ad.dtype = o.dtype; ad.alpha = 1.5f; ad.causal = 1; ad.block_q = 64; ad.block_k = 64; ad.n_bins = 16;
+  ad.scale = o.scale;
+  return derive(&ad, a);
+}
+
+// rows per piece of the summary-gradient product (k_dash_dks)
+constexpr int DASH_DKS_ROWS = 256;
+
+struct DashBwdLayout {
+  BwdLayout att;        // the attention backward's part (at offset 0)
+  size_t bmask, lp, dw, qc, dq32, dbias, du, dpart, total;
+  int W, NP;
+};
+static DashBwdLayout dash_bwd_ws(const DashDerived& o, const Derived& a) {
+  DashBwdLayout L;
+  L.att = bwd_ws(a);
+  const size_t rows = (size_t)o.b * o.hq, units = (size_t)o.b * o.hkv;
+  const int Tb = o.n / 64;
+  L.W = (Tb + 31) / 32;
+  L.NP = (o.n + DASH_DKS_ROWS - 1) / DASH_DKS_ROWS;
+  size_t off = L.att.total;
+  L.bmask = off; off += align256(rows * Tb * L.W * 4);
+  L.lp = off; off += align256(units * o.nc * o.n * 4);
+  L.dw = off; off += align256(units * o.nc * o.n * 4);
+  L.qc = off; off += align256(rows * o.n * o.D * o.es);
+  L.dq32 = off; off += align256(rows * o.n * o.D * 4);
+  L.dbias = off; off += align256(rows * (size_t)(o.n / 32) * o.n * 4);
+  L.du = off; off += align256(rows * o.nc * o.n * 4);
+  L.dpart = off; off += align256(units * o.Wc * L.NP * (size_t)o.D * 32 * 4);
+  L.total = off;
+  return L;
+}
+
+size_t entmax_dash_bwd_workspace_bytes(const entmax_dash_desc* desc) {
+  DashDerived o;
+  Derived a;
+  if (derive_dash(desc, o) != ENTMAX_OK || dash_attn_view(o, a) != ENTMAX_OK) return 0;
+  return dash_bwd_ws(o, a).total;
+}
+
+entmax_status entmax_dash_bwd(const entmax_dash_desc* desc, const void* q, const void* k, const void* v,
+                              const void* k_summary, const float* o_, const float* lse, const float* route_tau,
+                              const float* route_w, const uint32_t* chunk_mask, const void* dout, void* dq,
+                              void* dk, void* dv, void* dk_summary, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  DashDerived o;
+  entmax_status st = derive_dash(desc, o);
+  if (st != ENTMAX_OK) return st;
+  if ((size_t)o.b * o.hq * o.n == 0) return ENTMAX_OK;
+  Derived a;
+  if ((st = dash_attn_view(o, a)) != ENTMAX_OK) return st;
+  if (!q || !k || !v || !k_summary || !o_ || !lse || !route_tau || !route_w || !chunk_mask || !dout || !dq ||
+      !dk || !dv || !dk_summary)
+    return fail(ENTMAX_ERR_NULL, "every argument of entmax_dash_bwd is required");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(k_summary, 16) || !aligned(o_, 16) ||
+      !aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(dk_summary, 16) ||
+      !aligned(lse, 16) || !aligned(route_tau, 4) || !aligned(route_w, 16) || !aligned(chunk_mask, 4))
+    return fail(ENTMAX_ERR_ALIGN, "tensors need 16-byte alignment (route_tau and chunk_mask 4-byte)");
+  const DashBwdLayout L = dash_bwd_ws(o, a);
+  if (!workspace || workspace_bytes < L.total || !aligned(workspace, 256))
+    return fail(ENTMAX_ERR_WORKSPACE, "DashAttention backward workspace: need %zu bytes, 256-byte aligned (got %zu)",
+                L.total, workspace_bytes);
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+
+  DashParams dp{};
+  dp.q = q; dp.ks = k_summary; dp.rtau = const_cast<float*>(route_tau); dp.rw = const_cast<float*>(route_w);
+  dp.cmask = const_cast<uint32_t*>(chunk_mask);
+  dp.b = o.b; dp.hq = o.hq; dp.hkv = o.hkv; dp.n = o.n; dp.G = o.G; dp.C = o.C; dp.nc = o.nc; dp.Tr = o.Tr;
+  dp.Wc = o.Wc; dp.max_iters = o.max_iters;
+  dp.cx = (float)(((double)o.alpha - 1.0) * (double)o.gamma * (double)o.scale);
+  dp.alpha = o.alpha; dp.kappa = o.kappa; dp.tol = o.tol; dp.sigma = o.sigma;
+  dp.dbias = (const float*)(ws + L.dbias); dp.dq32 = (const float*)(ws + L.dq32); dp.dq = dq;
+  dp.lp = (float*)(ws + L.lp); dp.dw = (float*)(ws + L.dw); dp.du = (float*)(ws + L.du);
+  dp.qc = ws + L.qc; dp.dpart = (float*)(ws + L.dpart); dp.NP = L.NP; dp.PR = DASH_DKS_ROWS;
+  dp.dks = dk_summary; dp.bmask = (uint32_t*)(ws + L.bmask); dp.W = L.W;
+  dp.gs = (float)((double)o.gamma * (double)o.scale);
+  hipError_t e = launch_dash_bwd_setup(dp, s);
+  if (e != hipSuccess) return hip_fail(e, "DashAttention block mask and prior");
+
+  // stage 2: the attention backward in mode 3 (delta = dO . o)
+  const int hq_all = o.b * o.hq, hkv_all = o.b * o.hkv;
+  const BwdLayout& B = L.att;
+  PrepBatch pb{};
+  pb.job[0] = Relayout{dout, ws + B.dor, nullptr, o_, (float*)(ws + B.delta), hq_all, "do"};
+  pb.job[1] = Relayout{q, ws + B.qr, ws + L.qc, nullptr, nullptr, hq_all, "q"};
+  pb.job[2] = Relayout{k, ws + B.kr, nullptr, nullptr, nullptr, hkv_all, "k"};
+  pb.job[3] = Relayout{v, ws + B.vr, nullptr, nullptr, nullptr, hkv_all, "v"};
+  pb.njobs = 4;
+  pb.n = o.n;
+  pb.mask = dp.bmask;
+  pb.maskT = (uint32_t*)(ws + B.maskT);
+  pb.planes = hq_all; pb.Tr = a.Tr; pb.Tc = a.Tc; pb.W = a.W; pb.WT = a.WT;
+  e = launch_prep(pb, o.dtype, o.D, "dash_bwd_prep", s);
+  if (e != hipSuccess) return hip_fail(e, "DashAttention backward preparation");
+  BwdParams p{};
+  p.qr = ws + B.qr; p.dor = ws + B.dor; p.kr = ws + B.kr; p.vr = ws + B.vr;
+  p.tau = lse; p.delta = (const float*)(ws + B.delta);
+  p.mask = dp.bmask; p.maskT = (const uint32_t*)(ws + B.maskT);
+  p.dq = nullptr; p.dk = dk; p.dv = dv;
+  p.b = o.b; p.hq = o.hq; p.hkv = o.hkv; p.n = o.n; p.G = o.G;
+  p.causal = 1; p.Br = 64; p.Bc = 64;
+  p.cx = o.scale; p.scale = o.scale; p.kappa = 1.0f; p.am1 = 0.0f; p.slopes = nullptr;
+  p.Tr = a.Tr; p.Tc = a.Tc; p.W = a.W; p.WT = a.WT;
+  p.dense = 0;
+  p.lp = dp.lp; p.C = o.C;
+  p.dq32 = (float*)(ws + L.dq32); p.dbias = (float*)(ws + L.dbias);
+  p.map = make_map(o.b * o.hkv, a.Tc);
+  prof_begin("dash_bwd_dkv", s);
+  e = launch_bwd_dkv(p, o.dtype, o.D, MODE_DASH, s);
+  prof_end(s);
+  if (e != hipSuccess) return hip_fail(e, "DashAttention dK/dV kernel");
+  p.map = make_map(o.b * o.hkv, o.G * a.Tr);
+  prof_begin("dash_bwd_dq", s);
+  e = launch_bwd_dq(p, o.dtype, o.D, MODE_DASH, s);
+  prof_end(s);
+  if (e != hipSuccess) return hip_fail(e, "DashAttention dQ kernel");
+
+  // stage 1: the routing's share of dQ and the summaries' gradient
+  e = launch_dash_route_bwd(dp, o.dtype, o.D, o.mode, s);
+  if (e != hipSuccess) return hip_fail(e, "DashAttention routing backward");
+  return ENTMAX_OK;
+}
+
 const char* entmax_status_string(entmax_status s) {
   switch (s) {
     case ENTMAX_OK: return "ok";

@@ -164,7 +164,29 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void k_bwd_dkv(BwdParams p)
     const bool diag = p.causal && key0 + 31 > q0;
     f32x16 P, G;
     float mx = 0.f;
-    if (diag) {
+    if constexpr (MODE == MODE_DASH) {
+      // softmax with the routing prior: P = exp(scale s - lse + sigma ln wbar) on a routed
+      // chunk, exp(scale s - lse) on the query's own chunk (keys after the query masked);
+      // dS = P (dP - delta) is the softmax backward, so G = P
+      const int cJ = key0 / p.C;
+      if (q0 / p.C != cJ) {
+        const float* lr = p.lp + ((size_t)(bi * p.hkv + kvh) * (n / p.C) + cJ) * n + q0;
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const f32x4 lv = *reinterpret_cast<const f32x4*>(lr + 8 * g4 + 4 * h);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) off[4 * g4 + j] += lv[j];
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float tt = fmaf(cx, S[r], off[r]);
+        if (diag && key0 + c > q0 + acc_row(r, h)) tt = -INFINITY;
+        P[r] = exp2f(tt * 1.44269504088896341f);
+        G[r] = P[r];
+        mx = fmaxf(mx, P[r]);
+      }
+    } else if (diag) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         float tt = fmaf(cx, S[r], off[r]);
@@ -352,7 +374,19 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void k_bwd_dq(BwdParams p) 
     const bool diag = p.causal && key0 + 31 > q0;
     f32x16 G;
     float mx = 0.f;
-    if (diag) {
+    if constexpr (MODE == MODE_DASH) {
+      // softmax with the routing prior (see k_bwd_dkv); G = P
+      const int cJ = key0 / p.C;
+      float pr = 0.f;
+      if (q0 / p.C != cJ) pr = p.lp[((size_t)(bi * p.hkv + kvh) * (n / p.C) + cJ) * n + q0 + c];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float tt = fmaf(cx, S[r], off[r] + pr);
+        if (diag && key0 + acc_row(r, h) > q0 + c) tt = -INFINITY;
+        G[r] = exp2f(tt * 1.44269504088896341f);
+        mx = fmaxf(mx, G[r]);
+      }
+    } else if (diag) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         float tt = fmaf(cx, S[r], off[r]);
@@ -369,13 +403,27 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void k_bwd_dq(BwdParams p) 
         mx = fmaxf(mx, dm);
       }
     }
-    if (!p.dense && ballot(mx > 0.f) == 0) continue;   // an all-zero sub-tile
+    // (mode 3: the row's sum of dS over the sub-block, the gradient of its prior term)
+    float* const dbr = MODE == MODE_DASH ? p.dbias + ((size_t)(bi * p.hq + head) * (n >> 5) + kbk) * n + q0 + c
+                                         : nullptr;
+    if (!p.dense && ballot(mx > 0.f) == 0) {   // an all-zero sub-tile
+      if constexpr (MODE == MODE_DASH)
+        if (h == 0) *dbr = 0.f;
+      continue;
+    }
     f32x16 dP = f32x16{};
 #pragma unroll
     for (int s = 0; s < DS; ++s) mma16(dP, va[s], db[s]);   // dP^T[key][q]
     f32x16 dS;
 #pragma unroll
     for (int r = 0; r < 16; ++r) dS[r] = G[r] * (dP[r] - dq_delta);
+    if constexpr (MODE == MODE_DASH) {
+      float rs = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) rs += dS[r];
+      rs += xor32f(rs);
+      if (h == 0) *dbr = rs;
+    }
     Frag<T> kt[2][DC];                   // K^T of the sub-block (cols layout)
     rows_to_cols<T, DS>(kt, ka, eye);
 #pragma unroll
@@ -404,7 +452,19 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void k_bwd_dq(BwdParams p) 
         for (int r = 0; r < 16; ++r) dq[dc][r] += buf[(dc * 16 + r) * 64 + lane];
     }
   }
-  if (slot == 0) {
+  if (MODE == MODE_DASH && slot == 0) {
+    // stage-2 dQ in fp32; the routing backward adds its share and writes dQ
+    float* dQ = p.dq32 + (qrow0 + q0 + c) * D;
+    const float sc = p.scale;
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d0 = 32 * dc + 8 * g4 + 4 * h;
+        *reinterpret_cast<f32x4*>(dQ + d0) = f32x4{sc * dq[dc][4 * g4], sc * dq[dc][4 * g4 + 1],
+                                                  sc * dq[dc][4 * g4 + 2], sc * dq[dc][4 * g4 + 3]};
+      }
+  } else if (slot == 0) {
     T* dQ = reinterpret_cast<T*>(p.dq) + (qrow0 + q0 + c) * D;
     const float sc = p.scale;
 #pragma unroll
@@ -425,7 +485,9 @@ static hipError_t launch_dkv_t(const BwdParams& p, int mode, hipStream_t s) {
   const int grid = wgmap_grid(p.map);
   if (grid == 0) return hipSuccess;
   void (*fn)(BwdParams);
-  if (p.slopes)
+  if (mode == MODE_DASH)
+    fn = k_bwd_dkv<T, D, MODE_DASH, false>;
+  else if (p.slopes)
     fn = mode == 1 ? k_bwd_dkv<T, D, 1, true> : mode == 2 ? k_bwd_dkv<T, D, 2, true> : k_bwd_dkv<T, D, 0, true>;
   else
     fn = mode == 1 ? k_bwd_dkv<T, D, 1, false> : mode == 2 ? k_bwd_dkv<T, D, 2, false> : k_bwd_dkv<T, D, 0, false>;
@@ -440,7 +502,9 @@ static hipError_t launch_dq_t(const BwdParams& p, int mode, hipStream_t s) {
   const int grid = wgmap_grid(p.map);
   if (grid == 0) return hipSuccess;
   void (*fn)(BwdParams);
-  if (p.slopes)
+  if (mode == MODE_DASH)
+    fn = k_bwd_dq<T, D, MODE_DASH, false>;
+  else if (p.slopes)
     fn = mode == 1 ? k_bwd_dq<T, D, 1, true> : mode == 2 ? k_bwd_dq<T, D, 2, true> : k_bwd_dq<T, D, 0, true>;
   else
     fn = mode == 1 ? k_bwd_dq<T, D, 1, false> : mode == 2 ? k_bwd_dq<T, D, 2, false> : k_bwd_dq<T, D, 0, false>;

@@ -282,6 +282,349 @@ __global__ __launch_bounds__((64 * DASH_WAVES), (dash_attn_occ<T>())) void k_das
   if (p.lse && h == 0) p.lse[bh * n + qrow] = (mrun + log2f(lt)) * 0.69314718055994531f;
 }
 
+// ================================================================================ backward
+// The backward of stages 1-2 (DashAttention (it), stage 1: gradients flow back through the
+// routing to the chunk summaries). Stage 2 is softmax attention over the 64 x 64 blocks that
+// the routing and the diagonal branch select, with the prior sigma ln wbar as a per-(row,
+// chunk) additive term; its backward runs in the attention backward kernels (bwd.hip, mode
+// 3), which also leave, per row and 32-key sub-block, the sum of dS: the gradient of the
+// prior terms. Here:
+//   k_dash_bwd_setup -- the stage-2 block mask of each query head from the group's chunk
+//     mask (a key block is set when its chunk is routed by the query tile, or it lies in the
+//     tile's own chunk at or before the tile), and the prior table sigma ln wbar;
+//   k_dash_dw -- dwbar(c, i) = sigma / wbar(c, i) * (the group's dS sums over chunk c), and
+//     each head's routing weights take dwbar / G (stored as dw);
+//   k_dash_route_bwd -- per (batch, KV head, 64-row tile), a wave per 32 rows as in the
+//     routing forward: through the alpha-entmax Jacobian diag(g) - g g^T / sum g (g =
+//     [x - tau]_+^(kappa - 1), the forward's tau) the routing logits get
+//     du = g (dw - (g . dw) / sum g), stored for the summaries' gradient, and dQ = stage-2 dQ
+//     + gamma scale du . ksum (on the matrix cores, the forward's logit tiles);
+//   k_dash_dks -- the summaries' gradient, dksum(c) = gamma scale sum over the group's heads
+//     and rows of du(c, i) q_i, as a matrix product contracted over rows (Q^T from its
+//     fragment-major column copy, du^T as the B operand), one partial per (32-chunk block,
+//     piece of rows); k_dash_dks_reduce adds the pieces in order.
+
+__global__ void k_dash_bwd_setup(DashParams p) {
+  const int Tb = p.n / 64;
+  const size_t words = (size_t)p.b * p.hq * Tb * p.W;
+  const size_t id = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (id < words) {
+    const int wi = (int)(id % p.W);
+    const int I = (int)((id / p.W) % Tb);
+    const size_t bh = id / ((size_t)p.W * Tb);
+    const int bi = (int)(bh / p.hq), head = (int)(bh % p.hq);
+    const int unit = bi * p.hkv + head / p.G;
+    const int m = (I * 64) / p.C;                 // the tile's own chunk (every row shares it)
+    const uint32_t* cw = p.cmask + ((size_t)unit * p.Tr + I) * p.Wc;
+    uint32_t word = 0;
+    for (int b = 0; b < 32; ++b) {
+      const int J = wi * 32 + b;
+      if (J >= Tb) break;
+      const int cJ = (J * 64) / p.C;
+      bool on;
+      if (cJ < m) on = (cw[cJ >> 5] >> (cJ & 31)) & 1u;
+      else on = cJ == m && J <= I;
+      word |= (on ? 1u : 0u) << b;
+    }
+    p.bmask[id] = word;
+    return;
+  }
+  const size_t e = id - words;
+  if (e >= (size_t)p.b * p.hkv * p.nc * p.n) return;
+  const float wv = p.rw[e];
+  p.lp[e] = wv > 0.f ? p.sigma * logf(wv) : -INFINITY;
+}
+
+// dw(c, i) of a (unit, chunk, row): sigma / (G wbar) times the dS sums of the group's heads
+// over the chunk's sub-blocks (heads in order, sub-blocks in order); 0 off the support
+__global__ void k_dash_dw(DashParams p) {
+  const size_t id = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int n = p.n;
+  if (id >= (size_t)p.b * p.hkv * p.nc * n) return;
+  const int i = (int)(id % n);
+  const int cc = (int)((id / n) % p.nc);
+  const size_t unit = id / ((size_t)n * p.nc);
+  const float wv = p.rw[id];
+  float out = 0.f;
+  if (wv > 0.f) {
+    const int SB = p.C / 32;
+    const size_t bh0 = (unit / p.hkv) * p.hq + (unit % p.hkv) * p.G;
+    float s = 0.f;
+    for (int g = 0; g < p.G; ++g) {
+      const float* db = p.dbias + ((bh0 + g) * (size_t)(n >> 5) + (size_t)cc * SB) * n + i;
+      float sm = 0.f;
+      for (int u = 0; u < SB; ++u) sm += db[(size_t)u * n];
+      s += sm;
+    }
+    out = p.sigma / (float)p.G * s / wv;
+  }
+  p.dw[id] = out;
+}
+
+template <typename T, int D, int MODE>
+__global__ __launch_bounds__(64 * DASH_WAVES) void k_dash_route_bwd(DashParams p) {
+  constexpr int DS = D / 16, DC = D / 32;
+  const int U = p.b * p.hkv;
+  const int bid = blockIdx.x;
+  if (bid >= U * p.Tr) return;
+  const int t = p.Tr - 1 - bid / U;
+  const int unit = bid % U;
+  const int bi = unit / p.hkv, kvh = unit % p.hkv;
+  const int lane = lane_id(), c = lane & 31, h = lane >> 5;
+  const int w = uniform_i32(wave_id());
+  const int n = p.n;
+  const int qrow = t * 64 + w * 32 + c;
+  const int m = (t * 64) / p.C;
+  const int nb = (m + 31) >> 5;
+  const T* Ks = reinterpret_cast<const T*>(p.ks) + (size_t)unit * p.nc * D;
+  const float* dwr = p.dw + (size_t)unit * p.nc * n + qrow;   // + chunk * n
+  const float kappa = p.kappa;
+
+  Frag<T> eye[2];
+  eye_frags(eye, c, h);
+  for (int g = 0; g < p.G; ++g) {
+    const size_t bh = (size_t)bi * p.hq + kvh * p.G + g;
+    f32x16 dqr[DC];
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc) dqr[dc] = f32x16{};
+    float* du = p.du + bh * p.nc * n;
+    if (m > 0) {
+      const T* Q = reinterpret_cast<const T*>(p.q) + bh * n * D;
+      Frag<T> qf[DS];
+#pragma unroll
+      for (int s = 0; s < DS; ++s) load_frag(qf[s], Q + (size_t)qrow * D + 16 * s + 8 * h);
+      const float tau = p.rtau[bh * n + qrow];
+      // the routing logits of the forward (same products, same order), chunk block jb
+      auto logits = [&](int jb, Frag<T> (&kf)[DS]) -> f32x16 {
+        const int ch = 32 * jb + c;
+#pragma unroll
+        for (int s = 0; s < DS; ++s) {
+          if (ch < m) load_frag(kf[s], Ks + (size_t)ch * D + 16 * s + 8 * h);
+          else zero_frag(kf[s]);
+        }
+        f32x16 acc = f32x16{};
+#pragma unroll
+        for (int s = 0; s < DS; ++s) mma16(acc, kf[s], qf[s]);
+        f32x16 x;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) x[r] = (32 * jb + acc_row(r, h) < m) ? p.cx * acc[r] : -INFINITY;
+        return x;
+      };
+      auto dwv = [&](int jb, f32x16& v) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int cr = 32 * jb + acc_row(r, h);
+          v[r] = cr < m ? dwr[(size_t)cr * n] : 0.f;
+        }
+      };
+      // delta = (g . dw) / sum g over the row's chunks
+      float sg = 0.f, sgd = 0.f;
+      for (int jb = 0; jb < nb; ++jb) {
+        Frag<T> kf[DS];
+        f32x16 dv;
+        dwv(jb, dv);
+        const f32x16 x = logits(jb, kf);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float gg = Weight<MODE>::g(fmaxf(x[r] - tau, 0.f), kappa);
+          sg += gg;
+          sgd += gg * dv[r];
+        }
+      }
+      sg += xor32f(sg);
+      sgd += xor32f(sgd);
+      const float delta = sgd / sg;
+      for (int jb = 0; jb < nb; ++jb) {
+        Frag<T> kf[DS];
+        f32x16 dv;
+        dwv(jb, dv);
+        const f32x16 x = logits(jb, kf);
+        f32x16 dz;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float gg = Weight<MODE>::g(fmaxf(x[r] - tau, 0.f), kappa);
+          dz[r] = gg * (dv[r] - delta);
+          const int cr = 32 * jb + acc_row(r, h);
+          if (cr < p.nc) du[(size_t)cr * n + qrow] = dz[r];
+        }
+        // dQ^T[d][q] += ksum^T dz^T (the logit tile as the B operand)
+        Frag<T> kt[2][DC];
+        rows_to_cols<T, DS>(kt, kf, eye);
+#pragma unroll
+        for (int mm = 0; mm < 2; ++mm) {
+          Frag<T> zf;
+          acc_frag(zf, dz, mm);
+#pragma unroll
+          for (int dc = 0; dc < DC; ++dc) mma16(dqr[dc], kt[mm][dc], zf);
+        }
+      }
+    }
+    // chunks the row does not route (its own and later ones): no gradient
+    for (int jb = nb; 32 * jb < p.nc; ++jb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int cr = 32 * jb + acc_row(r, h);
+        if (cr < p.nc) du[(size_t)cr * n + qrow] = 0.f;
+      }
+    // dQ = stage-2 dQ + gamma scale dz . ksum
+    const float* d32 = p.dq32 + (bh * n + qrow) * D;
+    T* dQ = reinterpret_cast<T*>(p.dq) + (bh * n + qrow) * D;
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d0 = 32 * dc + 8 * g4 + 4 * h;
+        const f32x4 a = *reinterpret_cast<const f32x4*>(d32 + d0);
+        store4(dQ + d0, a[0] + p.gs * dqr[dc][4 * g4], a[1] + p.gs * dqr[dc][4 * g4 + 1],
+               a[2] + p.gs * dqr[dc][4 * g4 + 2], a[3] + p.gs * dqr[dc][4 * g4 + 3]);
+      }
+  }
+}
+
+// Partial summary gradients: work group (unit, 32-chunk block cb, row piece pc); its four
+// waves take the 32-row blocks of the piece in turn, for every head of the group, and add
+// dksum^T[d][c] += sum_i Q^T[d][i] du^T[i][c]. Rows before (32 cb + 1) C route none of the
+// block's chunks (du is 0 there) and are not visited.
+constexpr int DKS_WAVES = 4;
+
+template <typename T, int D>
+__global__ __launch_bounds__(64 * DKS_WAVES) void k_dash_dks(DashParams p) {
+  constexpr int DC = D / 32;
+  __shared__ float red[(DKS_WAVES - 1) * DC * 16 * 64];
+  const int U = p.b * p.hkv;
+  const int bid = blockIdx.x;
+  if (bid >= U * p.Wc * p.NP) return;
+  const int unit = bid % U;
+  const int cb = (bid / U) % p.Wc;
+  const int pc = bid / (U * p.Wc);
+  const int n = p.n;
+  const int start = (32 * cb + 1) * p.C;        // first row that routes a chunk of the block
+  const int r0 = max(pc * p.PR, start), r1 = min((pc + 1) * p.PR, n);
+  if (r0 >= r1) return;                         // whole work group (the reduction skips it)
+  const int lane = lane_id(), c = lane & 31, h = lane >> 5;
+  const int w = uniform_i32(wave_id());
+  const int bi = unit / p.hkv, kvh = unit % p.hkv;
+  const int ch = 32 * cb + c;
+  const bool live = ch < p.nc;
+  f32x16 acc[DC];
+#pragma unroll
+  for (int dc = 0; dc < DC; ++dc) acc[dc] = f32x16{};
+  for (int g = 0; g < p.G; ++g) {
+    const size_t bh = (size_t)bi * p.hq + kvh * p.G + g;
+    const T* Qc = reinterpret_cast<const T*>(p.qc) + bh * n * D;
+    const float* du = p.du + (bh * p.nc + (live ? ch : 0)) * n;
+    for (int b = r0 / 32 + w; b < r1 / 32; b += DKS_WAVES) {
+      Frag<T> a[DC][2], bf[2];
+#pragma unroll
+      for (int dc = 0; dc < DC; ++dc)
+#pragma unroll
+        for (int mm = 0; mm < 2; ++mm) load_frag(a[dc][mm], Qc + ((size_t)((b * DC + dc) * 2 + mm) * 64 + lane) * 8);
+#pragma unroll
+      for (int mm = 0; mm < 2; ++mm) {
+        // rows 16 mm + sigma(8 h + j) of the block: two runs of four
+        if (live) {
+          const f32x4 lo = *reinterpret_cast<const f32x4*>(du + 32 * b + 16 * mm + 4 * h);
+          const f32x4 hi = *reinterpret_cast<const f32x4*>(du + 32 * b + 16 * mm + 8 + 4 * h);
+          set_frag(bf[mm], lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]);
+        } else {
+          zero_frag(bf[mm]);
+        }
+      }
+#pragma unroll
+      for (int mm = 0; mm < 2; ++mm)
+#pragma unroll
+        for (int dc = 0; dc < DC; ++dc) mma16(acc[dc], a[dc][mm], bf[mm]);
+    }
+  }
+  // the waves' sums in order (wave 0 + 1 + 2 + 3)
+  if (w > 0) {
+    float* dst = red + (size_t)(w - 1) * DC * 16 * 64;
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dst[(dc * 16 + r) * 64 + lane] = acc[dc][r];
+  }
+  __syncthreads();
+  if (w == 0) {
+#pragma unroll
+    for (int v = 0; v < DKS_WAVES - 1; ++v)
+#pragma unroll
+      for (int dc = 0; dc < DC; ++dc)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[dc][r] += red[((size_t)v * DC * 16 + dc * 16 + r) * 64 + lane];
+    // accumulator rows are d, columns the block's chunks
+    float* out = p.dpart + (((size_t)unit * p.Wc + cb) * p.NP + pc) * D * 32;
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) out[(32 * dc + acc_row(r, h)) * 32 + c] = acc[dc][r];
+  }
+}
+
+// dksum(unit, chunk, d) = gamma scale * the pieces' partials in order
+template <typename T, int D>
+__global__ void k_dash_dks_reduce(DashParams p) {
+  const size_t id = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int U = p.b * p.hkv;
+  if (id >= (size_t)U * p.Wc * D * 32) return;
+  const int c = (int)(id & 31);
+  const int d = (int)((id >> 5) % D);
+  const int cb = (int)((id / (32 * D)) % p.Wc);
+  const int unit = (int)(id / ((size_t)32 * D * p.Wc));
+  const int ch = 32 * cb + c;
+  if (ch >= p.nc) return;
+  // the pieces whose work groups ran: from the one holding the block's first routing row on
+  // (none when no row routes a chunk of the block)
+  const int start = (32 * cb + 1) * p.C;
+  const int p0 = start < p.n ? start / p.PR : p.NP;
+  const float* part = p.dpart + ((size_t)unit * p.Wc + cb) * p.NP * D * 32 + d * 32 + c;
+  float tot = 0.f;
+  for (int pc = p0; pc < p.NP; ++pc) tot += part[(size_t)pc * D * 32];
+  reinterpret_cast<T*>(p.dks)[((size_t)unit * p.nc + ch) * D + d] = (T)(p.gs * tot);
+}
+
+hipError_t launch_dash_bwd_setup(const DashParams& p, hipStream_t s) {
+  const size_t items = (size_t)p.b * p.hq * (p.n / 64) * p.W + (size_t)p.b * p.hkv * p.nc * p.n;
+  if (items == 0) return hipSuccess;
+  prof_begin("dash_bwd_setup", s);
+  hipLaunchKernelGGL(k_dash_bwd_setup, dim3((unsigned)((items + 255) / 256)), dim3(256), 0, s, p);
+  prof_end(s);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+static hipError_t launch_dash_route_bwd_t(const DashParams& p, int mode, hipStream_t s) {
+  const int U = p.b * p.hkv;
+  if (U == 0 || p.Tr == 0) return hipSuccess;
+  const size_t cells = (size_t)U * p.nc * p.n;
+  prof_begin("dash_dw", s);
+  hipLaunchKernelGGL(k_dash_dw, dim3((unsigned)((cells + 255) / 256)), dim3(256), 0, s, p);
+  prof_end(s);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  void (*fn)(DashParams) = mode == 1 ? k_dash_route_bwd<T, D, 1> : mode == 2 ? k_dash_route_bwd<T, D, 2>
+                                                                            : k_dash_route_bwd<T, D, 0>;
+  prof_begin("dash_route_bwd", s);
+  hipLaunchKernelGGL(fn, dim3(U * p.Tr), dim3(64 * DASH_WAVES), 0, s, p);
+  prof_end(s);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  prof_begin("dash_dks", s);
+  hipLaunchKernelGGL((k_dash_dks<T, D>), dim3(U * p.Wc * p.NP), dim3(64 * DKS_WAVES), 0, s, p);
+  prof_end(s);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const size_t outs = (size_t)U * p.Wc * D * 32;
+  prof_begin("dash_dks_reduce", s);
+  hipLaunchKernelGGL((k_dash_dks_reduce<T, D>), dim3((unsigned)((outs + 255) / 256)), dim3(256), 0, s, p);
+  prof_end(s);
+  return hipGetLastError();
+}
+
+hipError_t launch_dash_route_bwd(const DashParams& p, int dtype, int D, int mode, hipStream_t s) {
+  if (dtype == 1)
+    return D == 64 ? launch_dash_route_bwd_t<__bf16, 64>(p, mode, s) : launch_dash_route_bwd_t<__bf16, 128>(p, mode, s);
+  return D == 64 ? launch_dash_route_bwd_t<float, 64>(p, mode, s) : launch_dash_route_bwd_t<float, 128>(p, mode, s);
+}
+
 // ================================================================================ launch
 template <typename T, int D>
 static hipError_t launch_dash_t(const DashParams& p, int mode, hipStream_t s) {

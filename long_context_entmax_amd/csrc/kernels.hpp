@@ -133,8 +133,18 @@ struct BwdParams {
   const float* slopes;   // optional [hq] position-bias slopes
   int Tr, Tc, W, WT;
   int dense;             // 1: every item of the mask multiplied in full (no zero-block skip)
+  // mode 3, the DashAttention stage-2 backward (softmax with the routing prior): tau holds
+  // the row's lse, cx the score scale; key j of a routed chunk c adds sigma ln wbar(c, i)
+  const float* lp;       // [b, hkv, nc, n] the prior sigma ln wbar (-inf where wbar = 0), chunk-major
+  int C;                 // keys per chunk
+  float* dq32;           // [b, hq, n, D] fp32 dQ (mode 3 writes here instead of dq)
+  float* dbias;          // [b, hq, n / 32, n] per (32-key sub-block, row) sums of dS (mode 3)
   WgMap map;
 };
+
+// Mode of the backward kernels for the DashAttention stage-2 softmax (modes 0-2 are the
+// alpha-entmax weights)
+constexpr int MODE_DASH = 3;
 
 // decode (decode.hip): the largest key slice of a score / histogram work group
 constexpr int DEC_SPLIT_MAX = 2048;
@@ -175,10 +185,26 @@ struct DashParams {
   float alpha, kappa, tol;
   float c2;              // scale * log2(e): token scores in base-2 units
   float sigma;
+  // backward (entmax_dash_bwd)
+  const float* dbias;    // [b, hq, n / 32, n] per (32-key sub-block, row) sums of the stage-2 dS
+  const float* dq32;     // [b, hq, n, D] stage-2 dQ (fp32)
+  void* dq;              // [b, hq, n, D] dQ out (dtype)
+  float* lp;             // [b, hkv, nc, n] the prior sigma ln wbar, -inf where wbar = 0
+  float* dw;             // [b, hkv, nc, n] gradient of each head's routing weights (chunk-major)
+  float* du;             // [b, hq, nc, n] routing-logit gradient (chunk-major)
+  const void* qc;        // Q, fragment-major columns
+  float* dpart;          // [b * hkv, Wc, NP, D, 32] partial summary gradients (per row piece)
+  void* dks;             // [b, hkv, nc, D] summary gradient out (dtype)
+  uint32_t* bmask;       // [b, hq, n / 64, W] 64 x 64 block mask of stage 2
+  int W;                 // words per block-mask row
+  int NP, PR;            // row pieces of the summary-gradient product and rows per piece
+  float gs;              // gamma * scale: d zbar / d (q . ksum)
 };
 
 hipError_t launch_fwd(const FwdParams& p, int dtype, int D, int mode, hipStream_t s);
 hipError_t launch_dash(const DashParams& p, int dtype, int D, int mode, hipStream_t s);
+hipError_t launch_dash_bwd_setup(const DashParams& p, hipStream_t s);
+hipError_t launch_dash_route_bwd(const DashParams& p, int dtype, int D, int mode, hipStream_t s);
 hipError_t launch_decode(const DecParams& p, int dtype, int D, int mode, hipStream_t s);
 hipError_t launch_prep(const PrepBatch& b, int dtype, int D, const char* name, hipStream_t s);
 hipError_t launch_bwd_dkv(const BwdParams& p, int dtype, int D, int mode, hipStream_t s);

@@ -167,10 +167,14 @@ def dash_fwd(q, k, v, ks, alpha: float, gamma: float, sigma: float, C: int,
 
 
 def dash_bwd(q, k, v, ks, dout, alpha: float, gamma: float, sigma: float, C: int,
-             scale: float | None = None) -> dict:
+             scale: float | None = None, rows=None) -> dict:
     """Gradients of stages 1-2 of a whole problem with respect to q, k, v and the summaries ks,
     given dO (the backward written out in the module docstring). Returns dq [b, hq, n, d],
-    dk, dv [b, hkv, n, d] and dks [b, hkv, nc, d]."""
+    dk, dv [b, hkv, n, d] and dks [b, hkv, nc, d].
+
+    With ``rows`` only those query rows are taken, and only their dq is returned
+    ([b, hq, len(rows), d]): a row's dq depends on that row alone, while dk, dv and dks sum
+    over every row."""
     q, k, v, ks, dout = _f64(q), _f64(k), _f64(v), _f64(ks), _f64(dout)
     b, hq, n, d = q.shape
     hkv, nc = k.shape[1], ks.shape[2]
@@ -179,10 +183,11 @@ def dash_bwd(q, k, v, ks, dout, alpha: float, gamma: float, sigma: float, C: int
         scale = 1.0 / np.sqrt(d)
     kappa = 1.0 / (alpha - 1.0)
     dq, dk, dv, dks = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v), np.zeros_like(ks)
+    row_list = range(n) if rows is None else [int(r) for r in rows]
     for bi in range(b):
         for g in range(hkv):
             kk, vv, kg = k[bi, g], v[bi, g], ks[bi, g]
-            for i in range(n):
+            for i in row_list:
                 m = i // C
                 # stage 1 forward of the row
                 zs, ps, taus = [], [], []
@@ -222,4 +227,6 @@ def dash_bwd(q, k, v, ks, dout, alpha: float, gamma: float, sigma: float, C: int
                     dz = gg * (dw - (gg @ dw) / gg.sum())
                     dq[bi, hh, i] += gamma * scale * (dz @ kg[:m])
                     dks[bi, g, :m] += gamma * scale * np.outer(dz, q[bi, hh, i])
+    if rows is not None:
+        return {"dq": dq[:, :, np.asarray(row_list, dtype=np.int64)]}
     return {"dq": dq, "dk": dk, "dv": dv, "dks": dks}

@@ -191,6 +191,9 @@ def test_dash_argument_errors(L, kw, status):
     f = ctypes.c_void_p(256)
     st = L.entmax_dash_fwd(ctypes.byref(d), f, f, f, f, f, None, None, f, f, f, 1 << 30, None)
     assert st == status, L.entmax_last_error()
+    assert L.entmax_dash_bwd_workspace_bytes(ctypes.byref(d)) == 0
+    st = L.entmax_dash_bwd(ctypes.byref(d), *([f] * 14), f, 1 << 30, None)
+    assert st == status, L.entmax_last_error()
 
 
 def test_dash_pointers_workspace_and_sizes(L):
@@ -211,6 +214,42 @@ def test_dash_pointers_workspace_and_sizes(L):
         e = _dash_desc(**kw)
         assert L.entmax_dash_fwd(ctypes.byref(e), None, None, None, None, None, None, None, None, None, None, 0,
                                  None) == 0
+
+
+def test_dash_bwd_pointers_workspace_and_sizes(L):
+    d = _dash_desc()
+    f = ctypes.c_void_p(4096)
+    mis = ctypes.c_void_p(4098)
+    need = L.entmax_dash_bwd_workspace_bytes(ctypes.byref(d))
+    b, hq, hkv, n, D, nc = 1, 4, 2, 1024, 64, 16
+    # at least: delta, the fragment-major copies of Q (rows and columns), dO, K and V, the
+    # block mask, the prior table and the weight gradient, fp32 dQ, the per-(sub-block, row)
+    # dS sums, the routing-logit gradient and the per-piece summary-gradient partials
+    low = (b * hq * n * 4 + 3 * b * hq * n * D * 2 + 2 * b * hkv * n * D * 2 + b * hq * (n // 64) * 4
+           + 2 * b * hkv * nc * n * 4 + b * hq * n * D * 4 + b * hq * (n // 32) * n * 4 + b * hq * nc * n * 4
+           + b * hkv * 1 * (n // 256) * D * 32 * 4)
+    assert low <= need <= low + 64 * 1024
+    args = [f] * 14
+
+    def call(i=None, val=None, ws=f, nbytes=need, desc=ctypes.byref(d)):
+        a = list(args)
+        if i is not None:
+            a[i] = val
+        return L.entmax_dash_bwd(desc, *a, ws, nbytes, None)
+
+    assert call(desc=None) == 1
+    for i in range(14):                       # every tensor is required
+        assert call(i, None) == 1, i
+    assert call(3, mis) == 5                  # k_summary
+    assert call(4, mis) == 5                  # o
+    assert call(9, mis) == 5                  # dout
+    assert call(13, mis) == 5                 # dk_summary
+    assert call(nbytes=need - 1) == 6
+    assert call(ws=None) == 6
+    assert call(ws=ctypes.c_void_p(4096 + 16)) == 6
+    for kw in (dict(batch=0), dict(seqlen=0)):
+        e = _dash_desc(**kw)
+        assert L.entmax_dash_bwd(ctypes.byref(e), *([None] * 14), None, 0, None) == 0
 
 
 def test_plain_c_program_uses_the_abi(L, tmp_path):

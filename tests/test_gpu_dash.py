@@ -1,4 +1,4 @@
-"""GPU parity of the DashAttention forward (stages 1-2, include/dash_attn.h) with the fp64
+"""GPU parity of the DashAttention forward and backward (stages 1-2, include/dash_attn.h) with the fp64
 oracle ``oracle.dash`` on the same seeded inputs (DashAttention (it), stages 1 and 2).
 
 Bars: bf16 -- max |d route_tau| <= 1e-3, max |d wbar| <= 1e-3, max |do| <= 1e-2,
@@ -18,7 +18,7 @@ import torch
 import oracle.dash as odash
 import synth
 import long_context_entmax_amd as lce
-from tests.gpu_helpers import dev, to64
+from tests.gpu_helpers import dev, rel_fro, to64
 
 pytestmark = pytest.mark.gpu
 
@@ -141,3 +141,94 @@ def test_dash_fullsize_sampled_rows():
     assert np.abs(g["lse"].numpy()[:, :, rows] - ref["lse"]).max() < 1e-3
     gm = g["chunk_mask"].numpy().astype(np.int64) & 0xFFFFFFFF
     np.testing.assert_array_equal(gm, _mask_from_w(g["route_w"].numpy().astype(np.float64), n))
+
+
+# ------------------------------------------------------------------------------ backward
+# Bars (relative Frobenius error of each gradient against the oracle's, as the attention
+# backward): bf16 2e-2, fp32 1e-4. Both sides see the same inputs; the kernel's backward
+# takes its own forward's o, lse, route_tau and route_w, the oracle recomputes them.
+
+def _run_bwd(q, k, v, ks, do, C, alpha, gamma, sigma):
+    d0 = dev()
+    q, k, v, ks, do = q.to(d0), k.to(d0), v.to(d0), ks.to(d0), do.to(d0)
+    r = lce.dash_fwd(q, k, v, ks, C, alpha, gamma, sigma)
+    gr = lce.dash_bwd(q, k, v, ks, do, r.o, r.lse, r.route_tau, r.route_w, r.chunk_mask, C, alpha, gamma, sigma)
+    torch.cuda.synchronize()
+    return {kk: getattr(gr, kk).float().cpu().numpy().astype(np.float64) for kk in ("dq", "dk", "dv", "dk_summary")}
+
+
+def _inputs_bwd(b, hq, hkv, n, d, dtype, C, seed, qk_scale=1.0):
+    w = synth.Workload("dash", b, hq, hkv, n, d, dtype, 1.5, True, 64, 64, 16, "normal",
+                       extra={"qk_scale": qk_scale}, seed=seed)
+    inp = synth.make_inputs(w, need_grad_inputs=True)
+    return inp["q"], inp["k"], inp["v"], synth.chunk_summaries(w, C), inp["do"]
+
+
+def _check_bwd(g, ref, bar):
+    for name, rname in (("dq", "dq"), ("dk", "dk"), ("dv", "dv"), ("dk_summary", "dks")):
+        if not np.any(ref[rname]):
+            assert not np.any(g[name]), name
+            continue
+        err = rel_fro(g[name], ref[rname])
+        print(f"  {name}: rel err {err:.2e}", flush=True)
+        assert err < bar, (name, err)
+
+
+DASH_BWD_CASES = [
+    # (b, hq, hkv, n, d, dtype, C, alpha, gamma, sigma)
+    (1, 4, 2, 1024, 64, "bf16", 64, 1.5, 8.0, 1.0),
+    (2, 2, 1, 1024, 128, "bf16", 128, 2.0, 16.0, 1.0),
+    (1, 6, 2, 768, 64, "bf16", 64, 1.25, 4.0, 0.5),      # GQA 3, routing alpha 1.25
+    (1, 4, 4, 1024, 64, "bf16", 64, 1.5, 1.0, 0.0),      # sigma 0: no gradient reaches the summaries
+    (1, 2, 2, 1536, 128, "bf16", 256, 1.5, 8.0, 2.0),    # chunk 256
+    (1, 8, 1, 512, 64, "bf16", 64, 1.5, 12.0, 1.0),      # GQA 8
+    (1, 2, 1, 64, 64, "bf16", 64, 1.5, 8.0, 1.0),        # one chunk: no routing, diagonal branch only
+]
+
+
+@pytest.mark.parametrize("case", DASH_BWD_CASES, ids=[str(c) for c in DASH_BWD_CASES])
+def test_dash_bwd_bf16(case):
+    b, hq, hkv, n, d, dt, C, alpha, gamma, sigma = case
+    print(f"[case] dash bwd {case}", flush=True)
+    q, k, v, ks, do = _inputs_bwd(b, hq, hkv, n, d, dt, C, zlib.crc32(str(case).encode()) & 0xFFFF)
+    ref = odash.dash_bwd(to64(q), to64(k), to64(v), to64(ks), to64(do), alpha, gamma, sigma, C)
+    g = _run_bwd(q, k, v, ks, do, C, alpha, gamma, sigma)
+    _check_bwd(g, ref, 2e-2)
+
+
+def test_dash_bwd_fp32():
+    b, hq, hkv, n, d, C = 1, 4, 2, 1024, 64, 64
+    print("[case] dash bwd fp32", flush=True)
+    q, k, v, ks, do = _inputs_bwd(b, hq, hkv, n, d, "f32", C, 91)
+    ref = odash.dash_bwd(to64(q), to64(k), to64(v), to64(ks), to64(do), 1.5, 8.0, 1.0, C)
+    g = _run_bwd(q, k, v, ks, do, C, 1.5, 8.0, 1.0)
+    _check_bwd(g, ref, 1e-4)
+
+
+def test_dash_bwd_fullsize_sampled_rows():
+    """The 16K benchmark shape in the benchmark's launch configuration: dq of 24 sampled rows
+    against the oracle (a row's dq depends on that row alone), and two sums that hold at any
+    size: per KV group, sum_j dv_j = sum over the group's rows of dO_i (each row's weights sum
+    to 1), and sum_j dk_j = 0 (each row's dS sums to 0)."""
+    import bench
+    w = bench.dash_workload()
+    C, gamma, sigma = bench.DASH_CHUNK, bench.DASH_GAMMA, bench.DASH_SIGMA
+    print(f"[case] dash bwd full size {w.name}", flush=True)
+    inp = synth.make_inputs(w, need_grad_inputs=True)
+    ks = synth.chunk_summaries(w, C)
+    g = _run_bwd(inp["q"], inp["k"], inp["v"], ks, inp["do"], C, w.alpha, gamma, sigma)
+    n = w.seqlen
+    rows = np.unique(np.concatenate([np.arange(0, 2), np.arange(63, 66), np.arange(n - 3, n),
+                                     np.linspace(100, n - 100, 16).astype(np.int64)]))
+    ref = odash.dash_bwd(to64(inp["q"]), to64(inp["k"]), to64(inp["v"]), to64(ks), to64(inp["do"]), w.alpha,
+                         gamma, sigma, C, rows=rows)
+    err = rel_fro(g["dq"][:, :, rows], ref["dq"])
+    print(f"  dq (sampled rows): rel err {err:.2e}", flush=True)
+    assert err < 2e-2
+    b, hq, hkv = w.batch, w.heads_q, w.heads_kv
+    G = hq // hkv
+    do64 = to64(inp["do"]).reshape(b, hkv, G, n, -1).sum(axis=(2, 3))
+    dv_sum = g["dv"].sum(axis=2)
+    assert rel_fro(dv_sum, do64) < 2e-2
+    dk_sum = g["dk"].sum(axis=2)
+    assert np.linalg.norm(dk_sum) < 2e-2 * np.linalg.norm(g["dk"])

@@ -406,6 +406,14 @@ def dash_bench(args, lce, dev):
     ms_fwd, r = timed(fwd)
     ms, _ = timed(train_step)
     wall = time.time() - t0
+    if args.copy_probe_mib > 0:
+        # a plain fp32 copy of known size, the reference for scaling the traffic counters
+        src = torch.ones(args.copy_probe_mib * (1 << 20) // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
     lce.profile(True)
     lce.profile_read()
     for _ in range(args.steps):

@@ -29,8 +29,18 @@ FLAGS = [
 ]
 
 
+# per-source flags: the backward kernels convert matrix-core results to operands on every
+# tile; with the results in VGPRs (not accumulation registers) no copy precedes each
+# conversion, which at head_dim 128 (one wave per SIMD, every register in use) removes
+# several hundred copies per tile
+FILE_FLAGS = {
+    "bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "dash.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def _compile(src: str, obj: str) -> None:
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)

@@ -604,12 +604,12 @@ entmax_status entmax_dash_fwd(const entmax_dash_desc* desc, const void* q, const
 }
 
 // ------------------------------------------------------------------------ DashAttention backward
-// Stage 2 runs through the attention backward (mode 3) as softmax attention over 64 x 64
+// Stage 2 runs through the attention backward (mode 3) as softmax attention over 32 x 64
 // blocks; this is its descriptor, and the layout of the backward's workspace.
 static entmax_status dash_attn_view(const DashDerived& o, Derived& a) {
   entmax_attn_desc ad{};
   ad.batch = o.b; ad.heads_q = o.hq; ad.heads_kv = o.hkv; ad.seqlen = o.n; ad.head_dim = o.D;
-  ad.dtype = o.dtype; ad.alpha = 1.5f; ad.causal = 1; ad.block_q = 64; ad.block_k = 64; ad.n_bins = 16;
+  ad.dtype = o.dtype; ad.alpha = 1.5f; ad.causal = 1; ad.block_q = 32; ad.block_k = 64; ad.n_bins = 16;
   ad.scale = o.scale;
   return derive(&ad, a);
 }
@@ -619,7 +619,7 @@ constexpr int DASH_DKS_ROWS = 256;
 
 struct DashBwdLayout {
   BwdLayout att;        // the attention backward's part (at offset 0)
-  size_t bmask, lp, dw, qc, dq32, dbias, du, dpart, total;
+  size_t fine, bmask, lp, dw, qc, dq32, dbias, du, dpart, total;
   int W, NP;
 };
 static DashBwdLayout dash_bwd_ws(const DashDerived& o, const Derived& a) {
@@ -630,7 +630,8 @@ static DashBwdLayout dash_bwd_ws(const DashDerived& o, const Derived& a) {
   L.W = (Tb + 31) / 32;
   L.NP = (o.n + DASH_DKS_ROWS - 1) / DASH_DKS_ROWS;
   size_t off = L.att.total;
-  L.bmask = off; off += align256(rows * Tb * L.W * 4);
+  L.fine = off; off += align256(units * (o.n / 32) * o.Wc * 4);
+  L.bmask = off; off += align256(rows * (o.n / 32) * L.W * 4);
   L.lp = off; off += align256(units * o.nc * o.n * 4);
   L.dw = off; off += align256(units * o.nc * o.n * 4);
   L.qc = off; off += align256(rows * o.n * o.D * o.es);
@@ -684,7 +685,7 @@ entmax_status entmax_dash_bwd(const entmax_dash_desc* desc, const void* q, const
   dp.dbias = (const float*)(ws + L.dbias); dp.dq32 = (const float*)(ws + L.dq32); dp.dq = dq;
   dp.lp = (float*)(ws + L.lp); dp.dw = (float*)(ws + L.dw); dp.du = (float*)(ws + L.du);
   dp.qc = ws + L.qc; dp.dpart = (float*)(ws + L.dpart); dp.NP = L.NP; dp.PR = DASH_DKS_ROWS;
-  dp.dks = dk_summary; dp.bmask = (uint32_t*)(ws + L.bmask); dp.W = L.W;
+  dp.dks = dk_summary; dp.fine = (uint32_t*)(ws + L.fine); dp.bmask = (uint32_t*)(ws + L.bmask); dp.W = L.W;
   dp.gs = (float)((double)o.gamma * (double)o.scale);
   hipError_t e = launch_dash_bwd_setup(dp, s);
   if (e != hipSuccess) return hip_fail(e, "DashAttention block mask and prior");
@@ -710,7 +711,7 @@ entmax_status entmax_dash_bwd(const entmax_dash_desc* desc, const void* q, const
   p.mask = dp.bmask; p.maskT = (const uint32_t*)(ws + B.maskT);
   p.dq = nullptr; p.dk = dk; p.dv = dv;
   p.b = o.b; p.hq = o.hq; p.hkv = o.hkv; p.n = o.n; p.G = o.G;
-  p.causal = 1; p.Br = 64; p.Bc = 64;
+  p.causal = 1; p.Br = a.Br; p.Bc = a.Bc;
   p.cx = o.scale; p.scale = o.scale; p.kappa = 1.0f; p.am1 = 0.0f; p.slopes = nullptr;
   p.Tr = a.Tr; p.Tc = a.Tc; p.W = a.W; p.WT = a.WT;
   p.dense = 0;

@@ -212,18 +212,28 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void k_bwd_dkv(BwdParams p)
     f32x16 dS;
 #pragma unroll
     for (int r = 0; r < 16; ++r) dS[r] = G[r] * (dP[r] - dl[r >> 2][r & 3]);
-    Frag<T> qt[2][DC], dt[2][DC];        // Q^T and dO^T of the chunk (cols layout)
-    rows_to_cols<T, DS>(qt, qa, eye);
-    rows_to_cols<T, DS>(dt, da, eye);
+    Frag<T> pf[2], sf[2];
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
-      Frag<T> pf, sf;
-      acc_frag(pf, P, m);
-      acc_frag(sf, dS, m);
+      acc_frag(pf[m], P, m);
+      acc_frag(sf[m], dS, m);
+    }
+    // Q^T and dO^T of the chunk (cols layout), one 32-wide block of the head dimension at a
+    // time, each used as soon as it is formed (fewer live registers at head_dim 128)
 #pragma unroll
-      for (int dc = 0; dc < DC; ++dc) {
-        mma16(dv[dc], dt[m][dc], pf);   // dV^T[d][key] += dO^T P
-        mma16(dk[dc], qt[m][dc], sf);   // dK^T[d][key] += Q^T dS
+    for (int dc = 0; dc < DC; ++dc) {
+      f32x16 tq = f32x16{}, td = f32x16{};
+      mma16(tq, qa[2 * dc], eye[0]);
+      mma16(td, da[2 * dc], eye[0]);
+      mma16(tq, qa[2 * dc + 1], eye[1]);
+      mma16(td, da[2 * dc + 1], eye[1]);
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        Frag<T> qt, dt;
+        acc_frag(qt, tq, m);
+        acc_frag(dt, td, m);
+        mma16(dv[dc], dt, pf[m]);   // dV^T[d][key] += dO^T P
+        mma16(dk[dc], qt, sf[m]);   // dK^T[d][key] += Q^T dS
       }
     }
   }

@@ -287,11 +287,12 @@ __global__ __launch_bounds__((64 * DASH_WAVES), (dash_attn_occ<T>())) void k_das
 // routing to the chunk summaries). Stage 2 is softmax attention over the 64 x 64 blocks that
 // the routing and the diagonal branch select, with the prior sigma ln wbar as a per-(row,
 // chunk) additive term; its backward runs in the attention backward kernels (bwd.hip, mode
-// 3), which also leave, per row and 32-key sub-block, the sum of dS: the gradient of the
+// 3, on 32-row query blocks: rows of a block route different chunks, and the union over 32
+// rows is the forward's visiting granularity too), which also leave, per row and 32-key sub-block, the sum of dS: the gradient of the
 // prior terms. Here:
-//   k_dash_bwd_setup -- the stage-2 block mask of each query head from the group's chunk
-//     mask (a key block is set when its chunk is routed by the query tile, or it lies in the
-//     tile's own chunk at or before the tile), and the prior table sigma ln wbar;
+//   k_dash_bwd_fine, k_dash_bwd_setup -- the stage-2 block mask of each query head at 32 x 64
+//     (a key block is set when its chunk is routed by some row of the 32-row block, or it
+//     lies in the block's own chunk at or before the block), and the prior table sigma ln wbar;
 //   k_dash_dw -- dwbar(c, i) = sigma / wbar(c, i) * (the group's dS sums over chunk c), and
 //     each head's routing weights take dwbar / G (stored as dw);
 //   k_dash_route_bwd -- per (batch, KV head, 64-row tile), a wave per 32 rows as in the
@@ -304,26 +305,57 @@ __global__ __launch_bounds__((64 * DASH_WAVES), (dash_attn_occ<T>())) void k_das
 //     fragment-major column copy, du^T as the B operand), one partial per (32-chunk block,
 //     piece of rows); k_dash_dks_reduce adds the pieces in order.
 
+// The chunk bits of each 32-row block: a half-wave per word, lane l of the half reads the
+// block's 32 weights of chunk 32 wi + l (one 128-byte line) and the ballot packs the bits.
+__global__ void k_dash_bwd_fine(DashParams p) {
+  const size_t id = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int R = p.n / 32;
+  const size_t words = (size_t)p.b * p.hkv * R * p.Wc;
+  const bool in = id < words * 32;
+  const int l = (int)(id & 31);
+  const size_t word = id >> 5;
+  bool on = false;
+  if (in) {
+    const int wi = (int)(word % p.Wc);
+    const int rb = (int)((word / p.Wc) % R);
+    const size_t unit = word / ((size_t)p.Wc * R);
+    const int ch = 32 * wi + l;
+    if (ch < p.nc) {
+      const f32x4* wr = reinterpret_cast<const f32x4*>(p.rw + (unit * p.nc + ch) * p.n + 32 * rb);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const f32x4 v = wr[j];
+        on |= (v[0] > 0.f) | (v[1] > 0.f) | (v[2] > 0.f) | (v[3] > 0.f);
+      }
+    }
+  }
+  const unsigned long long bal = __ballot(on);
+  if (in && l == 0) p.fine[word] = (uint32_t)(bal >> (threadIdx.x & 32));
+}
+
+// The stage-2 block mask at 32 x 64 (a key block is set when some row of the 32-row block
+// routes its chunk, or it lies in the block's own chunk at or before the block) and the
+// prior table sigma ln wbar.
 __global__ void k_dash_bwd_setup(DashParams p) {
-  const int Tb = p.n / 64;
-  const size_t words = (size_t)p.b * p.hq * Tb * p.W;
+  const int Tb = p.n / 64, R = p.n / 32;
+  const size_t words = (size_t)p.b * p.hq * R * p.W;
   const size_t id = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (id < words) {
     const int wi = (int)(id % p.W);
-    const int I = (int)((id / p.W) % Tb);
-    const size_t bh = id / ((size_t)p.W * Tb);
+    const int I = (int)((id / p.W) % R);
+    const size_t bh = id / ((size_t)p.W * R);
     const int bi = (int)(bh / p.hq), head = (int)(bh % p.hq);
     const int unit = bi * p.hkv + head / p.G;
-    const int m = (I * 64) / p.C;                 // the tile's own chunk (every row shares it)
-    const uint32_t* cw = p.cmask + ((size_t)unit * p.Tr + I) * p.Wc;
+    const int m = (I * 32) / p.C;                 // the block's own chunk (every row shares it)
+    const uint32_t* fw = p.fine + ((size_t)unit * R + I) * p.Wc;
     uint32_t word = 0;
     for (int b = 0; b < 32; ++b) {
       const int J = wi * 32 + b;
       if (J >= Tb) break;
       const int cJ = (J * 64) / p.C;
       bool on;
-      if (cJ < m) on = (cw[cJ >> 5] >> (cJ & 31)) & 1u;
-      else on = cJ == m && J <= I;
+      if (cJ < m) on = (fw[cJ >> 5] >> (cJ & 31)) & 1u;
+      else on = cJ == m && J * 64 <= I * 32 + 31;
       word |= (on ? 1u : 0u) << b;
     }
     p.bmask[id] = word;
@@ -584,12 +616,16 @@ __global__ void k_dash_dks_reduce(DashParams p) {
 }
 
 hipError_t launch_dash_bwd_setup(const DashParams& p, hipStream_t s) {
-  const size_t items = (size_t)p.b * p.hq * (p.n / 64) * p.W + (size_t)p.b * p.hkv * p.nc * p.n;
+  const size_t lanes = (size_t)p.b * p.hkv * (p.n / 32) * p.Wc * 32;
+  const size_t items = (size_t)p.b * p.hq * (p.n / 32) * p.W + (size_t)p.b * p.hkv * p.nc * p.n;
   if (items == 0) return hipSuccess;
   prof_begin("dash_bwd_setup", s);
-  hipLaunchKernelGGL(k_dash_bwd_setup, dim3((unsigned)((items + 255) / 256)), dim3(256), 0, s, p);
+  hipLaunchKernelGGL(k_dash_bwd_fine, dim3((unsigned)((lanes + 255) / 256)), dim3(256), 0, s, p);
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess)
+    hipLaunchKernelGGL(k_dash_bwd_setup, dim3((unsigned)((items + 255) / 256)), dim3(256), 0, s, p);
   prof_end(s);
-  return hipGetLastError();
+  return e != hipSuccess ? e : hipGetLastError();
 }
 
 template <typename T, int D>

@@ -195,7 +195,8 @@ struct DashParams {
   const void* qc;        // Q, fragment-major columns
   float* dpart;          // [b * hkv, Wc, NP, D, 32] partial summary gradients (per row piece)
   void* dks;             // [b, hkv, nc, D] summary gradient out (dtype)
-  uint32_t* bmask;       // [b, hq, n / 64, W] 64 x 64 block mask of stage 2
+  uint32_t* fine;        // [b, hkv, n / 32, Wc] chunk bits of each 32-row block (some row routes it)
+  uint32_t* bmask;       // [b, hq, n / 32, W] 32 x 64 block mask of stage 2
   int W;                 // words per block-mask row
   int NP, PR;            // row pieces of the summary-gradient product and rows per piece
   float gs;              // gamma * scale: d zbar / d (q . ksum)

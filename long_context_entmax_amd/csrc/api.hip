@@ -619,7 +619,7 @@ constexpr int DASH_DKS_ROWS = 256;
 
 struct DashBwdLayout {
   BwdLayout att;        // the attention backward's part (at offset 0)
-  size_t fine, bmask, lp, dw, qc, dq32, dbias, du, dpart, total;
+  size_t fine, bmask, lp, lse2, dw, qc, dq32, dbias, du, dpart, total;
   int W, NP;
 };
 static DashBwdLayout dash_bwd_ws(const DashDerived& o, const Derived& a) {
@@ -633,6 +633,7 @@ static DashBwdLayout dash_bwd_ws(const DashDerived& o, const Derived& a) {
   L.fine = off; off += align256(units * (o.n / 32) * o.Wc * 4);
   L.bmask = off; off += align256(rows * (o.n / 32) * L.W * 4);
   L.lp = off; off += align256(units * o.nc * o.n * 4);
+  L.lse2 = off; off += align256(rows * o.n * 4);
   L.dw = off; off += align256(units * o.nc * o.n * 4);
   L.qc = off; off += align256(rows * o.n * o.D * o.es);
   L.dq32 = off; off += align256(rows * o.n * o.D * 4);
@@ -684,6 +685,7 @@ entmax_status entmax_dash_bwd(const entmax_dash_desc* desc, const void* q, const
   dp.alpha = o.alpha; dp.kappa = o.kappa; dp.tol = o.tol; dp.sigma = o.sigma;
   dp.dbias = (const float*)(ws + L.dbias); dp.dq32 = (const float*)(ws + L.dq32); dp.dq = dq;
   dp.lp = (float*)(ws + L.lp); dp.dw = (float*)(ws + L.dw); dp.du = (float*)(ws + L.du);
+  dp.lse_in = lse; dp.lse2 = (float*)(ws + L.lse2);
   dp.qc = ws + L.qc; dp.dpart = (float*)(ws + L.dpart); dp.NP = L.NP; dp.PR = DASH_DKS_ROWS;
   dp.dks = dk_summary; dp.fine = (uint32_t*)(ws + L.fine); dp.bmask = (uint32_t*)(ws + L.bmask); dp.W = L.W;
   dp.gs = (float)((double)o.gamma * (double)o.scale);
@@ -707,12 +709,13 @@ entmax_status entmax_dash_bwd(const entmax_dash_desc* desc, const void* q, const
   if (e != hipSuccess) return hip_fail(e, "DashAttention backward preparation");
   BwdParams p{};
   p.qr = ws + B.qr; p.dor = ws + B.dor; p.kr = ws + B.kr; p.vr = ws + B.vr;
-  p.tau = lse; p.delta = (const float*)(ws + B.delta);
+  p.tau = dp.lse2; p.delta = (const float*)(ws + B.delta);
   p.mask = dp.bmask; p.maskT = (const uint32_t*)(ws + B.maskT);
   p.dq = nullptr; p.dk = dk; p.dv = dv;
   p.b = o.b; p.hq = o.hq; p.hkv = o.hkv; p.n = o.n; p.G = o.G;
   p.causal = 1; p.Br = a.Br; p.Bc = a.Bc;
-  p.cx = o.scale; p.scale = o.scale; p.kappa = 1.0f; p.am1 = 0.0f; p.slopes = nullptr;
+  p.cx = (float)((double)o.scale * 1.4426950408889634); p.scale = o.scale; p.kappa = 1.0f; p.am1 = 0.0f;
+  p.slopes = nullptr;
   p.Tr = a.Tr; p.Tc = a.Tc; p.W = a.W; p.WT = a.WT;
   p.dense = 0;
   p.lp = dp.lp; p.C = o.C;

@@ -165,9 +165,12 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void k_bwd_dkv(BwdParams p)
     f32x16 P, G;
     float mx = 0.f;
     if constexpr (MODE == MODE_DASH) {
-      // softmax with the routing prior: P = exp(scale s - lse + sigma ln wbar) on a routed
-      // chunk, exp(scale s - lse) on the query's own chunk (keys after the query masked);
-      // dS = P (dP - delta) is the softmax backward, so G = P
+      // softmax with the routing prior, in base-2 units (cx = scale log2 e, tau = lse log2 e,
+      // lp = sigma log2 wbar): P = 2^(cx s - tau + lp) on a routed chunk, 2^(cx s - tau) on
+      // the query's own chunk (keys after the query masked); dS = P (dP - delta) is the
+      // softmax backward, so G = P
+      // (the walk visits a sub-tile only when some row of its 32 routes the chunk, or on the
+      // diagonal, so no sub-tile is all zero and none is skipped)
       const int cJ = key0 / p.C;
       if (q0 / p.C != cJ) {
         const float* lr = p.lp + ((size_t)(bi * p.hkv + kvh) * (n / p.C) + cJ) * n + q0;
@@ -175,17 +178,17 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void k_bwd_dkv(BwdParams p)
         for (int g4 = 0; g4 < 4; ++g4) {
           const f32x4 lv = *reinterpret_cast<const f32x4*>(lr + 8 * g4 + 4 * h);
 #pragma unroll
-          for (int j = 0; j < 4; ++j) off[4 * g4 + j] += lv[j];
+          for (int j = 0; j < 4; ++j) P[4 * g4 + j] = exp2_fast(fmaf(cx, S[4 * g4 + j], lv[j] - tv[g4][j]));
         }
-      }
+      } else if (diag) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float tt = fmaf(cx, S[r], off[r]);
-        if (diag && key0 + c > q0 + acc_row(r, h)) tt = -INFINITY;
-        P[r] = exp2f(tt * 1.44269504088896341f);
-        G[r] = P[r];
-        mx = fmaxf(mx, P[r]);
+        for (int r = 0; r < 16; ++r)
+          P[r] = exp2_fast(key0 + c > q0 + acc_row(r, h) ? -INFINITY : fmaf(cx, S[r], -tv[r >> 2][r & 3]));
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) P[r] = exp2_fast(fmaf(cx, S[r], -tv[r >> 2][r & 3]));
       }
+      G = P;
     } else if (diag) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -205,7 +208,7 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void k_bwd_dkv(BwdParams p)
         mx = fmaxf(mx, dm);
       }
     }
-    if (!p.dense && ballot(mx > 0.f) == 0) continue;   // an all-zero sub-tile
+    if (MODE != MODE_DASH && !p.dense && ballot(mx > 0.f) == 0) continue;   // an all-zero sub-tile
     f32x16 dP = f32x16{};
 #pragma unroll
     for (int s = 0; s < DS; ++s) mma16(dP, da[s], vb[s]);  // dP[q][key]
@@ -385,16 +388,17 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void k_bwd_dq(BwdParams p) 
     f32x16 G;
     float mx = 0.f;
     if constexpr (MODE == MODE_DASH) {
-      // softmax with the routing prior (see k_bwd_dkv); G = P
+      // softmax with the routing prior in base-2 units (see k_bwd_dkv); G = P
       const int cJ = key0 / p.C;
-      float pr = 0.f;
-      if (q0 / p.C != cJ) pr = p.lp[((size_t)(bi * p.hkv + kvh) * (n / p.C) + cJ) * n + q0 + c];
+      float pr = -tq;
+      if (q0 / p.C != cJ) pr += p.lp[((size_t)(bi * p.hkv + kvh) * (n / p.C) + cJ) * n + q0 + c];
+      if (diag) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float tt = fmaf(cx, S[r], off[r] + pr);
-        if (diag && key0 + acc_row(r, h) > q0 + c) tt = -INFINITY;
-        G[r] = exp2f(tt * 1.44269504088896341f);
-        mx = fmaxf(mx, G[r]);
+        for (int r = 0; r < 16; ++r)
+          G[r] = exp2_fast(key0 + acc_row(r, h) > q0 + c ? -INFINITY : fmaf(cx, S[r], pr));
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) G[r] = exp2_fast(fmaf(cx, S[r], pr));
       }
     } else if (diag) {
 #pragma unroll
@@ -416,11 +420,7 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void k_bwd_dq(BwdParams p) 
     // (mode 3: the row's sum of dS over the sub-block, the gradient of its prior term)
     float* const dbr = MODE == MODE_DASH ? p.dbias + ((size_t)(bi * p.hq + head) * (n >> 5) + kbk) * n + q0 + c
                                          : nullptr;
-    if (!p.dense && ballot(mx > 0.f) == 0) {   // an all-zero sub-tile
-      if constexpr (MODE == MODE_DASH)
-        if (h == 0) *dbr = 0.f;
-      continue;
-    }
+    if (MODE != MODE_DASH && !p.dense && ballot(mx > 0.f) == 0) continue;   // an all-zero sub-tile
     f32x16 dP = f32x16{};
 #pragma unroll
     for (int s = 0; s < DS; ++s) mma16(dP, va[s], db[s]);   // dP^T[key][q]

@@ -281,6 +281,11 @@ __device__ __forceinline__ void write_lane(float& v, float x, int lane) {
   asm volatile("s_mov_b32 m0, %2\n s_nop 1\n v_writelane_b32 %0, %1, m0" : "+v"(v) : "s"(x), "s"(lane) : "m0");
 }
 
+// 2^x with the hardware exponential alone (no rescaling around denormal results): softmax
+// weights are exponentials of scores at or below the row's maximum, and one below 2^-126 of
+// it is 0 to working precision. -inf gives 0.
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // ------------------------------------------------------------------------------------------
 // the alpha-entmax weight: p = d^kappa, g = d^(kappa - 1) for d = x - tau > 0
 // MODE 1: kappa = 1 (alpha = 2); MODE 2: kappa = 2 (alpha = 1.5); MODE 0: any kappa.

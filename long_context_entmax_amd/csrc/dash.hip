@@ -246,7 +246,7 @@ __global__ __launch_bounds__((64 * DASH_WAVES), (dash_attn_occ<T>())) void k_das
     tm = fmaxf(tm, xor32f(tm));
     const float mnew = fmaxf(mrun, tm);
     if (mnew > mrun) {
-      const float sc = exp2f(mrun - mnew);
+      const float sc = exp2_fast(mrun - mnew);
       l *= sc;
 #pragma unroll
       for (int dc = 0; dc < DC; ++dc) oacc[dc] *= sc;
@@ -256,7 +256,7 @@ __global__ __launch_bounds__((64 * DASH_WAVES), (dash_attn_occ<T>())) void k_das
     f32x16 pw;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      pw[r] = exp2f(s[r] - msub);
+      pw[r] = exp2_fast(s[r] - msub);
       l += pw[r];
     }
 #pragma unroll
@@ -292,7 +292,8 @@ __global__ __launch_bounds__((64 * DASH_WAVES), (dash_attn_occ<T>())) void k_das
 // prior terms. Here:
 //   k_dash_bwd_fine, k_dash_bwd_setup -- the stage-2 block mask of each query head at 32 x 64
 //     (a key block is set when its chunk is routed by some row of the 32-row block, or it
-//     lies in the block's own chunk at or before the block), and the prior table sigma ln wbar;
+//     lies in the block's own chunk at or before the block), the prior table sigma log2 wbar
+//     and the rows' lse in base-2 units;
 //   k_dash_dw -- dwbar(c, i) = sigma / wbar(c, i) * (the group's dS sums over chunk c), and
 //     each head's routing weights take dwbar / G (stored as dw);
 //   k_dash_route_bwd -- per (batch, KV head, 64-row tile), a wave per 32 rows as in the
@@ -334,8 +335,8 @@ __global__ void k_dash_bwd_fine(DashParams p) {
 }
 
 // The stage-2 block mask at 32 x 64 (a key block is set when some row of the 32-row block
-// routes its chunk, or it lies in the block's own chunk at or before the block) and the
-// prior table sigma ln wbar.
+// routes its chunk, or it lies in the block's own chunk at or before the block), the prior
+// table sigma log2 wbar and the rows' lse in base-2 units.
 __global__ void k_dash_bwd_setup(DashParams p) {
   const int Tb = p.n / 64, R = p.n / 32;
   const size_t words = (size_t)p.b * p.hq * R * p.W;
@@ -361,10 +362,15 @@ __global__ void k_dash_bwd_setup(DashParams p) {
     p.bmask[id] = word;
     return;
   }
+  const size_t cells = (size_t)p.b * p.hkv * p.nc * p.n;
   const size_t e = id - words;
-  if (e >= (size_t)p.b * p.hkv * p.nc * p.n) return;
-  const float wv = p.rw[e];
-  p.lp[e] = wv > 0.f ? p.sigma * logf(wv) : -INFINITY;
+  if (e < cells) {
+    const float wv = p.rw[e];
+    p.lp[e] = wv > 0.f ? p.sigma * log2f(wv) : -INFINITY;
+    return;
+  }
+  const size_t r = e - cells;
+  if (r < (size_t)p.b * p.hq * p.n) p.lse2[r] = p.lse_in[r] * 1.44269504088896341f;
 }
 
 // dw(c, i) of a (unit, chunk, row): sigma / (G wbar) times the dS sums of the group's heads
@@ -617,7 +623,8 @@ __global__ void k_dash_dks_reduce(DashParams p) {
 
 hipError_t launch_dash_bwd_setup(const DashParams& p, hipStream_t s) {
   const size_t lanes = (size_t)p.b * p.hkv * (p.n / 32) * p.Wc * 32;
-  const size_t items = (size_t)p.b * p.hq * (p.n / 32) * p.W + (size_t)p.b * p.hkv * p.nc * p.n;
+  const size_t items = (size_t)p.b * p.hq * (p.n / 32) * p.W + (size_t)p.b * p.hkv * p.nc * p.n +
+                       (size_t)p.b * p.hq * p.n;
   if (items == 0) return hipSuccess;
   prof_begin("dash_bwd_setup", s);
   hipLaunchKernelGGL(k_dash_bwd_fine, dim3((unsigned)((lanes + 255) / 256)), dim3(256), 0, s, p);

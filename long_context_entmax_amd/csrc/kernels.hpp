@@ -133,9 +133,10 @@ struct BwdParams {
   const float* slopes;   // optional [hq] position-bias slopes
   int Tr, Tc, W, WT;
   int dense;             // 1: every item of the mask multiplied in full (no zero-block skip)
-  // mode 3, the DashAttention stage-2 backward (softmax with the routing prior): tau holds
-  // the row's lse, cx the score scale; key j of a routed chunk c adds sigma ln wbar(c, i)
-  const float* lp;       // [b, hkv, nc, n] the prior sigma ln wbar (-inf where wbar = 0), chunk-major
+  // mode 3, the DashAttention stage-2 backward (softmax with the routing prior), in base-2
+  // units: tau holds the row's lse log2 e, cx the score scale times log2 e; key j of a routed
+  // chunk c adds sigma log2 wbar(c, i)
+  const float* lp;       // [b, hkv, nc, n] the prior sigma log2 wbar (-inf where wbar = 0), chunk-major
   int C;                 // keys per chunk
   float* dq32;           // [b, hq, n, D] fp32 dQ (mode 3 writes here instead of dq)
   float* dbias;          // [b, hq, n / 32, n] per (32-key sub-block, row) sums of dS (mode 3)
@@ -189,7 +190,9 @@ struct DashParams {
   const float* dbias;    // [b, hq, n / 32, n] per (32-key sub-block, row) sums of the stage-2 dS
   const float* dq32;     // [b, hq, n, D] stage-2 dQ (fp32)
   void* dq;              // [b, hq, n, D] dQ out (dtype)
-  float* lp;             // [b, hkv, nc, n] the prior sigma ln wbar, -inf where wbar = 0
+  float* lp;             // [b, hkv, nc, n] the prior sigma log2 wbar, -inf where wbar = 0
+  const float* lse_in;   // [b, hq, n] stage-2 lse (natural log) of the forward
+  float* lse2;           // [b, hq, n] the same times log2 e
   float* dw;             // [b, hkv, nc, n] gradient of each head's routing weights (chunk-major)
   float* du;             // [b, hq, nc, n] routing-logit gradient (chunk-major)
   const void* qc;        // Q, fragment-major columns

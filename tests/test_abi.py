@@ -226,7 +226,7 @@ def test_dash_bwd_pointers_workspace_and_sizes(L):
     # block mask, the prior table and the weight gradient, fp32 dQ, the per-(sub-block, row)
     # dS sums, the routing-logit gradient and the per-piece summary-gradient partials
     low = (b * hq * n * 4 + 3 * b * hq * n * D * 2 + 2 * b * hkv * n * D * 2 + b * hq * (n // 32) * 4
-           + 2 * b * hkv * nc * n * 4 + b * hq * n * D * 4 + b * hq * (n // 32) * n * 4 + b * hq * nc * n * 4
+           + 2 * b * hkv * nc * n * 4 + b * hq * n * 4 + b * hq * n * D * 4 + b * hq * (n // 32) * n * 4 + b * hq * nc * n * 4
            + b * hkv * 1 * (n // 256) * D * 32 * 4)
     assert low <= need <= low + 64 * 1024
     args = [f] * 14

@@ -112,14 +112,16 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void k_bwd_dkv(BwdParams p)
   // (head_dim 128, one wave per SIMD: the dO rows too)
   constexpr bool DEEP = D == 128;
   Frag<T> qn[DS], dn[DEEP ? DS : 1];
+  // a head's Q and dO rows through buffer resources (a fixed lane offset, a scalar row
+  // offset: no vector address arithmetic per fragment)
+  using Ops = KvOps<T, D>;
+  const uint32_t head_bytes = (uint32_t)((size_t)n * D * sizeof(T));
   auto load_rows = [&](int gi, int q0i) {
     const T* Qr = reinterpret_cast<const T*>(p.qr) + row_base(gi) * D;
-#pragma unroll
-    for (int s = 0; s < DS; ++s) load_frag(qn[s], Qr + rows_off(q0i >> 5, s, DS, lane));
+    Ops::load_k_buf(qn, buffer_rsrc(Qr, head_bytes), q0i >> 5, lane);
     if constexpr (DEEP) {
       const T* DOn = reinterpret_cast<const T*>(p.dor) + row_base(gi) * D;
-#pragma unroll
-      for (int s = 0; s < DS; ++s) load_frag(dn[s], DOn + rows_off(q0i >> 5, s, DS, lane));
+      Ops::load_k_buf(dn, buffer_rsrc(DOn, head_bytes), q0i >> 5, lane);
     }
   };
   if (have) load_rows(g_next, q0_next);
@@ -136,8 +138,8 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void k_bwd_dkv(BwdParams p)
     for (int s = 0; s < DS; ++s) {
       qa[s] = qn[s];
       if constexpr (DEEP) da[s] = dn[s];
-      else load_frag(da[s], DOr + rows_off(qb, s, DS, lane));
     }
+    if constexpr (!DEEP) Ops::load_k_buf(da, buffer_rsrc(DOr, head_bytes), qb, lane);
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
       tv[g4] = *reinterpret_cast<const f32x4*>(p.tau + qrow0 + q0 + 8 * g4 + 4 * h);
@@ -351,28 +353,24 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void k_bwd_dq(BwdParams p) 
   };
   int kb_next = 0;
   bool have = next_item(kb_next);
+  // K and V fragments through buffer resources over the KV head's copies: a fixed lane
+  // offset and a scalar sub-block offset, so a load needs no vector address arithmetic
+  using Ops = KvOps<T, D>;
+  const __amdgpu_buffer_rsrc_t krs = buffer_rsrc(Kr, (uint32_t)((size_t)n * D * sizeof(T)));
+  const __amdgpu_buffer_rsrc_t vrs = buffer_rsrc(Vr, (uint32_t)((size_t)n * D * sizeof(T)));
   Frag<T> kn[DS];
-  if (have) {
-#pragma unroll
-    for (int s = 0; s < DS; ++s) load_frag(kn[s], Kr + rows_off(kb_next, s, DS, lane));
-  }
+  if (have) Ops::load_k_buf(kn, krs, kb_next, lane);
   while (have) {
     const int kbk = kb_next;
     const int key0 = kbk * 32;
     Frag<T> ka[DS], va[DS];
 #pragma unroll
-    for (int s = 0; s < DS; ++s) {
-      ka[s] = kn[s];
-      load_frag(va[s], Vr + rows_off(kbk, s, DS, lane));
-    }
+    for (int s = 0; s < DS; ++s) ka[s] = kn[s];
+    Ops::load_k_buf(va, vrs, kbk, lane);
     // loaded on every item (the current sub-block again after the last), so the waits
     // before the current item's operands do not drain the prefetch
     have = next_item(kb_next);
-    {
-      const int kbl = have ? kb_next : kbk;
-#pragma unroll
-      for (int s = 0; s < DS; ++s) load_frag(kn[s], Kr + rows_off(kbl, s, DS, lane));
-    }
+    Ops::load_k_buf(kn, krs, have ? kb_next : kbk, lane);
     f32x16 S = f32x16{};
 #pragma unroll
     for (int s = 0; s < DS; ++s) mma16(S, ka[s], qb[s]);   // S^T[key][q]

@@ -15,6 +15,7 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 import oracle.dash as odash
 import synth
 import long_context_entmax_amd as lce
@@ -232,3 +233,37 @@ def test_dash_bwd_fullsize_sampled_rows():
     assert rel_fro(dv_sum, do64) < 2e-2
     dk_sum = g["dk"].sum(axis=2)
     assert np.linalg.norm(dk_sum) < 2e-2 * np.linalg.norm(g["dk"])
+
+
+def test_dash_bwd_alpha3_conditioned_rows():
+    """Routing alpha 3 (the general-alpha weight, kappa = 1/2). There g = (x - tau)^(kappa - 1)
+    is singular at the support boundary, so du of a chunk whose logit lies just above tau
+    moves by a large factor for a tau change at rounding level: such rows carry no usable
+    reference. dO is zeroed on every row where some head of the group routes a chunk within
+    1e-2 of its tau (by the oracle's own tau), on both sides; those rows then contribute
+    nothing, and every gradient must still match to the bf16 bar."""
+    case = (1, 4, 2, 1024, 64, "bf16", 64, 3.0, 8.0, 1.0)
+    b, hq, hkv, n, d, dt, C, alpha, gamma, sigma = case
+    print(f"[case] dash bwd alpha 3 {case}", flush=True)
+    q, k, v, ks, do = _inputs_bwd(b, hq, hkv, n, d, dt, C, zlib.crc32(str(case).encode()) & 0xFFFF)
+    q64, ks64 = to64(q), to64(ks)
+    G = hq // hkv
+    scale = 1.0 / np.sqrt(d)
+    bad = np.zeros((b, hkv, n), dtype=bool)
+    for bi in range(b):
+        for hh in range(hq):
+            g = hh // G
+            for i in range(C, n):
+                m = i // C
+                z = gamma * scale * (ks64[bi, g, :m] @ q64[bi, hh, i])
+                x = (alpha - 1.0) * z
+                gap = x - oracle.entmax_tau(x, alpha)
+                if np.any((gap > 0.0) & (gap < 1e-2)):
+                    bad[bi, g, i] = True
+    print(f"  rows zeroed: {bad.mean():.3f}", flush=True)
+    assert bad.mean() < 0.5
+    keep = torch.from_numpy(~np.repeat(bad, G, axis=1)).to(do.dtype)[..., None]
+    do = (do * keep).contiguous()
+    ref = odash.dash_bwd(q64, to64(k), to64(v), ks64, to64(do), alpha, gamma, sigma, C)
+    g = _run_bwd(q, k, v, ks, do, C, alpha, gamma, sigma)
+    _check_bwd(g, ref, 2e-2)

@@ -438,7 +438,6 @@ def dash_fwd(q, k, v, k_summary, chunk: int = 64, route_alpha: float = 1.5, gamm
     route_tau [b, hq, n], route_w [b, hkv, n / chunk, n] (chunk-major group weights) and
     chunk_mask [b, hkv, n / 64, ceil(n_chunks / 32)] (int32 view of the uint32 words)."""
     torch = _torch()
-    _require_gpu(q, k, v, k_summary)
     if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape or k_summary.dim() != 4:
         raise ValueError("q [b, hq, n, d], k and v [b, hkv, n, d], k_summary [b, hkv, n_chunks, d]")
     b, hq, n, d = q.shape
@@ -447,6 +446,7 @@ def dash_fwd(q, k, v, k_summary, chunk: int = 64, route_alpha: float = 1.5, gamm
         raise ValueError("q, k, v and k_summary disagree in batch, heads, length, head_dim or dtype")
     if chunk <= 0 or n % chunk or k_summary.shape[2] != n // chunk:
         raise ValueError(f"k_summary needs seqlen / chunk = {n // max(chunk, 1)} rows")
+    _require_gpu(q, k, v, k_summary)
     dt = ENTMAX_BF16 if q.dtype == torch.bfloat16 else ENTMAX_F32
     desc = make_dash_desc(b, hq, k.shape[1], n, d, dt, chunk, route_alpha, gamma, sigma, scale, max_iters, tol)
     L = lib()
@@ -476,7 +476,8 @@ def dash_bwd(q, k, v, k_summary, do, o, lse, route_tau, route_w, chunk_mask, chu
     The gradient reaches q and k_summary through the routing (the alpha-entmax Jacobian) as
     well as through the prior term sigma * ln(routing weight) of stage 2."""
     torch = _torch()
-    _require_gpu(q, k, v, k_summary, do, o, lse, route_tau, route_w, chunk_mask)
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q [b, hq, n, d] and k [b, hkv, n, d]")
     b, hq, n, d = q.shape
     hkv = k.shape[1]
     if chunk <= 0 or n % chunk:
@@ -491,6 +492,7 @@ def dash_bwd(q, k, v, k_summary, do, o, lse, route_tau, route_w, chunk_mask, chu
     _expect("route_tau", route_tau, (b, hq, n), torch.float32, q.device)
     _expect("route_w", route_w, (b, hkv, nc, n), torch.float32, q.device)
     _expect("chunk_mask", chunk_mask, (b, hkv, n // 64, (nc + 31) // 32), torch.int32, q.device)
+    _require_gpu(q, k, v, k_summary, do, o, lse, route_tau, route_w, chunk_mask)
     dt = ENTMAX_BF16 if q.dtype == torch.bfloat16 else ENTMAX_F32
     desc = make_dash_desc(b, hq, hkv, n, d, dt, chunk, route_alpha, gamma, sigma, scale, max_iters, tol)
     L = lib()

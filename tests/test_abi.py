@@ -390,3 +390,45 @@ def test_noalloc_decode_rejects_problems_beyond_the_scratch(L):
     assert L.entmax_attn_decode_workspace_bytes(ctypes.byref(c5)) <= lce.DECODE_SCRATCH_BYTES
     bad = lce.make_desc(1, 32, 8, 131072, 64, lce.ENTMAX_BF16, 0.5, True, (32, 32), 16)
     assert L.entmax_attn_decode_noalloc(ctypes.byref(bad), 16, 16, 16, None, None, 16, 16, None, None, None) == 3
+
+
+def _dash_cpu_args():
+    import torch
+    b, hq, hkv, n, d, C = 1, 4, 2, 256, 64, 64
+    bf = torch.bfloat16
+    return dict(q=torch.zeros(b, hq, n, d, dtype=bf), k=torch.zeros(b, hkv, n, d, dtype=bf),
+                v=torch.zeros(b, hkv, n, d, dtype=bf), k_summary=torch.zeros(b, hkv, n // C, d, dtype=bf),
+                do=torch.zeros(b, hq, n, d, dtype=bf), o=torch.zeros(b, hq, n, d), lse=torch.zeros(b, hq, n),
+                route_tau=torch.zeros(b, hq, n), route_w=torch.zeros(b, hkv, n // C, n),
+                chunk_mask=torch.zeros(b, hkv, n // 64, 1, dtype=torch.int32))
+
+
+@pytest.mark.parametrize("name,bad,match", [
+    ("k", lambda a: a["k"][:, :, :128].contiguous(), "k must have shape"),
+    ("k_summary", lambda a: a["k_summary"][:, :, :2].contiguous(), "k_summary must have shape"),
+    ("do", lambda a: a["do"].float(), "do must be"),
+    ("o", lambda a: a["o"].bfloat16(), "o must be"),
+    ("lse", lambda a: a["lse"][:, :2].contiguous(), "lse must have shape"),
+    ("route_tau", lambda a: a["route_tau"].double(), "route_tau must be"),
+    ("route_w", lambda a: a["route_w"].transpose(2, 3).contiguous(), "route_w must have shape"),
+    ("chunk_mask", lambda a: a["chunk_mask"].long(), "chunk_mask must be"),
+])
+def test_dash_binding_checks_backward_tensors(name, bad, match):
+    """The DashAttention backward binding checks every tensor's shape and dtype before the
+    device check and before any pointer is taken."""
+    a = _dash_cpu_args()
+    a[name] = bad(a)
+    with pytest.raises(ValueError, match=match):
+        lce.dash_bwd(a["q"], a["k"], a["v"], a["k_summary"], a["do"], a["o"], a["lse"], a["route_tau"],
+                     a["route_w"], a["chunk_mask"], chunk=64)
+
+
+def test_dash_binding_consistent_cpu_tensors_stop_at_the_device_check():
+    a = _dash_cpu_args()
+    with pytest.raises(ValueError, match="GPU only"):
+        lce.dash_bwd(a["q"], a["k"], a["v"], a["k_summary"], a["do"], a["o"], a["lse"], a["route_tau"],
+                     a["route_w"], a["chunk_mask"], chunk=64)
+    with pytest.raises(ValueError, match="GPU only"):
+        lce.dash_fwd(a["q"], a["k"], a["v"], a["k_summary"], chunk=64)
+    with pytest.raises(ValueError, match="seqlen / chunk"):
+        lce.dash_fwd(a["q"], a["k"], a["v"], a["k_summary"][:, :, :2].contiguous(), chunk=64)

@@ -71,6 +71,14 @@ int main(void) {
     dbad.chunk = 96;
     EXPECT(entmax_dash_fwd(&dbad, p, p, p, p, p, NULL, NULL, p, p, p, big, NULL) == ENTMAX_ERR_UNSUPPORTED);
     EXPECT(entmax_dash_fwd(&dd, p, p, p, NULL, p, NULL, NULL, p, p, p, big, NULL) == ENTMAX_ERR_NULL);
+    /* the backward: a workspace of at least the fp32 dQ, the per-sub-block dS sums and the
+       routing-logit gradient; every tensor required; the forward's argument errors */
+    const size_t bws = entmax_dash_bwd_workspace_bytes(&dd);
+    EXPECT(bws >= (size_t)8 * 4096 * 128 * 4 + (size_t)8 * 128 * 4096 * 4 + (size_t)8 * 64 * 4096 * 4);
+    EXPECT(entmax_dash_bwd_workspace_bytes(&dbad) == 0);
+    EXPECT(entmax_dash_bwd(&dbad, p, p, p, p, p, p, p, p, p, p, p, p, p, p, p, big, NULL) == ENTMAX_ERR_UNSUPPORTED);
+    EXPECT(entmax_dash_bwd(&dd, p, p, p, p, p, p, NULL, p, p, p, p, p, p, p, p, big, NULL) == ENTMAX_ERR_NULL);
+    EXPECT(entmax_dash_bwd(&dd, p, p, p, p, p, p, p, p, p, p, p, p, p, p, p, bws - 1, NULL) == ENTMAX_ERR_WORKSPACE);
 
     printf("abi_check: ok\n");
     return 0;

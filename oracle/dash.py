@@ -222,7 +222,9 @@ def dash_bwd(q, k, v, ks, dout, alpha: float, gamma: float, sigma: float, C: int
                     hh = g * G + h
                     x = (alpha - 1.0) * zs[h]
                     dlt = np.maximum(x - taus[h], 0.0)
-                    gg = np.where(dlt > 0.0, dlt ** (kappa - 1.0), 0.0)
+                    gg = np.zeros_like(dlt)
+                    pos = dlt > 0.0
+                    gg[pos] = dlt[pos] ** (kappa - 1.0)
                     dw = dwbar / G
                     dz = gg * (dw - (gg @ dw) / gg.sum())
                     dq[bi, hh, i] += gamma * scale * (dz @ kg[:m])

@@ -172,9 +172,9 @@ def dash_bwd(q, k, v, ks, dout, alpha: float, gamma: float, sigma: float, C: int
     given dO (the backward written out in the module docstring). Returns dq [b, hq, n, d],
     dk, dv [b, hkv, n, d] and dks [b, hkv, nc, d].
 
-    With ``rows`` only those query rows are taken, and only their dq is returned
-    ([b, hq, len(rows), d]): a row's dq depends on that row alone, while dk, dv and dks sum
-    over every row."""
+    With ``rows`` only those query rows are taken: dq is returned for them alone
+    ([b, hq, len(rows), d]; a row's dq depends on that row alone), and dk, dv and dks are the
+    sums over those rows only (the whole gradients when dO is zero on every other row)."""
     q, k, v, ks, dout = _f64(q), _f64(k), _f64(v), _f64(ks), _f64(dout)
     b, hq, n, d = q.shape
     hkv, nc = k.shape[1], ks.shape[2]
@@ -230,5 +230,5 @@ def dash_bwd(q, k, v, ks, dout, alpha: float, gamma: float, sigma: float, C: int
                     dq[bi, hh, i] += gamma * scale * (dz @ kg[:m])
                     dks[bi, g, :m] += gamma * scale * np.outer(dz, q[bi, hh, i])
     if rows is not None:
-        return {"dq": dq[:, :, np.asarray(row_list, dtype=np.int64)]}
+        return {"dq": dq[:, :, np.asarray(row_list, dtype=np.int64)], "dk": dk, "dv": dv, "dks": dks}
     return {"dq": dq, "dk": dk, "dv": dv, "dks": dks}

@@ -207,32 +207,40 @@ def test_dash_bwd_fp32():
 
 
 def test_dash_bwd_fullsize_sampled_rows():
-    """The 16K benchmark shape in the benchmark's launch configuration: dq of 24 sampled rows
-    against the oracle (a row's dq depends on that row alone), and two sums that hold at any
-    size: per KV group, sum_j dv_j = sum over the group's rows of dO_i (each row's weights sum
-    to 1), and sum_j dk_j = 0 (each row's dS sums to 0)."""
+    """The 16K benchmark shape in the benchmark's launch configuration, dO kept on 24 sampled
+    rows (every head) and zero elsewhere, so that the oracle needs those rows only: dq of the
+    sampled rows, and the whole dk, dv and dk_summary (sums over the sampled rows) against
+    the oracle; dq of every other row is 0. Then, with the full dO, two sums that hold at any
+    size: per KV group, sum_j dv_j = sum over the group's rows of dO_i (each row's weights
+    sum to 1), and sum_j dk_j = 0 (each row's dS sums to 0)."""
     import bench
     w = bench.dash_workload()
     C, gamma, sigma = bench.DASH_CHUNK, bench.DASH_GAMMA, bench.DASH_SIGMA
     print(f"[case] dash bwd full size {w.name}", flush=True)
     inp = synth.make_inputs(w, need_grad_inputs=True)
     ks = synth.chunk_summaries(w, C)
-    g = _run_bwd(inp["q"], inp["k"], inp["v"], ks, inp["do"], C, w.alpha, gamma, sigma)
     n = w.seqlen
     rows = np.unique(np.concatenate([np.arange(0, 2), np.arange(63, 66), np.arange(n - 3, n),
                                      np.linspace(100, n - 100, 16).astype(np.int64)]))
-    ref = odash.dash_bwd(to64(inp["q"]), to64(inp["k"]), to64(inp["v"]), to64(ks), to64(inp["do"]), w.alpha,
+    keep = torch.zeros(n, dtype=inp["do"].dtype)
+    keep[torch.from_numpy(rows)] = 1
+    do_r = (inp["do"] * keep[None, None, :, None]).contiguous()
+    g = _run_bwd(inp["q"], inp["k"], inp["v"], ks, do_r, C, w.alpha, gamma, sigma)
+    ref = odash.dash_bwd(to64(inp["q"]), to64(inp["k"]), to64(inp["v"]), to64(ks), to64(do_r), w.alpha,
                          gamma, sigma, C, rows=rows)
-    err = rel_fro(g["dq"][:, :, rows], ref["dq"])
-    print(f"  dq (sampled rows): rel err {err:.2e}", flush=True)
-    assert err < 2e-2
+    for name, got, want in (("dq (sampled rows)", g["dq"][:, :, rows], ref["dq"]), ("dk", g["dk"], ref["dk"]),
+                            ("dv", g["dv"], ref["dv"]), ("dk_summary", g["dk_summary"], ref["dks"])):
+        err = rel_fro(got, want)
+        print(f"  {name}: rel err {err:.2e}", flush=True)
+        assert err < 2e-2, name
+    others = np.setdiff1d(np.arange(n), rows)
+    assert not np.any(g["dq"][:, :, others])
+    g = _run_bwd(inp["q"], inp["k"], inp["v"], ks, inp["do"], C, w.alpha, gamma, sigma)
     b, hq, hkv = w.batch, w.heads_q, w.heads_kv
     G = hq // hkv
     do64 = to64(inp["do"]).reshape(b, hkv, G, n, -1).sum(axis=(2, 3))
-    dv_sum = g["dv"].sum(axis=2)
-    assert rel_fro(dv_sum, do64) < 2e-2
-    dk_sum = g["dk"].sum(axis=2)
-    assert np.linalg.norm(dk_sum) < 2e-2 * np.linalg.norm(g["dk"])
+    assert rel_fro(g["dv"].sum(axis=2), do64) < 2e-2
+    assert np.linalg.norm(g["dk"].sum(axis=2)) < 2e-2 * np.linalg.norm(g["dk"])
 
 
 def test_dash_bwd_alpha3_conditioned_rows():

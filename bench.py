@@ -671,7 +671,7 @@ def sweep(args, lce, dev):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 (multi-GPU "
+        print(json.dumps({"error": "the benchmark runs on one GPU; --gpus must be 1 (multi-GPU "
                                    "sharding is described, not implemented)"}))
         sys.exit(2)
     import torch

@@ -298,10 +298,13 @@ __global__ __launch_bounds__(DEC_TAU_THREADS) void k_dec_tau(DecParams p) {
 }
 
 // ------------------------------------------------------------------------- 4. output
-template <typename T, int D, int MODE>
+// GM: a compile-time bound on the group's query heads (4 or 16), so the per-head loops carry
+// no branch; heads past G have tau = +inf, hence p = 0, and are not stored.
+template <typename T, int D, int MODE, int GM>
 __global__ __launch_bounds__(DEC_THREADS) void k_dec_out(DecParams p) {
   constexpr int E = D / 64;                       // head-dimension elements per lane
-  __shared__ float red[4][16][D];
+  __shared__ float red[4][GM][D];
+  __shared__ __align__(16) float pl[4][64][GM];   // a wave's weights of its 64 keys, key-major
   const int lane = lane_id();
   const int w = uniform_i32(wave_id());
   const int split = blockIdx.x, bk = blockIdx.y;
@@ -311,34 +314,43 @@ __global__ __launch_bounds__(DEC_THREADS) void k_dec_out(DecParams p) {
   const int k0 = split * p.osplit, k1 = min(k0 + p.osplit, L);
   if (k0 >= L) return;                            // whole work group: slice past the cache
   const size_t row0 = (size_t)bi * p.hq + (size_t)kvh * G;
-  float taug[16], oacc[16][E];
+  float taug[GM], oacc[GM][E];
 #pragma unroll
-  for (int g = 0; g < 16; ++g) {
+  for (int g = 0; g < GM; ++g) {
     taug[g] = g < G ? p.tau[row0 + g] : INFINITY;
 #pragma unroll
     for (int e = 0; e < E; ++e) oacc[g][e] = 0.0f;
   }
   const T* V = reinterpret_cast<const T*>(p.v) + ((size_t)bi * p.hkv + kvh) * n * D;
-  // scores of the G rows at key key0 + lane (-inf past the slice)
-  const auto load_x = [&](int key0, float (&xv)[16]) {
+  // scores of the G rows at key key0 + lane (-inf past the slice and for heads past G)
+  const auto load_x = [&](int key0, float (&xv)[GM]) {
     const int j = key0 + lane;
 #pragma unroll
-    for (int g = 0; g < 16; ++g) xv[g] = (g < G && j < k1) ? p.xs[(row0 + g) * p.ldx + j] : -INFINITY;
+    for (int g = 0; g < GM; ++g) xv[g] = (g < G && j < k1) ? p.xs[(row0 + g) * p.ldx + j] : -INFINITY;
   };
-  float xc[16];
+  float xc[GM];
   load_x(k0 + 64 * w, xc);
   for (int key0 = k0 + 64 * w; key0 < k1; key0 += 256) {
-    float xn[16];                                 // the next group's scores, in flight
+    float xn[GM];                                 // the next group's scores, in flight
     load_x(key0 + 256, xn);
-    float pr[16];
+    float pr[GM];
     bool any = false;
 #pragma unroll
-    for (int g = 0; g < 16; ++g) {
+    for (int g = 0; g < GM; ++g) {
       const float d = xc[g] - taug[g];
       pr[g] = d > 0.0f ? Weight<MODE>::p(d, p.kappa) : 0.0f;
       any = any || d > 0.0f;
     }
     uint64_t bits = ballot(any);
+    if (bits) {
+      // the key's weights for every lane: one broadcast LDS read per key (the same address
+      // in every lane)
+#pragma unroll
+      for (int g4 = 0; g4 < GM / 4; ++g4)
+        *reinterpret_cast<f32x4*>(&pl[w][lane][4 * g4]) =
+            f32x4{pr[4 * g4], pr[4 * g4 + 1], pr[4 * g4 + 2], pr[4 * g4 + 3]};
+      __builtin_amdgcn_wave_barrier();            // (a wave's LDS accesses complete in order)
+    }
     while (bits) {                                // keys with a non-zero weight, in order,
       int jj[8];                                  // eight V rows in flight at a time
 #pragma unroll
@@ -346,35 +358,37 @@ __global__ __launch_bounds__(DEC_THREADS) void k_dec_out(DecParams p) {
         jj[u] = bits ? __builtin_ctzll(bits) : -1;
         bits &= bits - 1;
       }
+      // every slot loads (the group's first key stands in for an empty one, with weight 0),
+      // so the loads go out back to back and no branch separates them
       float vv[8][E];
+      f32x4 pw[8][GM / 4];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        if (jj[u] >= 0) {
-          const T* vr = V + (size_t)(key0 + jj[u]) * D + lane * E;
+        const int ju = max(jj[u], 0);
+        const T* vr = V + (size_t)(key0 + ju) * D + lane * E;
 #pragma unroll
-          for (int e = 0; e < E; ++e) vv[u][e] = (float)vr[e];
-        }
+        for (int e = 0; e < E; ++e) vv[u][e] = (float)vr[e];
+#pragma unroll
+        for (int g4 = 0; g4 < GM / 4; ++g4) pw[u][g4] = *reinterpret_cast<const f32x4*>(&pl[w][ju][4 * g4]);
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        if (jj[u] < 0) break;
+        const float live = jj[u] >= 0 ? 1.0f : 0.0f;
 #pragma unroll
-        for (int g = 0; g < 16; ++g) {
-          if (g < G) {
-            const float pg = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pr[g]), jj[u]));
+        for (int g = 0; g < GM; ++g) {
+          const float pg = live * pw[u][g >> 2][g & 3];
 #pragma unroll
-            for (int e = 0; e < E; ++e) oacc[g][e] = fmaf(pg, vv[u][e], oacc[g][e]);
-          }
+          for (int e = 0; e < E; ++e) oacc[g][e] = fmaf(pg, vv[u][e], oacc[g][e]);
         }
       }
     }
 #pragma unroll
-    for (int g = 0; g < 16; ++g) xc[g] = xn[g];
+    for (int g = 0; g < GM; ++g) xc[g] = xn[g];
   }
 
   // sum the 4 waves' partials in wave order
 #pragma unroll
-  for (int g = 0; g < 16; ++g)
+  for (int g = 0; g < GM; ++g)
 #pragma unroll
     for (int e = 0; e < E; ++e)
       if (g < G) red[w][g][lane * E + e] = oacc[g][e];
@@ -430,8 +444,11 @@ static hipError_t launch_decode_t(const DecParams& p, int mode, hipStream_t s) {
   hipLaunchKernelGGL(tau_fn, dim3(p.b * p.hq), dim3(DEC_TAU_THREADS), 0, s, p);
   prof_end(s);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  void (*out_fn)(DecParams) =
-      mode == 1 ? k_dec_out<T, D, 1> : mode == 2 ? k_dec_out<T, D, 2> : k_dec_out<T, D, 0>;
+  void (*out_fn)(DecParams);
+  if (p.G <= 4)
+    out_fn = mode == 1 ? k_dec_out<T, D, 1, 4> : mode == 2 ? k_dec_out<T, D, 2, 4> : k_dec_out<T, D, 0, 4>;
+  else
+    out_fn = mode == 1 ? k_dec_out<T, D, 1, 16> : mode == 2 ? k_dec_out<T, D, 2, 16> : k_dec_out<T, D, 0, 16>;
   prof_begin("dec_out", s);
   hipLaunchKernelGGL(out_fn, go, dim3(DEC_THREADS), 0, s, p);
   prof_end(s);

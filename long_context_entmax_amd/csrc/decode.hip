@@ -50,6 +50,52 @@ __device__ __forceinline__ V block_reduce(V v, V* lds, Op op) {
   return r;
 }
 
+// A pass's row totals in one reduction: sums of F0, F1, Fh and of F2 (general alpha) or the
+// support size, and the minimum of the smallest positive gap's bits. Each value takes the
+// same shuffle and LDS order as block_reduce would give it alone (so the same bits), with
+// one pair of barriers for all of them.
+template <int NT, int MODE>
+__device__ __forceinline__ void block_reduce_pass(float (&f)[4], int& ci, uint32_t& mb, float (*lf)[NT / 64],
+                                                  int* li, uint32_t* lu) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (MODE == 0 || k != 2) f[k] += __shfl_xor(f[k], o);
+    if constexpr (MODE != 0) {
+      ci += __shfl_xor(ci, o);
+      mb = min(mb, (uint32_t)__shfl_xor((int)mb, o));
+    }
+  }
+  const int w = threadIdx.x >> 6;
+  __syncthreads();   // the arrays may still be read from the previous reduction
+  if ((threadIdx.x & 63) == 0) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) lf[k][w] = f[k];
+    li[w] = ci;
+    lu[w] = mb;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    float r = lf[k][0];
+#pragma unroll
+    for (int u = 1; u < NT / 64; ++u) r += lf[k][u];
+    f[k] = r;
+  }
+  if constexpr (MODE != 0) {
+    int r = li[0];
+    uint32_t m = lu[0];
+#pragma unroll
+    for (int u = 1; u < NT / 64; ++u) {
+      r += li[u];
+      m = min(m, lu[u]);
+    }
+    ci = r;
+    mb = m;
+  }
+}
+
 // the row's x_max from the per-slice maxima of the score kernel
 template <int NT>
 __device__ __forceinline__ float row_max(const DecParams& p, size_t row, int nsp, float* lds) {
@@ -170,15 +216,15 @@ __global__ __launch_bounds__(DEC_THREADS) void k_dec_hist(DecParams p) {
 
 // ------------------------------------------------------------------------- 3. threshold
 // candidates per thread kept in LDS for the refinement passes after the first
-constexpr int DEC_CAND = 8;
+constexpr int DEC_CAND = 32;
 
 // (query row): tau_h from the summed slice histograms (or the plain bracket from x_max),
 // then the solver passes. The first pass scans the stored row and keeps, per thread, the
-// scores that can still count: every later evaluation point lies at or above the bracket's
-// lower end, at least x_max - 1 - 1/(16B) in either start (tau_h >= T/B - 1, Proposition 1),
-// so only scores with x B > T - B - 1/16 matter. Each thread keeps its own (a fixed subset in
-// a fixed order, so the sums stay deterministic); if any thread has more than DEC_CAND,
-// every pass rescans the row.
+// scores that can still count: the safeguarded bracket only narrows, so every later
+// evaluation point lies at or above its starting lower end (just below tau_h, or x_max - 1
+// from the plain bracket), and a score at or below that end adds nothing to any sum. Each
+// thread keeps its own (a fixed subset in a fixed order, so the sums stay deterministic);
+// if any thread has more than DEC_CAND, every pass rescans the row.
 template <int MODE>
 __global__ __launch_bounds__(DEC_TAU_THREADS) void k_dec_tau(DecParams p) {
   constexpr int NT = DEC_TAU_THREADS;
@@ -186,6 +232,7 @@ __global__ __launch_bounds__(DEC_TAU_THREADS) void k_dec_tau(DecParams p) {
   __shared__ int cnt_tot[16];
   __shared__ int part_cnt[NT / 16][16];
   __shared__ float rf[NT / 64];
+  __shared__ float rf4[4][NT / 64];
   __shared__ int ri[NT / 64];
   __shared__ uint32_t ru[NT / 64];
   const int t = threadIdx.x;
@@ -252,7 +299,7 @@ __global__ __launch_bounds__(DEC_TAU_THREADS) void k_dec_tau(DecParams p) {
     st = RowState::from_max(m, (float)L, alpha);
   }
 
-  const float cand_lo = (float)(T - B) - 0.25f;   // x B above this can still count
+  const float cand_lo = st.lo;                     // a score above the bracket's lower end can still count
   const bool secant = alpha > 2.0f;
   int ncand = 0, over = 1;
   for (int npass = 0; npass < p.max_iters && !st.done;) {
@@ -263,7 +310,7 @@ __global__ __launch_bounds__(DEC_TAU_THREADS) void k_dec_tau(DecParams p) {
     if (first) {
       scan([&](float x) {
         s.add<MODE>(x - tau0, thi, secant, kappa);
-        if (x * (float)B > cand_lo) {
+        if (x > cand_lo) {
           if (ncand < DEC_CAND) cand[ncand][t] = x;
           ++ncand;
         }
@@ -275,19 +322,21 @@ __global__ __launch_bounds__(DEC_TAU_THREADS) void k_dec_tau(DecParams p) {
       for (int k = 0; k < ncand; ++k) s.add<MODE>(cand[k][t] - tau0, thi, false, kappa);
     }
     ++npass;
-    const auto fsum = [](float a, float b) { return a + b; };
+    float fr[4] = {s.F0, s.F1, s.F2, s.Fh};
+    int cr = s.cnt;
+    uint32_t mr = s.mrelb;
+    block_reduce_pass<NT, MODE>(fr, cr, mr, rf4, ri, ru);
     float tot[5];
-    tot[0] = block_reduce<NT>(s.F0, rf, fsum);
-    tot[1] = block_reduce<NT>(s.F1, rf, fsum);
+    tot[0] = fr[0];
+    tot[1] = fr[1];
     if constexpr (MODE == 0) {
-      tot[2] = block_reduce<NT>(s.F2, rf, fsum);
+      tot[2] = fr[2];
       tot[4] = INFINITY;
     } else {
-      tot[2] = (float)block_reduce<NT>(s.cnt, ri, [](int a, int b) { return a + b; });
-      const uint32_t mb = block_reduce<NT>(s.mrelb, ru, [](uint32_t a, uint32_t b) { return min(a, b); });
-      tot[4] = mb < 0x7F800000u ? __uint_as_float(mb) : INFINITY;
+      tot[2] = (float)cr;
+      tot[4] = mr < 0x7F800000u ? __uint_as_float(mr) : INFINITY;
     }
-    tot[3] = secant && first ? block_reduce<NT>(s.Fh, rf, fsum) : 0.0f;
+    tot[3] = secant && first ? fr[3] : 0.0f;
     st.update<MODE>(tot, npass, first, thi, kappa, alpha, p.tol);
   }
   if (t == 0) {

@@ -18,7 +18,7 @@
 //   4. k_dec_out     (p.osplit-key slice, KV head): p for the G rows, V rows read only for
 //      keys where some row has p > 0, partial o per slice (smaller slices than the score
 //      kernel: this pass waits on V loads key by key, so it wants more waves in flight).
-//   5. k_dec_reduce  (query row): o = sum of the slice partials in slice order.
+//   5. k_dec_reduce  (query row): o = sum of the slice partials in a fixed order.
 #include "common.hpp"
 #include "kernels.hpp"
 #include "solver.hpp"
@@ -207,9 +207,21 @@ __global__ __launch_bounds__(DEC_THREADS) void k_dec_hist(DecParams p) {
     if (y >= 0.0f && y < (float)B) cnt_lds[(int)y][t] += 1u;
   }
   __syncthreads();
+  // bin t / 16 over columns 16 (t % 16) .. + 15, then the 16 partial sums of each bin
+  // (integer counts: exact in any order)
+  __shared__ uint32_t part[16][16];
+  {
+    const int b = t >> 4, q = t & 15;
+    uint32_t sum = 0;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) sum += cnt_lds[b][16 * q + u];
+    part[b][q] = sum;
+  }
+  __syncthreads();
   if (t < B) {
     uint32_t sum = 0;
-    for (int u = 0; u < DEC_THREADS; ++u) sum += cnt_lds[t][u];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) sum += part[t][q];
     p.hcnt[(row * p.nsplit + split) * 16 + t] = (int)sum;
   }
 }
@@ -451,14 +463,15 @@ __global__ __launch_bounds__(DEC_THREADS) void k_dec_out(DecParams p) {
 
 // ------------------------------------------------------------------------- 5. reduce
 // thread (part, d) sums slices part, part + P, ... of element d; the P part sums are then
-// added in part order (P = 256 / D)
-__global__ __launch_bounds__(DEC_THREADS) void k_dec_reduce(DecParams p, int D) {
-  __shared__ float part_sum[DEC_THREADS];
+// added in part order (P = 1024 / D: a row's few hundred slices in a few dependent loads)
+constexpr int DEC_RED_THREADS = 1024;
+__global__ __launch_bounds__(DEC_RED_THREADS) void k_dec_reduce(DecParams p, int D) {
+  __shared__ float part_sum[DEC_RED_THREADS];
   const size_t row = blockIdx.x;
   const int bi = (int)(row / p.hq);
   const int nsp = (dec_len(p, bi) + p.osplit - 1) / p.osplit;
   const size_t rows = (size_t)p.b * p.hq;
-  const int P = DEC_THREADS / D;
+  const int P = DEC_RED_THREADS / D;
   const int d = threadIdx.x % D, part = threadIdx.x / D;
   float s = 0.0f;
 #pragma unroll 8
@@ -503,7 +516,7 @@ static hipError_t launch_decode_t(const DecParams& p, int mode, hipStream_t s) {
   prof_end(s);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   prof_begin("dec_reduce", s);
-  hipLaunchKernelGGL(k_dec_reduce, dim3(p.b * p.hq), dim3(DEC_THREADS), 0, s, p, D);
+  hipLaunchKernelGGL(k_dec_reduce, dim3(p.b * p.hq), dim3(DEC_RED_THREADS), 0, s, p, D);
   prof_end(s);
   return hipGetLastError();
 }

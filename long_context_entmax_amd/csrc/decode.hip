@@ -34,74 +34,93 @@ __device__ __forceinline__ int dec_len(const DecParams& p, int bi) {
   return p.lengths ? min(max(p.lengths[bi], 1), p.n) : p.n;
 }
 
-// work-group sum / min / max over NT threads in a fixed order; every thread gets the result
-// (lds holds one value per wave)
-template <int NT, typename V, typename Op>
-__device__ __forceinline__ V block_reduce(V v, V* lds, Op op) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = op(v, __shfl_xor(v, o));
-  const int w = threadIdx.x >> 6;
-  __syncthreads();   // lds may still be read from the previous reduction
-  if ((threadIdx.x & 63) == 0) lds[w] = v;
+// Wave-wide reductions in a fixed order with DPP row operations (no LDS traffic): butterflies
+// within each 16-lane row, then the row totals carried to lane 63; the result is uniform.
+#define DEC_DPP(v, ctrl, rmask) __builtin_amdgcn_update_dpp((v), (v), ctrl, rmask, 0xF, false)
+template <typename Op>
+__device__ __forceinline__ int wave_red(int v, Op op) {
+  v = op(v, DEC_DPP(v, 0xB1, 0xF));    // quad_perm [1,0,3,2]
+  v = op(v, DEC_DPP(v, 0x4E, 0xF));    // quad_perm [2,3,0,1]
+  v = op(v, DEC_DPP(v, 0x141, 0xF));   // row_half_mirror
+  v = op(v, DEC_DPP(v, 0x140, 0xF));   // row_mirror
+  v = op(v, DEC_DPP(v, 0x142, 0xA));   // row_bcast15 into rows 1 and 3
+  v = op(v, DEC_DPP(v, 0x143, 0xC));   // row_bcast31 into rows 2 and 3
+  return __builtin_amdgcn_readlane(v, 63);
+}
+__device__ __forceinline__ float wave_fsum(float v) {
+  return __int_as_float(wave_red(__float_as_int(v), [](int a, int b) {
+    return __float_as_int(__int_as_float(a) + __int_as_float(b)); }));
+}
+__device__ __forceinline__ float wave_fmax(float v) {
+  return __int_as_float(wave_red(__float_as_int(v), [](int a, int b) {
+    return __float_as_int(fmaxf(__int_as_float(a), __int_as_float(b))); }));
+}
+__device__ __forceinline__ int wave_isum(int v) {
+  return wave_red(v, [](int a, int b) { return a + b; });
+}
+__device__ __forceinline__ uint32_t wave_umin(uint32_t v) {
+  return (uint32_t)wave_red((int)v, [](int a, int b) { return (int)min((uint32_t)a, (uint32_t)b); });
+}
+
+// Work-group reductions: each wave's total through LDS, then the NT/64 totals reduced by the
+// same DPP steps in lanes 0..15 of every wave (fixed order, the same bits in every wave). The
+// LDS slots alternate between two halves (par), so one barrier per reduction suffices: no
+// wave can start the reduction after next before every wave has read this one.
+constexpr int DEC_RED_SLOTS = 6;
+struct DecRed {
+  uint32_t v[2][DEC_RED_SLOTS][16];
+};
+template <int NT>
+__device__ __forceinline__ uint32_t wg_gather(const DecRed* r, int par, int k, uint32_t ident) {
+  const int lane = threadIdx.x & 63;
+  return lane < NT / 64 ? r->v[par][k][lane] : ident;
+}
+
+template <int NT>
+__device__ __forceinline__ float block_max(float v, DecRed* r, int& par) {
+  v = wave_fmax(v);
+  if ((threadIdx.x & 63) == 0) r->v[par][0][threadIdx.x >> 6] = __float_as_uint(v);
   __syncthreads();
-  V r = lds[0];
-#pragma unroll
-  for (int u = 1; u < NT / 64; ++u) r = op(r, lds[u]);
-  return r;
+  v = wave_fmax(__uint_as_float(wg_gather<NT>(r, par, 0, __float_as_uint(-INFINITY))));
+  par ^= 1;
+  return v;
 }
 
 // A pass's row totals in one reduction: sums of F0, F1, Fh and of F2 (general alpha) or the
-// support size, and the minimum of the smallest positive gap's bits. Each value takes the
-// same shuffle and LDS order as block_reduce would give it alone (so the same bits), with
-// one pair of barriers for all of them.
+// support size, and the minimum of the smallest positive gap's bits.
 template <int NT, int MODE>
-__device__ __forceinline__ void block_reduce_pass(float (&f)[4], int& ci, uint32_t& mb, float (*lf)[NT / 64],
-                                                  int* li, uint32_t* lu) {
+__device__ __forceinline__ void block_reduce_pass(float (&f)[4], int& ci, uint32_t& mb, DecRed* r, int& par) {
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-      if (MODE == 0 || k != 2) f[k] += __shfl_xor(f[k], o);
-    if constexpr (MODE != 0) {
-      ci += __shfl_xor(ci, o);
-      mb = min(mb, (uint32_t)__shfl_xor((int)mb, o));
-    }
+  for (int k = 0; k < 4; ++k)
+    if (MODE == 0 || k != 2) f[k] = wave_fsum(f[k]);
+  if constexpr (MODE != 0) {
+    ci = wave_isum(ci);
+    mb = wave_umin(mb);
   }
-  const int w = threadIdx.x >> 6;
-  __syncthreads();   // the arrays may still be read from the previous reduction
   if ((threadIdx.x & 63) == 0) {
+    const int w = threadIdx.x >> 6;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) lf[k][w] = f[k];
-    li[w] = ci;
-    lu[w] = mb;
+    for (int k = 0; k < 4; ++k) r->v[par][k][w] = __float_as_uint(f[k]);
+    r->v[par][4][w] = (uint32_t)ci;
+    r->v[par][5][w] = mb;
   }
   __syncthreads();
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    float r = lf[k][0];
-#pragma unroll
-    for (int u = 1; u < NT / 64; ++u) r += lf[k][u];
-    f[k] = r;
-  }
+  for (int k = 0; k < 4; ++k)
+    if (MODE == 0 || k != 2) f[k] = wave_fsum(__uint_as_float(wg_gather<NT>(r, par, k, 0u)));
   if constexpr (MODE != 0) {
-    int r = li[0];
-    uint32_t m = lu[0];
-#pragma unroll
-    for (int u = 1; u < NT / 64; ++u) {
-      r += li[u];
-      m = min(m, lu[u]);
-    }
-    ci = r;
-    mb = m;
+    ci = wave_isum((int)wg_gather<NT>(r, par, 4, 0u));
+    mb = wave_umin(wg_gather<NT>(r, par, 5, 0xFFFFFFFFu));
   }
+  par ^= 1;
 }
 
 // the row's x_max from the per-slice maxima of the score kernel
 template <int NT>
-__device__ __forceinline__ float row_max(const DecParams& p, size_t row, int nsp, float* lds) {
+__device__ __forceinline__ float row_max(const DecParams& p, size_t row, int nsp, DecRed* r, int& par) {
   float m = -INFINITY;
   for (int s = threadIdx.x; s < nsp; s += NT) m = fmaxf(m, p.smax[row * p.nsplit + s]);
-  return block_reduce<NT>(m, lds, [](float a, float b) { return fmaxf(a, b); });
+  return block_max<NT>(m, r, par);
 }
 
 }  // namespace
@@ -180,7 +199,8 @@ __global__ __launch_bounds__(DEC_THREADS) void k_dec_scores(DecParams p) {
 // summed per slice so the row's histogram is their exact sum.
 __global__ __launch_bounds__(DEC_THREADS) void k_dec_hist(DecParams p) {
   __shared__ uint32_t cnt_lds[16][DEC_THREADS];   // a private column of counts per thread
-  __shared__ float rf[4];
+  __shared__ DecRed red;
+  int par = 0;
   const int t = threadIdx.x;
   const int split = blockIdx.x;
   const size_t row = blockIdx.y;
@@ -189,7 +209,7 @@ __global__ __launch_bounds__(DEC_THREADS) void k_dec_hist(DecParams p) {
   const int k0 = split * p.split, k1 = min(k0 + p.split, L);
   if (k0 >= L) return;                            // whole work group: slice past the cache
   const int B = p.B;
-  const float m = row_max<DEC_THREADS>(p, row, (L + p.split - 1) / p.split, rf);
+  const float m = row_max<DEC_THREADS>(p, row, (L + p.split - 1) / p.split, &red, par);
   const float base = (float)(cvt_floor(m * (float)B) - B + 1);   // x*B is exact: B = 2^k
 #pragma unroll
   for (int k = 0; k < 16; ++k) cnt_lds[k][t] = 0u;
@@ -243,10 +263,8 @@ __global__ __launch_bounds__(DEC_TAU_THREADS) void k_dec_tau(DecParams p) {
   __shared__ float cand[DEC_CAND][NT];            // a private column of candidate scores
   __shared__ int cnt_tot[16];
   __shared__ int part_cnt[NT / 16][16];
-  __shared__ float rf[NT / 64];
-  __shared__ float rf4[4][NT / 64];
-  __shared__ int ri[NT / 64];
-  __shared__ uint32_t ru[NT / 64];
+  __shared__ DecRed red;
+  int par = 0;
   const int t = threadIdx.x;
   const size_t row = blockIdx.x;
   const int bi = (int)(row / p.hq);
@@ -278,7 +296,7 @@ __global__ __launch_bounds__(DEC_TAU_THREADS) void k_dec_tau(DecParams p) {
     }
   };
 
-  const float m = row_max<NT>(p, row, nsp, rf);
+  const float m = row_max<NT>(p, row, nsp, &red, par);
   const float kappa = p.kappa, alpha = p.alpha;
   const int T = cvt_floor(m * (float)B);          // x*B is exact: B is a power of two
   int cnt[16];
@@ -327,7 +345,7 @@ __global__ __launch_bounds__(DEC_TAU_THREADS) void k_dec_tau(DecParams p) {
           ++ncand;
         }
       });
-      over = block_reduce<NT>(ncand > DEC_CAND ? 1 : 0, ri, [](int a, int b) { return a | b; });
+      over = block_max<NT>(ncand > DEC_CAND ? 1.0f : 0.0f, &red, par) > 0.0f;
     } else if (over) {
       scan([&](float x) { s.add<MODE>(x - tau0, thi, false, kappa); });
     } else {
@@ -337,7 +355,7 @@ __global__ __launch_bounds__(DEC_TAU_THREADS) void k_dec_tau(DecParams p) {
     float fr[4] = {s.F0, s.F1, s.F2, s.Fh};
     int cr = s.cnt;
     uint32_t mr = s.mrelb;
-    block_reduce_pass<NT, MODE>(fr, cr, mr, rf4, ri, ru);
+    block_reduce_pass<NT, MODE>(fr, cr, mr, &red, par);
     float tot[5];
     tot[0] = fr[0];
     tot[1] = fr[1];

@@ -191,6 +191,11 @@ __global__ __launch_bounds__(DEC_THREADS) void k_dec_scores(DecParams p) {
   const int t = threadIdx.x;
   if (t < G)
     p.smax[(row0 + t) * p.nsplit + split] = fmaxf(fmaxf(red[0][t], red[1][t]), fmaxf(red[2][t], red[3][t]));
+  // the slice holding the last key pads each row to a multiple of 4 scores with -inf, so the
+  // threshold kernel reads whole float4 groups without masking
+  const int pad = ((L + 3) & ~3) - L;
+  if (k0 <= L - 1 && L - 1 < k0 + p.split && t < G * pad)
+    p.xs[(row0 + t / pad) * p.ldx + L + t % pad] = -INFINITY;
 }
 
 // ------------------------------------------------------------------------- 2. histogram
@@ -260,7 +265,7 @@ constexpr int DEC_CAND = 32;
 template <int MODE>
 __global__ __launch_bounds__(DEC_TAU_THREADS) void k_dec_tau(DecParams p) {
   constexpr int NT = DEC_TAU_THREADS;
-  __shared__ float cand[DEC_CAND][NT];            // a private column of candidate scores
+  __shared__ float cand[DEC_CAND + 1][NT];        // a private column of candidate scores (+ a spill row)
   __shared__ int cnt_tot[16];
   __shared__ int part_cnt[NT / 16][16];
   __shared__ DecRed red;
@@ -277,7 +282,7 @@ __global__ __launch_bounds__(DEC_TAU_THREADS) void k_dec_tau(DecParams p) {
   const auto scan = [&](auto&& f) {
     constexpr int U = 8;
     const float4* x4 = reinterpret_cast<const float4*>(xr);
-    const int n4 = (L + 3) >> 2;
+    const int n4 = (L + 3) >> 2;                  // the score kernel pads the last group with -inf
     for (int i = t; i < n4; i += U * NT) {
       float4 v[U];
 #pragma unroll
@@ -287,11 +292,10 @@ __global__ __launch_bounds__(DEC_TAU_THREADS) void k_dec_tau(DecParams p) {
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int j0 = 4 * (i + u * NT);
-        f(j0 < L ? v[u].x : -INFINITY);
-        f(j0 + 1 < L ? v[u].y : -INFINITY);
-        f(j0 + 2 < L ? v[u].z : -INFINITY);
-        f(j0 + 3 < L ? v[u].w : -INFINITY);
+        f(v[u].x);
+        f(v[u].y);
+        f(v[u].z);
+        f(v[u].w);
       }
     }
   };
@@ -340,10 +344,10 @@ __global__ __launch_bounds__(DEC_TAU_THREADS) void k_dec_tau(DecParams p) {
     if (first) {
       scan([&](float x) {
         s.add<MODE>(x - tau0, thi, secant, kappa);
-        if (x > cand_lo) {
-          if (ncand < DEC_CAND) cand[ncand][t] = x;
-          ++ncand;
-        }
+        // every score goes to the slot after the last candidate (row DEC_CAND once full) and
+        // stays there only if it is one: no branch per score
+        cand[min(ncand, DEC_CAND)][t] = x;
+        ncand += x > cand_lo ? 1 : 0;
       });
       over = block_max<NT>(ncand > DEC_CAND ? 1.0f : 0.0f, &red, par) > 0.0f;
     } else if (over) {

@@ -214,10 +214,7 @@ __global__ __launch_bounds__(DEC_THREADS) void k_dec_hist(DecParams p) {
   const int k0 = split * p.split, k1 = min(k0 + p.split, L);
   if (k0 >= L) return;                            // whole work group: slice past the cache
   const int B = p.B;
-  const float m = row_max<DEC_THREADS>(p, row, (L + p.split - 1) / p.split, &red, par);
-  const float base = (float)(cvt_floor(m * (float)B) - B + 1);   // x*B is exact: B = 2^k
-#pragma unroll
-  for (int k = 0; k < 16; ++k) cnt_lds[k][t] = 0u;
+  // the slice's scores are loaded first, so their latency overlaps the row maximum's
   const float* xr = p.xs + row * p.ldx;
   constexpr int U = DEC_SPLIT_MAX / DEC_THREADS;
   float xv[U];
@@ -226,6 +223,10 @@ __global__ __launch_bounds__(DEC_THREADS) void k_dec_hist(DecParams p) {
     const int j = k0 + t + u * DEC_THREADS;
     xv[u] = j < k1 ? xr[j] : -INFINITY;
   }
+#pragma unroll
+  for (int k = 0; k < 16; ++k) cnt_lds[k][t] = 0u;
+  const float m = row_max<DEC_THREADS>(p, row, (L + p.split - 1) / p.split, &red, par);
+  const float base = (float)(cvt_floor(m * (float)B) - B + 1);   // x*B is exact: B = 2^k
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const float y = fmaf(xv[u], (float)B, -base);
@@ -277,12 +278,11 @@ __global__ __launch_bounds__(DEC_TAU_THREADS) void k_dec_tau(DecParams p) {
   const int B = p.B;
   const int nsp = (L + p.split - 1) / p.split;
   const float* xr = p.xs + row * p.ldx;
-  // every stored score of the row, four at a time with 32 in flight per thread (the row
-  // stride is a multiple of 4 floats; the tail past L reads as -inf)
+  constexpr int U = 8;
+  const float4* x4 = reinterpret_cast<const float4*>(xr);
+  const int n4 = (L + 3) >> 2;                    // the score kernel pads the last group with -inf
+  // every stored score of the row, four at a time with 32 in flight per thread
   const auto scan = [&](auto&& f) {
-    constexpr int U = 8;
-    const float4* x4 = reinterpret_cast<const float4*>(xr);
-    const int n4 = (L + 3) >> 2;                  // the score kernel pads the last group with -inf
     for (int i = t; i < n4; i += U * NT) {
       float4 v[U];
 #pragma unroll
@@ -300,6 +300,14 @@ __global__ __launch_bounds__(DEC_TAU_THREADS) void k_dec_tau(DecParams p) {
     }
   };
 
+  // thread (part, bin) sums slices part, part + NT/16, ...; the row maximum's barrier
+  // publishes the sums
+  if (p.tau_init == 0) {
+    const int bin = t & 15, part = t >> 4;
+    int sum = 0;
+    for (int s = part; s < nsp; s += NT / 16) sum += p.hcnt[(row * p.nsplit + s) * 16 + bin];
+    part_cnt[part][bin] = sum;
+  }
   const float m = row_max<NT>(p, row, nsp, &red, par);
   const float kappa = p.kappa, alpha = p.alpha;
   const int T = cvt_floor(m * (float)B);          // x*B is exact: B is a power of two
@@ -307,14 +315,7 @@ __global__ __launch_bounds__(DEC_TAU_THREADS) void k_dec_tau(DecParams p) {
   float tau_h;
   RowState st;
   if (p.tau_init == 0) {
-    // thread (part, bin) sums slices part, part + NT/16, ...; then the parts in order
-    {
-      const int bin = t & 15, part = t >> 4;
-      int sum = 0;
-      for (int s = part; s < nsp; s += NT / 16) sum += p.hcnt[(row * p.nsplit + s) * 16 + bin];
-      part_cnt[part][bin] = sum;
-    }
-    __syncthreads();
+    // then the parts in order
     if (t < B) {
       int sum = 0;
       for (int u = 0; u < NT / 16; ++u) sum += part_cnt[u][t];

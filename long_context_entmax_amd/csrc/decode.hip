@@ -126,9 +126,13 @@ __device__ __forceinline__ float row_max(const DecParams& p, size_t row, int nsp
 }  // namespace
 
 // ------------------------------------------------------------------------- 1. scores
-template <typename T, int D>
+// GM: a compile-time bound on the group's query heads (4 or 16). Query row g sits in
+// accumulator register r with acc_row(r, h) = g, so rows below GM use registers r < RM only.
+template <typename T, int D, int GM>
 __global__ __launch_bounds__(DEC_THREADS) void k_dec_scores(DecParams p) {
   constexpr int DS = D / 16;
+  constexpr int RM = GM <= 4 ? 4 : 8;
+  static_assert(acc_row(RM - 1, 1) >= GM - 1, "registers r < RM hold every row below GM");
   __shared__ float red[4][16];
   const int lane = lane_id(), c = lane & 31, h = lane >> 5;
   const int w = uniform_i32(wave_id());
@@ -148,28 +152,35 @@ __global__ __launch_bounds__(DEC_THREADS) void k_dec_scores(DecParams p) {
     else zero_frag(qf[s]);
   }
   // accumulator register r holds query row acc_row(r, h) of key c: its bias slope
-  float cmr[16], mx[16];
+  float cmr[RM], mx[RM];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
+  for (int r = 0; r < RM; ++r) {
     const int g = acc_row(r, h);
     cmr[r] = (p.slopes && g < G) ? p.slopes[kvh * G + g] * p.am1 : 0.0f;
     mx[r] = -INFINITY;
   }
   const T* K = reinterpret_cast<const T*>(p.k) + ((size_t)bi * p.hkv + kvh) * n * D;
-  for (int key0 = k0 + 32 * w; key0 < k1; key0 += 128) {
+  // K fragments of the 32 keys from key0 (zero past the slice: nothing is read there)
+  const auto load_tile = [&](int key0, Frag<T> (&f)[DS]) {
     const int j = key0 + c;
-    Frag<T> kf[DS];
 #pragma unroll
     for (int s = 0; s < DS; ++s) {
-      if (j < k1) load_frag(kf[s], K + (size_t)j * D + 16 * s + 8 * h);
-      else zero_frag(kf[s]);
+      if (j < k1) load_frag(f[s], K + (size_t)j * D + 16 * s + 8 * h);
+      else zero_frag(f[s]);
     }
+  };
+  Frag<T> kf[DS];
+  load_tile(k0 + 32 * w, kf);
+  for (int key0 = k0 + 32 * w; key0 < k1; key0 += 128) {
+    Frag<T> kn[DS];
+    load_tile(key0 + 128, kn);                    // the wave's next tile, in flight meanwhile
+    const int j = key0 + c;
     f32x16 acc = f32x16{};
 #pragma unroll
     for (int s = 0; s < DS; ++s) mma16(acc, qf[s], kf[s]);   // S[query row][key c]
     const float dist = (float)(L - 1 - j);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
+    for (int r = 0; r < RM; ++r) {
       const int g = acc_row(r, h);
       if (g < G && j < k1) {
         const float x = fmaf(p.cx, acc[r], -cmr[r] * dist);
@@ -177,10 +188,12 @@ __global__ __launch_bounds__(DEC_THREADS) void k_dec_scores(DecParams p) {
         mx[r] = fmaxf(mx[r], x);
       }
     }
+#pragma unroll
+    for (int s = 0; s < DS; ++s) kf[s] = kn[s];
   }
   // max over the 32 keys of each half-wave, then over the 4 waves
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
+  for (int r = 0; r < RM; ++r) {
     float m = mx[r];
 #pragma unroll
     for (int o = 1; o < 32; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
@@ -514,7 +527,8 @@ static hipError_t launch_decode_t(const DecParams& p, int mode, hipStream_t s) {
   const dim3 gs(p.nsplit, p.b * p.hkv);
   const dim3 go(p.nsplit_o, p.b * p.hkv);
   prof_begin("dec_scores", s);
-  hipLaunchKernelGGL((k_dec_scores<T, D>), gs, dim3(DEC_THREADS), 0, s, p);
+  if (p.G <= 4) hipLaunchKernelGGL((k_dec_scores<T, D, 4>), gs, dim3(DEC_THREADS), 0, s, p);
+  else hipLaunchKernelGGL((k_dec_scores<T, D, 16>), gs, dim3(DEC_THREADS), 0, s, p);
   prof_end(s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -11,13 +11,14 @@
 // of bf16 K per key and KV head, so the histogram and every refinement pass read the fp32
 // scores instead of recomputing them from K.
 //   1. k_dec_scores  (slice, KV head): x for the G query heads of the KV head on MFMA (the
-//      G query rows padded to 32), stored, plus the slice's max per row.
+//      G query rows padded to 32), stored (each row padded with -inf to whole float4
+//      groups), plus the slice's max per row.
 //   2. k_dec_hist    (slice, query row): the slice's counts on the row's anchored B-bin grid.
 //   3. k_dec_tau     (query row): the summed histogram, tau_h, then the solver passes over
 //      the stored scores (work-group reductions in a fixed order: deterministic).
 //   4. k_dec_out     (p.osplit-key slice, KV head): p for the G rows, V rows read only for
 //      keys where some row has p > 0, partial o per slice (smaller slices than the score
-//      kernel: this pass waits on V loads key by key, so it wants more waves in flight).
+//      kernel: more waves keep V loads in flight).
 //   5. k_dec_reduce  (query row): o = sum of the slice partials in a fixed order.
 #include "common.hpp"
 #include "kernels.hpp"

@@ -193,18 +193,22 @@ __global__ __launch_bounds__((64 * hist_waves<T, D>()), (hist_occ<T, D>())) void
   const __amdgpu_buffer_rsrc_t krs = buffer_rsrc(Kf, (uint32_t)((size_t)n * D * sizeof(T)));
   Ops::load_k_buf(kf, krs, 2 * last_pair, lane);
   Ops::load_k_buf(kf2, krs, min(2 * last_pair + 1, kb_end - 1), lane);
-  // x * B - base of sub-block kbb (with the head's position bias)
+  // x * B - base of sub-block kbb (with the head's position bias). Keys after the query
+  // under the causal mask are -inf, and so are keys past the last one without it (the
+  // second tile of the last pair when the sub-block count is odd): the score products mask
+  // keys above the row limit ml on the tiles that reach past it.
+  const int ml = p.causal ? qrow : n - 1, ml0 = p.causal ? row0 : n - 1;
   auto tile = [&](const Frag<T> (&kc)[DS], int kbb) -> f32x16 {
     if constexpr (BIAS) {
       const float d0 = (float)(qrow - 32 * kbb - 4 * h);
       if constexpr (QS)
-        return Ops::scores(kc, qf, kbb, row0, qrow, h, p.causal, bias16<-1>(-(float)base, cmB, d0, p.causal));
-      f32x16 a = Ops::scores(kc, qf, kbb, row0, qrow, h, p.causal);
+        return Ops::scores(kc, qf, kbb, ml0, ml, h, true, bias16<-1>(-(float)base, cmB, d0, p.causal));
+      f32x16 a = Ops::scores(kc, qf, kbb, ml0, ml, h, true);
       scale_add_bias16<-1>(a, cB, -(float)base, cmB, d0, p.causal);
       return a;
     } else {
-      if constexpr (QS) return Ops::scores(kc, qf, kbb, row0, qrow, h, p.causal, negb);
-      f32x16 a = Ops::scores(kc, qf, kbb, row0, qrow, h, p.causal);
+      if constexpr (QS) return Ops::scores(kc, qf, kbb, ml0, ml, h, true, negb);
+      f32x16 a = Ops::scores(kc, qf, kbb, ml0, ml, h, true);
       const float nb = -(float)base;
 #pragma unroll
       for (int r = 0; r < 16; ++r) a[r] = fmaf(cB, a[r], nb);
@@ -215,17 +219,11 @@ __global__ __launch_bounds__((64 * hist_waves<T, D>()), (hist_occ<T, D>())) void
   CountRegs cad{l4, l4, l4, l4};              // LDS addresses of counts: cell in the second byte
   const uint32_t one = 1u;
   for (int kb = 2 * last_pair; kb >= 0; kb -= 2) {
-    // The second tile of the last pair may lie past the last valid sub-block: under the causal
-    // mask every one of its keys comes after the wave's rows (so it is -inf already), and its
-    // loads past the end of K read zeros through the buffer bounds.
-    const bool two = kb + 1 < kb_end;
+    // The second tile of the last pair may lie past the last valid sub-block: every one of its
+    // keys is then masked to -inf, and its loads past the end of K read zeros through the
+    // buffer bounds.
     f32x16 acc0 = tile(kf, kb);
     f32x16 acc1 = tile(kf2, kb + 1);
-    if (!two) {
-      asm volatile("" ::: "memory");   // a branch taken once per wave at most: keep it one
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc1[r] = -INFINITY;
-    }
     // the next pair (every pair below the last one is whole); loaded on every step, the
     // first pair again at the end, so the waits at the next step count a fixed number of loads
     Ops::load_k_buf(kf, krs, max(kb - 2, 0), lane);
@@ -235,7 +233,8 @@ __global__ __launch_bounds__((64 * hist_waves<T, D>()), (hist_occ<T, D>())) void
     const float t1 = max16(acc1) + bF;
     const float nmB = fmaxf(mB, fmaxf(t0, t1));
     const bool fin = nmB > -INFINITY;
-    const int Tn = fin ? cvt_floor(nmB) : Tt;
+    const int Tfl = cvt_floor(nmB);
+    const int Tn = fin ? Tfl : Tt;
     // a tile is active for a lane when one of its scores lies at most two bins below
     // the lane's window
     const float thrB = (float)(Tn - B - 1);
@@ -246,14 +245,8 @@ __global__ __launch_bounds__((64 * hist_waves<T, D>()), (hist_occ<T, D>())) void
       // largest x*B of the 32 rows in each sub-block, kept by lane (sub-block mod 32)
       float cm0, cm1;
       pair_max_dpp(t0, t1, cm0, cm1);
-      if (b0) {
-        write_lane(dreg, cm0, kb & 31);
-        ++n_cand;
-      }
-      if (b1) {
-        write_lane(dreg, cm1, (kb + 1) & 31);
-        ++n_cand;
-      }
+      if (b0) write_lane(dreg, cm0, kb & 31);
+      if (b1) write_lane(dreg, cm1, (kb + 1) & 31);
       const bool act = act0 || act1;
       // slide a window up: cell k takes cell k + shift, the top cells start empty
       const bool slide = act && (!have || Tn > Tt) && p.tau_init == 0;
@@ -290,6 +283,7 @@ __global__ __launch_bounds__((64 * hist_waves<T, D>()), (hist_occ<T, D>())) void
       float wm, wm_hi;
       pair_max_dpp(dreg, dreg, wm, wm_hi);   // lanes 32..63 of dreg stay -inf
       if (lane == 0) wx_out[kb >> 5] = wm;
+      if (p.stats) n_cand += __builtin_popcountll(ballot(dreg != -INFINITY));   // a candidate's maximum is finite
       if (lane < 32 && kb + lane < kb_end) dmx[kb + lane] = dreg;
       dreg = -INFINITY;
     }

@@ -285,7 +285,7 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void k_bwd_dkv(BwdParams p)
 }
 
 template <typename T, int D, int MODE, bool BIAS>
-__global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void k_bwd_dq(BwdParams p) {
+__global__ __launch_bounds__(256, (D == 64 ? ((sizeof(T) == 2 && !BIAS && (MODE == 1 || MODE == 2)) ? 3 : 2) : 1)) void k_bwd_dq(BwdParams p) {
   constexpr int DS = D / 16, DC = D / 32;
   extern __shared__ float red[];
   int unit, rank;

@@ -79,13 +79,17 @@ def parse():
     return ap.parse_args()
 
 
+# the sources of the prefill forward/backward kernels and their launches (the decode and
+# DashAttention kernels live in files of their own and do not enter the prefill counters)
+PREFILL_SOURCES = ("api.hip", "bwd.hip", "common.hpp", "fwd.hip", "kernels.hpp", "prep.hip", "solver.hpp")
+
+
 def src_digest() -> str:
     h = hashlib.sha256()
     d = os.path.join(ROOT, "long_context_entmax_amd", "csrc")
-    for f in sorted(os.listdir(d)):
-        if f.endswith((".hip", ".hpp")):
-            with open(os.path.join(d, f), "rb") as fh:
-                h.update(f.encode() + fh.read())
+    for f in PREFILL_SOURCES:
+        with open(os.path.join(d, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
 
 

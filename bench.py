@@ -658,6 +658,11 @@ def sweep(args, lce, dev):
     print(json.dumps({"sweep_fits": fits}), flush=True)
     if args.sweep_md:
         with open(args.sweep_md, "w") as fh:
+            fh.write("# Block-sparsity sweep: alpha-entmax attention fwd+bwd on one MI355X\n\n"
+                     "Command: `python3 bench.py --sweep --sweep-md <this file>` (bench.py at the "
+                     f"repository root; kernel sources digest `{src_digest()}`). Step times in ms "
+                     "(forward + backward, inputs resident in HBM); the dense ablation multiplies "
+                     "every causally valid block; a and b fit ms = a + b * nnzb per sweep.\n\n")
             fh.write("| point | configured | sparsity | nnzb | ms/step | eff. TFLOP/s | alg. TFLOP/s | "
                      "sparse-block MFMA util | dense ablation ms | skip speed-up | passes |\n")
             fh.write("|---|---|---|---|---|---|---|---|---|---|---|\n")

@@ -195,20 +195,24 @@ __global__ __launch_bounds__((64 * hist_waves<T, D>()), (hist_occ<T, D>())) void
   Ops::load_k_buf(kf2, krs, min(2 * last_pair + 1, kb_end - 1), lane);
   // x * B - base of sub-block kbb (with the head's position bias). Keys after the query
   // under the causal mask are -inf, and so are keys past the last one without it (the
-  // second tile of the last pair when the sub-block count is odd): the score products mask
-  // keys above the row limit ml on the tiles that reach past it.
-  const int ml = p.causal ? qrow : n - 1, ml0 = p.causal ? row0 : n - 1;
+  // second tile of the last pair when the sub-block count is odd). At head_dim 64 the score
+  // products mask keys above the row limit ml on the tiles that reach past it (one rule, no
+  // branch per step); at head_dim 128 the limit's register would spill, so they mask the
+  // causal keys and the loop sets a tile past the last key to -inf.
+  constexpr bool UM = D == 64;
+  const int ml = UM ? (p.causal ? qrow : n - 1) : qrow, ml0 = UM ? (p.causal ? row0 : n - 1) : row0;
+  const bool mc = UM || p.causal;
   auto tile = [&](const Frag<T> (&kc)[DS], int kbb) -> f32x16 {
     if constexpr (BIAS) {
       const float d0 = (float)(qrow - 32 * kbb - 4 * h);
       if constexpr (QS)
-        return Ops::scores(kc, qf, kbb, ml0, ml, h, true, bias16<-1>(-(float)base, cmB, d0, p.causal));
-      f32x16 a = Ops::scores(kc, qf, kbb, ml0, ml, h, true);
+        return Ops::scores(kc, qf, kbb, ml0, ml, h, mc, bias16<-1>(-(float)base, cmB, d0, p.causal));
+      f32x16 a = Ops::scores(kc, qf, kbb, ml0, ml, h, mc);
       scale_add_bias16<-1>(a, cB, -(float)base, cmB, d0, p.causal);
       return a;
     } else {
-      if constexpr (QS) return Ops::scores(kc, qf, kbb, ml0, ml, h, true, negb);
-      f32x16 a = Ops::scores(kc, qf, kbb, ml0, ml, h, true);
+      if constexpr (QS) return Ops::scores(kc, qf, kbb, ml0, ml, h, mc, negb);
+      f32x16 a = Ops::scores(kc, qf, kbb, ml0, ml, h, mc);
       const float nb = -(float)base;
 #pragma unroll
       for (int r = 0; r < 16; ++r) a[r] = fmaf(cB, a[r], nb);
@@ -224,6 +228,13 @@ __global__ __launch_bounds__((64 * hist_waves<T, D>()), (hist_occ<T, D>())) void
     // buffer bounds.
     f32x16 acc0 = tile(kf, kb);
     f32x16 acc1 = tile(kf2, kb + 1);
+    if constexpr (!UM) {
+      if (kb + 1 >= kb_end) {
+        asm volatile("" ::: "memory");   // a branch taken once per wave at most: keep it one
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc1[r] = -INFINITY;
+      }
+    }
     // the next pair (every pair below the last one is whole); loaded on every step, the
     // first pair again at the end, so the waits at the next step count a fixed number of loads
     Ops::load_k_buf(kf, krs, max(kb - 2, 0), lane);

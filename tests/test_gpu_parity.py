@@ -73,6 +73,11 @@ CASES = [
     (1, 16, 1, 192, 64, 1.5, True, 64, 64, 16, 1.0),
     (2, 16, 1, 128, 128, 2.0, True, 32, 128, 8, 1.0),
     (1, 3, 1, 160, 64, 1.5, True, 32, 32, 16, 1.0),    # GQA 3: no power of two
+    # no causal mask and an odd number of 32-key sub-blocks: the histogram pass's last pair
+    # has a tile past the last key (masked by the score products at head_dim 64, set to -inf
+    # by a branch at head_dim 128)
+    (1, 2, 2, 96, 64, 2.0, False, 32, 32, 16, 1.0),
+    (1, 2, 1, 96, 128, 1.5, False, 32, 32, 8, 1.0),
 ]
 
 
